@@ -1,0 +1,234 @@
+"""CPU oracle for one Multi-head Latent Attention (MLA) decode step.
+
+TEST INFRASTRUCTURE.  Only the tests, the smoke check and the CPU-baseline leg
+of the benchmark may import this module.  It is never on the product path and
+shares no code with the HIP library.
+
+Everything is plain NumPy in float64, written to be checked by eye against
+the pages, with no blocking, fusion or reordering beyond what the definitions
+state.  Sources (page title, section):
+
+  [P1] "DeepSeek MLA, Built From the Paper" (yiqiao-yin deepspeed-course):
+       §1 the cache-size formulas, §2 decoupled RoPE, §3 matrix absorption.
+  [P2] "MLA from scratch" (shivam2003.com, DeepSeek 3.2): the MLAAttention
+       module (forward pass), KV cache management during decode, absorbing
+       projections, shape tracing.
+  [P3] "Build a DeepSeek Model (From Scratch)", chapter 3 (Manning preview):
+       figure captions on RoPE pairs and on the decoupled content/position
+       paths whose scores add.
+  [P5] "Multi-head latent attention" (octlm blog): the latent plus shared
+       RoPE key cache, and the `_project_mla` concatenated [content | rope]
+       query/key layout.
+
+Readings where the pages are silent or garbled (each also listed in the
+design notes):
+
+  * RoPE pairs adjacent dimensions (2i, 2i+1) and rotates pair i by the
+    angle pos * base**(-2i/d) (the RoFormer form the pages cite; [P3] keeps
+    only the captions "dimensions are paired" and "rotated by a
+    position-dependent angle", its formula figure is missing).
+  * The new token is appended to the cache first and then attended to, so a
+    sequence with L cached tokens attends over L + 1 rows; the query sits at
+    position L ([P2] concatenates the new latent before attention and its
+    shape trace grows the cache by one row per step).
+  * The cached RoPE keys are stored already rotated by their own positions
+    ([P5]: the shared key is rotated normally and cached).
+  * One RoPE key per token, shared by all heads ([P1] §2, [P5]).
+  * Softmax scale 1/sqrt(d_head + d_rope) is passed in by the caller.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+# ---------------------------------------------------------------------------
+# Cache-size formulas  [P1] §1 (values cached per token per layer)
+# ---------------------------------------------------------------------------
+
+
+def cache_values_mha(n_heads: int, d_head: int) -> int:
+    """Keys and values for every head: 2 * n_heads * d_head."""
+    return 2 * n_heads * d_head
+
+
+def cache_values_gqa(n_kv_heads: int, d_head: int) -> int:
+    """Keys and values for the shared kv heads only: 2 * n_kv_heads * d_head."""
+    return 2 * n_kv_heads * d_head
+
+
+def cache_values_mla(r_kv: int, d_rope: int) -> int:
+    """One latent of rank r_kv plus one shared RoPE key: r_kv + d_rope."""
+    return r_kv + d_rope
+
+
+# ---------------------------------------------------------------------------
+# Rotary position embedding  [P3] RoPE figure captions, [P5] shared RoPE key
+# ---------------------------------------------------------------------------
+
+
+def rope_frequencies(d: int, base: float) -> np.ndarray:
+    """theta_i = base**(-2i/d) for pair i = 0 .. d/2-1."""
+    if d % 2:
+        raise ValueError("RoPE width must be even")
+    i = np.arange(d // 2, dtype=np.float64)
+    return base ** (-2.0 * i / d)
+
+
+def rope(x: np.ndarray, pos: float, base: float) -> np.ndarray:
+    """Rotate each adjacent pair (x[2i], x[2i+1]) of the last axis by pos*theta_i."""
+    x = np.asarray(x, dtype=np.float64)
+    ang = float(pos) * rope_frequencies(x.shape[-1], base)
+    c, s = np.cos(ang), np.sin(ang)
+    xe, xo = x[..., 0::2], x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = xe * c - xo * s
+    out[..., 1::2] = xe * s + xo * c
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Softmax  [P2] MLAAttention forward (scaled scores, softmax over keys)
+# ---------------------------------------------------------------------------
+
+
+def softmax(s: np.ndarray) -> np.ndarray:
+    """Softmax over the last axis: subtract the max, exponentiate, normalise."""
+    s = np.asarray(s, dtype=np.float64)
+    m = np.max(s, axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def logsumexp(s: np.ndarray) -> np.ndarray:
+    s = np.asarray(s, dtype=np.float64)
+    m = np.max(s, axis=-1)
+    return m + np.log(np.sum(np.exp(s - m[..., None]), axis=-1))
+
+
+# ---------------------------------------------------------------------------
+# The append  [P2] KV cache management (new latent written at the current
+# position, cache grows by one row), [P5] the cache holds c_t and the rotated
+# shared key
+# ---------------------------------------------------------------------------
+
+
+def appended_row(c_new: np.ndarray, k_rope_new: np.ndarray, pos: int, base: float) -> np.ndarray:
+    """The cache row the step writes: [c_kv_new | RoPE(k_rope_new, pos)]."""
+    return np.concatenate([np.asarray(c_new, np.float64), rope(k_rope_new, pos, base)])
+
+
+def append(c_cached: np.ndarray, krot_cached: np.ndarray, c_new: np.ndarray,
+           k_rope_new: np.ndarray, base: float):
+    """Cache after the step: L cached rows plus the new one at position L."""
+    L = c_cached.shape[0]
+    row = appended_row(c_new, k_rope_new, L, base)
+    r = c_cached.shape[1]
+    C = np.vstack([np.asarray(c_cached, np.float64), row[None, :r]])
+    KR = np.vstack([np.asarray(krot_cached, np.float64), row[None, r:]])
+    return C, KR
+
+
+# ---------------------------------------------------------------------------
+# Naive decode: rebuild K and V for every cached token and head
+# [P2] MLAAttention forward (up-project all cached latents with W_UK, W_UV,
+# then standard attention), [P5] `_project_mla` (query and key are
+# [content | rope], the rope key broadcast to every head), [P3] the score is
+# the content score plus the position score
+# ---------------------------------------------------------------------------
+
+
+def naive_decode_seq(q_nope, q_rope, c_cached, krot_cached, c_new, k_rope_new,
+                     w_uk, w_uv, scale, base):
+    """Output [H, d_v] of one sequence's decode step, naive form.
+
+    q_nope [H, d_head], q_rope [H, d_rope] (unrotated), c_cached [L, r],
+    krot_cached [L, d_rope] (rotated), c_new [r], k_rope_new [d_rope]
+    (unrotated), w_uk [H, d_head, r], w_uv [H, d_v, r].
+    """
+    C, KR = append(c_cached, krot_cached, c_new, k_rope_new, base)
+    pos = c_cached.shape[0]
+    H = q_nope.shape[0]
+    out = np.empty((H, w_uv.shape[1]))
+    for h in range(H):
+        k_content = C @ w_uk[h].T                          # [L+1, d_head]
+        v = C @ w_uv[h].T                                  # [L+1, d_v]
+        k = np.concatenate([k_content, KR], axis=1)        # [L+1, d_head + d_rope]
+        q = np.concatenate([q_nope[h], rope(q_rope[h], pos, base)])
+        p = softmax(scale * (k @ q))
+        out[h] = p @ v
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Absorbed decode: attend in the latent space
+# [P1] §3 (q^T (W_UK c) = (W_UK^T q)^T c, keys never rebuilt), [P2] absorbing
+# projections (weights applied to the latents directly, W_UV after the
+# weighted sum), [P1] §2 / [P5] (the RoPE part scores against the shared key)
+# ---------------------------------------------------------------------------
+
+
+def absorbed_decode_seq(q_nope, q_rope, c_cached, krot_cached, c_new, k_rope_new,
+                        w_uk, w_uv, scale, base):
+    """Absorbed form of the same step; returns every intermediate.
+
+    Returns a dict with
+      q_lat   [H, r + d_rope]  [W_UK^T q_nope | RoPE(q_rope, L)]
+      new_row [r + d_rope]     the appended cache row
+      scores  [H, L+1]         scaled logits
+      lse     [H]              natural-log sum of exp(scores)
+      o_lat   [H, r]           softmax-weighted sum of latents
+      out     [H, d_v]         W_UV o_lat
+    """
+    C, KR = append(c_cached, krot_cached, c_new, k_rope_new, base)
+    pos = c_cached.shape[0]
+    H, r = q_nope.shape[0], C.shape[1]
+    q_tilde = np.stack([w_uk[h].T @ q_nope[h] for h in range(H)])        # [H, r]
+    q_r = np.stack([rope(q_rope[h], pos, base) for h in range(H)])       # [H, d_rope]
+    scores = scale * (q_tilde @ C.T + q_r @ KR.T)                        # [H, L+1]
+    p = softmax(scores)
+    o_lat = p @ C                                                        # [H, r]
+    out = np.stack([w_uv[h] @ o_lat[h] for h in range(H)])               # [H, d_v]
+    return dict(q_lat=np.concatenate([q_tilde, q_r], axis=1),
+                new_row=np.concatenate([C[-1], KR[-1]]),
+                scores=scores, lse=logsumexp(scores), o_lat=o_lat, out=out)
+
+
+# ---------------------------------------------------------------------------
+# Batched step over packed sequences
+# ---------------------------------------------------------------------------
+
+
+def decode_batch(seqs, q_nope, q_rope, c_new, k_rope_new, w_uk, w_uv, scale, base,
+                 form: str = "absorbed", batch_ids=None):
+    """Run the step for every sequence (or the listed ``batch_ids``).
+
+    ``seqs[b]`` is ``(c_cached [L_b, r], krot_cached [L_b, d_rope])`` in fp64.
+    For form="absorbed" returns a dict of stacked intermediates; for
+    form="naive" returns out [nb, H, d_v].
+    """
+    ids = range(len(seqs)) if batch_ids is None else batch_ids
+    if form == "naive":
+        return np.stack([naive_decode_seq(q_nope[b], q_rope[b], seqs[b][0], seqs[b][1],
+                                          c_new[b], k_rope_new[b], w_uk, w_uv, scale, base)
+                         for b in ids])
+    res = [absorbed_decode_seq(q_nope[b], q_rope[b], seqs[b][0], seqs[b][1],
+                               c_new[b], k_rope_new[b], w_uk, w_uv, scale, base) for b in ids]
+    keys = ("q_lat", "new_row", "lse", "o_lat", "out")
+    return {k: np.stack([x[k] for x in res]) for k in keys}
+
+
+def rope_through_projection_scores(q, w_uk, c, q_pos, k_pos, base):
+    """Coupled-RoPE scores, and the single-query absorption one might attempt.
+
+    With RoPE applied to the reconstructed content key, the score against
+    token t is (R_qpos q) . (R_t W_UK c_t).  Folding W_UK into one query
+    vector q~ = W_UK^T R_qpos q and scoring q~ . c_t drops R_t: the rotation
+    sits between q and W_UK and differs per token ([P1] §2, [P3] summary).
+    Returns (true scores [L], single-q~ scores [L]).
+    """
+    qr = rope(q, q_pos, base)
+    true = np.array([qr @ rope(w_uk @ c[t], k_pos[t], base) for t in range(c.shape[0])])
+    q_tilde = w_uk.T @ qr
+    folded = c @ q_tilde
+    return true, folded

@@ -1,0 +1,381 @@
+"""Pins for the CPU oracle (no GPU).
+
+Every check here ties the oracle to something other than itself: numbers the
+pages print (fixtures under tests/golden/), an exact identity, a textbook or
+library routine, a closed form, or brute force on tiny inputs.  Several
+checks plant a mistake in the oracle and require the same comparison to
+catch it, so that a loose tolerance cannot make a pin vacuous.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from head_latent_attention_12_amd import synthetic as syn
+from oracle import mla_oracle as orc
+from tests._util import normwise_rel, oracle_args, oracle_step
+
+IDENTITY_TOL = 1e-12
+
+
+def _load(golden_dir, name):
+    with open(os.path.join(golden_dir, name)) as f:
+        return json.load(f)
+
+
+def _rand_case(rng, H, dh, dv, r, dr, L):
+    return dict(
+        q_nope=rng.standard_normal((H, dh)), q_rope=rng.standard_normal((H, dr)),
+        c_cached=rng.standard_normal((L, r)), krot_cached=rng.standard_normal((L, dr)),
+        c_new=rng.standard_normal(r), k_rope_new=rng.standard_normal(dr),
+        w_uk=rng.standard_normal((H, dh, r)) / math.sqrt(r),
+        w_uv=rng.standard_normal((H, dv, r)) / math.sqrt(r),
+        scale=1.0 / math.sqrt(dh + dr), base=10000.0)
+
+
+# ---------------------------------------------------------------------------
+# Cache-size formulas against the pages' printed values
+# ---------------------------------------------------------------------------
+
+
+def test_cache_table_by_heads(golden_dir):
+    g = _load(golden_dir, "cache_table_by_heads.json")
+    for row in g["rows"]:
+        d_head = row["mha"] // (2 * row["n_heads"])
+        assert d_head == 64
+        assert orc.cache_values_mha(row["n_heads"], 64) == row["mha"]
+        assert orc.cache_values_gqa(row["kv_heads"], 64) == row["gqa"]
+        assert row["n_heads"] == 4 * row["kv_heads"]
+        # the MLA column does not move with the head count
+        assert orc.cache_values_mla(64, 16) == row["mla"]
+
+
+def test_cache_training_table(golden_dir):
+    g = _load(golden_dir, "cache_training_table.json")
+    d_head = g["hidden"] // g["n_heads"]
+    assert orc.cache_values_mha(g["n_heads"], d_head) == g["cache_per_token"]["mha"]
+    assert orc.cache_values_gqa(g["gqa_kv_heads"], d_head) == g["cache_per_token"]["gqa"]
+    assert g["cache_per_token"]["mha"] / g["cache_per_token"]["mla"] == pytest.approx(g["mha_over_mla"])
+
+
+def test_deepseek_v2_cache(golden_dir):
+    g = _load(golden_dir, "deepseek_v2_cache.json")
+    mla = orc.cache_values_mla(g["r_kv"], g["d_rope"])
+    mha = orc.cache_values_mha(g["n_heads"], g["d_head"])
+    assert mla == g["mla_values"] == 576
+    assert mha == g["mha_values"]
+    assert round(mha / mla) == g["saving_rounded"]
+    assert mha / g["r_kv"] == g["latent_only_ratio"]
+    assert round(100.0 * (1.0 - mla / mha), 1) == g["reduction_percent_1dp"]
+
+
+def test_gqa2_vs_mla_width256(golden_dir):
+    g = _load(golden_dir, "gqa2_vs_mla_width256.json")
+    d_head = g["width"] // g["n_heads"]
+    assert d_head == g["d_head"]
+    gqa2 = orc.cache_values_gqa(g["gqa_kv_heads"], d_head)
+    mla = orc.cache_values_mla(g["mla_rank"], g["mla_rope"])
+    assert gqa2 == g["gqa2_values"] and mla == g["mla_values"]
+    assert gqa2 / mla == pytest.approx(g["ratio"])
+    crossover = next(r for r in range(1, 1024) if orc.cache_values_mla(r, g["mla_rope"]) >= gqa2)
+    assert crossover == g["crossover_rank"]
+    assert orc.cache_values_mha(1, g["wide_model"]["width"]) == g["wide_model"]["mha_values"]
+
+
+def test_workload_shapes_match_pages(golden_dir):
+    g = _load(golden_dir, "hyperparameters.json")
+    s, d = g["small"], g["deepseek_v2"]
+    w = syn.WORKLOADS["small"]
+    assert (w["H"], w["d_head"], w["r"], w["d_rope"]) == (s["n_heads"], s["d_head"], s["d_c_kv"], s["d_head_rope"])
+    assert s["n_heads"] * s["d_head"] == s["d_kv_full"]
+    for name in ("dsv2", "dsv2_ragged", "dsv2_long"):
+        w = syn.WORKLOADS[name]
+        assert (w["H"], w["d_head"], w["d_v"], w["r"], w["d_rope"]) == (
+            d["n_heads"], d["d_head"], d["d_head"], d["d_c_kv"], d["d_head_rope"])
+        assert orc.cache_values_mla(w["r"], w["d_rope"]) == 576
+
+
+def test_append_grows_cache_by_one_row(golden_dir):
+    g = _load(golden_dir, "shape_trace.json")
+    rng = np.random.default_rng(5)
+    B, L, r, dr = g["B"], g["prefill_len"], g["d_c"], 8
+    caches = [(rng.standard_normal((L, r)), rng.standard_normal((L, dr))) for _ in range(B)]
+    shape = [B] + list(caches[0][0].shape)
+    assert shape == g["cache_after_prefill"]
+    grown = [orc.append(c, k, rng.standard_normal(r), rng.standard_normal(dr), 10000.0) for c, k in caches]
+    assert [B] + list(grown[0][0].shape) == g["cache_after_one_decode_step"]
+    for (c0, k0), (c1, k1) in zip(caches, grown):
+        np.testing.assert_array_equal(c1[:L], c0)      # old rows untouched
+        np.testing.assert_array_equal(k1[:L], k0)
+        assert k1.shape == (L + 1, dr)
+
+
+def test_appended_row_layout():
+    rng = np.random.default_rng(6)
+    c, k = rng.standard_normal(8), rng.standard_normal(4)
+    row = orc.appended_row(c, k, 0, 10000.0)          # position 0: no rotation
+    np.testing.assert_array_equal(row, np.concatenate([c, k]))
+
+
+# ---------------------------------------------------------------------------
+# RoPE
+# ---------------------------------------------------------------------------
+
+
+def test_rope_position_zero_is_identity():
+    x = np.random.default_rng(7).standard_normal((3, 16))
+    np.testing.assert_array_equal(orc.rope(x, 0, 10000.0), x)
+
+
+def test_rope_worked_values():
+    # pair 0 always has frequency 1: position 1 turns it by exactly 1 radian
+    x0, x1 = 0.3, -1.7
+    got = orc.rope(np.array([x0, x1]), 1, 10000.0)
+    assert got[0] == pytest.approx(x0 * math.cos(1.0) - x1 * math.sin(1.0), abs=1e-15)
+    assert got[1] == pytest.approx(x0 * math.sin(1.0) + x1 * math.cos(1.0), abs=1e-15)
+    # d=4, base 10000: pair 1 has frequency 10000**(-1/2) = 0.01, so position
+    # 100 turns dims (2, 3) by 1 radian and dims (0, 1) by 100 radians
+    e = np.eye(4)
+    r2 = orc.rope(e[2], 100, 10000.0)
+    np.testing.assert_allclose(r2, [0, 0, math.cos(1.0), math.sin(1.0)], atol=1e-13)
+    r0 = orc.rope(e[0], 100, 10000.0)
+    np.testing.assert_allclose(r0, [math.cos(100.0), math.sin(100.0), 0, 0], atol=1e-13)
+    # adjacent pairing: dim 0 never leaks into the upper half (it would if the
+    # halves (i, i + d/2) were paired instead)
+    r = orc.rope(np.eye(8)[0], 3, 10000.0)
+    assert np.all(r[2:] == 0) and r[1] != 0
+
+
+def test_rope_is_a_rotation():
+    rng = np.random.default_rng(8)
+    for d in (2, 16, 64):
+        x = rng.standard_normal(d)
+        for pos in (1, 17, 4096, 131072):
+            y = orc.rope(x, pos, 10000.0)
+            assert np.linalg.norm(y) == pytest.approx(np.linalg.norm(x), rel=1e-13)
+        # as a matrix: orthogonal with determinant 1
+        R = np.stack([orc.rope(e, 37, 10000.0) for e in np.eye(d)], axis=1)
+        np.testing.assert_allclose(R.T @ R, np.eye(d), atol=1e-13)
+        assert np.linalg.det(R) == pytest.approx(1.0, abs=1e-12)
+
+
+def test_rope_relative_position():
+    rng = np.random.default_rng(9)
+    q, k = rng.standard_normal(32), rng.standard_normal(32)
+    for m, n in ((5, 2), (100, 99), (4096, 17), (3, 3)):
+        lhs = orc.rope(q, m, 10000.0) @ orc.rope(k, n, 10000.0)
+        rhs = orc.rope(q, m - n, 10000.0) @ k
+        assert lhs == pytest.approx(rhs, rel=1e-9, abs=1e-11)
+
+
+def test_rope_does_not_commute_with_projection():
+    """Counterexample: RoPE on the rebuilt content key defeats absorption."""
+    rng = np.random.default_rng(10)
+    dh, r, L = 8, 6, 5
+    w_uk = rng.standard_normal((dh, r))
+    q = rng.standard_normal(dh)
+    c = rng.standard_normal((L, r))
+    true, folded = orc.rope_through_projection_scores(q, w_uk, c, q_pos=L, k_pos=np.arange(L), base=10000.0)
+    assert np.max(np.abs(true - folded)) > 1e-2
+    # without any rotation the same fold is exact
+    true0, folded0 = orc.rope_through_projection_scores(q, w_uk, c, q_pos=0, k_pos=np.zeros(L), base=10000.0)
+    np.testing.assert_allclose(true0, folded0, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Softmax
+# ---------------------------------------------------------------------------
+
+
+def test_softmax_brute_force():
+    rng = np.random.default_rng(11)
+    for n in (1, 2, 7, 50):
+        s = rng.uniform(-29, 29, n)
+        e = [math.exp(v) for v in s]
+        tot = math.fsum(e)
+        np.testing.assert_allclose(orc.softmax(s), [v / tot for v in e], rtol=1e-13, atol=0)
+        assert math.fsum(orc.softmax(s)) == pytest.approx(1.0, abs=1e-14)
+        np.testing.assert_allclose(orc.softmax(s + 123.0), orc.softmax(s), rtol=1e-12)
+        assert orc.logsumexp(s) == pytest.approx(math.log(tot), rel=1e-14)
+
+
+def test_softmax_large_logits_no_overflow():
+    p = orc.softmax(np.array([1000.0, 1000.0, 999.0]))
+    assert np.all(np.isfinite(p)) and p[0] == pytest.approx(p[1])
+
+
+# ---------------------------------------------------------------------------
+# The absorption identity (naive == absorbed) and its sensitivity
+# ---------------------------------------------------------------------------
+
+
+def _both(case):
+    naive = orc.naive_decode_seq(**case)
+    absorbed = orc.absorbed_decode_seq(**case)["out"]
+    return naive, absorbed
+
+
+def test_identity_tiny_shapes():
+    rng = np.random.default_rng(12)
+    for H, r, dr, L, dh, dv in itertools.product((1, 2, 3), (4, 8), (2, 4), (0, 1, 5), (3, 4), (2, 5)):
+        naive, absorbed = _both(_rand_case(rng, H, dh, dv, r, dr, L))
+        assert normwise_rel(absorbed, naive) <= IDENTITY_TOL, (H, r, dr, L, dh, dv)
+
+
+@pytest.mark.parametrize("name,override", [
+    ("tiny", {}),
+    ("small", {}),
+    ("dsv2", dict(lens=[257])),          # one DeepSeek-V2-shaped sequence
+])
+def test_identity_on_workloads(name, override):
+    step = syn.make_inputs(name, **override)
+    ids = [0, step.B - 1] if step.B > 1 else [0]
+    naive = oracle_step(step, form="naive", batch_ids=ids)
+    absorbed = oracle_step(step, batch_ids=ids)["out"]
+    assert normwise_rel(absorbed, naive) <= IDENTITY_TOL
+
+
+def test_identity_detects_planted_mistakes(monkeypatch):
+    """The same comparison must flag a genuine difference (several kinds)."""
+    rng = np.random.default_rng(13)
+    case = _rand_case(rng, 3, 8, 8, 16, 4, 9)
+    naive = orc.naive_decode_seq(**case)
+    # a slightly wrong W_UK entry in the absorbed path only
+    bad = dict(case, w_uk=case["w_uk"].copy())
+    bad["w_uk"][1, 2, 3] += 1e-3
+    assert normwise_rel(orc.absorbed_decode_seq(**bad)["out"], naive) > 1e3 * IDENTITY_TOL
+    # a slightly wrong W_UV entry
+    bad = dict(case, w_uv=case["w_uv"].copy())
+    bad["w_uv"][0, 1, 2] += 1e-3
+    assert normwise_rel(orc.absorbed_decode_seq(**bad)["out"], naive) > 1e3 * IDENTITY_TOL
+    # the RoPE term dropped from the score
+    bad = dict(case, q_rope=np.zeros_like(case["q_rope"]))
+    assert normwise_rel(orc.absorbed_decode_seq(**bad)["out"], naive) > 1e3 * IDENTITY_TOL
+    # the query rotated to the wrong position (off by one)
+    real_rope = orc.rope
+    monkeypatch.setattr(orc, "rope", lambda x, pos, base: real_rope(x, pos + 1, base))
+    shifted = orc.absorbed_decode_seq(**case)["out"]
+    monkeypatch.setattr(orc, "rope", real_rope)
+    assert normwise_rel(shifted, naive) > 1e3 * IDENTITY_TOL
+
+
+def test_naive_matches_library_attention():
+    """Per head, the naive form is plain scaled-dot-product attention."""
+    rng = np.random.default_rng(14)
+    H, dh, dv, r, dr, L = 4, 8, 6, 12, 4, 10
+    case = _rand_case(rng, H, dh, dv, r, dr, L)
+    out = orc.naive_decode_seq(**case)
+    C = np.vstack([case["c_cached"], case["c_new"]])
+    KR = np.vstack([case["krot_cached"], orc.rope(case["k_rope_new"], L, 10000.0)])
+    for h in range(H):
+        K = np.hstack([C @ case["w_uk"][h].T, KR])
+        V = C @ case["w_uv"][h].T
+        q = np.concatenate([case["q_nope"][h], orc.rope(case["q_rope"][h], L, 10000.0)])
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q)[None, None, None, :], torch.from_numpy(K)[None, None],
+            torch.from_numpy(V)[None, None], scale=case["scale"])
+        np.testing.assert_allclose(out[h], ref[0, 0, 0].numpy(), rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# Closed forms
+# ---------------------------------------------------------------------------
+
+
+def test_single_row_gives_projected_new_latent():
+    rng = np.random.default_rng(15)
+    case = _rand_case(rng, 3, 5, 4, 8, 4, 0)             # empty cache: only the new row
+    res = orc.absorbed_decode_seq(**case)
+    for h in range(3):
+        np.testing.assert_allclose(res["out"][h], case["w_uv"][h] @ case["c_new"], rtol=1e-13)
+    np.testing.assert_allclose(orc.naive_decode_seq(**case), res["out"], rtol=1e-13)
+
+
+def test_zero_query_gives_mean_latent():
+    rng = np.random.default_rng(16)
+    case = _rand_case(rng, 2, 6, 5, 8, 4, 7)
+    case.update(q_nope=np.zeros((2, 6)), q_rope=np.zeros((2, 4)))
+    res = orc.absorbed_decode_seq(**case)
+    mean_c = np.vstack([case["c_cached"], case["c_new"]]).mean(axis=0)
+    np.testing.assert_allclose(res["o_lat"], np.tile(mean_c, (2, 1)), rtol=1e-13)
+    np.testing.assert_allclose(res["lse"], math.log(8.0), rtol=1e-14)
+    for h in range(2):
+        np.testing.assert_allclose(res["out"][h], case["w_uv"][h] @ mean_c, rtol=1e-12)
+
+
+def test_identical_latents_ignore_weights():
+    rng = np.random.default_rng(17)
+    case = _rand_case(rng, 2, 6, 5, 8, 4, 6)
+    case["c_cached"] = np.tile(case["c_new"], (6, 1))     # every latent equal, RoPE keys differ
+    res = orc.absorbed_decode_seq(**case)
+    for h in range(2):
+        np.testing.assert_allclose(res["out"][h], case["w_uv"][h] @ case["c_new"], rtol=1e-12)
+
+
+def test_zero_w_uk_is_position_only_attention():
+    rng = np.random.default_rng(18)
+    case = _rand_case(rng, 2, 6, 5, 8, 4, 6)
+    case["w_uk"] = np.zeros_like(case["w_uk"])
+    a = orc.absorbed_decode_seq(**case)["out"]
+    b = orc.absorbed_decode_seq(**dict(case, q_nope=rng.standard_normal((2, 6))))["out"]
+    np.testing.assert_allclose(a, b, rtol=1e-14)
+    # and with equal RoPE keys on top, attention is uniform
+    case["krot_cached"] = np.tile(orc.rope(case["k_rope_new"], 6, 10000.0), (6, 1))
+    res = orc.absorbed_decode_seq(**case)
+    mean_c = np.vstack([case["c_cached"], case["c_new"]]).mean(axis=0)
+    np.testing.assert_allclose(res["o_lat"], np.tile(mean_c, (2, 1)), rtol=1e-12)
+
+
+def test_shift_by_one_row_changes_result():
+    """Dropping the appended row (attending T instead of T+1 rows) is visible."""
+    step = syn.make_inputs("tiny")
+    seqs, qn, qr, cn, kn, wuk, wuv = oracle_args(step)
+    full = orc.absorbed_decode_seq(qn[0], qr[0], seqs[0][0], seqs[0][1], cn[0], kn[0],
+                                   wuk, wuv, step.softmax_scale, step.rope_base)
+    # attend over the cached rows only, query still at position L
+    L = seqs[0][0].shape[0]
+    q_t = np.stack([wuk[h].T @ qn[0, h] for h in range(step.H)])
+    q_r = np.stack([orc.rope(qr[0, h], L, step.rope_base) for h in range(step.H)])
+    p = orc.softmax(step.softmax_scale * (q_t @ seqs[0][0].T + q_r @ seqs[0][1].T))
+    o = p @ seqs[0][0]
+    assert normwise_rel(o, full["o_lat"]) > 1e-2
+
+
+# ---------------------------------------------------------------------------
+# The seeded generator (input side only)
+# ---------------------------------------------------------------------------
+
+
+def test_bf16_rounding_is_nearest_even():
+    rng = np.random.default_rng(19)
+    x = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.integers(-6, 6, 20000),
+                        [0.0, -0.0, 1.0, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -8 + 2.0 ** -40]])
+    bits = syn.bf16_bits_from_f64(x)
+    y = syn.bf16_bits_to_f64(bits)
+    up = syn.bf16_bits_to_f64(bits + 1)
+    dn = syn.bf16_bits_to_f64(bits - 1)
+    nz = x != 0
+    err = np.abs(y - x)
+    assert np.all(err[nz] <= np.abs(up - x)[nz]) and np.all(err[nz] <= np.abs(dn - x)[nz])
+    assert y[-4] == 1.0
+    assert y[-3] == 1.0                       # 1 + half an ulp: tie -> even (down)
+    assert y[-2] == 1.0 + 2.0 ** -6           # 1 + 1.5 ulp: tie -> even (up)
+    assert y[-1] == 1.0 + 2.0 ** -7           # just above the tie rounds up
+
+
+def test_generator_layout_and_determinism():
+    a = syn.make_inputs("dsv2_ragged", B=5, T=(3, 9))
+    b = syn.make_inputs("dsv2_ragged", B=5, T=(3, 9))
+    np.testing.assert_array_equal(a.kv_cache, b.kv_cache)
+    assert np.all(a.lens >= 3) and np.all(a.lens <= 9)
+    ends = a.row_offsets + a.lens + 1
+    assert a.row_offsets[0] == 0 and np.all(a.row_offsets[1:] == ends[:-1]) and ends[-1] == a.total_rows
+    for bi in range(a.B):
+        slot = a.kv_cache[a.row_offsets[bi] + a.lens[bi]]
+        assert np.all(slot == 0x7FC0)         # append slot holds NaN
+        rows = a.cached_rows_f64(bi)[:, :a.r]
+        np.testing.assert_allclose(np.sqrt(np.mean(rows ** 2, axis=1)), 1.0, atol=1e-2)

@@ -1,0 +1,934 @@
+// Absorbed Multi-head Latent Attention decode for MI355X (gfx950 / CDNA4).
+//
+// Five kernels behind the C ABI declared in include/mla.h:
+//   absorb_q_kernel       q~ = W_UK^T q_nope                (32x32 MFMA, W_UK staged in LDS)
+//   rope_append_kernel    RoPE(q_rope), append [c_kv_new | RoPE(k_rope_new)]
+//   decode_latent_kernel  split-KV flash decode over the latent cache (32x32 MFMA)
+//   combine_kernel        log-sum-exp merge of the splits
+//   up_v_kernel           out = W_UV o_lat                   (32x32 MFMA)
+//
+// Sources (page title, section): "DeepSeek MLA, Built From the Paper" section 3
+// (absorption identity) and section 2 (decoupled RoPE key shared by the heads);
+// "MLA from scratch" (MLAAttention weight shapes, decode-time cache append,
+// absorbing projections); "Build a DeepSeek Model (From Scratch)" chapter 3
+// figure captions (RoPE pairs, content score plus position score);
+// "Multi-head latent attention" (octlm: latent plus shared rotated RoPE key).
+//
+// MFMA operand layouts used below (v_mfma_f32_32x32x16_bf16 and
+// v_mfma_f32_32x32x2f32, wave64):
+//   A[m][k]: lane i holds row m = i%32 and KPL consecutive k starting at KPL*(i/32)
+//   B[k][n]: lane i holds column n = i%32 and the same k slots
+//   C[m][n]: lane i, accumulator r holds row 8*(r/4) + 4*(i/32) + r%4, column i%32
+// Only the pairing of k slots between A and B matters for a dot product, so a
+// kernel may assign any set of k indices to a lane's slots as long as both
+// operands use the same assignment.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <string>
+
+#include "mla.h"
+
+namespace {
+
+using u16 = uint16_t;
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
+// Softmax reference: each head's exponent reference is fixed at the first tile
+// of a split, and p = 2^(s - ref) is accepted up to 2^kRefSlack (finite in fp32
+// and bf16, no overflow of the sums).  If a later score exceeds ref + kRefSlack,
+// the work-group runs a scores-only pass over the split to find each head's
+// exact maximum and then redoes the split with that reference (p <= 1), so the
+// accumulators are never rescaled inside the loop and at most one redo happens.
+constexpr float kRefSlack = 64.0f;
+
+// ---------------------------------------------------------------------------
+// bf16 helpers (storage type u16 holds bf16 bits)
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf2f(u16 b) { return __uint_as_float((uint32_t)b << 16); }
+
+__device__ __forceinline__ u16 f2bf(float f) {  // round to nearest even
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u16)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (u16)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack2bf(float a, float b) {
+  return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+}
+
+// Round a finite fp32 value to the nearest bf16 (ties to even), kept as fp32.
+__device__ __forceinline__ float round_bf16_finite(float a) {
+  uint32_t u = __float_as_uint(a);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return __uint_as_float(u & 0xffff0000u);
+}
+
+// Pack two fp32 values that are already bf16-representable into bf16x2.
+__device__ __forceinline__ uint32_t pack_hi16(float a, float b) {
+  return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
+}
+
+// double -> bf16 with a single rounding: round to odd into fp32, then nearest
+// even into bf16 (fp32 keeps more than two extra bits, so the result is the
+// correctly rounded bf16).
+__device__ __forceinline__ u16 d2bf(double x) {
+  float f = (float)x;
+  double fd = (double)f;
+  uint32_t u = __float_as_uint(f);
+  if (fd != x) {
+    if (fabs(fd) > fabs(x)) u -= 1u;  // step toward zero (same sign)
+    u |= 1u;
+  }
+  return f2bf(__uint_as_float(u));
+}
+
+template <typename T> __device__ __forceinline__ double load_d(T v);
+template <> __device__ __forceinline__ double load_d<u16>(u16 v) { return (double)bf2f(v); }
+template <> __device__ __forceinline__ double load_d<float>(float v) { return (double)v; }
+template <typename T> __device__ __forceinline__ T store_d(double v);
+template <> __device__ __forceinline__ u16 store_d<u16>(double v) { return d2bf(v); }
+template <> __device__ __forceinline__ float store_d<float>(double v) { return (float)v; }
+
+// ---------------------------------------------------------------------------
+// MFMA traits
+// ---------------------------------------------------------------------------
+
+template <typename T> struct Mma;
+template <> struct Mma<u16> {
+  static constexpr int KSTEP = 16;  // k per instruction (8 per lane)
+  using Frag = i16x8;
+  __device__ static __forceinline__ f32x16 mma(Frag a, Frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+};
+template <> struct Mma<float> {
+  static constexpr int KSTEP = 2;  // k per instruction (1 per lane)
+  using Frag = float;
+  __device__ static __forceinline__ f32x16 mma(Frag a, Frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+};
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) z[r] = 0.f;
+  return z;
+}
+
+// ---------------------------------------------------------------------------
+// Row-major LDS tiles with 16-byte chunks XOR-swizzled within groups of 8.
+// For rows t..t+7 the swizzle is a permutation of the chunk slots, so a b128
+// read of one chunk across 8 rows and a transpose read of 2 chunks across 4
+// aligned rows both touch distinct bank groups.
+// ---------------------------------------------------------------------------
+
+template <int NCH>
+__device__ __forceinline__ int swz_chunk(int t, int c) {
+  if constexpr (NCH % 8 == 0) {
+    return c ^ (((t & 3) << 1) | ((t >> 2) & 1));
+  } else {
+    return c;
+  }
+}
+
+template <int ROWB, int NCH>
+__device__ __forceinline__ int tile_off(int t, int byte_in_row) {
+  return t * ROWB + 16 * swz_chunk<NCH>(t, byte_in_row >> 4) + (byte_in_row & 15);
+}
+
+// B/A operand "column of 8 rows" for bf16 via two ds_read_b64_tr_b16: lane i
+// (16-lane group G = i/16, m = i%16) receives column col0 + 16*(G%2) + m of
+// rows rowA..rowA+3 (slots 0-3) and rowB..rowB+3 (slots 4-7).  Within a
+// 16-lane group, source lane 4j+q supplies the 8 bytes at row (base + j),
+// columns 4q..4q+3; lane m then receives element m%4 from lanes 4j + m/4.
+template <int ROWB, int NCH>
+__device__ __forceinline__ i16x8 load_col8_tr(const char* tile, int col0, int rowA, int rowB, int lane) {
+  const int m = lane & 15;
+  const int col = col0 + 16 * ((lane >> 4) & 1) + 4 * (m & 3);
+  const int ra = rowA + (m >> 2), rb = rowB + (m >> 2);
+  LDS_AS char* base = (LDS_AS char*)tile;
+  i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(base + tile_off<ROWB, NCH>(ra, 2 * col)));
+  i16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(base + tile_off<ROWB, NCH>(rb, 2 * col)));
+  return __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm_then_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// ---------------------------------------------------------------------------
+// K3: split-KV attention over the latent cache.
+//
+// One work-group per (sequence b, split s, head group g); NW waves, wave w
+// owns 32 heads.  Rows stream HBM -> LDS in 32-row tiles through a 4-stage
+// ring filled by global_load_lds (no register staging).  Per tile and wave:
+//   S^T[t][h] = sum_k cache[t][k] q_lat[h][k]       (A = cache rows, B = q_lat^T
+//                                                    held in registers)
+//   online softmax over t per head (the accumulator layout puts one head per
+//   lane, so max/sum need only lane-local work plus one xor-32 exchange)
+//   O^T[c][h] += sum_t cache[t][c] P[h][t]           (A = cache^T via transpose
+//                                                    reads, B = P^T straight
+//                                                    from the S^T accumulators)
+// ---------------------------------------------------------------------------
+
+template <typename T, int H, int R, int DR, int NW>
+struct DecodeShape {
+  static constexpr int W = R + DR;
+  static constexpr int ES = (int)sizeof(T);
+  static constexpr int ROWB = W * ES;
+  static constexpr int NCH = ROWB / 16;
+  static constexpr int TILE = 32;
+  static constexpr int STAGES = 4;
+  static constexpr int TILE_BYTES = TILE * ROWB;
+  static constexpr int DMA_PER_TILE = TILE * NCH / 64;
+  static constexpr int DMA_PER_WAVE = DMA_PER_TILE / NW;
+  static constexpr int KS = W / Mma<T>::KSTEP;
+  static constexpr int CB = R / 32;
+  static constexpr int HEADS_PER_GROUP = 32 * NW;
+  static constexpr int GROUPS = (H + HEADS_PER_GROUP - 1) / HEADS_PER_GROUP;
+  static_assert(ROWB % 16 == 0, "cache row must be a whole number of 16-byte chunks");
+  static_assert((TILE * NCH) % (64 * NW) == 0, "tile must split evenly over the waves");
+  static_assert(W % Mma<T>::KSTEP == 0 && R % 32 == 0, "shape");
+  static_assert(DMA_PER_WAVE * 2 <= 63, "vmcnt range");
+  static_assert(STAGES * TILE_BYTES <= 160 * 1024, "LDS");
+};
+
+template <typename T, int H, int R, int DR, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
+    const T* __restrict__ q_lat, const T* __restrict__ cache, const int64_t* __restrict__ row_offsets,
+    const int32_t* __restrict__ seq_lens, int64_t total_rows, int32_t num_splits, int32_t chunk,
+    float* __restrict__ o_part, float* __restrict__ lse_part, float scale_log2) {
+  using S = DecodeShape<T, H, R, DR, NW>;
+  using M = Mma<T>;
+  constexpr int W = S::W, ROWB = S::ROWB, NCH = S::NCH, TILE = S::TILE, STAGES = S::STAGES;
+  constexpr int DPW = S::DMA_PER_WAVE, KS = S::KS, CB = S::CB, TB = S::TILE_BYTES;
+  constexpr bool BF16 = sizeof(T) == 2;
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * TB];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (LDS DMA base)
+  const int hf = lane >> 5, l32 = lane & 31;
+  int bid = blockIdx.x;
+  const int g = bid % S::GROUPS;
+  bid /= S::GROUPS;
+  const int s = bid % num_splits;
+  const int b = bid / num_splits;
+  const int head = g * S::HEADS_PER_GROUP + wave * 32 + l32;
+  const bool head_ok = head < H;
+
+  const int seq_len = seq_lens[b];
+  const int r0 = s * chunk;
+  const int r1 = min(r0 + chunk, seq_len);
+  float* lse_out = lse_part + ((int64_t)b * num_splits + s) * H;
+  if (r0 >= r1) {  // empty split (block-uniform)
+    if (hf == 0 && head_ok) lse_out[head] = -INFINITY;
+    return;
+  }
+  const int ntiles = (r1 - r0 + TILE - 1) / TILE;
+  // Absolute cache rows of this split, clamped into the cache: inconsistent
+  // metadata can then only produce wrong numbers, never a stray access.
+  int64_t row_lo = row_offsets[b] + r0, row_hi = row_offsets[b] + r1 - 1;
+  row_lo = row_lo < 0 ? 0 : (row_lo > total_rows - 1 ? total_rows - 1 : row_lo);
+  row_hi = row_hi < row_lo ? row_lo : (row_hi > total_rows - 1 ? total_rows - 1 : row_hi);
+  const char* split_base = (const char*)cache + row_lo * ROWB;
+  const int last_rel = (int)(row_hi - row_lo);  // last valid row relative to row_lo
+
+  // DMA: wave instruction n of a tile fills LDS bytes [gi*1024, gi*1024 + 1024)
+  // of the stage (gi = wave*DPW + n); lane l writes 16 bytes at gi*1024 + 16*l,
+  // which is physical chunk p = gi*64 + l = row t, swizzled slot p % NCH.  The
+  // per-lane (t, chunk) pairs are recomputed at each issue from an opaque copy
+  // of the lane id, so they do not occupy registers across the loop.
+  auto issue_tile = [&](int tile, int stage) {
+    const int rel0 = tile * TILE;
+    LDS_AS char* dst = (LDS_AS char*)smem + stage * TB + wave * DPW * 1024;
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int n = 0; n < DPW; ++n) {
+      const int p = (wave * DPW + n) * 64 + ln;
+      const int t = p / NCH;
+      const int c = swz_chunk<NCH>(t, p - t * NCH);
+      const int rel = min(rel0 + t, last_rel);
+      const char* src = split_base + (int64_t)rel * ROWB + c * 16;
+      __builtin_amdgcn_global_load_lds(src, dst + n * 1024, 16, 0, 0);
+    }
+  };
+
+#pragma unroll
+  for (int k = 0; k < STAGES - 1; ++k)
+    if (k < ntiles) issue_tile(k, k);
+
+  // q_lat^T fragments (B operand of the score product), one head per lane.
+  typename M::Frag qf[KS];
+  {
+    const T* qrow = q_lat + ((int64_t)b * H + (head_ok ? head : 0)) * W;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      if constexpr (BF16) {
+        i16x8 v = *(const i16x8*)(qrow + kk * 16 + hf * 8);
+        qf[kk] = head_ok ? v : i16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      } else {
+        float v = qrow[kk * 2 + hf];
+        qf[kk] = head_ok ? v : 0.f;
+      }
+    }
+  }
+
+  // Lane base offsets inside a stage.  Scores (bf16): row l32, logical chunk
+  // 2*kk + hf; the swizzle only permutes the low 3 bits, so chunk 8a + x sits at
+  // 16*(8a + (x ^ swz)) and four bases (kk % 4) plus immediates cover all kk.
+  // Transpose reads: the swizzle of rows 16*ks + 8*sel + 4*hf + j does not
+  // depend on (ks, sel), and logical chunk 4*cb + 2*cg + q/2 needs only the
+  // parity of cb, so two bases cover all 2*CB*2 reads.
+  int s_base[4];
+  int tr_base[2];
+  if constexpr (BF16) {
+    const int sw = swz_chunk<NCH>(l32, 0) ^ 0;  // swizzle value of row l32
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s_base[q] = l32 * ROWB + 16 * ((2 * q + hf) ^ sw);
+    const int m = lane & 15, cg = (lane >> 4) & 1;
+    const int trow = 4 * hf + (m >> 2);
+    const int tsw = swz_chunk<NCH>(trow, 0);
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+      tr_base[par] = trow * ROWB + 16 * ((4 * par + 2 * cg + ((m & 3) >> 1)) ^ tsw) + 8 * (m & 1);
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s_base[q] = 0;
+    tr_base[0] = tr_base[1] = 0;
+  }
+
+  __shared__ int redo_stamp[2];
+  if (threadIdx.x < 2) redo_stamp[threadIdx.x] = -1;  // ordered by the first barrier below
+
+  f32x16 o[CB];
+  float m_ref = -INFINITY;   // exponent reference of this lane's head (log2 units)
+  float m_seen = -INFINITY;  // largest score seen so far
+  float l_sum = 0.f;
+  int step = 0;              // block-uniform iteration stamp, never reused
+  // pass 0: normal; pass 1: scores only, to get the exact max (after an
+  // overflow); pass 2: final pass with that max as the reference
+  for (int pass = 0;; ++pass) {
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) o[cb] = zero16();
+    l_sum = 0.f;
+    if (pass > 0) {
+#pragma unroll
+      for (int k = 0; k < STAGES - 1; ++k)
+        if (k < ntiles) issue_tile(k, k);
+    }
+    bool redo = false;
+    for (int it = 0; it < ntiles; ++it) {
+      const int ahead = min(STAGES - 2, ntiles - 1 - it);
+      if (ahead >= 2) wait_vm_then_barrier<2 * DPW>();
+      else if (ahead == 1) wait_vm_then_barrier<DPW>();
+      else wait_vm_then_barrier<0>();
+      if (pass == 0 && it > 0 && redo_stamp[(step - 1) & 1] == step - 1) {  // previous tile overflowed
+        redo = true;
+        break;
+      }
+      if (it + STAGES - 1 < ntiles) issue_tile(it + STAGES - 1, (it + STAGES - 1) % STAGES);
+      const int stage_off = (it % STAGES) * TB;
+      const char* tile = smem + stage_off;
+      ++step;
+
+      // scores S^T[t][h]: lane row t = l32 of the A operand
+      f32x16 sacc = zero16();
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        typename M::Frag a;
+        if constexpr (BF16) {
+          a = *(const i16x8*)(tile + s_base[kk & 3] + 128 * (kk >> 2));
+        } else {
+          a = *(const float*)(tile + tile_off<ROWB, NCH>(l32, (kk * 2 + hf) * 4));
+        }
+        sacc = M::mma(a, qf[kk], sacc);
+        if constexpr (BF16) {
+          if ((kk & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+
+      // softmax weights (log2 domain) in place; head = this lane's column
+      const int valid = r1 - (r0 + it * TILE);
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = 8 * (r >> 2) + 4 * hf + (r & 3);
+        sacc[r] = t < valid ? sacc[r] * scale_log2 : -INFINITY;
+        mx = fmaxf(mx, sacc[r]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      m_seen = fmaxf(m_seen, mx);
+      if (pass == 1) continue;  // max scan only
+      if (m_ref == -INFINITY) m_ref = mx;
+      if (pass == 0 && __any(mx > m_ref + kRefSlack)) {
+        if (lane == 0) redo_stamp[(step - 1) & 1] = step - 1;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pr = __builtin_amdgcn_exp2f(fminf(sacc[r] - m_ref, kRefSlack));
+        if constexpr (BF16) pr = round_bf16_finite(pr);  // the weight P*V will see
+        sacc[r] = pr;
+        l_sum += pr;
+      }
+      const f32x16& p = sacc;
+
+      // O^T[c][h] += cache^T P^T
+      if constexpr (BF16) {
+        i16x8 pf[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+          pf[ks] = __builtin_bit_cast(i16x8, u32x4{pack_hi16(p[8 * ks + 0], p[8 * ks + 1]),
+                                                   pack_hi16(p[8 * ks + 2], p[8 * ks + 3]),
+                                                   pack_hi16(p[8 * ks + 4], p[8 * ks + 5]),
+                                                   pack_hi16(p[8 * ks + 6], p[8 * ks + 7])});
+        }
+        LDS_AS char* tl = (LDS_AS char*)tile;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const int off = tr_base[cb & 1] + 128 * (cb >> 1) + 16 * ks * ROWB;
+            i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(tl + off));
+            i16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(tl + off + 8 * ROWB));
+            o[cb] = M::mma(__builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7), pf[ks], o[cb]);
+          }
+          if ((cb & 1) == 1) __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int t = 8 * (r >> 2) + 4 * hf + (r & 3);
+            const float a = *(const float*)(tile + tile_off<ROWB, NCH>(t, (32 * cb + l32) * 4));
+            o[cb] = M::mma(a, p[r], o[cb]);
+          }
+        }
+      }
+    }
+    if (pass == 0 && !redo) {  // the last tile may have overflowed too
+      wait_vm_then_barrier<0>();
+      redo = redo_stamp[(step - 1) & 1] == step - 1;
+    }
+    if (pass != 1 && !redo) break;
+    // every wave is here and its loads have landed: refill the ring from tile 0
+    wait_vm_then_barrier<0>();
+    if (pass == 1) m_ref = m_seen;  // exact max of the split: p <= 1 in the final pass
+  }
+
+  const float l_tot = l_sum + __shfl_xor(l_sum, 32);
+  if (head_ok) {
+    const float inv = 1.f / l_tot;
+    float* op = o_part + (((int64_t)b * num_splits + s) * H + head) * R;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        f32x4 v = {o[cb][4 * q] * inv, o[cb][4 * q + 1] * inv, o[cb][4 * q + 2] * inv, o[cb][4 * q + 3] * inv};
+        *(f32x4*)(op + 32 * cb + 8 * q + 4 * hf) = v;
+      }
+    }
+    if (hf == 0) lse_out[head] = (m_ref + __log2f(l_tot)) * kLn2;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// K4: merge the splits.  One thread owns 4 consecutive latent columns of one
+// (b, h); R/4 threads per head.
+// ---------------------------------------------------------------------------
+
+template <int R>
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ o_part,
+                                                      const float* __restrict__ lse_part, int num_splits,
+                                                      int H, int BH, float* __restrict__ o_lat,
+                                                      float* __restrict__ lse_out) {
+  constexpr int TPH = R / 4;
+  constexpr int HPB = 256 / TPH;
+  static_assert(TPH <= 256 && 256 % TPH == 0, "R");
+  const int bh = blockIdx.x * HPB + (int)threadIdx.x / TPH;
+  if (bh >= BH) return;
+  const int b = bh / H, h = bh - b * H;
+  const int c = ((int)threadIdx.x % TPH) * 4;
+  const float* lp = lse_part + (int64_t)b * num_splits * H + h;
+  float m = -INFINITY;
+  for (int s = 0; s < num_splits; ++s) m = fmaxf(m, lp[(int64_t)s * H]);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+  for (int s = 0; s < num_splits; ++s) {
+    const float l = lp[(int64_t)s * H];
+    if (l == -INFINITY) continue;
+    const float w = __expf(l - m);
+    wsum += w;
+    const f32x4 v = *(const f32x4*)(o_part + (((int64_t)b * num_splits + s) * H + h) * R + c);
+    acc += w * v;
+  }
+  const float inv = 1.f / wsum;
+  *(f32x4*)(o_lat + (int64_t)bh * R + c) = acc * inv;
+  if (lse_out != nullptr && c == 0) lse_out[bh] = m + __logf(wsum);
+}
+
+// ---------------------------------------------------------------------------
+// K1: q~^T[j][b] = sum_d W_UK[h][d][j] q_nope[b][h][d].  One work-group per
+// (head, block of 32*NW latent columns); W_UK[h][:, block] is staged in LDS
+// (row-major, swizzled) and read as columns with transpose reads.
+// ---------------------------------------------------------------------------
+
+template <typename T, int NW, int DH>
+__global__ __launch_bounds__(NW * 64) void absorb_q_kernel(const T* __restrict__ q_nope,
+                                                           const T* __restrict__ w_uk, int B, int H, int R,
+                                                           T* __restrict__ q_lat, int W) {
+  using M = Mma<T>;
+  constexpr int ES = (int)sizeof(T);
+  constexpr int COLS = 32 * NW;
+  constexpr int ROWB = COLS * ES;
+  constexpr int NCH = ROWB / 16;
+  constexpr int KS = DH / M::KSTEP;
+  static_assert(ROWB % 16 == 0 && DH % M::KSTEP == 0, "shape");
+  __shared__ __attribute__((aligned(16))) char smem[DH * ROWB];
+
+  const int nblk = R / COLS;
+  const int h = blockIdx.x / nblk;
+  const int j0 = (blockIdx.x - h * nblk) * COLS;
+  for (int idx = threadIdx.x; idx < DH * NCH; idx += NW * 64) {
+    const int d = idx / NCH, c = idx - (idx / NCH) * NCH;
+    const int4 v = *(const int4*)((const char*)(w_uk + ((int64_t)h * DH + d) * R + j0) + 16 * c);
+    *(int4*)(smem + d * ROWB + 16 * swz_chunk<NCH>(d, c)) = v;
+  }
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int hf = lane >> 5, l32 = lane & 31;
+  typename M::Frag af[KS];
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+    if constexpr (ES == 2) {
+      af[kk] = load_col8_tr<ROWB, NCH>(smem, 32 * wave, 16 * kk + 8 * hf, 16 * kk + 8 * hf + 4, lane);
+    } else {
+      af[kk] = *(const float*)(smem + tile_off<ROWB, NCH>(2 * kk + hf, (32 * wave + l32) * 4));
+    }
+  }
+  const int jw = j0 + 32 * wave;
+  for (int b0 = 0; b0 < B; b0 += 32) {
+    const int bb = b0 + l32;
+    const bool bok = bb < B;
+    const T* qrow = q_nope + ((int64_t)(bok ? bb : 0) * H + h) * DH;
+    f32x16 acc = zero16();
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      typename M::Frag bq;
+      if constexpr (ES == 2) {
+        i16x8 v = *(const i16x8*)(qrow + 16 * kk + 8 * hf);
+        bq = bok ? v : i16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      } else {
+        float v = qrow[2 * kk + hf];
+        bq = bok ? v : 0.f;
+      }
+      acc = M::mma(af[kk], bq, acc);
+    }
+    if (bok) {
+      T* dst = q_lat + ((int64_t)bb * H + h) * W + jw;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int j = 8 * q + 4 * hf;
+        if constexpr (ES == 2) {
+          typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+          *(u32x2*)(dst + j) = u32x2{pack2bf(acc[4 * q], acc[4 * q + 1]), pack2bf(acc[4 * q + 2], acc[4 * q + 3])};
+        } else {
+          *(f32x4*)(dst + j) = f32x4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// K5: out^T[d][b] = sum_j W_UV[h][d][j] o_lat[b][h][j].  One wave per
+// (head, 32 output rows); W_UV rows are read straight from HBM, each lane
+// taking 64 contiguous bytes per 4 MFMA steps.  With bf16 weights the fp32
+// o_lat enters as hi + lo bf16 parts (two MFMAs per step).
+// ---------------------------------------------------------------------------
+
+template <typename T, int NW>
+__global__ __launch_bounds__(NW * 64) void up_v_kernel(const float* __restrict__ o_lat, const T* __restrict__ w_uv,
+                                                       int B, int H, int DV, int R, float* __restrict__ out) {
+  using M = Mma<T>;
+  constexpr int ES = (int)sizeof(T);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int hf = lane >> 5, l32 = lane & 31;
+  const int nblk = (DV + 32 * NW - 1) / (32 * NW);
+  const int h = blockIdx.x / nblk;
+  const int d0 = (blockIdx.x - h * nblk) * 32 * NW + wave * 32;
+  if (d0 >= DV) return;
+  const T* wrow = w_uv + ((int64_t)h * DV + d0 + l32) * R;
+  for (int b0 = 0; b0 < B; b0 += 32) {
+    const int bb = b0 + l32;
+    const bool bok = bb < B;
+    const float* orow = o_lat + ((int64_t)(bok ? bb : 0) * H + h) * R;
+    f32x16 acc = zero16();
+    if constexpr (ES == 2) {
+      // per group of 4 steps a lane covers j in [64*g + 32*hf, 64*g + 32*hf + 32)
+      for (int g = 0; g < R / 64; ++g) {
+        const int jb = 64 * g + 32 * hf;
+        i16x8 a4[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) a4[u] = *(const i16x8*)(wrow + jb + 8 * u);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          f32x4 x0 = *(const f32x4*)(orow + jb + 8 * u);
+          f32x4 x1 = *(const f32x4*)(orow + jb + 8 * u + 4);
+          if (!bok) { x0 = f32x4{0, 0, 0, 0}; x1 = x0; }
+          float xv[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+          uint32_t hi[4], lo[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const u16 h0 = f2bf(xv[2 * e]), h1 = f2bf(xv[2 * e + 1]);
+            hi[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+            lo[e] = pack2bf(xv[2 * e] - bf2f(h0), xv[2 * e + 1] - bf2f(h1));
+          }
+          typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+          const i16x8 bh = __builtin_bit_cast(i16x8, u32x4{hi[0], hi[1], hi[2], hi[3]});
+          const i16x8 bl = __builtin_bit_cast(i16x8, u32x4{lo[0], lo[1], lo[2], lo[3]});
+          acc = M::mma(a4[u], bh, acc);
+          acc = M::mma(a4[u], bl, acc);
+        }
+      }
+    } else {
+      for (int kk = 0; kk < R / 2; ++kk) {
+        const float a = wrow[2 * kk + hf];
+        const float x = bok ? orow[2 * kk + hf] : 0.f;
+        acc = M::mma(a, x, acc);
+      }
+    }
+    if (bok) {
+      float* dst = out + ((int64_t)bb * H + h) * DV + d0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *(f32x4*)(dst + 8 * q + 4 * hf) = f32x4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// K2: RoPE on q_rope and on the new token's shared key; append the new row.
+// Angles, rotations and the final rounding are done in double precision.
+// ---------------------------------------------------------------------------
+
+template <typename T>
+__global__ __launch_bounds__(256) void rope_append_kernel(const T* __restrict__ q_rope, const T* __restrict__ c_kv_new,
+                                                          const T* __restrict__ k_rope_new,
+                                                          const int32_t* __restrict__ positions,
+                                                          const int64_t* __restrict__ row_offsets, int64_t total_rows,
+                                                          int H, int R, int DR, double rope_base,
+                                                          T* __restrict__ q_lat, T* __restrict__ cache) {
+  __shared__ double cs[2][256];
+  const int b = blockIdx.x;
+  const int pos = positions[b];
+  const int half = DR / 2;
+  for (int i = threadIdx.x; i < half; i += blockDim.x) {
+    const double theta = pow(rope_base, -2.0 * (double)i / (double)DR);
+    const double ang = (double)pos * theta;
+    cs[0][i] = cos(ang);
+    cs[1][i] = sin(ang);
+  }
+  __syncthreads();
+  const int W = R + DR;
+  for (int idx = threadIdx.x; idx < H * half; idx += blockDim.x) {
+    const int hh = idx / half, i = idx - hh * half;
+    const T* src = q_rope + ((int64_t)b * H + hh) * DR + 2 * i;
+    const double x0 = load_d<T>(src[0]), x1 = load_d<T>(src[1]);
+    const double c = cs[0][i], s = cs[1][i];
+    T* dst = q_lat + ((int64_t)b * H + hh) * W + R + 2 * i;
+    dst[0] = store_d<T>(x0 * c - x1 * s);
+    dst[1] = store_d<T>(x0 * s + x1 * c);
+  }
+  int64_t row = row_offsets[b] + pos;
+  row = row < 0 ? 0 : (row >= total_rows ? total_rows - 1 : row);
+  T* crow = cache + row * W;
+  for (int k = threadIdx.x; k < R; k += blockDim.x) crow[k] = c_kv_new[(int64_t)b * R + k];
+  for (int i = threadIdx.x; i < half; i += blockDim.x) {
+    const T* src = k_rope_new + (int64_t)b * DR + 2 * i;
+    const double x0 = load_d<T>(src[0]), x1 = load_d<T>(src[1]);
+    const double c = cs[0][i], s = cs[1][i];
+    crow[R + 2 * i] = store_d<T>(x0 * c - x1 * s);
+    crow[R + 2 * i + 1] = store_d<T>(x0 * s + x1 * c);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side: validation, dispatch, launch
+// ---------------------------------------------------------------------------
+
+thread_local std::string g_last_error;
+
+mla_status fail(mla_status st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+
+enum Inst { kInstNone = -1, kF32H8R64D16 = 0, kF32H16R64D32 = 1, kBf16H128R512D64 = 2 };
+
+int find_inst(const mla_dims& d) {
+  if (d.dtype == MLA_F32 && d.heads == 8 && d.rank == 64 && d.d_rope == 16) return kF32H8R64D16;
+  if (d.dtype == MLA_F32 && d.heads == 16 && d.rank == 64 && d.d_rope == 32) return kF32H16R64D32;
+  if (d.dtype == MLA_BF16 && d.heads == 128 && d.rank == 512 && d.d_rope == 64) return kBf16H128R512D64;
+  return kInstNone;
+}
+
+mla_status check_dims_impl(const mla_dims* d) {
+  if (d == nullptr) return fail(MLA_ERR_INVALID_ARG, "dims is NULL");
+  if (d->batch < 1 || d->heads < 1 || d->d_head < 1 || d->d_v < 1 || d->rank < 1 || d->d_rope < 1)
+    return fail(MLA_ERR_INVALID_ARG, "every dimension must be >= 1");
+  if (d->d_rope % 2 != 0) return fail(MLA_ERR_INVALID_ARG, "d_rope must be even (RoPE rotates pairs)");
+  if (d->dtype != MLA_F32 && d->dtype != MLA_BF16) return fail(MLA_ERR_INVALID_ARG, "dtype must be MLA_F32 or MLA_BF16");
+  if (d->batch > (1 << 20)) return fail(MLA_ERR_UNSUPPORTED, "batch above 2^20");
+  if (find_inst(*d) == kInstNone)
+    return fail(MLA_ERR_UNSUPPORTED,
+                "no kernel for (dtype, heads, rank, d_rope); supported: (F32,8,64,16) (F32,16,64,32) (BF16,128,512,64)");
+  if (d->d_head != 32 && d->d_head != 64 && d->d_head != 128 && d->d_head != 256)
+    return fail(MLA_ERR_UNSUPPORTED, "d_head must be 32, 64, 128 or 256");
+  if (d->d_v % 32 != 0 || d->d_v > 1024) return fail(MLA_ERR_UNSUPPORTED, "d_v must be a multiple of 32, at most 1024");
+  return MLA_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+mla_status check_ptrs(std::initializer_list<const void*> ps) {
+  for (const void* p : ps) {
+    if (p == nullptr) return fail(MLA_ERR_INVALID_ARG, "a required pointer is NULL");
+    if (!aligned16(p)) return fail(MLA_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
+  }
+  return MLA_OK;
+}
+
+mla_status launch_result(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  return MLA_OK;
+}
+
+float scale_of(const mla_dims& d) {
+  return d.softmax_scale > 0.f ? d.softmax_scale : (float)(1.0 / std::sqrt((double)(d.d_head + d.d_rope)));
+}
+
+int32_t chunk_rows(int32_t max_seq_len, int32_t num_splits) {
+  const int64_t c = ((int64_t)max_seq_len + num_splits - 1) / num_splits;
+  return (int32_t)(((c + 31) / 32) * 32);
+}
+
+constexpr int kMaxSplits = 4096;
+
+template <typename T, int H, int R, int DR, int NW>
+mla_status launch_decode(const mla_dims& d, const void* q_lat, const void* cache, const int64_t* row_offsets,
+                         const int32_t* seq_lens, int64_t total_rows, int32_t max_seq_len, int32_t num_splits,
+                         float* o_part, float* lse_part, hipStream_t stream) {
+  using S = DecodeShape<T, H, R, DR, NW>;
+  const int64_t blocks = (int64_t)d.batch * num_splits * S::GROUPS;
+  if (blocks > 0x7fffffff) return fail(MLA_ERR_UNSUPPORTED, "grid too large");
+  const float scale_log2 = scale_of(d) * kLog2e;
+  hipLaunchKernelGGL((decode_latent_kernel<T, H, R, DR, NW>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream,
+                     (const T*)q_lat, (const T*)cache, row_offsets, seq_lens, total_rows, num_splits,
+                     chunk_rows(max_seq_len, num_splits), o_part, lse_part, scale_log2);
+  return launch_result("mla_decode_latent");
+}
+
+template <typename T, int NW, int DH>
+mla_status launch_absorb(const mla_dims& d, const void* q_nope, const void* w_uk, void* q_lat, hipStream_t stream) {
+  if (d.rank % (32 * NW) != 0) return fail(MLA_ERR_UNSUPPORTED, "rank must be a multiple of the column block");
+  const int blocks = d.heads * (d.rank / (32 * NW));
+  hipLaunchKernelGGL((absorb_q_kernel<T, NW, DH>), dim3(blocks), dim3(NW * 64), 0, stream, (const T*)q_nope,
+                     (const T*)w_uk, d.batch, d.heads, d.rank, (T*)q_lat, d.rank + d.d_rope);
+  return launch_result("mla_absorb_q");
+}
+
+template <typename T, int NW>
+mla_status launch_absorb_dh(const mla_dims& d, const void* q_nope, const void* w_uk, void* q_lat, hipStream_t stream) {
+  switch (d.d_head) {
+    case 32: return launch_absorb<T, NW, 32>(d, q_nope, w_uk, q_lat, stream);
+    case 64: return launch_absorb<T, NW, 64>(d, q_nope, w_uk, q_lat, stream);
+    case 128: return launch_absorb<T, NW, 128>(d, q_nope, w_uk, q_lat, stream);
+    case 256: return launch_absorb<T, NW, 256>(d, q_nope, w_uk, q_lat, stream);
+    default: return fail(MLA_ERR_UNSUPPORTED, "d_head");
+  }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------------
+
+extern "C" {
+
+mla_status mla_check_dims(const mla_dims* dims) { return check_dims_impl(dims); }
+
+const char* mla_status_string(mla_status status) {
+  switch (status) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED";
+    case MLA_ERR_ALIGNMENT: return "MLA_ERR_ALIGNMENT";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP";
+  }
+  return "MLA_ERR_UNKNOWN";
+}
+
+const char* mla_last_error(void) { return g_last_error.c_str(); }
+
+mla_status mla_absorb_q(const mla_dims* dims, const void* q_nope, const void* w_uk, void* q_lat, void* stream) {
+  mla_status st = check_dims_impl(dims);
+  if (st != MLA_OK) return st;
+  if ((st = check_ptrs({q_nope, w_uk, q_lat})) != MLA_OK) return st;
+  g_last_error.clear();
+  hipStream_t s = (hipStream_t)stream;
+  switch (find_inst(*dims)) {
+    case kF32H8R64D16:
+    case kF32H16R64D32: return launch_absorb_dh<float, 1>(*dims, q_nope, w_uk, q_lat, s);
+    case kBf16H128R512D64: return launch_absorb_dh<u16, 4>(*dims, q_nope, w_uk, q_lat, s);
+  }
+  return fail(MLA_ERR_UNSUPPORTED, "no instantiation");
+}
+
+mla_status mla_rope_append(const mla_dims* dims, const void* q_rope, const void* c_kv_new, const void* k_rope_new,
+                           const int32_t* positions, const int64_t* row_offsets, int64_t total_rows, void* q_lat,
+                           void* kv_cache, void* stream) {
+  mla_status st = check_dims_impl(dims);
+  if (st != MLA_OK) return st;
+  if (positions == nullptr || row_offsets == nullptr) return fail(MLA_ERR_INVALID_ARG, "positions/row_offsets NULL");
+  if ((st = check_ptrs({q_rope, c_kv_new, k_rope_new, q_lat, kv_cache})) != MLA_OK) return st;
+  if (total_rows < 1) return fail(MLA_ERR_INVALID_ARG, "total_rows must be >= 1");
+  if (dims->d_rope > 512) return fail(MLA_ERR_UNSUPPORTED, "d_rope above 512");
+  g_last_error.clear();
+  hipStream_t s = (hipStream_t)stream;
+  const double base = dims->rope_base > 0.f ? (double)dims->rope_base : 10000.0;
+  if (dims->dtype == MLA_BF16) {
+    hipLaunchKernelGGL((rope_append_kernel<u16>), dim3(dims->batch), dim3(256), 0, s, (const u16*)q_rope,
+                       (const u16*)c_kv_new, (const u16*)k_rope_new, positions, row_offsets, total_rows,
+                       dims->heads, dims->rank, dims->d_rope, base, (u16*)q_lat, (u16*)kv_cache);
+  } else {
+    hipLaunchKernelGGL((rope_append_kernel<float>), dim3(dims->batch), dim3(256), 0, s, (const float*)q_rope,
+                       (const float*)c_kv_new, (const float*)k_rope_new, positions, row_offsets, total_rows,
+                       dims->heads, dims->rank, dims->d_rope, base, (float*)q_lat, (float*)kv_cache);
+  }
+  return launch_result("mla_rope_append");
+}
+
+mla_status mla_decode_latent(const mla_dims* dims, const void* q_lat, const void* kv_cache, const int64_t* row_offsets,
+                             const int32_t* seq_lens, int64_t total_rows, int32_t max_seq_len, int32_t num_splits,
+                             float* o_part, float* lse_part, void* stream) {
+  mla_status st = check_dims_impl(dims);
+  if (st != MLA_OK) return st;
+  if (row_offsets == nullptr || seq_lens == nullptr) return fail(MLA_ERR_INVALID_ARG, "row_offsets/seq_lens NULL");
+  if ((st = check_ptrs({q_lat, kv_cache, o_part, lse_part})) != MLA_OK) return st;
+  if (total_rows < 1 || max_seq_len < 1) return fail(MLA_ERR_INVALID_ARG, "total_rows and max_seq_len must be >= 1");
+  if (num_splits < 1) return fail(MLA_ERR_INVALID_ARG, "num_splits must be >= 1");
+  if (num_splits > kMaxSplits) return fail(MLA_ERR_WORKSPACE, "num_splits above 4096");
+  g_last_error.clear();
+  hipStream_t s = (hipStream_t)stream;
+  switch (find_inst(*dims)) {
+    case kF32H8R64D16:
+      return launch_decode<float, 8, 64, 16, 1>(*dims, q_lat, kv_cache, row_offsets, seq_lens, total_rows,
+                                                max_seq_len, num_splits, o_part, lse_part, s);
+    case kF32H16R64D32:
+      return launch_decode<float, 16, 64, 32, 1>(*dims, q_lat, kv_cache, row_offsets, seq_lens, total_rows,
+                                                 max_seq_len, num_splits, o_part, lse_part, s);
+    case kBf16H128R512D64:
+      return launch_decode<u16, 128, 512, 64, 4>(*dims, q_lat, kv_cache, row_offsets, seq_lens, total_rows,
+                                                 max_seq_len, num_splits, o_part, lse_part, s);
+  }
+  return fail(MLA_ERR_UNSUPPORTED, "no instantiation");
+}
+
+mla_status mla_combine(const mla_dims* dims, const float* o_part, const float* lse_part, int32_t num_splits,
+                       float* o_lat, float* lse, void* stream) {
+  mla_status st = check_dims_impl(dims);
+  if (st != MLA_OK) return st;
+  if ((st = check_ptrs({o_part, lse_part, o_lat})) != MLA_OK) return st;
+  if (num_splits < 1) return fail(MLA_ERR_INVALID_ARG, "num_splits must be >= 1");
+  if (num_splits > kMaxSplits) return fail(MLA_ERR_WORKSPACE, "num_splits above 4096");
+  g_last_error.clear();
+  hipStream_t s = (hipStream_t)stream;
+  const int BH = dims->batch * dims->heads;
+  switch (dims->rank) {
+    case 64:
+      hipLaunchKernelGGL((combine_kernel<64>), dim3((BH + 15) / 16), dim3(256), 0, s, o_part, lse_part, num_splits,
+                         dims->heads, BH, o_lat, lse);
+      break;
+    case 512:
+      hipLaunchKernelGGL((combine_kernel<512>), dim3((BH + 1) / 2), dim3(256), 0, s, o_part, lse_part, num_splits,
+                         dims->heads, BH, o_lat, lse);
+      break;
+    default: return fail(MLA_ERR_UNSUPPORTED, "rank");
+  }
+  return launch_result("mla_combine");
+}
+
+mla_status mla_up_v(const mla_dims* dims, const float* o_lat, const void* w_uv, float* out, void* stream) {
+  mla_status st = check_dims_impl(dims);
+  if (st != MLA_OK) return st;
+  if ((st = check_ptrs({o_lat, w_uv, out})) != MLA_OK) return st;
+  g_last_error.clear();
+  hipStream_t s = (hipStream_t)stream;
+  if (dims->dtype == MLA_BF16) {
+    if (dims->rank % 64 != 0) return fail(MLA_ERR_UNSUPPORTED, "rank must be a multiple of 64 for bf16");
+    const int nblk = (dims->d_v + 127) / 128;
+    hipLaunchKernelGGL((up_v_kernel<u16, 4>), dim3(dims->heads * nblk), dim3(256), 0, s, o_lat, (const u16*)w_uv,
+                       dims->batch, dims->heads, dims->d_v, dims->rank, out);
+  } else {
+    const int nblk = (dims->d_v + 31) / 32;
+    hipLaunchKernelGGL((up_v_kernel<float, 1>), dim3(dims->heads * nblk), dim3(64), 0, s, o_lat,
+                       (const float*)w_uv, dims->batch, dims->heads, dims->d_v, dims->rank, out);
+  }
+  return launch_result("mla_up_v");
+}
+
+mla_status mla_partials_size(const mla_dims* dims, int32_t num_splits, size_t* o_part_bytes, size_t* lse_part_bytes) {
+  mla_status st = check_dims_impl(dims);
+  if (st != MLA_OK) return st;
+  if (num_splits < 1) return fail(MLA_ERR_INVALID_ARG, "num_splits must be >= 1");
+  if (num_splits > kMaxSplits) return fail(MLA_ERR_WORKSPACE, "num_splits above 4096");
+  if (o_part_bytes == nullptr || lse_part_bytes == nullptr) return fail(MLA_ERR_INVALID_ARG, "NULL output");
+  const size_t bsh = (size_t)dims->batch * (size_t)num_splits * (size_t)dims->heads;
+  *o_part_bytes = bsh * (size_t)dims->rank * sizeof(float);
+  *lse_part_bytes = bsh * sizeof(float);
+  return MLA_OK;
+}
+
+int32_t mla_plan_splits(const mla_dims* dims, int32_t max_seq_len, int64_t total_rows, int32_t num_cus) {
+  if (check_dims_impl(dims) != MLA_OK) return 0;
+  if (max_seq_len < 1 || total_rows < 1) return 0;
+  if (num_cus <= 0) {
+    int dev = 0;
+    hipDeviceProp_t prop;
+    if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess) return 0;
+    num_cus = prop.multiProcessorCount;
+  }
+  // One work-group per compute unit: split rows so that (splits in use) fit
+  // the CUs, keeping room for the partial last split of every sequence.
+  const int64_t slots = std::max<int64_t>(1, (int64_t)num_cus - dims->batch / 2);
+  int64_t chunk = (total_rows + slots - 1) / slots;
+  chunk = std::max<int64_t>(32, ((chunk + 31) / 32) * 32);
+  int64_t splits = ((int64_t)max_seq_len + chunk - 1) / chunk;
+  if (splits > kMaxSplits) splits = kMaxSplits;
+  return (int32_t)std::max<int64_t>(1, splits);
+}
+
+}  // extern "C"

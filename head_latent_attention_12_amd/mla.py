@@ -1,0 +1,141 @@
+"""Python binding of libmla.so (ctypes).  Argument marshalling only.
+
+Each function takes torch tensors (device memory) and passes their data
+pointers and the stream to the C entry point of the same name declared in
+include/mla.h.  All arithmetic of the decode step runs in the HIP kernels of
+libmla.so; if the library is missing the binding raises instead of computing
+anything itself.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmla.so")
+
+MLA_F32 = 0
+MLA_BF16 = 1
+
+STATUS = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARG", 2: "MLA_ERR_UNSUPPORTED", 3: "MLA_ERR_ALIGNMENT",
+          4: "MLA_ERR_WORKSPACE", 5: "MLA_ERR_HIP"}
+
+EXPORTS = ("mla_absorb_q", "mla_rope_append", "mla_decode_latent", "mla_combine", "mla_up_v",
+           "mla_partials_size", "mla_plan_splits", "mla_check_dims", "mla_status_string", "mla_last_error")
+
+
+class MlaDims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("d_head", ctypes.c_int32),
+                ("d_v", ctypes.c_int32), ("rank", ctypes.c_int32), ("d_rope", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float), ("rope_base", ctypes.c_float)]
+
+
+class MlaError(RuntimeError):
+    def __init__(self, fn: str, status: int, detail: str):
+        super().__init__(f"{fn}: {STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmla.so from the package directory (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m head_latent_attention_12_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        D = ctypes.POINTER(MlaDims)
+        i32, i64 = ctypes.c_int32, ctypes.c_int64
+        sig = {
+            "mla_absorb_q": (i32, [D, P, P, P, P]),
+            "mla_rope_append": (i32, [D, P, P, P, P, P, i64, P, P, P]),
+            "mla_decode_latent": (i32, [D, P, P, P, P, i64, i32, i32, P, P, P]),
+            "mla_combine": (i32, [D, P, P, i32, P, P, P]),
+            "mla_up_v": (i32, [D, P, P, P, P]),
+            "mla_partials_size": (i32, [D, i32, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]),
+            "mla_plan_splits": (i32, [D, i32, i64, i32]),
+            "mla_check_dims": (i32, [D]),
+            "mla_status_string": (ctypes.c_char_p, [i32]),
+            "mla_last_error": (ctypes.c_char_p, []),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def make_dims(batch, heads, d_head, d_v, rank, d_rope, dtype, softmax_scale=0.0, rope_base=0.0) -> MlaDims:
+    return MlaDims(int(batch), int(heads), int(d_head), int(d_v), int(rank), int(d_rope), int(dtype),
+                   float(softmax_scale), float(rope_base))
+
+
+def _p(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _s(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(fn: str, st: int) -> None:
+    if st != 0:
+        raise MlaError(fn, st, lib().mla_last_error().decode())
+
+
+def mla_absorb_q(dims, q_nope, w_uk, q_lat, stream=None):
+    _check("mla_absorb_q", lib().mla_absorb_q(ctypes.byref(dims), _p(q_nope), _p(w_uk), _p(q_lat), _s(stream)))
+
+
+def mla_rope_append(dims, q_rope, c_kv_new, k_rope_new, positions, row_offsets, total_rows, q_lat, kv_cache,
+                    stream=None):
+    _check("mla_rope_append", lib().mla_rope_append(
+        ctypes.byref(dims), _p(q_rope), _p(c_kv_new), _p(k_rope_new), _p(positions), _p(row_offsets),
+        int(total_rows), _p(q_lat), _p(kv_cache), _s(stream)))
+
+
+def mla_decode_latent(dims, q_lat, kv_cache, row_offsets, seq_lens, total_rows, max_seq_len, num_splits, o_part,
+                      lse_part, stream=None):
+    _check("mla_decode_latent", lib().mla_decode_latent(
+        ctypes.byref(dims), _p(q_lat), _p(kv_cache), _p(row_offsets), _p(seq_lens), int(total_rows),
+        int(max_seq_len), int(num_splits), _p(o_part), _p(lse_part), _s(stream)))
+
+
+def mla_combine(dims, o_part, lse_part, num_splits, o_lat, lse=None, stream=None):
+    _check("mla_combine", lib().mla_combine(ctypes.byref(dims), _p(o_part), _p(lse_part), int(num_splits),
+                                            _p(o_lat), _p(lse), _s(stream)))
+
+
+def mla_up_v(dims, o_lat, w_uv, out, stream=None):
+    _check("mla_up_v", lib().mla_up_v(ctypes.byref(dims), _p(o_lat), _p(w_uv), _p(out), _s(stream)))
+
+
+def mla_partials_size(dims, num_splits):
+    a, b = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check("mla_partials_size", lib().mla_partials_size(ctypes.byref(dims), int(num_splits), ctypes.byref(a),
+                                                        ctypes.byref(b)))
+    return a.value, b.value
+
+
+def mla_plan_splits(dims, max_seq_len, total_rows, num_cus=0) -> int:
+    n = lib().mla_plan_splits(ctypes.byref(dims), int(max_seq_len), int(total_rows), int(num_cus))
+    if n < 1:
+        raise MlaError("mla_plan_splits", 1, lib().mla_last_error().decode())
+    return n
+
+
+def mla_check_dims(dims) -> int:
+    return lib().mla_check_dims(ctypes.byref(dims))

@@ -1,0 +1,102 @@
+"""One decode step on the GPU: upload seeded inputs, run the five C-ABI calls.
+
+Marshalling only: buffers are torch tensors (device memory), every step of
+the computation runs in libmla.so.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import mla
+from .synthetic import BF16, StepInputs
+
+
+def _dev(a: np.ndarray, device) -> torch.Tensor:
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def bits_to_f64(t: torch.Tensor, dtype: str) -> np.ndarray:
+    """Device tensor in storage form -> fp64 numpy."""
+    a = t.detach().cpu().numpy()
+    if dtype == BF16:
+        return (a.view(np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+class DeviceStep:
+    """Device buffers of one step and the five calls that compute it."""
+
+    def __init__(self, inp: StepInputs, num_splits: int | None = None, device: str = "cuda:0",
+                 weights: "DeviceStep | None" = None):
+        self.inp = inp
+        self.device = device
+        self.dims = mla.make_dims(inp.B, inp.H, inp.d_head, inp.d_v, inp.r, inp.d_rope,
+                                  mla.MLA_BF16 if inp.dtype == BF16 else mla.MLA_F32,
+                                  inp.softmax_scale, inp.rope_base)
+        st = torch.int16 if inp.dtype == BF16 else torch.float32
+        if weights is None:
+            self.w_uk = _dev(inp.w_uk, device)
+            self.w_uv = _dev(inp.w_uv, device)
+        else:  # share weights with another step (e.g. several caches, one layer)
+            self.w_uk, self.w_uv = weights.w_uk, weights.w_uv
+        self.q_nope = _dev(inp.q_nope, device)
+        self.q_rope = _dev(inp.q_rope, device)
+        self.kv_cache = _dev(inp.kv_cache, device)
+        self.c_kv_new = _dev(inp.c_kv_new, device)
+        self.k_rope_new = _dev(inp.k_rope_new, device)
+        self.positions = _dev(inp.positions.astype(np.int32), device)
+        self.row_offsets = _dev(inp.row_offsets.astype(np.int64), device)
+        self.seq_lens = _dev(inp.seq_lens.astype(np.int32), device)
+        self.q_lat = torch.zeros((inp.B, inp.H, inp.W), dtype=st, device=device)
+        self.set_splits(num_splits)
+        self.o_lat = torch.empty((inp.B, inp.H, inp.r), dtype=torch.float32, device=device)
+        self.lse = torch.empty((inp.B, inp.H), dtype=torch.float32, device=device)
+        self.out = torch.empty((inp.B, inp.H, inp.d_v), dtype=torch.float32, device=device)
+
+    def set_splits(self, num_splits: int | None) -> None:
+        inp = self.inp
+        if num_splits is None:
+            num_splits = mla.mla_plan_splits(self.dims, inp.max_seq_len, inp.total_rows)
+        self.num_splits = int(num_splits)
+        self.o_part = torch.empty((inp.B, self.num_splits, inp.H, inp.r), dtype=torch.float32, device=self.device)
+        self.lse_part = torch.empty((inp.B, self.num_splits, inp.H), dtype=torch.float32, device=self.device)
+
+    # the five calls -------------------------------------------------------
+    def absorb_q(self, stream=None):
+        mla.mla_absorb_q(self.dims, self.q_nope, self.w_uk, self.q_lat, stream)
+
+    def rope_append(self, stream=None):
+        mla.mla_rope_append(self.dims, self.q_rope, self.c_kv_new, self.k_rope_new, self.positions,
+                            self.row_offsets, self.inp.total_rows, self.q_lat, self.kv_cache, stream)
+
+    def decode_latent(self, stream=None):
+        mla.mla_decode_latent(self.dims, self.q_lat, self.kv_cache, self.row_offsets, self.seq_lens,
+                              self.inp.total_rows, self.inp.max_seq_len, self.num_splits, self.o_part,
+                              self.lse_part, stream)
+
+    def combine(self, stream=None):
+        mla.mla_combine(self.dims, self.o_part, self.lse_part, self.num_splits, self.o_lat, self.lse, stream)
+
+    def up_v(self, stream=None):
+        mla.mla_up_v(self.dims, self.o_lat, self.w_uv, self.out, stream)
+
+    def run(self, stream=None):
+        self.absorb_q(stream)
+        self.rope_append(stream)
+        self.decode_latent(stream)
+        self.combine(stream)
+        self.up_v(stream)
+
+    # results ----------------------------------------------------------------
+    def q_lat_f64(self) -> np.ndarray:
+        return bits_to_f64(self.q_lat, self.inp.dtype)
+
+    def cache_f64(self) -> np.ndarray:
+        return bits_to_f64(self.kv_cache, self.inp.dtype)
+
+    def cache_raw(self) -> np.ndarray:
+        a = self.kv_cache.cpu().numpy()
+        return a.view(np.uint16) if self.inp.dtype == BF16 else a

@@ -1,0 +1,181 @@
+/*
+ * mla.h - absorbed Multi-head Latent Attention (MLA) decode on AMD MI355X (gfx950).
+ *
+ * One decode step for a batch of sequences, split into five calls that run in
+ * stream order:
+ *
+ *   mla_absorb_q      q~ = W_UK^T q_nope per head (the content query folded into
+ *                     the latent space)
+ *   mla_rope_append   rotate q_rope and the new token's shared RoPE key; write
+ *                     the new cache row [c_kv_new | RoPE(k_rope_new)]
+ *   mla_decode_latent split-KV attention over the latent cache: scores
+ *                     q~.c_kv + q_rope.k_rope, online softmax, softmax-weighted
+ *                     sum of the latents, one partial result per split
+ *   mla_combine       log-sum-exp merge of the splits into o_lat
+ *   mla_up_v          out = W_UV o_lat per head
+ *
+ * Sources (page title, section):
+ *   [P1] "DeepSeek MLA, Built From the Paper": section 1 (the cache holds
+ *        r_kv + d_rope values per token and layer), section 2 (a decoupled
+ *        RoPE key shared by all heads), section 3 (matrix absorption:
+ *        q^T (W_UK c) equals (W_UK^T q)^T c, so keys are never rebuilt).
+ *   [P2] "MLA from scratch" (DeepSeek 3.2 series): module structure and
+ *        MLAAttention (weight shapes, latent cache), KV cache management
+ *        during decode (the new latent is written at the current position and
+ *        the cache grows by one row), absorbing projections (attention weights
+ *        applied to the latents directly, W_UV after).
+ *   [P3] "Build a DeepSeek Model (From Scratch)", chapter 3: figure captions
+ *        on RoPE (dimensions rotated in pairs by a position-dependent angle)
+ *        and on the decoupled architecture (content score + position score).
+ *   [P5] "Multi-head latent attention" (octlm blog): the cache holds the
+ *        latent and one RoPE key of width d_rope shared across heads.
+ *
+ * Conventions (readings where the pages leave a step open):
+ *   - RoPE pairs adjacent dimensions (2i, 2i+1); pair i is turned by the angle
+ *     pos * rope_base^(-2i/d_rope).  Angles and rotations are evaluated in
+ *     double precision and rounded once to the storage dtype.
+ *   - The new token is appended first and then attended to: a sequence with
+ *     L cached tokens attends over L + 1 rows and its query sits at position L.
+ *   - Cached RoPE keys are stored already rotated by their own positions.
+ *   - softmax_scale <= 0 selects 1/sqrt(d_head + d_rope).
+ *
+ * Data layout (all row-major, contiguous, little-endian):
+ *   q_nope   [B][H][d_head]          storage dtype
+ *   q_rope   [B][H][d_rope]          storage dtype (not yet rotated)
+ *   w_uk     [H][d_head][r]          storage dtype; the weight of a
+ *                                    Linear(r -> H*d_head) reshaped per head
+ *   w_uv     [H][d_v][r]             storage dtype; same for values
+ *   q_lat    [B][H][r + d_rope]      storage dtype; [q~ | RoPE(q_rope)]
+ *   kv_cache [total_rows][r + d_rope] storage dtype; row = [c_kv | rotated k_rope]
+ *   c_kv_new [B][r], k_rope_new [B][d_rope]   storage dtype
+ *   positions   [B] int32    L_b: cached tokens before the step = the new
+ *                            token's position and its row index in the sequence
+ *   row_offsets [B] int64    first cache row of sequence b
+ *   seq_lens    [B] int32    rows attended = L_b + 1 (after the append)
+ *   o_part   [B][num_splits][H][r] float32, lse_part [B][num_splits][H] float32
+ *   o_lat    [B][H][r] float32, lse [B][H] float32, out [B][H][d_v] float32
+ *   Sequence b owns cache rows [row_offsets[b], row_offsets[b] + seq_lens[b]).
+ *
+ * Splits: with chunk = ceil(max_seq_len / num_splits), split s of sequence b
+ * covers in-sequence rows [s*chunk, min((s+1)*chunk, seq_lens[b])).  A split
+ * with no rows writes lse_part = -inf and leaves its o_part untouched;
+ * mla_combine skips it.
+ *
+ * Ownership and execution: the caller allocates every buffer (device memory,
+ * 16-byte aligned) and owns it; the library allocates nothing, keeps no state
+ * between calls and is safe to call from several host threads.  Every call
+ * validates its arguments on the host, then only enqueues work on `stream`
+ * (a hipStream_t; NULL = the default stream) and returns; the caller
+ * synchronises.  On any error nothing is enqueued and a status code is
+ * returned; nothing is thrown and nothing aborts.  Device-side metadata
+ * (row_offsets, seq_lens, positions) cannot be checked on the host: rows are
+ * clamped into [0, total_rows) so that inconsistent metadata gives wrong
+ * numbers, never an out-of-bounds access.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = 1,  /* null pointer, non-positive size, odd d_rope, bad split count */
+  MLA_ERR_UNSUPPORTED = 2,  /* no kernel instantiation for these dims/dtype */
+  MLA_ERR_ALIGNMENT = 3,    /* a device pointer is not 16-byte aligned */
+  MLA_ERR_WORKSPACE = 4,    /* num_splits exceeds what the kernels support */
+  MLA_ERR_HIP = 5           /* the HIP runtime reported an error (see mla_last_error) */
+} mla_status;
+
+typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
+
+typedef struct {
+  int32_t batch;        /* B: sequences in the step */
+  int32_t heads;        /* H */
+  int32_t d_head;       /* content query/key width per head */
+  int32_t d_v;          /* value width per head */
+  int32_t rank;         /* r: latent width (c_kv) */
+  int32_t d_rope;       /* width of the shared RoPE key, even */
+  int32_t dtype;        /* mla_dtype: storage dtype of q, weights, q_lat, cache */
+  float softmax_scale;  /* <= 0: 1/sqrt(d_head + d_rope) */
+  float rope_base;      /* <= 0: 10000 */
+} mla_dims;
+
+/* Supported shapes: (dtype, H, r, d_rope) in
+ *   (F32, 8, 64, 16), (F32, 16, 64, 32), (BF16, 128, 512, 64),
+ * with d_head and d_v multiples of 32 (F32) or of 32 up to 512 (BF16). */
+
+/* Fold W_UK into the query ([P1] section 3): for every b, h, j
+ *   q_lat[b][h][j] = sum_d w_uk[h][d][j] * q_nope[b][h][d],   j < r,
+ * accumulated in fp32 and rounded once to the storage dtype.  Columns
+ * [r, r + d_rope) of q_lat are not touched. */
+mla_status mla_absorb_q(const mla_dims* dims, const void* q_nope, const void* w_uk,
+                        void* q_lat, void* stream);
+
+/* Rotate the query's RoPE part and append the new token ([P2] cache
+ * management, [P5], [P1] section 2): for every b,
+ *   q_lat[b][h][r + k]           = RoPE(q_rope[b][h], positions[b])[k]
+ *   kv_cache[row_offsets[b] + positions[b]] = [c_kv_new[b] | RoPE(k_rope_new[b], positions[b])]
+ * c_kv_new is copied bit for bit.  total_rows bounds the cache. */
+mla_status mla_rope_append(const mla_dims* dims, const void* q_rope, const void* c_kv_new,
+                           const void* k_rope_new, const int32_t* positions,
+                           const int64_t* row_offsets, int64_t total_rows, void* q_lat,
+                           void* kv_cache, void* stream);
+
+/* Attention in the latent space ([P1] section 3, [P2] absorbing projections,
+ * [P3] content score + position score): for every b, h and split s with rows
+ * t in the split,
+ *   score_t = softmax_scale * (q_lat[b][h][0:r] . c_kv_t + q_lat[b][h][r:] . k_rope_t)
+ *   o_part[b][s][h] = sum_t softmax(score)_t * c_kv_t    (softmax within the split)
+ *   lse_part[b][s][h] = ln sum_t exp(score_t)
+ * fp32 accumulation; bf16 storage computes the products in bf16 with fp32
+ * sums.  max_seq_len must be >= every seq_lens[b]; rows beyond
+ * num_splits * chunk are not read.  1 <= num_splits <= 4096. */
+mla_status mla_decode_latent(const mla_dims* dims, const void* q_lat, const void* kv_cache,
+                             const int64_t* row_offsets, const int32_t* seq_lens,
+                             int64_t total_rows, int32_t max_seq_len, int32_t num_splits,
+                             float* o_part, float* lse_part, void* stream);
+
+/* Merge the splits (softmax over the union of the splits' rows):
+ *   m = max_s lse_part[b][s][h];  w_s = exp(lse_part[b][s][h] - m)
+ *   o_lat[b][h] = sum_s w_s o_part[b][s][h] / sum_s w_s
+ *   lse[b][h]   = m + ln sum_s w_s                (lse may be NULL)
+ * Splits whose lse_part is -inf are skipped. */
+mla_status mla_combine(const mla_dims* dims, const float* o_part, const float* lse_part,
+                       int32_t num_splits, float* o_lat, float* lse, void* stream);
+
+/* Apply W_UV after the weighted sum ([P2] absorbing projections):
+ *   out[b][h][d] = sum_j w_uv[h][d][j] * o_lat[b][h][j]
+ * fp32 accumulation; with bf16 weights, o_lat enters the product as the sum
+ * of two bf16 terms (high and low part), which keeps it exact to ~2^-16. */
+mla_status mla_up_v(const mla_dims* dims, const float* o_lat, const void* w_uv, float* out,
+                    void* stream);
+
+/* Bytes of o_part and lse_part for `num_splits` splits. */
+mla_status mla_partials_size(const mla_dims* dims, int32_t num_splits, size_t* o_part_bytes,
+                             size_t* lse_part_bytes);
+
+/* Split count the library would choose: enough work-groups to cover the
+ * device's compute units with splits of at least a few hundred rows.
+ * Returns a value >= 1, or <= 0 on invalid arguments.  num_cus <= 0 queries
+ * the current device. */
+int32_t mla_plan_splits(const mla_dims* dims, int32_t max_seq_len, int64_t total_rows,
+                        int32_t num_cus);
+
+/* MLA_OK if the dims are valid and have a kernel instantiation. */
+mla_status mla_check_dims(const mla_dims* dims);
+
+const char* mla_status_string(mla_status status);
+
+/* Text of the last error on the calling host thread ("" if none). */
+const char* mla_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

@@ -32,6 +32,8 @@
 
 #include "mla.h"
 
+#include "decode_asm.inc"  // hand-scheduled inner blocks of the bf16 decode tile
+
 namespace {
 
 using u16 = uint16_t;
@@ -74,6 +76,13 @@ __device__ __forceinline__ float round_bf16_finite(float a) {
   uint32_t u = __float_as_uint(a);
   u += 0x7fffu + ((u >> 16) & 1u);
   return __uint_as_float(u & 0xffff0000u);
+}
+
+// Two fp32 values rounded to bf16 (nearest even, v_cvt_pk_bf16_f32), packed.
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
 
 // Pack two fp32 values that are already bf16-representable into bf16x2.
@@ -167,6 +176,31 @@ __device__ __forceinline__ i16x8 load_col8_tr(const char* tile, int col0, int ro
   return __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// The bf16 decode tile runs its two inner phases as hand-scheduled asm blocks
+// (decode_asm.inc): the 32x512 fp32 output block lives in AGPRs and the q
+// fragments in VGPRs, which the register allocator does not find on its own,
+// and LDS reads are pipelined ahead of the MFMAs they feed.  The compiler
+// cannot see those MFMAs, so acc_fence() supplies the wait states around the
+// accumulators: after zeroing them and before reading them back (24 cycles,
+// above the 12 a VALU/AGPR read of an 8-pass 32x32x16 result needs).
+template <int CB>
+__device__ __forceinline__ void acc_fence(f32x16 (&o)[CB]) {
+  static_assert(CB == 16, "acc_fence is written for 16 accumulator blocks");
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(o[4]), "+a"(o[5]), "+a"(o[6]),
+                 "+a"(o[7]), "+a"(o[8]), "+a"(o[9]), "+a"(o[10]), "+a"(o[11]), "+a"(o[12]), "+a"(o[13]),
+                 "+a"(o[14]), "+a"(o[15]));
+}
+
+// Combine a value with the one held by lane ^ 32 (v_permlane32_swap: the two
+// results together hold both halves' values in every lane).
+template <typename F>
+__device__ __forceinline__ float xor32(float v, F op) {
+  const uint32_t u = __float_as_uint(v);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vm_then_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
@@ -219,6 +253,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
   constexpr int W = S::W, ROWB = S::ROWB, NCH = S::NCH, TILE = S::TILE, STAGES = S::STAGES;
   constexpr int DPW = S::DMA_PER_WAVE, KS = S::KS, CB = S::CB, TB = S::TILE_BYTES;
   constexpr bool BF16 = sizeof(T) == 2;
+  static_assert(!BF16 || (ROWB == 1152 && KS == 36 && CB == 16), "asm blocks are generated for 576-wide rows, r = 512");
   __shared__ __attribute__((aligned(1024))) char smem[STAGES * TB];
 
   const int lane = threadIdx.x & 63;
@@ -251,22 +286,33 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
 
   // DMA: wave instruction n of a tile fills LDS bytes [gi*1024, gi*1024 + 1024)
   // of the stage (gi = wave*DPW + n); lane l writes 16 bytes at gi*1024 + 16*l,
-  // which is physical chunk p = gi*64 + l = row t, swizzled slot p % NCH.  The
-  // per-lane (t, chunk) pairs are recomputed at each issue from an opaque copy
-  // of the lane id, so they do not occupy registers across the loop.
+  // which is physical chunk p = gi*64 + l = row t, swizzled slot p % NCH.  A
+  // full tile is 32 consecutive cache rows, so the source is the tile base plus
+  // 16 * (p ^ swz(t)) (the swizzle only flips the low 3 bits, and NCH % 8 == 0);
+  // only the last, partial tile clamps its rows.  Offsets are recomputed at
+  // each issue from an opaque copy of the lane id so they do not stay live.
   auto issue_tile = [&](int tile, int stage) {
     const int rel0 = tile * TILE;
     LDS_AS char* dst = (LDS_AS char*)smem + stage * TB + wave * DPW * 1024;
     int ln = lane;
     asm volatile("" : "+v"(ln));
+    if (rel0 + TILE - 1 <= last_rel) {
+      const char* tbase = split_base + (int64_t)rel0 * ROWB;
 #pragma unroll
-    for (int n = 0; n < DPW; ++n) {
-      const int p = (wave * DPW + n) * 64 + ln;
-      const int t = p / NCH;
-      const int c = swz_chunk<NCH>(t, p - t * NCH);
-      const int rel = min(rel0 + t, last_rel);
-      const char* src = split_base + (int64_t)rel * ROWB + c * 16;
-      __builtin_amdgcn_global_load_lds(src, dst + n * 1024, 16, 0, 0);
+      for (int n = 0; n < DPW; ++n) {
+        const int p = (wave * DPW + n) * 64 + ln;
+        const uint32_t off = (uint32_t)(16 * (p ^ swz_chunk<NCH>(p / NCH, 0)));
+        __builtin_amdgcn_global_load_lds(tbase + off, dst + n * 1024, 16, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int n = 0; n < DPW; ++n) {
+        const int p = (wave * DPW + n) * 64 + ln;
+        const int t = p / NCH;
+        const int rel = min(rel0 + t, last_rel);
+        const char* src = split_base + (int64_t)rel * ROWB + 16 * swz_chunk<NCH>(t, p - t * NCH);
+        __builtin_amdgcn_global_load_lds(src, dst + n * 1024, 16, 0, 0);
+      }
     }
   };
 
@@ -296,6 +342,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
   // Transpose reads: the swizzle of rows 16*ks + 8*sel + 4*hf + j does not
   // depend on (ks, sel), and logical chunk 4*cb + 2*cg + q/2 needs only the
   // parity of cb, so two bases cover all 2*CB*2 reads.
+  const int lds_base = (int)(uintptr_t)((LDS_AS char*)smem);  // byte address of the ring in LDS
   int s_base[4];
   int tr_base[2];
   if constexpr (BF16) {
@@ -327,6 +374,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
   for (int pass = 0;; ++pass) {
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) o[cb] = zero16();
+    if constexpr (BF16) acc_fence(o);
     l_sum = 0.f;
     if (pass > 0) {
 #pragma unroll
@@ -349,43 +397,75 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
       ++step;
 
       // scores S^T[t][h]: lane row t = l32 of the A operand
-      f32x16 sacc = zero16();
+      f32x16 sacc;
+      if constexpr (BF16) {
+        const int sb0 = lds_base + stage_off + s_base[0], sb1 = lds_base + stage_off + s_base[1];
+        const int sb2 = lds_base + stage_off + s_base[2], sb3 = lds_base + stage_off + s_base[3];
+        asm volatile(MLA_ASM_SCORE_BLOCK0
+                     : [acc] "=&v"(sacc)
+                     : [q0] "v"(qf[0]), [q1] "v"(qf[1]), [q2] "v"(qf[2]), [q3] "v"(qf[3]), [q4] "v"(qf[4]),
+                       [q5] "v"(qf[5]), [q6] "v"(qf[6]), [q7] "v"(qf[7]), [q8] "v"(qf[8]), [q9] "v"(qf[9]),
+                       [q10] "v"(qf[10]), [q11] "v"(qf[11]), [q12] "v"(qf[12]), [q13] "v"(qf[13]),
+                       [q14] "v"(qf[14]), [q15] "v"(qf[15]), [q16] "v"(qf[16]), [q17] "v"(qf[17]),
+                       [b0] "v"(sb0), [b1] "v"(sb1), [b2] "v"(sb2), [b3] "v"(sb3)
+                     : "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", "v248", "v249", "v250",
+                       "v251", "v252", "v253", "v254", "v255", "memory");  // keeps the tile DMA issue above
+        asm volatile(MLA_ASM_SCORE_BLOCK1
+                     : [acc] "+v"(sacc)
+                     : [q0] "v"(qf[18]), [q1] "v"(qf[19]), [q2] "v"(qf[20]), [q3] "v"(qf[21]), [q4] "v"(qf[22]),
+                       [q5] "v"(qf[23]), [q6] "v"(qf[24]), [q7] "v"(qf[25]), [q8] "v"(qf[26]), [q9] "v"(qf[27]),
+                       [q10] "v"(qf[28]), [q11] "v"(qf[29]), [q12] "v"(qf[30]), [q13] "v"(qf[31]),
+                       [q14] "v"(qf[32]), [q15] "v"(qf[33]), [q16] "v"(qf[34]), [q17] "v"(qf[35]),
+                       [b0] "v"(sb0), [b1] "v"(sb1), [b2] "v"(sb2), [b3] "v"(sb3)
+                     : "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", "v248", "v249", "v250",
+                       "v251", "v252", "v253", "v254", "v255");
+      } else {
+        sacc = zero16();
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
-        typename M::Frag a;
-        if constexpr (BF16) {
-          a = *(const i16x8*)(tile + s_base[kk & 3] + 128 * (kk >> 2));
-        } else {
-          a = *(const float*)(tile + tile_off<ROWB, NCH>(l32, (kk * 2 + hf) * 4));
-        }
-        sacc = M::mma(a, qf[kk], sacc);
-        if constexpr (BF16) {
-          if ((kk & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+        for (int kk = 0; kk < KS; ++kk) {
+          const float a = *(const float*)(tile + tile_off<ROWB, NCH>(l32, (kk * 2 + hf) * 4));
+          sacc = M::mma(a, qf[kk], sacc);
         }
       }
 
-      // softmax weights (log2 domain) in place; head = this lane's column
+      // softmax weights (log2 domain) in place; head = this lane's column.
+      // Rows past the split end exist only in its last tile.
       const int valid = r1 - (r0 + it * TILE);
-      float mx = -INFINITY;
+      if (valid < TILE) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int t = 8 * (r >> 2) + 4 * hf + (r & 3);
-        sacc[r] = t < valid ? sacc[r] * scale_log2 : -INFINITY;
-        mx = fmaxf(mx, sacc[r]);
+        for (int r = 0; r < 16; ++r) {
+          const int t = 8 * (r >> 2) + 4 * hf + (r & 3);
+          if (t >= valid) sacc[r] = -INFINITY;
+        }
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      float mx = sacc[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
+      mx = fmaxf(mx, xor32(mx, [](float a, float b) { return fmaxf(a, b); })) * scale_log2;
       m_seen = fmaxf(m_seen, mx);
       if (pass == 1) continue;  // max scan only
       if (m_ref == -INFINITY) m_ref = mx;
       if (pass == 0 && __any(mx > m_ref + kRefSlack)) {
         if (lane == 0) redo_stamp[(step - 1) & 1] = step - 1;
       }
+      // p = 2^(s*scale - ref).  In a pass that overflows (a score above
+      // ref + kRefSlack) p may be huge or infinite; that pass is discarded.
+      if constexpr (BF16) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pr = __builtin_amdgcn_exp2f(fminf(sacc[r] - m_ref, kRefSlack));
-        if constexpr (BF16) pr = round_bf16_finite(pr);  // the weight P*V will see
-        sacc[r] = pr;
-        l_sum += pr;
+        for (int r = 0; r < 16; r += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[r], scale_log2, -m_ref));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[r + 1], scale_log2, -m_ref));
+          const uint32_t h = cvt_pk_bf16(p0, p1);  // the weights P*V will see
+          sacc[r] = __uint_as_float(h << 16);
+          sacc[r + 1] = __uint_as_float(h & 0xffff0000u);
+          l_sum += sacc[r] + sacc[r + 1];
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          sacc[r] = __builtin_amdgcn_exp2f(fmaf(sacc[r], scale_log2, -m_ref));
+          l_sum += sacc[r];
+        }
       }
       const f32x16& p = sacc;
 
@@ -400,18 +480,16 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
                                                    pack_hi16(p[8 * ks + 4], p[8 * ks + 5]),
                                                    pack_hi16(p[8 * ks + 6], p[8 * ks + 7])});
         }
-        LDS_AS char* tl = (LDS_AS char*)tile;
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            const int off = tr_base[cb & 1] + 128 * (cb >> 1) + 16 * ks * ROWB;
-            i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(tl + off));
-            i16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(tl + off + 8 * ROWB));
-            o[cb] = M::mma(__builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7), pf[ks], o[cb]);
-          }
-          if ((cb & 1) == 1) __builtin_amdgcn_sched_barrier(0);
-        }
+        const int tb0 = lds_base + stage_off + tr_base[0], tb1 = lds_base + stage_off + tr_base[1];
+        asm volatile(MLA_ASM_PV_BLOCK
+                     : [o0] "+a"(o[0]), [o1] "+a"(o[1]), [o2] "+a"(o[2]), [o3] "+a"(o[3]), [o4] "+a"(o[4]),
+                       [o5] "+a"(o[5]), [o6] "+a"(o[6]), [o7] "+a"(o[7]), [o8] "+a"(o[8]), [o9] "+a"(o[9]),
+                       [o10] "+a"(o[10]), [o11] "+a"(o[11]), [o12] "+a"(o[12]), [o13] "+a"(o[13]),
+                       [o14] "+a"(o[14]), [o15] "+a"(o[15])
+                     : [p0] "v"(pf[0]), [p1] "v"(pf[1]), [t0] "v"(tb0), [t1] "v"(tb1)
+                     : "v224", "v225", "v226", "v227", "v228", "v229", "v230", "v231", "v232", "v233", "v234",
+                       "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244", "v245",
+                       "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255");
       } else {
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
@@ -424,6 +502,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
         }
       }
     }
+    if constexpr (BF16) acc_fence(o);  // last MFMA -> readout / re-zeroing
     if (pass == 0 && !redo) {  // the last tile may have overflowed too
       wait_vm_then_barrier<0>();
       redo = redo_stamp[(step - 1) & 1] == step - 1;
@@ -434,7 +513,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
     if (pass == 1) m_ref = m_seen;  // exact max of the split: p <= 1 in the final pass
   }
 
-  const float l_tot = l_sum + __shfl_xor(l_sum, 32);
+  const float l_tot = xor32(l_sum, [](float a, float b) { return a + b; });
   if (head_ok) {
     const float inv = 1.f / l_tot;
     float* op = o_part + (((int64_t)b * num_splits + s) * H + head) * R;

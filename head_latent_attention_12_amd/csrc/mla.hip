@@ -5,7 +5,7 @@
 //   rope_append_kernel    RoPE(q_rope), append [c_kv_new | RoPE(k_rope_new)]
 //   decode_latent_kernel  split-KV flash decode over the latent cache (32x32 MFMA)
 //   combine_kernel        log-sum-exp merge of the splits
-//   up_v_kernel           out = W_UV o_lat                   (32x32 MFMA)
+//   up_v_*_kernel         out = W_UV o_lat                   (32x32 MFMA)
 //
 // Sources (page title, section): "DeepSeek MLA, Built From the Paper" section 3
 // (absorption identity) and section 2 (decoupled RoPE key shared by the heads);
@@ -530,38 +530,70 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// K4: merge the splits.  One thread owns 4 consecutive latent columns of one
-// (b, h); R/4 threads per head.
+// K4: merge the splits.  One work-group per (b, h) row: R/4 threads cover the
+// row (4 columns each) and 256/(R/4) split groups take every SG-th split; the
+// groups' weighted sums are added through LDS.  Split weights come from the
+// log-sum-exps, read first (they are small).
 // ---------------------------------------------------------------------------
 
 template <int R>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ o_part,
                                                       const float* __restrict__ lse_part, int num_splits,
-                                                      int H, int BH, float* __restrict__ o_lat,
-                                                      float* __restrict__ lse_out) {
-  constexpr int TPH = R / 4;
-  constexpr int HPB = 256 / TPH;
+                                                      int H, float* __restrict__ o_lat, float* __restrict__ lse_out) {
+  constexpr int TPH = R / 4;        // threads across the row
+  constexpr int SG = 256 / TPH;     // split groups
+  constexpr int U = 4;              // splits in flight per thread
   static_assert(TPH <= 256 && 256 % TPH == 0, "R");
-  const int bh = blockIdx.x * HPB + (int)threadIdx.x / TPH;
-  if (bh >= BH) return;
+  __shared__ f32x4 part[SG][TPH];
+  __shared__ float wpart[SG];
+  const int bh = blockIdx.x;
   const int b = bh / H, h = bh - b * H;
   const int c = ((int)threadIdx.x % TPH) * 4;
+  const int sg = (int)threadIdx.x / TPH;
   const float* lp = lse_part + (int64_t)b * num_splits * H + h;
   float m = -INFINITY;
   for (int s = 0; s < num_splits; ++s) m = fmaxf(m, lp[(int64_t)s * H]);
+  const float* op = o_part + ((int64_t)b * num_splits * H + h) * R + c;
+  const int64_t sstride = (int64_t)H * R;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
-  for (int s = 0; s < num_splits; ++s) {
+  int s = sg;
+  for (; s + (U - 1) * SG < num_splits; s += U * SG) {
+    float l[U];
+    f32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) l[u] = lp[(int64_t)(s + u * SG) * H];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = *(const f32x4*)(op + (s + u * SG) * sstride);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (l[u] == -INFINITY) continue;  // empty split: its o_part was never written
+      const float w = __expf(l[u] - m);
+      wsum += w;
+      acc += w * v[u];
+    }
+  }
+  for (; s < num_splits; s += SG) {
     const float l = lp[(int64_t)s * H];
     if (l == -INFINITY) continue;
     const float w = __expf(l - m);
     wsum += w;
-    const f32x4 v = *(const f32x4*)(o_part + (((int64_t)b * num_splits + s) * H + h) * R + c);
-    acc += w * v;
+    acc += w * *(const f32x4*)(op + s * sstride);
   }
-  const float inv = 1.f / wsum;
-  *(f32x4*)(o_lat + (int64_t)bh * R + c) = acc * inv;
-  if (lse_out != nullptr && c == 0) lse_out[bh] = m + __logf(wsum);
+  part[sg][threadIdx.x % TPH] = acc;
+  if (threadIdx.x % TPH == 0) wpart[sg] = wsum;
+  __syncthreads();
+  if (sg == 0) {
+    f32x4 tot = part[0][threadIdx.x];
+    float wt = wpart[0];
+#pragma unroll
+    for (int g = 1; g < SG; ++g) {
+      tot += part[g][threadIdx.x];
+      wt += wpart[g];
+    }
+    *(f32x4*)(o_lat + (int64_t)bh * R + c) = tot * (1.f / wt);
+    if (lse_out != nullptr && c == 0) lse_out[bh] = m + __logf(wt);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -609,18 +641,25 @@ __global__ __launch_bounds__(NW * 64) void absorb_q_kernel(const T* __restrict__
     const int bb = b0 + l32;
     const bool bok = bb < B;
     const T* qrow = q_nope + ((int64_t)(bok ? bb : 0) * H + h) * DH;
+    typename M::Frag bq[KS];  // loaded before the MFMA chain
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      if constexpr (ES == 2) {
+        bq[kk] = *(const i16x8*)(qrow + 16 * kk + 8 * hf);
+      } else {
+        bq[kk] = qrow[2 * kk + hf];
+      }
+    }
     f32x16 acc = zero16();
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-      typename M::Frag bq;
+      typename M::Frag b = bq[kk];
       if constexpr (ES == 2) {
-        i16x8 v = *(const i16x8*)(qrow + 16 * kk + 8 * hf);
-        bq = bok ? v : i16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        if (!bok) b = i16x8{0, 0, 0, 0, 0, 0, 0, 0};
       } else {
-        float v = qrow[2 * kk + hf];
-        bq = bok ? v : 0.f;
+        if (!bok) b = 0.f;
       }
-      acc = M::mma(af[kk], bq, acc);
+      acc = M::mma(af[kk], b, acc);
     }
     if (bok) {
       T* dst = q_lat + ((int64_t)bb * H + h) * W + jw;
@@ -639,62 +678,93 @@ __global__ __launch_bounds__(NW * 64) void absorb_q_kernel(const T* __restrict__
 }
 
 // ---------------------------------------------------------------------------
-// K5: out^T[d][b] = sum_j W_UV[h][d][j] o_lat[b][h][j].  One wave per
-// (head, 32 output rows); W_UV rows are read straight from HBM, each lane
-// taking 64 contiguous bytes per 4 MFMA steps.  With bf16 weights the fp32
-// o_lat enters as hi + lo bf16 parts (two MFMAs per step).
+// K5: out^T[d][b] = sum_j W_UV[h][d][j] o_lat[b][h][j].
+// bf16: one work-group per (head, 32 output rows); its 4 waves split the
+// j range, issue all their weight loads up front (each lane 64 contiguous
+// bytes per 4 MFMA steps), and sum their 32x32 partial tiles through LDS, each
+// wave finishing one quarter of the rows.  The fp32 o_lat enters as hi + lo
+// bf16 parts (two MFMAs per step), keeping it exact to about 2^-16.
+// fp32: one wave per (head, 32 rows), fp32 MFMA over the whole j range.
 // ---------------------------------------------------------------------------
 
-template <typename T, int NW>
-__global__ __launch_bounds__(NW * 64) void up_v_kernel(const float* __restrict__ o_lat, const T* __restrict__ w_uv,
-                                                       int B, int H, int DV, int R, float* __restrict__ out) {
-  using M = Mma<T>;
-  constexpr int ES = (int)sizeof(T);
+template <int R>
+__global__ __launch_bounds__(256) void up_v_bf16_kernel(const float* __restrict__ o_lat, const u16* __restrict__ w_uv,
+                                                        int B, int H, int DV, float* __restrict__ out) {
+  using M = Mma<u16>;
+  constexpr int JW = R / 4;        // j range of one wave
+  constexpr int G4 = JW / 64;      // groups of 4 MFMA steps
+  static_assert(R % 256 == 0, "R");
+  __shared__ f32x4 red[4][4][64];  // [wave][row quarter][lane]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int hf = lane >> 5, l32 = lane & 31;
-  const int nblk = (DV + 32 * NW - 1) / (32 * NW);
+  const int nblk = DV / 32;
   const int h = blockIdx.x / nblk;
-  const int d0 = (blockIdx.x - h * nblk) * 32 * NW + wave * 32;
-  if (d0 >= DV) return;
-  const T* wrow = w_uv + ((int64_t)h * DV + d0 + l32) * R;
+  const int d0 = (blockIdx.x - h * nblk) * 32;
+  const int jw = wave * JW;
+  const u16* wrow = w_uv + ((int64_t)h * DV + d0 + l32) * R + jw;
+  i16x8 a[G4][4];
+#pragma unroll
+  for (int g = 0; g < G4; ++g)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) a[g][u] = *(const i16x8*)(wrow + 64 * g + 32 * hf + 8 * u);
+  for (int b0 = 0; b0 < B; b0 += 32) {
+    const int bb = b0 + l32;
+    const bool bok = bb < B;
+    const float* orow = o_lat + ((int64_t)(bok ? bb : 0) * H + h) * R + jw;
+    f32x4 xs[G4][4][2];  // all of this lane's o_lat values, loaded before the MFMA chain
+#pragma unroll
+    for (int g = 0; g < G4; ++g)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < 2; ++v) xs[g][u][v] = *(const f32x4*)(orow + 64 * g + 32 * hf + 8 * u + 4 * v);
+    f32x16 acc = zero16();
+#pragma unroll
+    for (int g = 0; g < G4; ++g) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        f32x4 x0 = xs[g][u][0], x1 = xs[g][u][1];
+        if (!bok) { x0 = f32x4{0, 0, 0, 0}; x1 = x0; }
+        const float xv[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          hi[e] = cvt_pk_bf16(xv[2 * e], xv[2 * e + 1]);
+          lo[e] = cvt_pk_bf16(xv[2 * e] - __uint_as_float(hi[e] << 16),
+                              xv[2 * e + 1] - __uint_as_float(hi[e] & 0xffff0000u));
+        }
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        acc = M::mma(a[g][u], __builtin_bit_cast(i16x8, u32x4{hi[0], hi[1], hi[2], hi[3]}), acc);
+        acc = M::mma(a[g][u], __builtin_bit_cast(i16x8, u32x4{lo[0], lo[1], lo[2], lo[3]}), acc);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) red[wave][q][lane] = f32x4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+    __syncthreads();
+    // wave w sums row quarter q = w (rows 8w + 4hf + 0..3 of the 32-row block)
+    f32x4 sum = red[0][wave][lane] + red[1][wave][lane] + red[2][wave][lane] + red[3][wave][lane];
+    if (bok) *(f32x4*)(out + ((int64_t)bb * H + h) * DV + d0 + 8 * wave + 4 * hf) = sum;
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(64) void up_v_f32_kernel(const float* __restrict__ o_lat, const float* __restrict__ w_uv,
+                                                      int B, int H, int DV, int R, float* __restrict__ out) {
+  using M = Mma<float>;
+  const int lane = threadIdx.x & 63;
+  const int hf = lane >> 5, l32 = lane & 31;
+  const int nblk = DV / 32;
+  const int h = blockIdx.x / nblk;
+  const int d0 = (blockIdx.x - h * nblk) * 32;
+  const float* wrow = w_uv + ((int64_t)h * DV + d0 + l32) * R;
   for (int b0 = 0; b0 < B; b0 += 32) {
     const int bb = b0 + l32;
     const bool bok = bb < B;
     const float* orow = o_lat + ((int64_t)(bok ? bb : 0) * H + h) * R;
     f32x16 acc = zero16();
-    if constexpr (ES == 2) {
-      // per group of 4 steps a lane covers j in [64*g + 32*hf, 64*g + 32*hf + 32)
-      for (int g = 0; g < R / 64; ++g) {
-        const int jb = 64 * g + 32 * hf;
-        i16x8 a4[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) a4[u] = *(const i16x8*)(wrow + jb + 8 * u);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          f32x4 x0 = *(const f32x4*)(orow + jb + 8 * u);
-          f32x4 x1 = *(const f32x4*)(orow + jb + 8 * u + 4);
-          if (!bok) { x0 = f32x4{0, 0, 0, 0}; x1 = x0; }
-          float xv[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-          uint32_t hi[4], lo[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const u16 h0 = f2bf(xv[2 * e]), h1 = f2bf(xv[2 * e + 1]);
-            hi[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-            lo[e] = pack2bf(xv[2 * e] - bf2f(h0), xv[2 * e + 1] - bf2f(h1));
-          }
-          typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-          const i16x8 bh = __builtin_bit_cast(i16x8, u32x4{hi[0], hi[1], hi[2], hi[3]});
-          const i16x8 bl = __builtin_bit_cast(i16x8, u32x4{lo[0], lo[1], lo[2], lo[3]});
-          acc = M::mma(a4[u], bh, acc);
-          acc = M::mma(a4[u], bl, acc);
-        }
-      }
-    } else {
-      for (int kk = 0; kk < R / 2; ++kk) {
-        const float a = wrow[2 * kk + hf];
-        const float x = bok ? orow[2 * kk + hf] : 0.f;
-        acc = M::mma(a, x, acc);
-      }
+    for (int kk = 0; kk < R / 2; ++kk) {
+      const float x = bok ? orow[2 * kk + hf] : 0.f;
+      acc = M::mma(wrow[2 * kk + hf], x, acc);
     }
     if (bok) {
       float* dst = out + ((int64_t)bb * H + h) * DV + d0;
@@ -707,30 +777,48 @@ __global__ __launch_bounds__(NW * 64) void up_v_kernel(const float* __restrict__
 
 // ---------------------------------------------------------------------------
 // K2: RoPE on q_rope and on the new token's shared key; append the new row.
-// Angles, rotations and the final rounding are done in double precision.
+// One work-group per (sequence, block of 16 heads); the work-group of head
+// block 0 also writes the cache row.  Pair frequencies come from the host (in
+// double); each angle pos * theta_i is reduced modulo 2*pi in double (two-
+// part constant) before sincos, and rotations and the final rounding are done
+// in double precision.
 // ---------------------------------------------------------------------------
+
+struct RopeFreqs {
+  double theta[256];  // theta_i = base^(-2i/d_rope), i < d_rope/2
+};
+
+__device__ __forceinline__ void sincos_reduced(double ang, double* s, double* c) {
+  // 2*pi = P1 + P2 (P1 the double nearest 2*pi); fma keeps each k*Pn exact
+  // inside its subtraction, so |r| <= pi with an error of a few 1e-16
+  constexpr double kInv2Pi = 0.15915494309189533577;
+  constexpr double P1 = 6.28318530717958623200e+00;
+  constexpr double P2 = 2.44929359829470635445e-16;
+  const double k = rint(ang * kInv2Pi);
+  double r = fma(-k, P1, ang);
+  r = fma(-k, P2, r);
+  sincos(r, s, c);
+}
 
 template <typename T>
 __global__ __launch_bounds__(256) void rope_append_kernel(const T* __restrict__ q_rope, const T* __restrict__ c_kv_new,
                                                           const T* __restrict__ k_rope_new,
                                                           const int32_t* __restrict__ positions,
                                                           const int64_t* __restrict__ row_offsets, int64_t total_rows,
-                                                          int H, int R, int DR, double rope_base,
+                                                          int H, int R, int DR, RopeFreqs freqs,
                                                           T* __restrict__ q_lat, T* __restrict__ cache) {
   __shared__ double cs[2][256];
-  const int b = blockIdx.x;
+  const int hblocks = (H + 15) / 16;
+  const int b = blockIdx.x / hblocks;
+  const int hb = blockIdx.x - b * hblocks;
   const int pos = positions[b];
   const int half = DR / 2;
-  for (int i = threadIdx.x; i < half; i += blockDim.x) {
-    const double theta = pow(rope_base, -2.0 * (double)i / (double)DR);
-    const double ang = (double)pos * theta;
-    cs[0][i] = cos(ang);
-    cs[1][i] = sin(ang);
-  }
+  for (int i = threadIdx.x; i < half; i += blockDim.x) sincos_reduced((double)pos * freqs.theta[i], &cs[1][i], &cs[0][i]);
   __syncthreads();
   const int W = R + DR;
-  for (int idx = threadIdx.x; idx < H * half; idx += blockDim.x) {
-    const int hh = idx / half, i = idx - hh * half;
+  const int h0 = hb * 16, h1 = min(H, h0 + 16);
+  for (int idx = threadIdx.x; idx < (h1 - h0) * half; idx += blockDim.x) {
+    const int hh = h0 + idx / half, i = idx % half;
     const T* src = q_rope + ((int64_t)b * H + hh) * DR + 2 * i;
     const double x0 = load_d<T>(src[0]), x1 = load_d<T>(src[1]);
     const double c = cs[0][i], s = cs[1][i];
@@ -738,6 +826,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(const T* __restrict__ 
     dst[0] = store_d<T>(x0 * c - x1 * s);
     dst[1] = store_d<T>(x0 * s + x1 * c);
   }
+  if (hb != 0) return;
   int64_t row = row_offsets[b] + pos;
   row = row < 0 ? 0 : (row >= total_rows ? total_rows - 1 : row);
   T* crow = cache + row * W;
@@ -881,7 +970,7 @@ mla_status mla_absorb_q(const mla_dims* dims, const void* q_nope, const void* w_
   switch (find_inst(*dims)) {
     case kF32H8R64D16:
     case kF32H16R64D32: return launch_absorb_dh<float, 1>(*dims, q_nope, w_uk, q_lat, s);
-    case kBf16H128R512D64: return launch_absorb_dh<u16, 4>(*dims, q_nope, w_uk, q_lat, s);
+    case kBf16H128R512D64: return launch_absorb_dh<u16, 2>(*dims, q_nope, w_uk, q_lat, s);
   }
   return fail(MLA_ERR_UNSUPPORTED, "no instantiation");
 }
@@ -898,14 +987,17 @@ mla_status mla_rope_append(const mla_dims* dims, const void* q_rope, const void*
   g_last_error.clear();
   hipStream_t s = (hipStream_t)stream;
   const double base = dims->rope_base > 0.f ? (double)dims->rope_base : 10000.0;
+  RopeFreqs freqs;
+  for (int i = 0; i < dims->d_rope / 2; ++i) freqs.theta[i] = std::pow(base, -2.0 * (double)i / (double)dims->d_rope);
+  const int blocks = dims->batch * ((dims->heads + 15) / 16);
   if (dims->dtype == MLA_BF16) {
-    hipLaunchKernelGGL((rope_append_kernel<u16>), dim3(dims->batch), dim3(256), 0, s, (const u16*)q_rope,
+    hipLaunchKernelGGL((rope_append_kernel<u16>), dim3(blocks), dim3(256), 0, s, (const u16*)q_rope,
                        (const u16*)c_kv_new, (const u16*)k_rope_new, positions, row_offsets, total_rows,
-                       dims->heads, dims->rank, dims->d_rope, base, (u16*)q_lat, (u16*)kv_cache);
+                       dims->heads, dims->rank, dims->d_rope, freqs, (u16*)q_lat, (u16*)kv_cache);
   } else {
-    hipLaunchKernelGGL((rope_append_kernel<float>), dim3(dims->batch), dim3(256), 0, s, (const float*)q_rope,
+    hipLaunchKernelGGL((rope_append_kernel<float>), dim3(blocks), dim3(256), 0, s, (const float*)q_rope,
                        (const float*)c_kv_new, (const float*)k_rope_new, positions, row_offsets, total_rows,
-                       dims->heads, dims->rank, dims->d_rope, base, (float*)q_lat, (float*)kv_cache);
+                       dims->heads, dims->rank, dims->d_rope, freqs, (float*)q_lat, (float*)kv_cache);
   }
   return launch_result("mla_rope_append");
 }
@@ -948,12 +1040,12 @@ mla_status mla_combine(const mla_dims* dims, const float* o_part, const float* l
   const int BH = dims->batch * dims->heads;
   switch (dims->rank) {
     case 64:
-      hipLaunchKernelGGL((combine_kernel<64>), dim3((BH + 15) / 16), dim3(256), 0, s, o_part, lse_part, num_splits,
-                         dims->heads, BH, o_lat, lse);
+      hipLaunchKernelGGL((combine_kernel<64>), dim3(BH), dim3(256), 0, s, o_part, lse_part, num_splits, dims->heads,
+                         o_lat, lse);
       break;
     case 512:
-      hipLaunchKernelGGL((combine_kernel<512>), dim3((BH + 1) / 2), dim3(256), 0, s, o_part, lse_part, num_splits,
-                         dims->heads, BH, o_lat, lse);
+      hipLaunchKernelGGL((combine_kernel<512>), dim3(BH), dim3(256), 0, s, o_part, lse_part, num_splits, dims->heads,
+                         o_lat, lse);
       break;
     default: return fail(MLA_ERR_UNSUPPORTED, "rank");
   }
@@ -967,13 +1059,11 @@ mla_status mla_up_v(const mla_dims* dims, const float* o_lat, const void* w_uv, 
   g_last_error.clear();
   hipStream_t s = (hipStream_t)stream;
   if (dims->dtype == MLA_BF16) {
-    if (dims->rank % 64 != 0) return fail(MLA_ERR_UNSUPPORTED, "rank must be a multiple of 64 for bf16");
-    const int nblk = (dims->d_v + 127) / 128;
-    hipLaunchKernelGGL((up_v_kernel<u16, 4>), dim3(dims->heads * nblk), dim3(256), 0, s, o_lat, (const u16*)w_uv,
-                       dims->batch, dims->heads, dims->d_v, dims->rank, out);
+    if (dims->rank != 512) return fail(MLA_ERR_UNSUPPORTED, "bf16 up_v is built for rank 512");
+    hipLaunchKernelGGL((up_v_bf16_kernel<512>), dim3(dims->heads * (dims->d_v / 32)), dim3(256), 0, s, o_lat,
+                       (const u16*)w_uv, dims->batch, dims->heads, dims->d_v, out);
   } else {
-    const int nblk = (dims->d_v + 31) / 32;
-    hipLaunchKernelGGL((up_v_kernel<float, 1>), dim3(dims->heads * nblk), dim3(64), 0, s, o_lat,
+    hipLaunchKernelGGL(up_v_f32_kernel, dim3(dims->heads * (dims->d_v / 32)), dim3(64), 0, s, o_lat,
                        (const float*)w_uv, dims->batch, dims->heads, dims->d_v, dims->rank, out);
   }
   return launch_result("mla_up_v");

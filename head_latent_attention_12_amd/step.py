@@ -30,7 +30,11 @@ class DeviceStep:
     """Device buffers of one step and the five calls that compute it."""
 
     def __init__(self, inp: StepInputs, num_splits: int | None = None, device: str = "cuda:0",
-                 weights: "DeviceStep | None" = None):
+                 weights: "DeviceStep | None" = None, scratch: "DeviceStep | None" = None):
+        """``weights``: share W_UK/W_UV with another step (same layer).
+        ``scratch``: share the per-step temporaries (q_lat, split partials,
+        o_lat, lse, out) with another step of the same shape, as successive
+        layers of one decode step would."""
         self.inp = inp
         self.device = device
         self.dims = mla.make_dims(inp.B, inp.H, inp.d_head, inp.d_v, inp.r, inp.d_rope,
@@ -50,6 +54,10 @@ class DeviceStep:
         self.positions = _dev(inp.positions.astype(np.int32), device)
         self.row_offsets = _dev(inp.row_offsets.astype(np.int64), device)
         self.seq_lens = _dev(inp.seq_lens.astype(np.int32), device)
+        if scratch is not None:
+            self.q_lat, self.o_lat, self.lse, self.out = scratch.q_lat, scratch.o_lat, scratch.lse, scratch.out
+            self.num_splits, self.o_part, self.lse_part = scratch.num_splits, scratch.o_part, scratch.lse_part
+            return
         self.q_lat = torch.zeros((inp.B, inp.H, inp.W), dtype=st, device=device)
         self.set_splits(num_splits)
         self.o_lat = torch.empty((inp.B, inp.H, inp.r), dtype=torch.float32, device=device)

@@ -3,29 +3,42 @@
     python gen_decode_asm.py > decode_asm.inc
 
 Shape: 32-row tiles of 576-wide bf16 cache rows (1152 bytes), 32 heads per
-wave, 512 latent columns.  Two kinds of blocks:
+wave, 512 latent columns.  Blocks:
 
   score block (18 k-steps): S^T[t][h] += cache[t][k..k+16) . q^T, A fragments
     streamed from LDS with ds_read_b128 through a 4-deep rolling window held in
     v[240:255]; B fragments (q) and the accumulator are asm operands.
-  P*V block (16 column blocks): O^T[c][h] += cache^T P^T; cache^T fragments
-    from ds_read_b64_tr_b16 in groups of 4 fragments (2 column blocks x 2
-    k-halves), double-buffered in v[224:255]; accumulators are AGPR operands.
+  fused block: the scores of the next tile (36 k-steps into v[208:223]), then
+    the P*V product of the current tile, O^T[c][h] += cache^T P^T (16 column
+    blocks x 2 k-halves; cache^T fragments from pairs of ds_read_b64_tr_b16
+    through the same kind of 4-deep rolling window; accumulators are AGPR
+    operands), with the next tile's softmax (mask of rows past the split end,
+    tile max, exponentials, bf16 packing, running sum) interleaved between
+    the P*V MFMAs so that it runs while the matrix core is busy; the LDS DMA
+    of a later tile is spread over the score MFMAs.
 
 Every LDS read issued by a block is waited for inside that block, so no load
 is in flight when the asm statement ends.  The dependency rules observed in
 compiler output for gfx950 are followed: an MFMA may overwrite nothing its
 neighbours still read, an accumulation on the same destination may follow
-directly, and a VALU read of a 32x32x16 result needs at least 12 wait states
-(the score block ends with 20).
+directly, a VALU read of a 32x32x16 result needs at least 12 wait states
+(20 are given), a VALU read of a transcendental result needs one
+instruction in between, and v_permlane32_swap reads a VGPR written by a VALU
+op no sooner than two wait states later.
 """
 import sys
 
 ROWB = 1152          # bytes per cache row
 S_DEPTH = 4          # score-phase fragments in flight
+KS = 36              # k-steps of 16 over the 576-wide row
+SACC = 208           # first VGPR of the next tile's score accumulator (16 regs)
+TMP = 204            # softmax temporaries v204, v205
+VLIM = 206           # per-lane row limit of the mask, then a softmax temporary
+MFMA_TO_VALU = 20    # wait states between the last score MFMA and a VALU read of it
 
 
-def score_block(k0: int, steps: int, first: bool, last: bool) -> str:
+def _score_lines(k0, steps, first, acc, qname):
+    """LDS-fed score MFMAs for k-steps k0..k0+steps-1 (4 bases b0..b3)."""
     buf = [f"v[{240 + 4 * j}:{243 + 4 * j}]" for j in range(S_DEPTH)]
     out = ["s_waitcnt lgkmcnt(0)"]
 
@@ -38,45 +51,173 @@ def score_block(k0: int, steps: int, first: bool, last: bool) -> str:
     for j in range(steps):
         issued = min(steps, j + S_DEPTH)
         out.append(f"s_waitcnt lgkmcnt({issued - j - 1})")
-        src_c = "0" if (first and j == 0) else "%[acc]"
-        out.append(f"v_mfma_f32_32x32x16_bf16 %[acc], {buf[j % S_DEPTH]}, %[q{j}], {src_c}")
+        src_c = "0" if (first and j == 0) else acc
+        out.append(f"v_mfma_f32_32x32x16_bf16 {acc}, {buf[j % S_DEPTH]}, {qname(j)}, {src_c}")
         if j + S_DEPTH < steps:
             out.append(read(j + S_DEPTH))
+    return out
+
+
+def score_block(k0: int, steps: int, first: bool, last: bool) -> str:
+    out = _score_lines(k0, steps, first, "%[acc]", lambda j: f"%[q{j}]")
     if last:
         out += ["s_nop 15", "s_nop 3"]
     return "\\n\\t".join(out)
 
 
-def pv_block(cb_blocks: int = 16) -> str:
-    groups = cb_blocks // 2
+PV_FRAGS = [(2 * g + dc, ks) for g in range(8) for dc, ks in ((0, 0), (1, 0), (0, 1), (1, 1))]
+PV_DEPTH = 4         # P*V fragments in flight (rolling window v[240:255], as for the scores)
 
-    def frag_regs(buffer, f):
-        base = 224 + 16 * buffer + 4 * f
-        return base
 
-    def group_reads(g, buffer):
-        lines = []
-        for f, (dc, ks) in enumerate(((0, 0), (1, 0), (0, 1), (1, 1))):
-            cb = 2 * g + dc
-            r = frag_regs(buffer, f)
-            off = 128 * (cb >> 1) + 16 * ks * ROWB
-            lines.append(f"ds_read_b64_tr_b16 v[{r}:{r + 1}], %[t{cb & 1}] offset:{off}")
-            lines.append(f"ds_read_b64_tr_b16 v[{r + 2}:{r + 3}], %[t{cb & 1}] offset:{off + 8 * ROWB}")
-        return lines
+def _pv_reads(n):
+    """The two transpose reads of P*V fragment n (column block cb, k-half ks)
+    into window slot n % PV_DEPTH."""
+    cb, ks = PV_FRAGS[n]
+    r = 256 - 4 * PV_DEPTH + 4 * (n % PV_DEPTH)
+    off = 128 * (cb >> 1) + 16 * ks * ROWB
+    # rows 16*ks + j (base t0/t1) and 16*ks + 8 + j (base t2/t3: rows 8 on
+    # have their own swizzle), j = 4*(lane/32) + (lane%16)/4
+    return [f"ds_read_b64_tr_b16 v[{r}:{r + 1}], %[t{cb & 1}] offset:{off}",
+            f"ds_read_b64_tr_b16 v[{r + 2}:{r + 3}], %[t{2 + (cb & 1)}] offset:{off}"]
 
-    out = ["s_waitcnt lgkmcnt(0)"]
-    out += group_reads(0, 0)
-    for g in range(groups):
-        b = g & 1
-        if g + 1 < groups:
-            out += group_reads(g + 1, b ^ 1)
-            out.append("s_waitcnt lgkmcnt(8)")
-        else:
-            out.append("s_waitcnt lgkmcnt(0)")
-        for f, (dc, pk) in enumerate(((0, 0), (1, 0), (0, 1), (1, 1))):
-            cb = 2 * g + dc
-            r = frag_regs(b, f)
-            out.append(f"v_mfma_f32_32x32x16_bf16 %[o{cb}], v[{r}:{r + 3}], %[p{pk}], %[o{cb}]")
+
+def _pv_lines(valu=None, first_valu_after=0, prelude=None):
+    """P*V MFMAs over the 32 fragments (16 column blocks x 2 k-halves), fed
+    through a rolling window: the reads of fragment n + PV_DEPTH go into the
+    slot of fragment n right after its MFMA has been issued.  `valu` (list of
+    instructions) is spread between the MFMAs, starting once
+    `first_valu_after` wait states have passed since the block start;
+    `prelude` (a list of lines) is emitted whole at that point."""
+    valu = list(valu or [])
+    nfr = len(PV_FRAGS)
+    out = []
+    waited = 0  # wait states since the block start
+
+    def emit(line):
+        nonlocal waited
+        out.append(line)
+        waited += int(line.split()[1]) + 1 if line.startswith("s_nop") else 1
+
+    last_trans = [None]
+
+    def emit_valu(op):
+        # one instruction between a transcendental and a VALU read of its result
+        if last_trans[0] is not None and last_trans[0] in op.split(",", 1)[-1]:
+            emit("s_nop 0")
+        emit(op)
+        last_trans[0] = op.split()[1].rstrip(",") if op.startswith("v_exp_f32") else None
+
+    for n in range(min(PV_DEPTH, nfr)):
+        for line in _pv_reads(n):
+            emit(line)
+    per_slot = None
+    for n in range(nfr):
+        issued = min(nfr, n + PV_DEPTH)
+        emit(f"s_waitcnt lgkmcnt({2 * (issued - n - 1)})")
+        cb, ks = PV_FRAGS[n]
+        r = 256 - 4 * PV_DEPTH + 4 * (n % PV_DEPTH)
+        emit(f"v_mfma_f32_32x32x16_bf16 %[o{cb}], v[{r}:{r + 3}], %[p{ks}], %[o{cb}]")
+        last_trans[0] = None
+        if n + PV_DEPTH < nfr:
+            for line in _pv_reads(n + PV_DEPTH):
+                emit(line)
+        if valu:
+            if waited < first_valu_after:
+                emit(f"s_nop {first_valu_after - waited - 1}")
+            if prelude:
+                for line in prelude:
+                    emit(line)
+                prelude = None
+            if per_slot is None:
+                per_slot = -(-len(valu) // (nfr - n))
+            for _ in range(min(per_slot, len(valu))):
+                emit_valu(valu.pop(0))
+    while valu:  # (not reached with the shapes generated here)
+        emit_valu(valu.pop(0))
+    return out
+
+
+def _mask_block():
+    """Rows past the split end get -inf (only when %[valid] < 32, a tile that
+    is the split's last or past it): register r holds row c + 4*(lane/32) with
+    c = 8*(r/4) + r%4, valid iff c < %[valid] - 4*(lane/32)."""
+    s = [f"v{SACC + r}" for r in range(16)]
+    vl, ninf = f"v{VLIM}", f"v{TMP + 1}"
+    out = ["s_cmp_ge_i32 %[valid], 32", "s_cbranch_scc1 .Lmla_full_%=",
+           f"v_mbcnt_lo_u32_b32 {vl}, -1, 0", f"v_mbcnt_hi_u32_b32 {vl}, -1, {vl}",
+           f"v_bfe_u32 {vl}, {vl}, 5, 1", f"v_lshlrev_b32_e32 {vl}, 2, {vl}", f"v_sub_u32_e32 {vl}, %[valid], {vl}",
+           f"v_mov_b32_e32 {ninf}, 0xff800000"]  # -inf (a literal and vcc cannot share the bus)
+    for r in range(16):
+        c = 8 * (r // 4) + r % 4
+        out.append(f"v_cmp_lt_i32_e32 vcc, {c}, {vl}")
+        out.append(f"v_cndmask_b32_e32 {s[r]}, {ninf}, {s[r]}, vcc")
+    out.append(".Lmla_full_%=:")
+    return out
+
+
+def _softmax_ops():
+    """Softmax of the next tile on v[208:223] (accumulator register r holds
+    row 8*(r/4) + 4*(lane/32) + r%4 of the tile, head = lane%32):
+    outputs %[mx] (tile max per head, log2 units), %[w0..w7] (bf16 pairs of
+    2^(s*scale - mref)) and %[l] += the sum of those rounded weights.
+    Ordered so that no instruction waits on a recent result: two interleaved
+    max chains, the exponent arguments (in place, after the max has read the
+    scores), the exponentials, then the packing and the running sum."""
+    s = [f"v{SACC + r}" for r in range(16)]
+    m, m2, t = f"v{TMP}", f"v{TMP + 1}", f"v{VLIM}"
+
+    def fma(r):
+        return f"v_fma_f32 {s[r]}, {s[r]}, %[sc], -%[mref]"
+
+    ops = [f"v_max3_f32 {m}, {s[0]}, {s[1]}, {s[2]}", f"v_max3_f32 {m2}, {s[8]}, {s[9]}, {s[10]}",
+           f"v_max3_f32 {m}, {m}, {s[3]}, {s[4]}", f"v_max3_f32 {m2}, {m2}, {s[11]}, {s[12]}",
+           f"v_max3_f32 {m}, {m}, {s[5]}, {s[6]}", f"v_max3_f32 {m2}, {m2}, {s[13]}, {s[14]}",
+           f"v_max_f32_e32 {m}, {m}, {s[7]}", f"v_max_f32_e32 {m2}, {m2}, {s[15]}",
+           f"v_max_f32_e32 {m}, {m}, {m2}",
+           # max with lane ^ 32: swap the upper half of m with the lower half of
+           # a copy (two wait states after the VALU writes it reads)
+           f"v_mov_b32_e32 {t}, {m}", fma(0), fma(1),
+           f"v_permlane32_swap_b32_e32 {m}, {t}", fma(2),
+           f"v_max_f32_e32 {m}, {m}, {t}", fma(3),
+           f"v_mul_f32_e32 %[mx], %[sc], {m}"]
+    ops += [fma(r) for r in range(4, 16)]
+    ops += [f"v_exp_f32_e32 {s[r]}, {s[r]}" for r in range(16)]
+    # round pairs to bf16 (the weights P*V uses), then add them to the sum
+    ops += [f"v_cvt_pk_bf16_f32 %[w{j}], {s[2 * j]}, {s[2 * j + 1]}" for j in range(8)]
+    ops += [f"v_dot2c_f32_bf16_e32 %[l], 0x3f803f80, %[w{j}]" for j in range(8)]
+    return ops
+
+
+DMA_PER_WAVE = 9     # 16-byte-per-lane LDS DMA instructions per wave and tile
+
+
+def _dma_lines(n):
+    """LDS DMA n of a later tile (skipped when %[dma] = 0): lane l copies 16
+    bytes from %[tbase] + %[d<n>] to LDS %[ldst] + 1024*n + 16*l."""
+    return ["s_cmp_eq_u32 %[dma], 0", f"s_cbranch_scc1 .Lmla_nodma{n}_%=",
+            f"s_add_u32 m0, %[ldst], {1024 * n}", "s_nop 0",
+            f"global_load_lds_dwordx4 %[d{n}], %[tbase]", f".Lmla_nodma{n}_%=:"]
+
+
+def fused_block() -> str:
+    # %[nx] = 0 at the last tile of a split: no next tile, the scores are
+    # skipped and %[valid] = 0 masks every row, so the softmax part yields
+    # weights 0, sum += 0 and max = -inf.  The DMA of a later tile is spread
+    # over the score MFMAs so that its issue never queues up.
+    # m0 (which the DMA uses) is saved and restored: the compiler reserves it
+    out = ["s_mov_b32 %[m0save], m0", "s_waitcnt lgkmcnt(0)", "s_cmp_eq_u32 %[nx], 0", "s_cbranch_scc1 .Lmla_pv_%="]
+    score = _score_lines(0, KS, True, f"v[{SACC}:{SACC + 15}]", lambda j: f"%[q{j}]")
+    mfma_at = [k for k, line in enumerate(score) if line.startswith("v_mfma")]
+    after = {mfma_at[3 + 4 * n]: n for n in range(DMA_PER_WAVE)}
+    for k, line in enumerate(score):
+        out.append(line)
+        if k in after:
+            out += _dma_lines(after[k])
+    out.append(".Lmla_pv_%=:")
+    # P*V of the current tile; the first VALU read of the scores comes at
+    # least MFMA_TO_VALU wait states after the last score MFMA
+    out += _pv_lines(_softmax_ops(), MFMA_TO_VALU, _mask_block())
+    out.append("s_mov_b32 m0, %[m0save]")
     return "\\n\\t".join(out)
 
 
@@ -86,7 +227,7 @@ def main():
     w("// Inner blocks of the bf16 decode kernel (32-row tile, 32 heads per wave).\n\n")
     w(f'#define MLA_ASM_SCORE_BLOCK0 "{score_block(0, 18, True, False)}"\n\n')
     w(f'#define MLA_ASM_SCORE_BLOCK1 "{score_block(18, 18, False, True)}"\n\n')
-    w(f'#define MLA_ASM_PV_BLOCK "{pv_block()}"\n')
+    w(f'#define MLA_ASM_FUSED_BLOCK "{fused_block()}"\n')
 
 
 if __name__ == "__main__":

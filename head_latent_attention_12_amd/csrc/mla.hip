@@ -141,15 +141,19 @@ __device__ __forceinline__ f32x16 zero16() {
 
 // ---------------------------------------------------------------------------
 // Row-major LDS tiles with 16-byte chunks XOR-swizzled within groups of 8.
-// For rows t..t+7 the swizzle is a permutation of the chunk slots, so a b128
-// read of one chunk across 8 rows and a transpose read of 2 chunks across 4
-// aligned rows both touch distinct bank groups.
+// The LDS has 64 four-byte banks and serves a b128 read 16 lanes at a time;
+// a 1152-byte cache row is 288 banks, so odd rows start 32 banks later than
+// even ones.  Row t XORs its chunk slot with 4*((t>>1)&1) + ((t>>2)&3): the
+// 8 even and the 8 odd rows of a 16-row block then hold one logical chunk in
+// 8 distinct slots, so a b128 read of that chunk over 16 rows touches 16
+// distinct 4-bank groups, and a transpose read of 4 aligned chunks over 4
+// aligned rows (the two even rows differ in bit 2 of the XOR) does too.
 // ---------------------------------------------------------------------------
 
 template <int NCH>
 __device__ __forceinline__ int swz_chunk(int t, int c) {
   if constexpr (NCH % 8 == 0) {
-    return c ^ (((t & 3) << 1) | ((t >> 2) & 1));
+    return c ^ ((((t >> 1) & 1) << 2) | ((t >> 2) & 3));
   } else {
     return c;
   }
@@ -253,7 +257,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
   constexpr int W = S::W, ROWB = S::ROWB, NCH = S::NCH, TILE = S::TILE, STAGES = S::STAGES;
   constexpr int DPW = S::DMA_PER_WAVE, KS = S::KS, CB = S::CB, TB = S::TILE_BYTES;
   constexpr bool BF16 = sizeof(T) == 2;
-  static_assert(!BF16 || (ROWB == 1152 && KS == 36 && CB == 16), "asm blocks are generated for 576-wide rows, r = 512");
+  static_assert(!BF16 || (ROWB == 1152 && KS == 36 && CB == 16 && DPW == 9), "asm blocks are generated for 576-wide rows, r = 512, 4 waves");
   __shared__ __attribute__((aligned(1024))) char smem[STAGES * TB];
 
   const int lane = threadIdx.x & 63;
@@ -288,23 +292,33 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
   // of the stage (gi = wave*DPW + n); lane l writes 16 bytes at gi*1024 + 16*l,
   // which is physical chunk p = gi*64 + l = row t, swizzled slot p % NCH.  A
   // full tile is 32 consecutive cache rows, so the source is the tile base plus
-  // 16 * (p ^ swz(t)) (the swizzle only flips the low 3 bits, and NCH % 8 == 0);
-  // only the last, partial tile clamps its rows.  Offsets are recomputed at
-  // each issue from an opaque copy of the lane id so they do not stay live.
+  // 16 * (p ^ swz(t)) (the swizzle only flips the low 3 bits, and NCH % 8 == 0),
+  // the same lane offsets for every tile: they are computed once.  Only the
+  // last, partial tile clamps its rows.
+  uint32_t dma_off[DPW];
+#pragma unroll
+  for (int n = 0; n < DPW; ++n) {
+    const int p = (wave * DPW + n) * 64 + lane;
+    dma_off[n] = (uint32_t)(16 * (p ^ swz_chunk<NCH>(p / NCH, 0)));
+  }
+  // 32 consecutive 1152-byte rows at tbase into a stage
+  auto issue_rows = [&](const char* tbase, int stage) {
+    LDS_AS char* dst = (LDS_AS char*)smem + stage * TB + wave * DPW * 1024;
+#pragma unroll
+    for (int n = 0; n < DPW; ++n) {
+      uint32_t off = dma_off[n];
+      asm volatile("" : "+v"(off));  // keeps the 64-bit address sums from being hoisted out of the loop
+      __builtin_amdgcn_global_load_lds(tbase + off, dst + n * 1024, 16, 0, 0);
+    }
+  };
   auto issue_tile = [&](int tile, int stage) {
     const int rel0 = tile * TILE;
     LDS_AS char* dst = (LDS_AS char*)smem + stage * TB + wave * DPW * 1024;
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
     if (rel0 + TILE - 1 <= last_rel) {
-      const char* tbase = split_base + (int64_t)rel0 * ROWB;
-#pragma unroll
-      for (int n = 0; n < DPW; ++n) {
-        const int p = (wave * DPW + n) * 64 + ln;
-        const uint32_t off = (uint32_t)(16 * (p ^ swz_chunk<NCH>(p / NCH, 0)));
-        __builtin_amdgcn_global_load_lds(tbase + off, dst + n * 1024, 16, 0, 0);
-      }
+      issue_rows(split_base + (int64_t)rel0 * ROWB, stage);
     } else {
+      int ln = lane;
+      asm volatile("" : "+v"(ln));  // recomputed here, not kept live
 #pragma unroll
       for (int n = 0; n < DPW; ++n) {
         const int p = (wave * DPW + n) * 64 + ln;
@@ -316,23 +330,16 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
     }
   };
 
+  typename M::Frag qf[KS];  // q_lat^T fragments (B operand of the score product), one head per lane
+  if constexpr (!BF16) {
 #pragma unroll
-  for (int k = 0; k < STAGES - 1; ++k)
-    if (k < ntiles) issue_tile(k, k);
-
-  // q_lat^T fragments (B operand of the score product), one head per lane.
-  typename M::Frag qf[KS];
-  {
+    for (int k = 0; k < STAGES - 1; ++k)
+      if (k < ntiles) issue_tile(k, k);
     const T* qrow = q_lat + ((int64_t)b * H + (head_ok ? head : 0)) * W;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-      if constexpr (BF16) {
-        i16x8 v = *(const i16x8*)(qrow + kk * 16 + hf * 8);
-        qf[kk] = head_ok ? v : i16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      } else {
-        float v = qrow[kk * 2 + hf];
-        qf[kk] = head_ok ? v : 0.f;
-      }
+      float v = qrow[kk * 2 + hf];
+      qf[kk] = head_ok ? v : 0.f;
     }
   }
 
@@ -340,35 +347,110 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
   // 2*kk + hf; the swizzle only permutes the low 3 bits, so chunk 8a + x sits at
   // 16*(8a + (x ^ swz)) and four bases (kk % 4) plus immediates cover all kk.
   // Transpose reads: the swizzle of rows 16*ks + 8*sel + 4*hf + j does not
-  // depend on (ks, sel), and logical chunk 4*cb + 2*cg + q/2 needs only the
-  // parity of cb, so two bases cover all 2*CB*2 reads.
+  // depend on ks, and logical chunk 4*cb + 2*cg + q/2 needs only the parity
+  // of cb, so four bases (sel, parity of cb) cover all 2*CB*2 reads.
   const int lds_base = (int)(uintptr_t)((LDS_AS char*)smem);  // byte address of the ring in LDS
   int s_base[4];
-  int tr_base[2];
+  int tr_base[4];
   if constexpr (BF16) {
     const int sw = swz_chunk<NCH>(l32, 0) ^ 0;  // swizzle value of row l32
 #pragma unroll
     for (int q = 0; q < 4; ++q) s_base[q] = l32 * ROWB + 16 * ((2 * q + hf) ^ sw);
     const int m = lane & 15, cg = (lane >> 4) & 1;
-    const int trow = 4 * hf + (m >> 2);
-    const int tsw = swz_chunk<NCH>(trow, 0);
 #pragma unroll
-    for (int par = 0; par < 2; ++par)
-      tr_base[par] = trow * ROWB + 16 * ((4 * par + 2 * cg + ((m & 3) >> 1)) ^ tsw) + 8 * (m & 1);
+    for (int sel = 0; sel < 2; ++sel) {
+      const int trow = 8 * sel + 4 * hf + (m >> 2);
+      const int tsw = swz_chunk<NCH>(trow, 0);
+#pragma unroll
+      for (int par = 0; par < 2; ++par)
+        tr_base[2 * sel + par] = trow * ROWB + 16 * ((4 * par + 2 * cg + ((m & 3) >> 1)) ^ tsw) + 8 * (m & 1);
+    }
   } else {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) s_base[q] = 0;
-    tr_base[0] = tr_base[1] = 0;
+    for (int q = 0; q < 4; ++q) s_base[q] = tr_base[q] = 0;
   }
 
-  __shared__ int redo_stamp[2];
+  if constexpr (BF16) {
+    // q_lat[b] is 128 rows of 1152 bytes, like four cache tiles: it is copied
+    // into the four stages with the tiles' coalesced DMA (heads 32g.. into
+    // stage g), each wave reads its 32 heads' fragments with the score-phase
+    // addressing, and only then do the first tiles overwrite the ring.
+    static_assert(H == STAGES * 32 && W * S::ES == ROWB, "q_lat of one sequence fills the ring");
+    const char* qbase = (const char*)(q_lat + (int64_t)b * H * W);
+#pragma unroll
+    for (int g = 0; g < STAGES; ++g) issue_rows(qbase + (int64_t)g * TB, g);
+    wait_vm_then_barrier<0>();
+    const char* mine = smem + wave * TB;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) qf[kk] = *(const i16x8*)(mine + s_base[kk & 3] + 128 * (kk >> 2));
+    wait_vm_then_barrier<0>();  // every wave holds its fragments: the ring is free
+#pragma unroll
+    for (int k = 0; k < STAGES - 1; ++k)
+      if (k < ntiles) issue_tile(k, k);
+  }
+
+  __shared__ int redo_stamp[2];  // fp32 path: iteration stamp of an overflowed tile
+  __shared__ int redo_flag;      // bf16 path: some wave overflowed in pass 0
   if (threadIdx.x < 2) redo_stamp[threadIdx.x] = -1;  // ordered by the first barrier below
+  if (threadIdx.x == 0) redo_flag = 0;
 
   f32x16 o[CB];
   float m_ref = -INFINITY;   // exponent reference of this lane's head (log2 units)
   float m_seen = -INFINITY;  // largest score seen so far
   float l_sum = 0.f;
-  int step = 0;              // block-uniform iteration stamp, never reused
+
+  // scores S^T[t][h] of the tile in a stage: lane row t = l32 of the A operand
+  auto score_tile = [&](int stage_off) -> f32x16 {
+    f32x16 sacc;
+    if constexpr (BF16) {
+      const int sb0 = lds_base + stage_off + s_base[0], sb1 = lds_base + stage_off + s_base[1];
+      const int sb2 = lds_base + stage_off + s_base[2], sb3 = lds_base + stage_off + s_base[3];
+      asm volatile(MLA_ASM_SCORE_BLOCK0
+                   : [acc] "=&v"(sacc)
+                   : [q0] "v"(qf[0]), [q1] "v"(qf[1]), [q2] "v"(qf[2]), [q3] "v"(qf[3]), [q4] "v"(qf[4]),
+                     [q5] "v"(qf[5]), [q6] "v"(qf[6]), [q7] "v"(qf[7]), [q8] "v"(qf[8]), [q9] "v"(qf[9]),
+                     [q10] "v"(qf[10]), [q11] "v"(qf[11]), [q12] "v"(qf[12]), [q13] "v"(qf[13]),
+                     [q14] "v"(qf[14]), [q15] "v"(qf[15]), [q16] "v"(qf[16]), [q17] "v"(qf[17]),
+                     [b0] "v"(sb0), [b1] "v"(sb1), [b2] "v"(sb2), [b3] "v"(sb3)
+                   : "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", "v248", "v249", "v250",
+                     "v251", "v252", "v253", "v254", "v255", "memory");  // keeps the tile DMA issue above
+      asm volatile(MLA_ASM_SCORE_BLOCK1
+                   : [acc] "+v"(sacc)
+                   : [q0] "v"(qf[18]), [q1] "v"(qf[19]), [q2] "v"(qf[20]), [q3] "v"(qf[21]), [q4] "v"(qf[22]),
+                     [q5] "v"(qf[23]), [q6] "v"(qf[24]), [q7] "v"(qf[25]), [q8] "v"(qf[26]), [q9] "v"(qf[27]),
+                     [q10] "v"(qf[28]), [q11] "v"(qf[29]), [q12] "v"(qf[30]), [q13] "v"(qf[31]),
+                     [q14] "v"(qf[32]), [q15] "v"(qf[33]), [q16] "v"(qf[34]), [q17] "v"(qf[35]),
+                     [b0] "v"(sb0), [b1] "v"(sb1), [b2] "v"(sb2), [b3] "v"(sb3)
+                   : "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", "v248", "v249", "v250",
+                     "v251", "v252", "v253", "v254", "v255");
+    } else {
+      const char* tile = smem + stage_off;
+      sacc = zero16();
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        const float a = *(const float*)(tile + tile_off<ROWB, NCH>(l32, (kk * 2 + hf) * 4));
+        sacc = M::mma(a, qf[kk], sacc);
+      }
+    }
+    return sacc;
+  };
+
+  // Rows past the split end (only in its last tile) get -inf; returns the
+  // tile's max score of this lane's head in log2 units.
+  auto tile_max = [&](f32x16& sacc, int valid) -> float {
+    if (valid < TILE) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = 8 * (r >> 2) + 4 * hf + (r & 3);
+        if (t >= valid) sacc[r] = -INFINITY;
+      }
+    }
+    float mx = sacc[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
+    return fmaxf(mx, xor32(mx, [](float a, float c) { return fmaxf(a, c); })) * scale_log2;
+  };
+
   // pass 0: normal; pass 1: scores only, to get the exact max (after an
   // overflow); pass 2: final pass with that max as the reference
   for (int pass = 0;; ++pass) {
@@ -382,147 +464,176 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
         if (k < ntiles) issue_tile(k, k);
     }
     bool redo = false;
-    for (int it = 0; it < ntiles; ++it) {
-      const int ahead = min(STAGES - 2, ntiles - 1 - it);
-      if (ahead >= 2) wait_vm_then_barrier<2 * DPW>();
-      else if (ahead == 1) wait_vm_then_barrier<DPW>();
+    if (BF16 && pass != 1) {
+      // Software-pipelined tile loop.  Iteration i computes the scores of tile
+      // i+1 and then P*V of tile i, with the softmax of tile i+1 running on the
+      // VALU between the P*V MFMAs (one asm block).  Tile 0's scores and
+      // softmax come first.  A stage is refilled (tile i+3 into the stage of
+      // tile i-1) once every wave has passed the barrier of iteration i.  An
+      // overflow (pass 0) is only recorded; the pass runs to its end and the
+      // work-group then decides on a redo.
+      if (ntiles >= 3) wait_vm_then_barrier<2 * DPW>();
+      else if (ntiles == 2) wait_vm_then_barrier<DPW>();
       else wait_vm_then_barrier<0>();
-      if (pass == 0 && it > 0 && redo_stamp[(step - 1) & 1] == step - 1) {  // previous tile overflowed
-        redo = true;
-        break;
-      }
-      if (it + STAGES - 1 < ntiles) issue_tile(it + STAGES - 1, (it + STAGES - 1) % STAGES);
-      const int stage_off = (it % STAGES) * TB;
-      const char* tile = smem + stage_off;
-      ++step;
-
-      // scores S^T[t][h]: lane row t = l32 of the A operand
-      f32x16 sacc;
-      if constexpr (BF16) {
-        const int sb0 = lds_base + stage_off + s_base[0], sb1 = lds_base + stage_off + s_base[1];
-        const int sb2 = lds_base + stage_off + s_base[2], sb3 = lds_base + stage_off + s_base[3];
-        asm volatile(MLA_ASM_SCORE_BLOCK0
-                     : [acc] "=&v"(sacc)
-                     : [q0] "v"(qf[0]), [q1] "v"(qf[1]), [q2] "v"(qf[2]), [q3] "v"(qf[3]), [q4] "v"(qf[4]),
-                       [q5] "v"(qf[5]), [q6] "v"(qf[6]), [q7] "v"(qf[7]), [q8] "v"(qf[8]), [q9] "v"(qf[9]),
-                       [q10] "v"(qf[10]), [q11] "v"(qf[11]), [q12] "v"(qf[12]), [q13] "v"(qf[13]),
-                       [q14] "v"(qf[14]), [q15] "v"(qf[15]), [q16] "v"(qf[16]), [q17] "v"(qf[17]),
-                       [b0] "v"(sb0), [b1] "v"(sb1), [b2] "v"(sb2), [b3] "v"(sb3)
-                     : "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", "v248", "v249", "v250",
-                       "v251", "v252", "v253", "v254", "v255", "memory");  // keeps the tile DMA issue above
-        asm volatile(MLA_ASM_SCORE_BLOCK1
-                     : [acc] "+v"(sacc)
-                     : [q0] "v"(qf[18]), [q1] "v"(qf[19]), [q2] "v"(qf[20]), [q3] "v"(qf[21]), [q4] "v"(qf[22]),
-                       [q5] "v"(qf[23]), [q6] "v"(qf[24]), [q7] "v"(qf[25]), [q8] "v"(qf[26]), [q9] "v"(qf[27]),
-                       [q10] "v"(qf[28]), [q11] "v"(qf[29]), [q12] "v"(qf[30]), [q13] "v"(qf[31]),
-                       [q14] "v"(qf[32]), [q15] "v"(qf[33]), [q16] "v"(qf[34]), [q17] "v"(qf[35]),
-                       [b0] "v"(sb0), [b1] "v"(sb1), [b2] "v"(sb2), [b3] "v"(sb3)
-                     : "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", "v248", "v249", "v250",
-                       "v251", "v252", "v253", "v254", "v255");
-      } else {
-        sacc = zero16();
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-          const float a = *(const float*)(tile + tile_off<ROWB, NCH>(l32, (kk * 2 + hf) * 4));
-          sacc = M::mma(a, qf[kk], sacc);
-        }
-      }
-
-      // softmax weights (log2 domain) in place; head = this lane's column.
-      // Rows past the split end exist only in its last tile.
-      const int valid = r1 - (r0 + it * TILE);
-      if (valid < TILE) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int t = 8 * (r >> 2) + 4 * hf + (r & 3);
-          if (t >= valid) sacc[r] = -INFINITY;
-        }
-      }
-      float mx = sacc[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
-      mx = fmaxf(mx, xor32(mx, [](float a, float b) { return fmaxf(a, b); })) * scale_log2;
-      m_seen = fmaxf(m_seen, mx);
-      if (pass == 1) continue;  // max scan only
-      if (m_ref == -INFINITY) m_ref = mx;
-      if (pass == 0 && __any(mx > m_ref + kRefSlack)) {
-        if (lane == 0) redo_stamp[(step - 1) & 1] = step - 1;
-      }
-      // p = 2^(s*scale - ref).  In a pass that overflows (a score above
-      // ref + kRefSlack) p may be huge or infinite; that pass is discarded.
-      if constexpr (BF16) {
+      i16x8 pf[2];
+      bool ovf = false;  // wave-uniform: a score above m_ref + kRefSlack was seen
+      {
+        f32x16 sacc = score_tile(0);
+        const float mx = tile_max(sacc, r1 - r0);
+        if (m_ref == -INFINITY) m_ref = mx;
+        // p = 2^(s*scale - ref), rounded to the bf16 that P*V sees.  In a pass
+        // that overflows (a score above ref + kRefSlack) p may be huge or
+        // infinite; that pass is discarded.
+        uint32_t w[8];
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
           const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[r], scale_log2, -m_ref));
           const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[r + 1], scale_log2, -m_ref));
-          const uint32_t h = cvt_pk_bf16(p0, p1);  // the weights P*V will see
-          sacc[r] = __uint_as_float(h << 16);
-          sacc[r + 1] = __uint_as_float(h & 0xffff0000u);
-          l_sum += sacc[r] + sacc[r + 1];
+          w[r / 2] = cvt_pk_bf16(p0, p1);
+          l_sum += __uint_as_float(w[r / 2] << 16) + __uint_as_float(w[r / 2] & 0xffff0000u);
         }
-      } else {
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        pf[0] = __builtin_bit_cast(i16x8, u32x4{w[0], w[1], w[2], w[3]});
+        pf[1] = __builtin_bit_cast(i16x8, u32x4{w[4], w[5], w[6], w[7]});
+      }
+      for (int i = 0; i < ntiles; ++i) {
+        // tile i+1 has landed (tile i+2 may still be in flight) and every wave
+        // has finished iteration i-1
+        if (i + 2 < ntiles) wait_vm_then_barrier<DPW>();
+        else wait_vm_then_barrier<0>();
+        // tile i+3 into the stage of tile i-1: a full tile is copied by the
+        // asm block below (spread over its score MFMAs), a partial one here
+        const int t3 = i + STAGES - 1;
+        int dma = 0, ldst = 0;
+        uint64_t tbase = (uint64_t)split_base;
+        if (t3 < ntiles) {
+          if (t3 * TILE + TILE - 1 <= last_rel) {
+            dma = 1;
+            tbase += (uint64_t)t3 * TILE * ROWB;
+            ldst = lds_base + (t3 % STAGES) * TB + wave * DPW * 1024;
+          } else {
+            issue_tile(t3, t3 % STAGES);
+          }
+        }
+        dma = __builtin_amdgcn_readfirstlane(dma);
+        ldst = __builtin_amdgcn_readfirstlane(ldst);
+        // (readfirstlane returns int: each half goes through uint32_t so that
+        // the low half is not sign-extended into the high one)
+        const uint64_t tb_s = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(tbase >> 32)) << 32) |
+                              (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)tbase);
+        // iteration i: scores and softmax of tile i+1 (skipped at the last
+        // tile: nx = 0, every row masked, weights 0, max -inf), P*V of tile i
+        const int nx = __builtin_amdgcn_readfirstlane((i + 1 < ntiles) ? 1 : 0);
+        const int cur = lds_base + (i % STAGES) * TB;
+        const int nxt = lds_base + ((i + 1) % STAGES) * TB;
+        const int tb0 = cur + tr_base[0], tb1 = cur + tr_base[1], tb2 = cur + tr_base[2], tb3 = cur + tr_base[3];
+        const int sb0 = nxt + s_base[0], sb1 = nxt + s_base[1], sb2 = nxt + s_base[2], sb3 = nxt + s_base[3];
+        // rows of the next tile before the split end (the mask inside the block)
+        const int valid = __builtin_amdgcn_readfirstlane(nx ? r1 - (r0 + (i + 1) * TILE) : 0);
+        uint32_t w0, w1, w2, w3, w4, w5, w6, w7, m0save;
+        float mx;
+        asm volatile(MLA_ASM_FUSED_BLOCK
+                     : [o0] "+a"(o[0]), [o1] "+a"(o[1]), [o2] "+a"(o[2]), [o3] "+a"(o[3]), [o4] "+a"(o[4]),
+                       [o5] "+a"(o[5]), [o6] "+a"(o[6]), [o7] "+a"(o[7]), [o8] "+a"(o[8]), [o9] "+a"(o[9]),
+                       [o10] "+a"(o[10]), [o11] "+a"(o[11]), [o12] "+a"(o[12]), [o13] "+a"(o[13]),
+                       [o14] "+a"(o[14]), [o15] "+a"(o[15]), [w0] "=&v"(w0), [w1] "=&v"(w1), [w2] "=&v"(w2),
+                       [w3] "=&v"(w3), [w4] "=&v"(w4), [w5] "=&v"(w5), [w6] "=&v"(w6), [w7] "=&v"(w7),
+                       [mx] "=&v"(mx), [l] "+v"(l_sum), [m0save] "=&s"(m0save)
+                     : [q0] "v"(qf[0]), [q1] "v"(qf[1]), [q2] "v"(qf[2]), [q3] "v"(qf[3]), [q4] "v"(qf[4]),
+                       [q5] "v"(qf[5]), [q6] "v"(qf[6]), [q7] "v"(qf[7]), [q8] "v"(qf[8]), [q9] "v"(qf[9]),
+                       [q10] "v"(qf[10]), [q11] "v"(qf[11]), [q12] "v"(qf[12]), [q13] "v"(qf[13]),
+                       [q14] "v"(qf[14]), [q15] "v"(qf[15]), [q16] "v"(qf[16]), [q17] "v"(qf[17]),
+                       [q18] "v"(qf[18]), [q19] "v"(qf[19]), [q20] "v"(qf[20]), [q21] "v"(qf[21]),
+                       [q22] "v"(qf[22]), [q23] "v"(qf[23]), [q24] "v"(qf[24]), [q25] "v"(qf[25]),
+                       [q26] "v"(qf[26]), [q27] "v"(qf[27]), [q28] "v"(qf[28]), [q29] "v"(qf[29]),
+                       [q30] "v"(qf[30]), [q31] "v"(qf[31]), [q32] "v"(qf[32]), [q33] "v"(qf[33]),
+                       [q34] "v"(qf[34]), [q35] "v"(qf[35]), [p0] "v"(pf[0]), [p1] "v"(pf[1]), [b0] "v"(sb0),
+                       [b1] "v"(sb1), [b2] "v"(sb2), [b3] "v"(sb3), [t0] "v"(tb0), [t1] "v"(tb1),
+                       [t2] "v"(tb2), [t3] "v"(tb3), [mref] "v"(m_ref), [sc] "s"(scale_log2), [valid] "s"(valid), [nx] "s"(nx),
+                       [dma] "s"(dma), [ldst] "s"(ldst), [tbase] "s"(tb_s), [d0] "v"(dma_off[0]),
+                       [d1] "v"(dma_off[1]), [d2] "v"(dma_off[2]), [d3] "v"(dma_off[3]), [d4] "v"(dma_off[4]),
+                       [d5] "v"(dma_off[5]), [d6] "v"(dma_off[6]), [d7] "v"(dma_off[7]), [d8] "v"(dma_off[8])
+                     : "v204", "v205", "v206", "v208", "v209", "v210", "v211", "v212", "v213", "v214", "v215", "v216",
+                       "v217", "v218", "v219", "v220", "v221", "v222", "v223", "v240", "v241", "v242", "v243",
+                       "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254",
+                       "v255", "vcc", "scc", "memory");
+        ovf = ovf || __any(mx > m_ref + kRefSlack);
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        pf[0] = __builtin_bit_cast(i16x8, u32x4{w0, w1, w2, w3});
+        pf[1] = __builtin_bit_cast(i16x8, u32x4{w4, w5, w6, w7});
+      }
+      if (pass == 0) {  // redo if any wave overflowed
+        if (ovf && lane == 0) redo_flag = 1;
+        wait_vm_then_barrier<0>();
+        redo = redo_flag != 0;
+      }
+    } else {
+      // One tile per iteration: scores, softmax, P*V (fp32), or scores only
+      // (the max scan of pass 1).  An overflow stamped for a tile is seen by
+      // every wave at the next barrier.
+      int step = 0;  // block-uniform iteration stamp within the pass
+      for (int it = 0; it < ntiles; ++it) {
+        const int ahead = min(STAGES - 2, ntiles - 1 - it);
+        if (ahead >= 2) wait_vm_then_barrier<2 * DPW>();
+        else if (ahead == 1) wait_vm_then_barrier<DPW>();
+        else wait_vm_then_barrier<0>();
+        if (pass == 0 && it > 0 && redo_stamp[(step - 1) & 1] == step - 1) {  // previous tile overflowed
+          redo = true;
+          break;
+        }
+        if (it + STAGES - 1 < ntiles) issue_tile(it + STAGES - 1, (it + STAGES - 1) % STAGES);
+        const int stage_off = (it % STAGES) * TB;
+        ++step;
+        f32x16 sacc = score_tile(stage_off);
+        const float mx = tile_max(sacc, r1 - (r0 + it * TILE));
+        m_seen = fmaxf(m_seen, mx);
+        if (BF16 || pass == 1) continue;  // max scan only (bf16 reaches here in pass 1 only)
+        if (m_ref == -INFINITY) m_ref = mx;
+        if (pass == 0 && __any(mx > m_ref + kRefSlack)) {
+          if (lane == 0) redo_stamp[(step - 1) & 1] = step - 1;
+        }
+        // fp32: p = 2^(s*scale - ref); O^T[c][h] += cache^T P^T
+        const char* tile = smem + stage_off;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           sacc[r] = __builtin_amdgcn_exp2f(fmaf(sacc[r], scale_log2, -m_ref));
           l_sum += sacc[r];
         }
-      }
-      const f32x16& p = sacc;
-
-      // O^T[c][h] += cache^T P^T
-      if constexpr (BF16) {
-        i16x8 pf[2];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-          pf[ks] = __builtin_bit_cast(i16x8, u32x4{pack_hi16(p[8 * ks + 0], p[8 * ks + 1]),
-                                                   pack_hi16(p[8 * ks + 2], p[8 * ks + 3]),
-                                                   pack_hi16(p[8 * ks + 4], p[8 * ks + 5]),
-                                                   pack_hi16(p[8 * ks + 6], p[8 * ks + 7])});
-        }
-        const int tb0 = lds_base + stage_off + tr_base[0], tb1 = lds_base + stage_off + tr_base[1];
-        asm volatile(MLA_ASM_PV_BLOCK
-                     : [o0] "+a"(o[0]), [o1] "+a"(o[1]), [o2] "+a"(o[2]), [o3] "+a"(o[3]), [o4] "+a"(o[4]),
-                       [o5] "+a"(o[5]), [o6] "+a"(o[6]), [o7] "+a"(o[7]), [o8] "+a"(o[8]), [o9] "+a"(o[9]),
-                       [o10] "+a"(o[10]), [o11] "+a"(o[11]), [o12] "+a"(o[12]), [o13] "+a"(o[13]),
-                       [o14] "+a"(o[14]), [o15] "+a"(o[15])
-                     : [p0] "v"(pf[0]), [p1] "v"(pf[1]), [t0] "v"(tb0), [t1] "v"(tb1)
-                     : "v224", "v225", "v226", "v227", "v228", "v229", "v230", "v231", "v232", "v233", "v234",
-                       "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244", "v245",
-                       "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255");
-      } else {
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int t = 8 * (r >> 2) + 4 * hf + (r & 3);
             const float a = *(const float*)(tile + tile_off<ROWB, NCH>(t, (32 * cb + l32) * 4));
-            o[cb] = M::mma(a, p[r], o[cb]);
+            o[cb] = M::mma(a, sacc[r], o[cb]);
           }
         }
       }
+      if (!BF16 && pass == 0 && !redo) {  // the last tile may have overflowed too
+        wait_vm_then_barrier<0>();
+        redo = redo_stamp[(step - 1) & 1] == step - 1;
+      }
     }
     if constexpr (BF16) acc_fence(o);  // last MFMA -> readout / re-zeroing
-    if (pass == 0 && !redo) {  // the last tile may have overflowed too
-      wait_vm_then_barrier<0>();
-      redo = redo_stamp[(step - 1) & 1] == step - 1;
-    }
     if (pass != 1 && !redo) break;
     // every wave is here and its loads have landed: refill the ring from tile 0
     wait_vm_then_barrier<0>();
     if (pass == 1) m_ref = m_seen;  // exact max of the split: p <= 1 in the final pass
   }
 
+  // o_part of split (b, s) is [R/4][H][4]: column quad cq = 8*cb + 2*q + hf of
+  // this lane's head sits at (cq*H + head)*4, so the 32 lanes of a half-wave
+  // store 512 contiguous bytes per instruction.
   const float l_tot = xor32(l_sum, [](float a, float b) { return a + b; });
   if (head_ok) {
     const float inv = 1.f / l_tot;
-    float* op = o_part + (((int64_t)b * num_splits + s) * H + head) * R;
+    float* op = o_part + ((int64_t)b * num_splits + s) * H * R + (int64_t)(hf * H + head) * 4;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         f32x4 v = {o[cb][4 * q] * inv, o[cb][4 * q + 1] * inv, o[cb][4 * q + 2] * inv, o[cb][4 * q + 3] * inv};
-        *(f32x4*)(op + 32 * cb + 8 * q + 4 * hf) = v;
+        *(f32x4*)(op + (int64_t)(8 * cb + 2 * q) * H * 4) = v;
       }
     }
     if (hf == 0) lse_out[head] = (m_ref + __log2f(l_tot)) * kLn2;
@@ -530,31 +641,33 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// K4: merge the splits.  One work-group per (b, h) row: R/4 threads cover the
-// row (4 columns each) and 256/(R/4) split groups take every SG-th split; the
-// groups' weighted sums are added through LDS.  Split weights come from the
-// log-sum-exps, read first (they are small).
+// K4: merge the splits.  The partials of split (b, s) are [R/4][H][4]
+// (column quads, heads, 4 columns); quad Q = cq*H + h.  One work-group per
+// (b, 64 consecutive quads): 64 threads cover the quads (1 KB per split, one
+// head per thread) and 4 split groups take every 4th split; the groups' sums
+// are added through LDS.  Split weights come from the log-sum-exps.
 // ---------------------------------------------------------------------------
 
+constexpr int kCombineQuads = 64;
+constexpr int kCombineGroups = 4;
+
 template <int R>
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ o_part,
-                                                      const float* __restrict__ lse_part, int num_splits,
-                                                      int H, float* __restrict__ o_lat, float* __restrict__ lse_out) {
-  constexpr int TPH = R / 4;        // threads across the row
-  constexpr int SG = 256 / TPH;     // split groups
-  constexpr int U = 4;              // splits in flight per thread
-  static_assert(TPH <= 256 && 256 % TPH == 0, "R");
-  __shared__ f32x4 part[SG][TPH];
-  __shared__ float wpart[SG];
-  const int bh = blockIdx.x;
-  const int b = bh / H, h = bh - b * H;
-  const int c = ((int)threadIdx.x % TPH) * 4;
-  const int sg = (int)threadIdx.x / TPH;
+__global__ __launch_bounds__(kCombineQuads * kCombineGroups) void combine_kernel(
+    const float* __restrict__ o_part, const float* __restrict__ lse_part, int num_splits, int H,
+    float* __restrict__ o_lat, float* __restrict__ lse_out) {
+  constexpr int TQ = kCombineQuads, SG = kCombineGroups, U = 4;
+  __shared__ f32x4 part[SG][TQ];
+  __shared__ float wpart[SG][TQ];
+  const int blocks_per_b = (R / 4) * H / TQ;
+  const int b = (int)blockIdx.x / blocks_per_b;
+  const int quad = ((int)blockIdx.x - b * blocks_per_b) * TQ + (int)threadIdx.x % TQ;
+  const int sg = (int)threadIdx.x / TQ;
+  const int cq = quad / H, h = quad - cq * H;
   const float* lp = lse_part + (int64_t)b * num_splits * H + h;
   float m = -INFINITY;
   for (int s = 0; s < num_splits; ++s) m = fmaxf(m, lp[(int64_t)s * H]);
-  const float* op = o_part + ((int64_t)b * num_splits * H + h) * R + c;
   const int64_t sstride = (int64_t)H * R;
+  const float* op = o_part + (int64_t)b * num_splits * sstride + (int64_t)quad * 4;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
   int s = sg;
@@ -580,19 +693,20 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     wsum += w;
     acc += w * *(const f32x4*)(op + s * sstride);
   }
-  part[sg][threadIdx.x % TPH] = acc;
-  if (threadIdx.x % TPH == 0) wpart[sg] = wsum;
+  part[sg][threadIdx.x % TQ] = acc;
+  wpart[sg][threadIdx.x % TQ] = wsum;
   __syncthreads();
   if (sg == 0) {
     f32x4 tot = part[0][threadIdx.x];
-    float wt = wpart[0];
+    float wt = wpart[0][threadIdx.x];
 #pragma unroll
     for (int g = 1; g < SG; ++g) {
       tot += part[g][threadIdx.x];
-      wt += wpart[g];
+      wt += wpart[g][threadIdx.x];
     }
-    *(f32x4*)(o_lat + (int64_t)bh * R + c) = tot * (1.f / wt);
-    if (lse_out != nullptr && c == 0) lse_out[bh] = m + __logf(wt);
+    const int64_t row = (int64_t)b * H + h;
+    *(f32x4*)(o_lat + row * R + 4 * cq) = tot * (1.f / wt);
+    if (lse_out != nullptr && cq == 0) lse_out[row] = m + __logf(wt);
   }
 }
 
@@ -1037,15 +1151,18 @@ mla_status mla_combine(const mla_dims* dims, const float* o_part, const float* l
   if (num_splits > kMaxSplits) return fail(MLA_ERR_WORKSPACE, "num_splits above 4096");
   g_last_error.clear();
   hipStream_t s = (hipStream_t)stream;
-  const int BH = dims->batch * dims->heads;
+  const int64_t quads = (int64_t)(dims->rank / 4) * dims->heads;  // column quads x heads per split
+  if (quads % kCombineQuads != 0) return fail(MLA_ERR_UNSUPPORTED, "rank/4 * heads must be a multiple of 64");
+  const dim3 grid((unsigned)(dims->batch * (quads / kCombineQuads)));
+  const dim3 block(kCombineQuads * kCombineGroups);
   switch (dims->rank) {
     case 64:
-      hipLaunchKernelGGL((combine_kernel<64>), dim3(BH), dim3(256), 0, s, o_part, lse_part, num_splits, dims->heads,
-                         o_lat, lse);
+      hipLaunchKernelGGL((combine_kernel<64>), grid, block, 0, s, o_part, lse_part, num_splits, dims->heads, o_lat,
+                         lse);
       break;
     case 512:
-      hipLaunchKernelGGL((combine_kernel<512>), dim3(BH), dim3(256), 0, s, o_part, lse_part, num_splits, dims->heads,
-                         o_lat, lse);
+      hipLaunchKernelGGL((combine_kernel<512>), grid, block, 0, s, o_part, lse_part, num_splits, dims->heads, o_lat,
+                         lse);
       break;
     default: return fail(MLA_ERR_UNSUPPORTED, "rank");
   }

@@ -39,8 +39,22 @@ def build(verbose: bool = False, extra=()) -> str:
         sys.stderr.write(res.stdout + res.stderr)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}): {' '.join(cmd)}")
+    _check_kernel_stubs(tmp)
     os.replace(tmp, LIB)
     return LIB
+
+
+def _check_kernel_stubs(path: str) -> None:
+    """Fail if a kernel's host launch stub is referenced but not defined (the
+    library would then not load): the host pass can drop the stub of a kernel
+    template instance without an error."""
+    nm = shutil.which("nm")
+    if nm is None:
+        return
+    res = subprocess.run([nm, "-D", "--undefined-only", path], capture_output=True, text=True)
+    missing = [line.split()[-1] for line in res.stdout.splitlines() if "__device_stub__" in line]
+    if missing:
+        raise RuntimeError(f"{path}: kernel launch stubs missing: {missing}")
 
 
 if __name__ == "__main__":

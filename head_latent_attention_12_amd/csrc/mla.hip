@@ -251,7 +251,7 @@ template <typename T, int H, int R, int DR, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
     const T* __restrict__ q_lat, const T* __restrict__ cache, const int64_t* __restrict__ row_offsets,
     const int32_t* __restrict__ seq_lens, int64_t total_rows, int32_t num_splits, int32_t chunk,
-    float* __restrict__ o_part, float* __restrict__ lse_part, float scale_log2) {
+    T* __restrict__ o_part, float* __restrict__ lse_part, float scale_log2) {
   using S = DecodeShape<T, H, R, DR, NW>;
   using M = Mma<T>;
   constexpr int W = S::W, ROWB = S::ROWB, NCH = S::NCH, TILE = S::TILE, STAGES = S::STAGES;
@@ -621,19 +621,27 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
     if (pass == 1) m_ref = m_seen;  // exact max of the split: p <= 1 in the final pass
   }
 
-  // o_part of split (b, s) is [R/4][H][4]: column quad cq = 8*cb + 2*q + hf of
-  // this lane's head sits at (cq*H + head)*4, so the 32 lanes of a half-wave
-  // store 512 contiguous bytes per instruction.
+  // o_part of split (b, s) is [R/4][H][4] in the storage dtype: column quad
+  // cq = 8*cb + 2*q + hf of this lane's head sits at (cq*H + head)*4, so the 32
+  // lanes of a half-wave store contiguous bytes.  bf16 partials are the fp32
+  // softmax-weighted means rounded once (relative error <= 2^-9 of each value).
   const float l_tot = xor32(l_sum, [](float a, float b) { return a + b; });
   if (head_ok) {
     const float inv = 1.f / l_tot;
-    float* op = o_part + ((int64_t)b * num_splits + s) * H * R + (int64_t)(hf * H + head) * 4;
+    T* op = o_part + ((int64_t)b * num_splits + s) * H * R + (int64_t)(hf * H + head) * 4;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        f32x4 v = {o[cb][4 * q] * inv, o[cb][4 * q + 1] * inv, o[cb][4 * q + 2] * inv, o[cb][4 * q + 3] * inv};
-        *(f32x4*)(op + (int64_t)(8 * cb + 2 * q) * H * 4) = v;
+        T* dst = op + (int64_t)(8 * cb + 2 * q) * H * 4;
+        if constexpr (BF16) {
+          typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+          *(u32x2*)dst = u32x2{cvt_pk_bf16(o[cb][4 * q] * inv, o[cb][4 * q + 1] * inv),
+                               cvt_pk_bf16(o[cb][4 * q + 2] * inv, o[cb][4 * q + 3] * inv)};
+        } else {
+          *(f32x4*)dst = f32x4{o[cb][4 * q] * inv, o[cb][4 * q + 1] * inv, o[cb][4 * q + 2] * inv,
+                               o[cb][4 * q + 3] * inv};
+        }
       }
     }
     if (hf == 0) lse_out[head] = (m_ref + __log2f(l_tot)) * kLn2;
@@ -644,69 +652,93 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
 // K4: merge the splits.  The partials of split (b, s) are [R/4][H][4]
 // (column quads, heads, 4 columns); quad Q = cq*H + h.  One work-group per
 // (b, 64 consecutive quads): 64 threads cover the quads (1 KB per split, one
-// head per thread) and 4 split groups take every 4th split; the groups' sums
-// are added through LDS.  Split weights come from the log-sum-exps.
+// head per thread) and blockDim/64 split groups take every group-th split.
+// Each thread keeps a running maximum of the log-sum-exps it has seen and
+// rescales its sums when it grows (four splits per step, loads issued
+// together); the groups' results are merged through LDS the same way.
 // ---------------------------------------------------------------------------
 
 constexpr int kCombineQuads = 64;
-constexpr int kCombineGroups = 4;
+constexpr int kCombineMaxGroups = 16;
 
-template <int R>
-__global__ __launch_bounds__(kCombineQuads * kCombineGroups) void combine_kernel(
-    const float* __restrict__ o_part, const float* __restrict__ lse_part, int num_splits, int H,
+// a column quad of a partial in its storage dtype
+template <typename PT> __device__ __forceinline__ f32x4 load_quad(const PT* p);
+template <> __device__ __forceinline__ f32x4 load_quad<float>(const float* p) { return *(const f32x4*)p; }
+template <> __device__ __forceinline__ f32x4 load_quad<u16>(const u16* p) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 v = *(const u32x2*)p;
+  return f32x4{__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xffff0000u), __uint_as_float(v[1] << 16),
+               __uint_as_float(v[1] & 0xffff0000u)};
+}
+
+template <int R, typename PT>
+__global__ __launch_bounds__(kCombineQuads * kCombineMaxGroups) void combine_kernel(
+    const PT* __restrict__ o_part, const float* __restrict__ lse_part, int num_splits, int H,
     float* __restrict__ o_lat, float* __restrict__ lse_out) {
-  constexpr int TQ = kCombineQuads, SG = kCombineGroups, U = 4;
-  __shared__ f32x4 part[SG][TQ];
-  __shared__ float wpart[SG][TQ];
+  constexpr int TQ = kCombineQuads, U = 4;
+  __shared__ f32x4 part[kCombineMaxGroups][TQ];
+  __shared__ float wpart[kCombineMaxGroups][TQ];
+  __shared__ float mpart[kCombineMaxGroups][TQ];
+  const int SG = (int)blockDim.x / TQ;
   const int blocks_per_b = (R / 4) * H / TQ;
   const int b = (int)blockIdx.x / blocks_per_b;
-  const int quad = ((int)blockIdx.x - b * blocks_per_b) * TQ + (int)threadIdx.x % TQ;
+  const int tq = (int)threadIdx.x % TQ;
+  const int quad = ((int)blockIdx.x - b * blocks_per_b) * TQ + tq;
   const int sg = (int)threadIdx.x / TQ;
   const int cq = quad / H, h = quad - cq * H;
   const float* lp = lse_part + (int64_t)b * num_splits * H + h;
-  float m = -INFINITY;
-  for (int s = 0; s < num_splits; ++s) m = fmaxf(m, lp[(int64_t)s * H]);
   const int64_t sstride = (int64_t)H * R;
-  const float* op = o_part + (int64_t)b * num_splits * sstride + (int64_t)quad * 4;
+  const PT* op = o_part + (int64_t)b * num_splits * sstride + (int64_t)quad * 4;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float wsum = 0.f;
-  int s = sg;
-  for (; s + (U - 1) * SG < num_splits; s += U * SG) {
+  float wsum = 0.f, m = -INFINITY;
+  for (int s0 = sg; s0 < num_splits; s0 += U * SG) {
     float l[U];
     f32x4 v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) l[u] = lp[(int64_t)(s + u * SG) * H];
-#pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = *(const f32x4*)(op + (s + u * SG) * sstride);
+    for (int u = 0; u < U; ++u) {
+      const int s = s0 + u * SG;
+      l[u] = s < num_splits ? lp[(int64_t)s * H] : -INFINITY;
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (l[u] == -INFINITY) continue;  // empty split: its o_part was never written
-      const float w = __expf(l[u] - m);
+      const int s = s0 + u * SG;
+      // an empty split (lse -inf) never wrote its partial: not read
+      v[u] = (s < num_splits && l[u] != -INFINITY) ? load_quad(op + s * sstride) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    float mn = m;
+#pragma unroll
+    for (int u = 0; u < U; ++u) mn = fmaxf(mn, l[u]);
+    if (mn == -INFINITY) continue;
+    const float sc = __expf(m - mn);  // 0 when m = -inf
+    acc *= sc;
+    wsum *= sc;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float w = __expf(l[u] - mn);  // 0 for an empty split
       wsum += w;
       acc += w * v[u];
     }
+    m = mn;
   }
-  for (; s < num_splits; s += SG) {
-    const float l = lp[(int64_t)s * H];
-    if (l == -INFINITY) continue;
-    const float w = __expf(l - m);
-    wsum += w;
-    acc += w * *(const f32x4*)(op + s * sstride);
-  }
-  part[sg][threadIdx.x % TQ] = acc;
-  wpart[sg][threadIdx.x % TQ] = wsum;
+  part[sg][tq] = acc;
+  wpart[sg][tq] = wsum;
+  mpart[sg][tq] = m;
   __syncthreads();
   if (sg == 0) {
-    f32x4 tot = part[0][threadIdx.x];
-    float wt = wpart[0][threadIdx.x];
-#pragma unroll
-    for (int g = 1; g < SG; ++g) {
-      tot += part[g][threadIdx.x];
-      wt += wpart[g][threadIdx.x];
+    float mt = m;
+    for (int g = 1; g < SG; ++g) mt = fmaxf(mt, mpart[g][tq]);
+    f32x4 tot = {0.f, 0.f, 0.f, 0.f};
+    float wt = 0.f;
+    for (int g = 0; g < SG; ++g) {
+      const float mg = mpart[g][tq];
+      if (mg == -INFINITY) continue;  // a group that saw only empty splits
+      const float sc = __expf(mg - mt);
+      tot += sc * part[g][tq];
+      wt += sc * wpart[g][tq];
     }
     const int64_t row = (int64_t)b * H + h;
     *(f32x4*)(o_lat + row * R + 4 * cq) = tot * (1.f / wt);
-    if (lse_out != nullptr && cq == 0) lse_out[row] = m + __logf(wt);
+    if (lse_out != nullptr && cq == 0) lse_out[row] = mt + __logf(wt);
   }
 }
 
@@ -1020,14 +1052,14 @@ constexpr int kMaxSplits = 4096;
 template <typename T, int H, int R, int DR, int NW>
 mla_status launch_decode(const mla_dims& d, const void* q_lat, const void* cache, const int64_t* row_offsets,
                          const int32_t* seq_lens, int64_t total_rows, int32_t max_seq_len, int32_t num_splits,
-                         float* o_part, float* lse_part, hipStream_t stream) {
+                         void* o_part, float* lse_part, hipStream_t stream) {
   using S = DecodeShape<T, H, R, DR, NW>;
   const int64_t blocks = (int64_t)d.batch * num_splits * S::GROUPS;
   if (blocks > 0x7fffffff) return fail(MLA_ERR_UNSUPPORTED, "grid too large");
   const float scale_log2 = scale_of(d) * kLog2e;
   hipLaunchKernelGGL((decode_latent_kernel<T, H, R, DR, NW>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream,
                      (const T*)q_lat, (const T*)cache, row_offsets, seq_lens, total_rows, num_splits,
-                     chunk_rows(max_seq_len, num_splits), o_part, lse_part, scale_log2);
+                     chunk_rows(max_seq_len, num_splits), (T*)o_part, lse_part, scale_log2);
   return launch_result("mla_decode_latent");
 }
 
@@ -1118,7 +1150,7 @@ mla_status mla_rope_append(const mla_dims* dims, const void* q_rope, const void*
 
 mla_status mla_decode_latent(const mla_dims* dims, const void* q_lat, const void* kv_cache, const int64_t* row_offsets,
                              const int32_t* seq_lens, int64_t total_rows, int32_t max_seq_len, int32_t num_splits,
-                             float* o_part, float* lse_part, void* stream) {
+                             void* o_part, float* lse_part, void* stream) {
   mla_status st = check_dims_impl(dims);
   if (st != MLA_OK) return st;
   if (row_offsets == nullptr || seq_lens == nullptr) return fail(MLA_ERR_INVALID_ARG, "row_offsets/seq_lens NULL");
@@ -1142,7 +1174,7 @@ mla_status mla_decode_latent(const mla_dims* dims, const void* q_lat, const void
   return fail(MLA_ERR_UNSUPPORTED, "no instantiation");
 }
 
-mla_status mla_combine(const mla_dims* dims, const float* o_part, const float* lse_part, int32_t num_splits,
+mla_status mla_combine(const mla_dims* dims, const void* o_part, const float* lse_part, int32_t num_splits,
                        float* o_lat, float* lse, void* stream) {
   mla_status st = check_dims_impl(dims);
   if (st != MLA_OK) return st;
@@ -1154,17 +1186,19 @@ mla_status mla_combine(const mla_dims* dims, const float* o_part, const float* l
   const int64_t quads = (int64_t)(dims->rank / 4) * dims->heads;  // column quads x heads per split
   if (quads % kCombineQuads != 0) return fail(MLA_ERR_UNSUPPORTED, "rank/4 * heads must be a multiple of 64");
   const dim3 grid((unsigned)(dims->batch * (quads / kCombineQuads)));
-  const dim3 block(kCombineQuads * kCombineGroups);
-  switch (dims->rank) {
-    case 64:
-      hipLaunchKernelGGL((combine_kernel<64>), grid, block, 0, s, o_part, lse_part, num_splits, dims->heads, o_lat,
-                         lse);
-      break;
-    case 512:
-      hipLaunchKernelGGL((combine_kernel<512>), grid, block, 0, s, o_part, lse_part, num_splits, dims->heads, o_lat,
-                         lse);
-      break;
-    default: return fail(MLA_ERR_UNSUPPORTED, "rank");
+  // split groups: enough for about four splits per thread, at most 16
+  int groups = 1;
+  while (groups < kCombineMaxGroups && groups * 4 < num_splits) groups *= 2;
+  const dim3 block(kCombineQuads * groups);
+  // partials are stored in the dtype of the cache (see the decode kernel)
+  if (dims->dtype == MLA_BF16 && dims->rank == 512) {
+    hipLaunchKernelGGL((combine_kernel<512, u16>), grid, block, 0, s, (const u16*)o_part, lse_part, num_splits,
+                       dims->heads, o_lat, lse);
+  } else if (dims->dtype == MLA_F32 && dims->rank == 64) {
+    hipLaunchKernelGGL((combine_kernel<64, float>), grid, block, 0, s, (const float*)o_part, lse_part, num_splits,
+                       dims->heads, o_lat, lse);
+  } else {
+    return fail(MLA_ERR_UNSUPPORTED, "rank");
   }
   return launch_result("mla_combine");
 }
@@ -1193,7 +1227,7 @@ mla_status mla_partials_size(const mla_dims* dims, int32_t num_splits, size_t* o
   if (num_splits > kMaxSplits) return fail(MLA_ERR_WORKSPACE, "num_splits above 4096");
   if (o_part_bytes == nullptr || lse_part_bytes == nullptr) return fail(MLA_ERR_INVALID_ARG, "NULL output");
   const size_t bsh = (size_t)dims->batch * (size_t)num_splits * (size_t)dims->heads;
-  *o_part_bytes = bsh * (size_t)dims->rank * sizeof(float);
+  *o_part_bytes = bsh * (size_t)dims->rank * (dims->dtype == MLA_BF16 ? sizeof(uint16_t) : sizeof(float));
   *lse_part_bytes = bsh * sizeof(float);
   return MLA_OK;
 }

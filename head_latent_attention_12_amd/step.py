@@ -69,7 +69,8 @@ class DeviceStep:
         if num_splits is None:
             num_splits = mla.mla_plan_splits(self.dims, inp.max_seq_len, inp.total_rows)
         self.num_splits = int(num_splits)
-        self.o_part = torch.empty((inp.B, self.num_splits, inp.H, inp.r), dtype=torch.float32, device=self.device)
+        o_bytes, _ = mla.mla_partials_size(self.dims, self.num_splits)
+        self.o_part = torch.empty((o_bytes // 4,), dtype=torch.int32, device=self.device)  # raw partials buffer
         self.lse_part = torch.empty((inp.B, self.num_splits, inp.H), dtype=torch.float32, device=self.device)
 
     # the five calls -------------------------------------------------------

@@ -52,14 +52,23 @@
  *                            token's position and its row index in the sequence
  *   row_offsets [B] int64    first cache row of sequence b
  *   seq_lens    [B] int32    rows attended = L_b + 1 (after the append)
- *   o_part   [B][num_splits][H][r] float32, lse_part [B][num_splits][H] float32
+ *   o_part   [B][num_splits][r/4][H][4] in the storage dtype (float32 for
+ *            MLA_F32, bf16 for MLA_BF16): the split partials with the columns
+ *            taken four at a time and the heads interleaved, i.e.
+ *            o_part(b, s, h, c) is element
+ *            ((b*num_splits + s)*(r/4) + c/4)*H*4 + h*4 + c%4, so that the
+ *            heads of one column quad are contiguous (coalesced stores from
+ *            the decode kernel, whose lanes hold one head each).  A bf16
+ *            partial is the fp32 result rounded once to nearest even.
+ *   lse_part [B][num_splits][H] float32
  *   o_lat    [B][H][r] float32, lse [B][H] float32, out [B][H][d_v] float32
  *   Sequence b owns cache rows [row_offsets[b], row_offsets[b] + seq_lens[b]).
  *
- * Splits: with chunk = ceil(max_seq_len / num_splits), split s of sequence b
- * covers in-sequence rows [s*chunk, min((s+1)*chunk, seq_lens[b])).  A split
- * with no rows writes lse_part = -inf and leaves its o_part untouched;
- * mla_combine skips it.
+ * Splits: with chunk = ceil(max_seq_len / num_splits) rounded up to a
+ * multiple of 32 (the kernel's row tile), split s of sequence b covers
+ * in-sequence rows [s*chunk, min((s+1)*chunk, seq_lens[b])).  A split with no
+ * rows writes lse_part = -inf and leaves its o_part untouched; mla_combine
+ * skips it.
  *
  * Ownership and execution: the caller allocates every buffer (device memory,
  * 16-byte aligned) and owns it; the library allocates nothing, keeps no state
@@ -107,7 +116,7 @@ typedef struct {
 
 /* Supported shapes: (dtype, H, r, d_rope) in
  *   (F32, 8, 64, 16), (F32, 16, 64, 32), (BF16, 128, 512, 64),
- * with d_head and d_v multiples of 32 (F32) or of 32 up to 512 (BF16). */
+ * with d_head in {32, 64, 128, 256} and d_v a multiple of 32, at most 1024. */
 
 /* Fold W_UK into the query ([P1] section 3): for every b, h, j
  *   q_lat[b][h][j] = sum_d w_uk[h][d][j] * q_nope[b][h][d],   j < r,
@@ -130,22 +139,22 @@ mla_status mla_rope_append(const mla_dims* dims, const void* q_rope, const void*
  * [P3] content score + position score): for every b, h and split s with rows
  * t in the split,
  *   score_t = softmax_scale * (q_lat[b][h][0:r] . c_kv_t + q_lat[b][h][r:] . k_rope_t)
- *   o_part[b][s][h] = sum_t softmax(score)_t * c_kv_t    (softmax within the split)
- *   lse_part[b][s][h] = ln sum_t exp(score_t)
+ *   o_part(b, s, h, :) = sum_t softmax(score)_t * c_kv_t    (softmax within the split)
+ *   lse_part[b][s][h]  = ln sum_t exp(score_t)
  * fp32 accumulation; bf16 storage computes the products in bf16 with fp32
  * sums.  max_seq_len must be >= every seq_lens[b]; rows beyond
  * num_splits * chunk are not read.  1 <= num_splits <= 4096. */
 mla_status mla_decode_latent(const mla_dims* dims, const void* q_lat, const void* kv_cache,
                              const int64_t* row_offsets, const int32_t* seq_lens,
                              int64_t total_rows, int32_t max_seq_len, int32_t num_splits,
-                             float* o_part, float* lse_part, void* stream);
+                             void* o_part, float* lse_part, void* stream);
 
 /* Merge the splits (softmax over the union of the splits' rows):
  *   m = max_s lse_part[b][s][h];  w_s = exp(lse_part[b][s][h] - m)
- *   o_lat[b][h] = sum_s w_s o_part[b][s][h] / sum_s w_s
+ *   o_lat[b][h] = sum_s w_s o_part(b, s, h, :) / sum_s w_s
  *   lse[b][h]   = m + ln sum_s w_s                (lse may be NULL)
  * Splits whose lse_part is -inf are skipped. */
-mla_status mla_combine(const mla_dims* dims, const float* o_part, const float* lse_part,
+mla_status mla_combine(const mla_dims* dims, const void* o_part, const float* lse_part,
                        int32_t num_splits, float* o_lat, float* lse, void* stream);
 
 /* Apply W_UV after the weighted sum ([P2] absorbing projections):

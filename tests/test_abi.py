@@ -101,9 +101,13 @@ def test_split_count_limits():
 
 
 def test_partials_size():
+    # partials are stored in the cache dtype: bf16 here, fp32 for MLA_F32
     d = dsv2()
     o, l = mla.mla_partials_size(d, 7)
-    assert o == 16 * 7 * 128 * 512 * 4 and l == 16 * 7 * 128 * 4
+    assert o == 16 * 7 * 128 * 512 * 2 and l == 16 * 7 * 128 * 4
+    f = mla.make_dims(8, 16, 64, 64, 64, 32, mla.MLA_F32)
+    o, l = mla.mla_partials_size(f, 3)
+    assert o == 8 * 3 * 16 * 64 * 4 and l == 8 * 3 * 16 * 4
 
 
 @pytest.mark.parametrize("B,T,total,cus,expect_max_wgs", [

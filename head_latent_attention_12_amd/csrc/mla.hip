@@ -650,95 +650,126 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
 
 // ---------------------------------------------------------------------------
 // K4: merge the splits.  The partials of split (b, s) are [R/4][H][4]
-// (column quads, heads, 4 columns); quad Q = cq*H + h.  One work-group per
-// (b, 64 consecutive quads): 64 threads cover the quads (1 KB per split, one
-// head per thread) and blockDim/64 split groups take every group-th split.
-// Each thread keeps a running maximum of the log-sum-exps it has seen and
-// rescales its sums when it grows (four splits per step, loads issued
-// together); the groups' results are merged through LDS the same way.
+// (column quads, heads, 4 columns), so quad pair P (quads 2P, 2P+1: heads h,
+// h+1 of one column quad, H even) is 8 contiguous values.  A work-group of 256
+// threads is SG split groups x TQ = 256/SG threads; thread t of a group takes
+// quad pair (block*TQ + t) of every SG-th split, eight splits per step with
+// the loads issued together, keeping a running maximum of the log-sum-exps
+// (sums rescaled when it grows).  The groups are merged through LDS the same
+// way.  SG grows with the split count so that a thread sees about eight.
 // ---------------------------------------------------------------------------
 
-constexpr int kCombineQuads = 64;
+constexpr int kCombineThreads = 256;
 constexpr int kCombineMaxGroups = 16;
 
-// a column quad of a partial in its storage dtype
-template <typename PT> __device__ __forceinline__ f32x4 load_quad(const PT* p);
-template <> __device__ __forceinline__ f32x4 load_quad<float>(const float* p) { return *(const f32x4*)p; }
-template <> __device__ __forceinline__ f32x4 load_quad<u16>(const u16* p) {
-  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-  const u32x2 v = *(const u32x2*)p;
-  return f32x4{__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xffff0000u), __uint_as_float(v[1] << 16),
-               __uint_as_float(v[1] & 0xffff0000u)};
-}
+// four (two) consecutive values of a partial in its storage dtype, as fp32
+template <typename PT> struct Pair8;
+template <> struct Pair8<float> {
+  static __device__ __forceinline__ void load(const float* p, f32x4& a, f32x4& b) {
+    a = *(const f32x4*)p;
+    b = *(const f32x4*)(p + 4);
+  }
+};
+template <> struct Pair8<u16> {
+  static __device__ __forceinline__ void load(const u16* p, f32x4& a, f32x4& b) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = *(const u32x4*)p;
+    a = f32x4{__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xffff0000u), __uint_as_float(v[1] << 16),
+              __uint_as_float(v[1] & 0xffff0000u)};
+    b = f32x4{__uint_as_float(v[2] << 16), __uint_as_float(v[2] & 0xffff0000u), __uint_as_float(v[3] << 16),
+              __uint_as_float(v[3] & 0xffff0000u)};
+  }
+};
 
 template <int R, typename PT>
-__global__ __launch_bounds__(kCombineQuads * kCombineMaxGroups) void combine_kernel(
-    const PT* __restrict__ o_part, const float* __restrict__ lse_part, int num_splits, int H,
-    float* __restrict__ o_lat, float* __restrict__ lse_out) {
-  constexpr int TQ = kCombineQuads, U = 4;
-  __shared__ f32x4 part[kCombineMaxGroups][TQ];
-  __shared__ float wpart[kCombineMaxGroups][TQ];
-  __shared__ float mpart[kCombineMaxGroups][TQ];
-  const int SG = (int)blockDim.x / TQ;
-  const int blocks_per_b = (R / 4) * H / TQ;
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(const PT* __restrict__ o_part,
+                                                                  const float* __restrict__ lse_part,
+                                                                  int num_splits, int H, int SG,
+                                                                  float* __restrict__ o_lat,
+                                                                  float* __restrict__ lse_out) {
+  constexpr int U = 8;
+  __shared__ f32x4 part[kCombineThreads][2];
+  __shared__ float wpart[kCombineThreads][2], mpart[kCombineThreads][2];
+  const int TQ = (int)blockDim.x / SG;
+  const int pairs = (R / 4) * H / 2;            // quad pairs per split
+  const int blocks_per_b = pairs / TQ;
   const int b = (int)blockIdx.x / blocks_per_b;
-  const int tq = (int)threadIdx.x % TQ;
-  const int quad = ((int)blockIdx.x - b * blocks_per_b) * TQ + tq;
-  const int sg = (int)threadIdx.x / TQ;
-  const int cq = quad / H, h = quad - cq * H;
+  const int t = (int)threadIdx.x % TQ, sg = (int)threadIdx.x / TQ;
+  const int pair = ((int)blockIdx.x - b * blocks_per_b) * TQ + t;
+  const int q0 = 2 * pair, cq = q0 / H, h = q0 - cq * H;  // heads h, h+1 of column quad cq
   const float* lp = lse_part + (int64_t)b * num_splits * H + h;
   const int64_t sstride = (int64_t)H * R;
-  const PT* op = o_part + (int64_t)b * num_splits * sstride + (int64_t)quad * 4;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float wsum = 0.f, m = -INFINITY;
+  const PT* op = o_part + (int64_t)b * num_splits * sstride + (int64_t)q0 * 4;
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+  float w0 = 0.f, w1 = 0.f, m0 = -INFINITY, m1 = -INFINITY;
   for (int s0 = sg; s0 < num_splits; s0 += U * SG) {
-    float l[U];
-    f32x4 v[U];
+    float l0[U], l1[U];
+    f32x4 va[U], vb[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int s = s0 + u * SG;
-      l[u] = s < num_splits ? lp[(int64_t)s * H] : -INFINITY;
+      const bool ok = s < num_splits;
+      l0[u] = ok ? lp[(int64_t)s * H] : -INFINITY;
+      l1[u] = ok ? lp[(int64_t)s * H + 1] : -INFINITY;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int s = s0 + u * SG;
-      // an empty split (lse -inf) never wrote its partial: not read
-      v[u] = (s < num_splits && l[u] != -INFINITY) ? load_quad(op + s * sstride) : f32x4{0.f, 0.f, 0.f, 0.f};
+      // an empty split (lse -inf for every head) never wrote its partial
+      if (s < num_splits && l0[u] != -INFINITY) {
+        Pair8<PT>::load(op + s * sstride, va[u], vb[u]);
+      } else {
+        va[u] = vb[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
     }
-    float mn = m;
-#pragma unroll
-    for (int u = 0; u < U; ++u) mn = fmaxf(mn, l[u]);
-    if (mn == -INFINITY) continue;
-    const float sc = __expf(m - mn);  // 0 when m = -inf
-    acc *= sc;
-    wsum *= sc;
+    float n0 = m0, n1 = m1;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float w = __expf(l[u] - mn);  // 0 for an empty split
-      wsum += w;
-      acc += w * v[u];
+      n0 = fmaxf(n0, l0[u]);
+      n1 = fmaxf(n1, l1[u]);
     }
-    m = mn;
+    if (n0 == -INFINITY) continue;  // only empty splits so far (then n1 is -inf too)
+    const float c0 = __expf(m0 - n0), c1 = __expf(m1 - n1);  // 0 while m = -inf
+    acc0 *= c0;
+    w0 *= c0;
+    acc1 *= c1;
+    w1 *= c1;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float e0 = __expf(l0[u] - n0), e1 = __expf(l1[u] - n1);
+      w0 += e0;
+      w1 += e1;
+      acc0 += e0 * va[u];
+      acc1 += e1 * vb[u];
+    }
+    m0 = n0;
+    m1 = n1;
   }
-  part[sg][tq] = acc;
-  wpart[sg][tq] = wsum;
-  mpart[sg][tq] = m;
+  part[threadIdx.x][0] = acc0;
+  part[threadIdx.x][1] = acc1;
+  wpart[threadIdx.x][0] = w0;
+  wpart[threadIdx.x][1] = w1;
+  mpart[threadIdx.x][0] = m0;
+  mpart[threadIdx.x][1] = m1;
   __syncthreads();
   if (sg == 0) {
-    float mt = m;
-    for (int g = 1; g < SG; ++g) mt = fmaxf(mt, mpart[g][tq]);
-    f32x4 tot = {0.f, 0.f, 0.f, 0.f};
-    float wt = 0.f;
-    for (int g = 0; g < SG; ++g) {
-      const float mg = mpart[g][tq];
-      if (mg == -INFINITY) continue;  // a group that saw only empty splits
-      const float sc = __expf(mg - mt);
-      tot += sc * part[g][tq];
-      wt += sc * wpart[g][tq];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      float mt = -INFINITY;
+      for (int g = 0; g < SG; ++g) mt = fmaxf(mt, mpart[g * TQ + t][k]);
+      f32x4 tot = {0.f, 0.f, 0.f, 0.f};
+      float wt = 0.f;
+      for (int g = 0; g < SG; ++g) {
+        const float mg = mpart[g * TQ + t][k];
+        if (mg == -INFINITY) continue;  // a group that saw only empty splits
+        const float c = __expf(mg - mt);
+        tot += c * part[g * TQ + t][k];
+        wt += c * wpart[g * TQ + t][k];
+      }
+      const int64_t row = (int64_t)b * H + h + k;
+      *(f32x4*)(o_lat + row * R + 4 * cq) = tot * (1.f / wt);
+      if (lse_out != nullptr && cq == 0) lse_out[row] = mt + __logf(wt);
     }
-    const int64_t row = (int64_t)b * H + h;
-    *(f32x4*)(o_lat + row * R + 4 * cq) = tot * (1.f / wt);
-    if (lse_out != nullptr && cq == 0) lse_out[row] = mt + __logf(wt);
   }
 }
 
@@ -764,6 +795,24 @@ __global__ __launch_bounds__(NW * 64) void absorb_q_kernel(const T* __restrict__
   const int nblk = R / COLS;
   const int h = blockIdx.x / nblk;
   const int j0 = (blockIdx.x - h * nblk) * COLS;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int hf = lane >> 5, l32 = lane & 31;
+  // the first 32 queries' fragments are requested before the weight tile, so
+  // the two loads overlap
+  typename M::Frag bq[KS];
+  auto load_q = [&](int b0) {
+    const int bb = b0 + l32;
+    const T* qrow = q_nope + ((int64_t)(bb < B ? bb : 0) * H + h) * DH;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      if constexpr (ES == 2) {
+        bq[kk] = *(const i16x8*)(qrow + 16 * kk + 8 * hf);
+      } else {
+        bq[kk] = qrow[2 * kk + hf];
+      }
+    }
+  };
+  load_q(0);
   for (int idx = threadIdx.x; idx < DH * NCH; idx += NW * 64) {
     const int d = idx / NCH, c = idx - (idx / NCH) * NCH;
     const int4 v = *(const int4*)((const char*)(w_uk + ((int64_t)h * DH + d) * R + j0) + 16 * c);
@@ -771,8 +820,6 @@ __global__ __launch_bounds__(NW * 64) void absorb_q_kernel(const T* __restrict__
   }
   __syncthreads();
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int hf = lane >> 5, l32 = lane & 31;
   typename M::Frag af[KS];
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk) {
@@ -786,16 +833,7 @@ __global__ __launch_bounds__(NW * 64) void absorb_q_kernel(const T* __restrict__
   for (int b0 = 0; b0 < B; b0 += 32) {
     const int bb = b0 + l32;
     const bool bok = bb < B;
-    const T* qrow = q_nope + ((int64_t)(bok ? bb : 0) * H + h) * DH;
-    typename M::Frag bq[KS];  // loaded before the MFMA chain
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      if constexpr (ES == 2) {
-        bq[kk] = *(const i16x8*)(qrow + 16 * kk + 8 * hf);
-      } else {
-        bq[kk] = qrow[2 * kk + hf];
-      }
-    }
+    if (b0 > 0) load_q(b0);
     f32x16 acc = zero16();
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
@@ -1183,20 +1221,22 @@ mla_status mla_combine(const mla_dims* dims, const void* o_part, const float* ls
   if (num_splits > kMaxSplits) return fail(MLA_ERR_WORKSPACE, "num_splits above 4096");
   g_last_error.clear();
   hipStream_t s = (hipStream_t)stream;
-  const int64_t quads = (int64_t)(dims->rank / 4) * dims->heads;  // column quads x heads per split
-  if (quads % kCombineQuads != 0) return fail(MLA_ERR_UNSUPPORTED, "rank/4 * heads must be a multiple of 64");
-  const dim3 grid((unsigned)(dims->batch * (quads / kCombineQuads)));
-  // split groups: enough for about four splits per thread, at most 16
+  // split groups: about eight splits per thread, 1 to 16 groups
   int groups = 1;
-  while (groups < kCombineMaxGroups && groups * 4 < num_splits) groups *= 2;
-  const dim3 block(kCombineQuads * groups);
+  while (groups < kCombineMaxGroups && groups * 8 < num_splits) groups *= 2;
+  const int64_t pairs = (int64_t)(dims->rank / 4) * dims->heads / 2;  // quad pairs per split
+  const int tq = (int)std::min<int64_t>(kCombineThreads / groups, pairs);
+  if (dims->heads % 2 != 0 || pairs % tq != 0)
+    return fail(MLA_ERR_UNSUPPORTED, "heads must be even and rank/8 * heads a power-of-two multiple");
+  const dim3 grid((unsigned)(dims->batch * (pairs / tq)));
+  const dim3 block((unsigned)(tq * groups));
   // partials are stored in the dtype of the cache (see the decode kernel)
   if (dims->dtype == MLA_BF16 && dims->rank == 512) {
     hipLaunchKernelGGL((combine_kernel<512, u16>), grid, block, 0, s, (const u16*)o_part, lse_part, num_splits,
-                       dims->heads, o_lat, lse);
+                       dims->heads, groups, o_lat, lse);
   } else if (dims->dtype == MLA_F32 && dims->rank == 64) {
     hipLaunchKernelGGL((combine_kernel<64, float>), grid, block, 0, s, (const float*)o_part, lse_part, num_splits,
-                       dims->heads, o_lat, lse);
+                       dims->heads, groups, o_lat, lse);
   } else {
     return fail(MLA_ERR_UNSUPPORTED, "rank");
   }

@@ -75,6 +75,72 @@ def counter_traffic(workload: str):
     return e.get("hbm_bytes_per_launch")
 
 
+CALIB_BYTES = 512 * 2 ** 20     # calibration kernel: reads and writes this many bytes (above the 256 MB MALL)
+CALIB_KERNEL = "neg_kernel"     # torch.neg on float32: one read and one write per element
+
+
+def counters_run(workload: str, steps: int, warmup: int) -> None:
+    """The workload's timed steps, then the calibration kernel 4 times: the
+    program rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE profiles."""
+    import torch
+    run_workload(workload, steps, warmup, min_sets=5, verbose=True)
+    src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(4):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(f"# counters run done: {workload}, {steps} steps; calibration {CALIB_KERNEL} x4 of {CALIB_BYTES} bytes",
+          file=sys.stderr, flush=True)
+
+
+def _per_dispatch(run_dir: str, counter: str):
+    """{kernel name: [value per dispatch]} from a rocprofv3 --pmc csv run."""
+    import csv
+    import glob
+    per = {}
+    for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        for row in csv.DictReader(open(f)):
+            if row.get("Counter_Name") != counter:
+                continue
+            key = (row["Kernel_Name"], row.get("Dispatch_Id") or row.get("Correlation_Id"))
+            per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
+    out = {}
+    for (name, _), v in per.items():
+        out.setdefault(name, []).append(v)
+    return out
+
+
+def ingest_counters(workload: str, fetch_dir: str, write_dir: str, command: str) -> dict:
+    """Per-launch HBM bytes of the decode kernel from FETCH_SIZE and WRITE_SIZE
+    runs (KiB per dispatch), each scaled by what the same counter reads for the
+    calibration kernel of known size; written to profiles/decode_latent_counters.json."""
+    res = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        per = _per_dispatch(d, counter)
+        dec = [v for n, vs in per.items() if "decode_latent_kernel" in n for v in vs]
+        cal = [v for n, vs in per.items() if CALIB_KERNEL in n for v in vs]
+        if not dec or not cal:
+            raise SystemExit(f"{d}: no {counter} rows for the decode or calibration kernel")
+        kib = float(np.mean(dec))
+        scale = (CALIB_BYTES / 1024.0) / float(np.median(cal))
+        res[counter] = {"kib_per_launch": kib, "dispatches": len(dec), "calibration_kib": float(np.median(cal)),
+                        "scale": scale, "bytes_per_launch": kib * 1024.0 * scale}
+    entry = {
+        "hbm_bytes_per_launch": res["FETCH_SIZE"]["bytes_per_launch"] + res["WRITE_SIZE"]["bytes_per_launch"],
+        "fetch": res["FETCH_SIZE"], "write": res["WRITE_SIZE"],
+        "calibration": f"torch.neg over {CALIB_BYTES} bytes of float32 (reads and writes that many bytes)",
+        "source_sha": source_hash(), "command": command,
+    }
+    try:
+        rec = json.load(open(COUNTERS))
+    except (OSError, ValueError):
+        rec = {}
+    rec[workload] = entry
+    with open(COUNTERS, "w") as f:
+        json.dump(rec, f, indent=1)
+    return entry
+
+
 def cpu_baseline(inp, budget_s: float):
     """Time the fp64 oracle (absorbed form) on this machine's host cores."""
     from threadpoolctl import threadpool_info
@@ -186,7 +252,15 @@ def main():
     ap.add_argument("--workload", default="dsv2", choices=["tiny", "small", "dsv2", "dsv2_ragged", "dsv2_long"])
     ap.add_argument("--no-others", action="store_true", help="skip the other DeepSeek-V2-shaped workloads")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--counters-run", action="store_true",
+                    help="run the workload's steps and the calibration kernel only (profiled with rocprofv3 --pmc)")
+    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn rocprofv3 FETCH_SIZE / WRITE_SIZE csv runs into profiles/decode_latent_counters.json")
+    ap.add_argument("--counters-command", default="", help="command line recorded with ingested counters")
     args = ap.parse_args()
+    if args.ingest_counters:
+        print(json.dumps(ingest_counters(args.workload, *args.ingest_counters, args.counters_command), indent=1))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
               "Sequences are independent, so batch data-parallel scaling across GPUs needs no exchange.",
@@ -199,6 +273,9 @@ def main():
         sys.exit(1)
     from head_latent_attention_12_amd import mla
     mla.lib()
+    if args.counters_run:
+        counters_run(args.workload, args.steps, args.warmup)
+        return
 
     main_res = run_workload(args.workload, args.steps, args.warmup, min_sets=5)
     others = {}
@@ -242,6 +319,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": (round(traffic / (main_res["decode_kernel_ms"] * 1e-3) / 1e9, 1) if traffic else None),
+            "traffic_bytes_per_launch": (round(traffic) if traffic else None),
             "algorithmic_bytes_per_launch": main_res["k3_bytes"],
             "avg_launch_us": round(main_res["decode_kernel_ms"] * 1e3, 2),
             "mfma_tflops": round(main_res["decode_kernel_TFLOPs"], 1),

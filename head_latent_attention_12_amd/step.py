@@ -99,6 +99,20 @@ class DeviceStep:
         self.combine(stream)
         self.up_v(stream)
 
+    def capture(self) -> "torch.cuda.CUDAGraph":
+        """The five calls recorded once as a HIP graph (the library launches
+        kernels only: no allocation, copy or memset), replayed with
+        ``graph.replay()`` on the current stream."""
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.run()  # one eager pass on the capture stream before recording
+        torch.cuda.current_stream().wait_stream(side)
+        with torch.cuda.graph(graph):
+            self.run()
+        return graph
+
     # results ----------------------------------------------------------------
     def q_lat_f64(self) -> np.ndarray:
         return bits_to_f64(self.q_lat, self.inp.dtype)

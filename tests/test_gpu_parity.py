@@ -203,3 +203,25 @@ def test_large_score_growth_redo(name, override, factor, qf):
     rel = normwise_rel(out, ref["out"])
     print(f"[{name} redo] normwise rel err {rel:.3e}", flush=True)
     assert rel <= (1e-4 if inp.dtype == syn.F32 else 2e-2)
+
+
+@pytest.mark.parametrize("name,override", [("small", {}), ("dsv2", dict(B=4, T=2000))])
+def test_graph_replay_matches_eager(name, override):
+    """The step recorded as a HIP graph: every replay, with eager work and
+    synchronisation between replays, reproduces the eager result bit for bit."""
+    inp = syn.make_inputs(name, **override)
+    ds = _run(inp)
+    eager = {k: getattr(ds, k).clone() for k in ("out", "o_lat", "lse", "q_lat", "kv_cache")}
+    graph = ds.capture()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for k in ("out", "o_lat", "lse"):
+            getattr(ds, k).fill_(float("nan"))  # eager work on the buffers the graph writes
+        junk = torch.randn(1 << 20, device=ds.out.device).sum()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        for k, v in eager.items():
+            assert torch.equal(getattr(ds, k), v), f"replay {rep}: {k} differs from the eager run"
+    check_out(inp, ds.out.cpu().numpy().astype(np.float64), oracle_step(inp)["out"], tag=f"{name} graph")

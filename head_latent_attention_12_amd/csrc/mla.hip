@@ -53,6 +53,8 @@ constexpr float kLog2e = 1.44269504088896340736f;
 // exact maximum and then redoes the split with that reference (p <= 1), so the
 // accumulators are never rescaled inside the loop and at most one redo happens.
 constexpr float kRefSlack = 64.0f;
+// MI355X: 8 accelerator complex dies (XCDs), each with its own L2
+constexpr int kXcds = 8;
 
 // ---------------------------------------------------------------------------
 // bf16 helpers (storage type u16 holds bf16 bits)
@@ -205,6 +207,54 @@ __device__ __forceinline__ float xor32(float v, F op) {
   return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// A 64-bit value known to be uniform across the wave, in SGPRs
+// (readfirstlane returns int: each half goes through uint32_t so that the low
+// half is not sign-extended into the high one).
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
+  return ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32)) << 32) |
+         (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+}
+
+// Nine 1 KB LDS DMA copies (16 bytes per lane): lane l of copy n moves 16
+// bytes from sbase + off[n] to LDS byte ldst + 1024*n + 16*l.  Issued from
+// inline asm: the compiler cannot tell which LDS bytes a DMA writes and would
+// otherwise wait for every copy in flight (vmcnt(0)) before any later LDS
+// read; each wait on these copies is explicit instead (wait_vm_then_barrier).
+// m0, which the DMA uses as its LDS base, is saved and restored.
+#define MLA_DMA9_BODY(ADDR)                                                                                       \
+  "s_mov_b32 %[sv], m0\n\ts_mov_b32 m0, %[l]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[o0], " ADDR "\n\t"          \
+  "s_add_u32 m0, %[l], 1024\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[o1], " ADDR "\n\t"                              \
+  "s_add_u32 m0, %[l], 2048\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[o2], " ADDR "\n\t"                              \
+  "s_add_u32 m0, %[l], 3072\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[o3], " ADDR "\n\t"                              \
+  "s_add_u32 m0, %[l], 4096\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[o4], " ADDR "\n\t"                              \
+  "s_add_u32 m0, %[l], 5120\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[o5], " ADDR "\n\t"                              \
+  "s_add_u32 m0, %[l], 6144\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[o6], " ADDR "\n\t"                              \
+  "s_add_u32 m0, %[l], 7168\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[o7], " ADDR "\n\t"                              \
+  "s_add_u32 m0, %[l], 8192\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[o8], " ADDR "\n\t"                              \
+  "s_mov_b32 m0, %[sv]"
+
+// from a uniform base plus 32-bit lane offsets
+__device__ __forceinline__ void lds_dma9(uint64_t sbase, int ldst, const uint32_t (&off)[9]) {
+  uint32_t save;
+  asm volatile(MLA_DMA9_BODY("%[tb]")
+               : [sv] "=&s"(save)
+               : [tb] "s"(uniform_u64(sbase)), [l] "s"(__builtin_amdgcn_readfirstlane(ldst)), [o0] "v"(off[0]),
+                 [o1] "v"(off[1]), [o2] "v"(off[2]), [o3] "v"(off[3]), [o4] "v"(off[4]), [o5] "v"(off[5]),
+                 [o6] "v"(off[6]), [o7] "v"(off[7]), [o8] "v"(off[8])
+               : "memory", "scc");
+}
+
+// from per-lane 64-bit addresses
+__device__ __forceinline__ void lds_dma9(int ldst, const uint64_t (&addr)[9]) {
+  uint32_t save;
+  asm volatile(MLA_DMA9_BODY("off")
+               : [sv] "=&s"(save)
+               : [l] "s"(__builtin_amdgcn_readfirstlane(ldst)), [o0] "v"(addr[0]), [o1] "v"(addr[1]),
+                 [o2] "v"(addr[2]), [o3] "v"(addr[3]), [o4] "v"(addr[4]), [o5] "v"(addr[5]), [o6] "v"(addr[6]),
+                 [o7] "v"(addr[7]), [o8] "v"(addr[8])
+               : "memory", "scc");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vm_then_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
@@ -250,7 +300,7 @@ struct DecodeShape {
 template <typename T, int H, int R, int DR, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
     const T* __restrict__ q_lat, const T* __restrict__ cache, const int64_t* __restrict__ row_offsets,
-    const int32_t* __restrict__ seq_lens, int64_t total_rows, int32_t num_splits, int32_t chunk,
+    const int32_t* __restrict__ seq_lens, int64_t total_rows, int32_t batch, int32_t num_splits, int32_t chunk,
     T* __restrict__ o_part, float* __restrict__ lse_part, float scale_log2) {
   using S = DecodeShape<T, H, R, DR, NW>;
   using M = Mma<T>;
@@ -263,7 +313,14 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (LDS DMA base)
   const int hf = lane >> 5, l32 = lane & 31;
-  int bid = blockIdx.x;
+  // Work-groups are dealt to the 8 XCDs round-robin (blockIdx % 8).  Work
+  // item L = (b*num_splits + s)*GROUPS + g goes to XCD L / per, so that the
+  // splits of one sequence share an XCD and its L2 serves their common q_lat;
+  // the grid is padded to 8*per and the padding work-groups exit at once.
+  const int items = batch * num_splits * S::GROUPS;
+  const int per = (items + kXcds - 1) / kXcds;
+  int bid = ((int)blockIdx.x % kXcds) * per + (int)blockIdx.x / kXcds;
+  if (bid >= items) return;
   const int g = bid % S::GROUPS;
   bid /= S::GROUPS;
   const int s = bid % num_splits;
@@ -304,11 +361,15 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
   // 32 consecutive 1152-byte rows at tbase into a stage
   auto issue_rows = [&](const char* tbase, int stage) {
     LDS_AS char* dst = (LDS_AS char*)smem + stage * TB + wave * DPW * 1024;
+    if constexpr (BF16) {
+      lds_dma9((uint64_t)tbase, (int)(uintptr_t)dst, dma_off);
+    } else {
 #pragma unroll
-    for (int n = 0; n < DPW; ++n) {
-      uint32_t off = dma_off[n];
-      asm volatile("" : "+v"(off));  // keeps the 64-bit address sums from being hoisted out of the loop
-      __builtin_amdgcn_global_load_lds(tbase + off, dst + n * 1024, 16, 0, 0);
+      for (int n = 0; n < DPW; ++n) {
+        uint32_t off = dma_off[n];
+        asm volatile("" : "+v"(off));  // keeps the 64-bit address sums from being hoisted out of the loop
+        __builtin_amdgcn_global_load_lds(tbase + off, dst + n * 1024, 16, 0, 0);
+      }
     }
   };
   auto issue_tile = [&](int tile, int stage) {
@@ -319,16 +380,33 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
     } else {
       int ln = lane;
       asm volatile("" : "+v"(ln));  // recomputed here, not kept live
+      if constexpr (BF16) {
+        uint64_t addr[DPW];
 #pragma unroll
-      for (int n = 0; n < DPW; ++n) {
-        const int p = (wave * DPW + n) * 64 + ln;
-        const int t = p / NCH;
-        const int rel = min(rel0 + t, last_rel);
-        const char* src = split_base + (int64_t)rel * ROWB + 16 * swz_chunk<NCH>(t, p - t * NCH);
-        __builtin_amdgcn_global_load_lds(src, dst + n * 1024, 16, 0, 0);
+        for (int n = 0; n < DPW; ++n) {
+          const int p = (wave * DPW + n) * 64 + ln;
+          const int t = p / NCH;
+          const int rel = min(rel0 + t, last_rel);
+          addr[n] = (uint64_t)(split_base + (int64_t)rel * ROWB + 16 * swz_chunk<NCH>(t, p - t * NCH));
+        }
+        lds_dma9((int)(uintptr_t)dst, addr);
+      } else {
+#pragma unroll
+        for (int n = 0; n < DPW; ++n) {
+          const int p = (wave * DPW + n) * 64 + ln;
+          const int t = p / NCH;
+          const int rel = min(rel0 + t, last_rel);
+          const char* src = split_base + (int64_t)rel * ROWB + 16 * swz_chunk<NCH>(t, p - t * NCH);
+          __builtin_amdgcn_global_load_lds(src, dst + n * 1024, 16, 0, 0);
+        }
       }
     }
   };
+
+  // Tile t lives in stage stg(t).  The bf16 prologue stages q_lat through
+  // stages 0 and 1 while tiles 0 and 1 land in stages 2 and 3, hence the shift.
+  constexpr int SOFF = BF16 ? 2 : 0;
+  auto stg = [](int t) { return (t + SOFF) % STAGES; };
 
   typename M::Frag qf[KS];  // q_lat^T fragments (B operand of the score product), one head per lane
   if constexpr (!BF16) {
@@ -371,22 +449,31 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
   }
 
   if constexpr (BF16) {
-    // q_lat[b] is 128 rows of 1152 bytes, like four cache tiles: it is copied
-    // into the four stages with the tiles' coalesced DMA (heads 32g.. into
-    // stage g), each wave reads its 32 heads' fragments with the score-phase
-    // addressing, and only then do the first tiles overwrite the ring.
+    // q_lat[b] is 128 rows of 1152 bytes, like four cache tiles, copied with
+    // the tiles' coalesced DMA in two halves through stages 0 and 1 (heads
+    // 32g.. of half h into stage g, read by wave 2h + g with the score-phase
+    // addressing) while tiles 0 and 1 stream into stages 2 and 3.
     static_assert(H == STAGES * 32 && W * S::ES == ROWB, "q_lat of one sequence fills the ring");
     const char* qbase = (const char*)(q_lat + (int64_t)b * H * W);
+    issue_rows(qbase, 0);
+    issue_rows(qbase + TB, 1);
+    if (ntiles > 0) issue_tile(0, stg(0));
+    if (ntiles > 1) issue_tile(1, stg(1));
+    if (ntiles > 1) wait_vm_then_barrier<2 * DPW>();  // the first half has landed (the tiles may not)
+    else wait_vm_then_barrier<DPW>();
+    auto read_q = [&](int stage) {
+      const char* mine = smem + stage * TB;
 #pragma unroll
-    for (int g = 0; g < STAGES; ++g) issue_rows(qbase + (int64_t)g * TB, g);
+      for (int kk = 0; kk < KS; ++kk) qf[kk] = *(const i16x8*)(mine + s_base[kk & 3] + 128 * (kk >> 2));
+    };
+    if (wave < 2) read_q(wave);
+    wait_vm_then_barrier<2 * DPW>();  // stages 0 and 1 are read (lgkmcnt(0) in the barrier)
+    issue_rows(qbase + 2 * TB, 0);
+    issue_rows(qbase + 3 * TB, 1);
     wait_vm_then_barrier<0>();
-    const char* mine = smem + wave * TB;
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) qf[kk] = *(const i16x8*)(mine + s_base[kk & 3] + 128 * (kk >> 2));
-    wait_vm_then_barrier<0>();  // every wave holds its fragments: the ring is free
-#pragma unroll
-    for (int k = 0; k < STAGES - 1; ++k)
-      if (k < ntiles) issue_tile(k, k);
+    if (wave >= 2) read_q(wave - 2);
+    wait_vm_then_barrier<0>();  // every wave holds its fragments: stages 0 and 1 are free
+    if (ntiles > 2) issue_tile(2, stg(2));
   }
 
   __shared__ int redo_stamp[2];  // fp32 path: iteration stamp of an overflowed tile
@@ -461,7 +548,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
     if (pass > 0) {
 #pragma unroll
       for (int k = 0; k < STAGES - 1; ++k)
-        if (k < ntiles) issue_tile(k, k);
+        if (k < ntiles) issue_tile(k, stg(k));
     }
     bool redo = false;
     if (BF16 && pass != 1) {
@@ -478,7 +565,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
       i16x8 pf[2];
       bool ovf = false;  // wave-uniform: a score above m_ref + kRefSlack was seen
       {
-        f32x16 sacc = score_tile(0);
+        f32x16 sacc = score_tile(stg(0) * TB);
         const float mx = tile_max(sacc, r1 - r0);
         if (m_ref == -INFINITY) m_ref = mx;
         // p = 2^(s*scale - ref), rounded to the bf16 that P*V sees.  In a pass
@@ -510,22 +597,19 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
           if (t3 * TILE + TILE - 1 <= last_rel) {
             dma = 1;
             tbase += (uint64_t)t3 * TILE * ROWB;
-            ldst = lds_base + (t3 % STAGES) * TB + wave * DPW * 1024;
+            ldst = lds_base + stg(t3) * TB + wave * DPW * 1024;
           } else {
-            issue_tile(t3, t3 % STAGES);
+            issue_tile(t3, stg(t3));
           }
         }
         dma = __builtin_amdgcn_readfirstlane(dma);
         ldst = __builtin_amdgcn_readfirstlane(ldst);
-        // (readfirstlane returns int: each half goes through uint32_t so that
-        // the low half is not sign-extended into the high one)
-        const uint64_t tb_s = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(tbase >> 32)) << 32) |
-                              (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)tbase);
+        const uint64_t tb_s = uniform_u64(tbase);
         // iteration i: scores and softmax of tile i+1 (skipped at the last
         // tile: nx = 0, every row masked, weights 0, max -inf), P*V of tile i
         const int nx = __builtin_amdgcn_readfirstlane((i + 1 < ntiles) ? 1 : 0);
-        const int cur = lds_base + (i % STAGES) * TB;
-        const int nxt = lds_base + ((i + 1) % STAGES) * TB;
+        const int cur = lds_base + stg(i) * TB;
+        const int nxt = lds_base + stg(i + 1) * TB;
         const int tb0 = cur + tr_base[0], tb1 = cur + tr_base[1], tb2 = cur + tr_base[2], tb3 = cur + tr_base[3];
         const int sb0 = nxt + s_base[0], sb1 = nxt + s_base[1], sb2 = nxt + s_base[2], sb3 = nxt + s_base[3];
         // rows of the next tile before the split end (the mask inside the block)
@@ -581,8 +665,8 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
           redo = true;
           break;
         }
-        if (it + STAGES - 1 < ntiles) issue_tile(it + STAGES - 1, (it + STAGES - 1) % STAGES);
-        const int stage_off = (it % STAGES) * TB;
+        if (it + STAGES - 1 < ntiles) issue_tile(it + STAGES - 1, stg(it + STAGES - 1));
+        const int stage_off = stg(it) * TB;
         ++step;
         f32x16 sacc = score_tile(stage_off);
         const float mx = tile_max(sacc, r1 - (r0 + it * TILE));
@@ -1092,11 +1176,12 @@ mla_status launch_decode(const mla_dims& d, const void* q_lat, const void* cache
                          const int32_t* seq_lens, int64_t total_rows, int32_t max_seq_len, int32_t num_splits,
                          void* o_part, float* lse_part, hipStream_t stream) {
   using S = DecodeShape<T, H, R, DR, NW>;
-  const int64_t blocks = (int64_t)d.batch * num_splits * S::GROUPS;
+  const int64_t items = (int64_t)d.batch * num_splits * S::GROUPS;
+  const int64_t blocks = (items + kXcds - 1) / kXcds * kXcds;  // padded to whole rounds over the XCDs
   if (blocks > 0x7fffffff) return fail(MLA_ERR_UNSUPPORTED, "grid too large");
   const float scale_log2 = scale_of(d) * kLog2e;
   hipLaunchKernelGGL((decode_latent_kernel<T, H, R, DR, NW>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream,
-                     (const T*)q_lat, (const T*)cache, row_offsets, seq_lens, total_rows, num_splits,
+                     (const T*)q_lat, (const T*)cache, row_offsets, seq_lens, total_rows, d.batch, num_splits,
                      chunk_rows(max_seq_len, num_splits), (T*)o_part, lse_part, scale_log2);
   return launch_result("mla_decode_latent");
 }

@@ -947,11 +947,13 @@ __global__ __launch_bounds__(NW * 64) void absorb_q_kernel(const T* __restrict__
 
 // ---------------------------------------------------------------------------
 // K5: out^T[d][b] = sum_j W_UV[h][d][j] o_lat[b][h][j].
-// bf16: one work-group per (head, 32 output rows); its 4 waves split the
-// j range, issue all their weight loads up front (each lane 64 contiguous
-// bytes per 4 MFMA steps), and sum their 32x32 partial tiles through LDS, each
-// wave finishing one quarter of the rows.  The fp32 o_lat enters as hi + lo
-// bf16 parts (two MFMAs per step), keeping it exact to about 2^-16.
+// bf16: one work-group per (head, 32 output rows).  The weight tile (32 rows of
+// R bf16) and the o_lat rows of 16 sequences at a time are copied into LDS by
+// coalesced DMA (one 1 KB row slice per instruction), their 16-byte chunks
+// XOR-swizzled by row so that fragment reads are conflict-free.  The 4 waves
+// split the j range and sum their 32x32 partial tiles through LDS, each wave
+// finishing one quarter of the rows.  The fp32 o_lat enters as hi + lo bf16
+// parts (two MFMAs per step), keeping it exact to about 2^-16.
 // fp32: one wave per (head, 32 rows), fp32 MFMA over the whole j range.
 // ---------------------------------------------------------------------------
 
@@ -959,40 +961,60 @@ template <int R>
 __global__ __launch_bounds__(256) void up_v_bf16_kernel(const float* __restrict__ o_lat, const u16* __restrict__ w_uv,
                                                         int B, int H, int DV, float* __restrict__ out) {
   using M = Mma<u16>;
-  constexpr int JW = R / 4;        // j range of one wave
-  constexpr int G4 = JW / 64;      // groups of 4 MFMA steps
-  static_assert(R % 256 == 0, "R");
-  __shared__ f32x4 red[4][4][64];  // [wave][row quarter][lane]
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int JW = R / 4;          // j range of one wave
+  constexpr int G4 = JW / 64;        // groups of 4 MFMA steps
+  constexpr int WROW = R * 2;        // bytes of a weight row
+  constexpr int OROW = R * 4;        // bytes of an o_lat row
+  constexpr int BCH = 16;            // sequences per o_lat chunk
+  static_assert(R == 512, "one 1 KB DMA per weight row and two per o_lat row");
+  __shared__ __attribute__((aligned(16))) char wt[32 * WROW];
+  __shared__ __attribute__((aligned(16))) char ot[BCH * OROW];
+  __shared__ f32x4 red[4][4][64];    // [wave][row quarter][lane]
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hf = lane >> 5, l32 = lane & 31;
   const int nblk = DV / 32;
   const int h = blockIdx.x / nblk;
   const int d0 = (blockIdx.x - h * nblk) * 32;
+
+  // weight rows 8*wave .. 8*wave+7: LDS chunk l of row n holds source chunk l ^ (n & 15)
+  {
+    const char* wbase = (const char*)(w_uv + ((int64_t)h * DV + d0) * R);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int n = 8 * wave + i;
+      const char* src = wbase + (int64_t)n * WROW + 16 * (lane ^ (n & 15));
+      __builtin_amdgcn_global_load_lds(src, (LDS_AS char*)wt + n * WROW, 16, 0, 0);
+    }
+  }
   const int jw = wave * JW;
-  const u16* wrow = w_uv + ((int64_t)h * DV + d0 + l32) * R + jw;
-  i16x8 a[G4][4];
+  for (int b0 = 0; b0 < B; b0 += BCH) {
+    // o_lat rows b0 .. b0+15 (two 1 KB halves each, chunk c at c ^ (row & 15))
 #pragma unroll
-  for (int g = 0; g < G4; ++g)
-#pragma unroll
-    for (int u = 0; u < 4; ++u) a[g][u] = *(const i16x8*)(wrow + 64 * g + 32 * hf + 8 * u);
-  for (int b0 = 0; b0 < B; b0 += 32) {
+    for (int i = 0; i < 2 * BCH / 4; ++i) {
+      const int k = wave * (2 * BCH / 4) + i;  // copy k: row k/2, half k%2
+      const int r = k >> 1, half = k & 1;
+      if (b0 + r < B) {
+        const char* src = (const char*)(o_lat + ((int64_t)(b0 + r) * H + h) * R) + 16 * ((64 * half + lane) ^ (r & 15));
+        __builtin_amdgcn_global_load_lds(src, (LDS_AS char*)ot + r * OROW + half * 1024, 16, 0, 0);
+      }
+    }
+    __syncthreads();  // (waits for the DMA of this work-group)
     const int bb = b0 + l32;
-    const bool bok = bb < B;
-    const float* orow = o_lat + ((int64_t)(bok ? bb : 0) * H + h) * R + jw;
-    f32x4 xs[G4][4][2];  // all of this lane's o_lat values, loaded before the MFMA chain
-#pragma unroll
-    for (int g = 0; g < G4; ++g)
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int v = 0; v < 2; ++v) xs[g][u][v] = *(const f32x4*)(orow + 64 * g + 32 * hf + 8 * u + 4 * v);
+    const bool bok = l32 < BCH && bb < B;
     f32x16 acc = zero16();
 #pragma unroll
     for (int g = 0; g < G4; ++g) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        f32x4 x0 = xs[g][u][0], x1 = xs[g][u][1];
-        if (!bok) { x0 = f32x4{0, 0, 0, 0}; x1 = x0; }
+        const int kw = jw + 64 * g + 16 * u + 8 * hf;  // this lane's 8 k slots: kw .. kw+7
+        const i16x8 a = *(const i16x8*)(wt + l32 * WROW + 16 * ((kw >> 3) ^ (l32 & 15)));
+        f32x4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = x0;
+        if (bok) {
+          const int c = kw >> 2;  // fp32 chunks c, c+1
+          x0 = *(const f32x4*)(ot + l32 * OROW + 16 * (c ^ (l32 & 15)));
+          x1 = *(const f32x4*)(ot + l32 * OROW + 16 * ((c + 1) ^ (l32 & 15)));
+        }
         const float xv[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
         uint32_t hi[4], lo[4];
 #pragma unroll
@@ -1002,8 +1024,8 @@ __global__ __launch_bounds__(256) void up_v_bf16_kernel(const float* __restrict_
                               xv[2 * e + 1] - __uint_as_float(hi[e] & 0xffff0000u));
         }
         typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-        acc = M::mma(a[g][u], __builtin_bit_cast(i16x8, u32x4{hi[0], hi[1], hi[2], hi[3]}), acc);
-        acc = M::mma(a[g][u], __builtin_bit_cast(i16x8, u32x4{lo[0], lo[1], lo[2], lo[3]}), acc);
+        acc = M::mma(a, __builtin_bit_cast(i16x8, u32x4{hi[0], hi[1], hi[2], hi[3]}), acc);
+        acc = M::mma(a, __builtin_bit_cast(i16x8, u32x4{lo[0], lo[1], lo[2], lo[3]}), acc);
       }
     }
 #pragma unroll
@@ -1012,7 +1034,7 @@ __global__ __launch_bounds__(256) void up_v_bf16_kernel(const float* __restrict_
     // wave w sums row quarter q = w (rows 8w + 4hf + 0..3 of the 32-row block)
     f32x4 sum = red[0][wave][lane] + red[1][wave][lane] + red[2][wave][lane] + red[3][wave][lane];
     if (bok) *(f32x4*)(out + ((int64_t)bb * H + h) * DV + d0 + 8 * wave + 4 * hf) = sum;
-    __syncthreads();
+    __syncthreads();  // red and ot are reused by the next chunk
   }
 }
 
@@ -1075,33 +1097,53 @@ __global__ __launch_bounds__(256) void rope_append_kernel(const T* __restrict__ 
                                                           const int64_t* __restrict__ row_offsets, int64_t total_rows,
                                                           int H, int R, int DR, RopeFreqs freqs,
                                                           T* __restrict__ q_lat, T* __restrict__ cache) {
+  constexpr int QP = 2;  // q_rope pairs per thread (16 heads x d_rope/2 <= 256 * QP)
   __shared__ double cs[2][256];
   const int hblocks = (H + 15) / 16;
   const int b = blockIdx.x / hblocks;
   const int hb = blockIdx.x - b * hblocks;
-  const int pos = positions[b];
   const int half = DR / 2;
-  for (int i = threadIdx.x; i < half; i += blockDim.x) sincos_reduced((double)pos * freqs.theta[i], &cs[1][i], &cs[0][i]);
-  __syncthreads();
   const int W = R + DR;
   const int h0 = hb * 16, h1 = min(H, h0 + 16);
-  for (int idx = threadIdx.x; idx < (h1 - h0) * half; idx += blockDim.x) {
+  const int npairs = (h1 - h0) * half;
+  // every global load is issued before the sincos work that waits on positions
+  T qx[QP][2];
+#pragma unroll
+  for (int u = 0; u < QP; ++u) {
+    const int idx = (int)threadIdx.x + u * (int)blockDim.x;
     const int hh = h0 + idx / half, i = idx % half;
-    const T* src = q_rope + ((int64_t)b * H + hh) * DR + 2 * i;
-    const double x0 = load_d<T>(src[0]), x1 = load_d<T>(src[1]);
+    const T* src = q_rope + ((int64_t)b * H + (idx < npairs ? hh : h0)) * DR + 2 * i;
+    qx[u][0] = src[0];
+    qx[u][1] = src[1];
+  }
+  const bool row_block = hb == 0;
+  T kx[2] = {T(0), T(0)};
+  if (row_block && (int)threadIdx.x < half) {
+    kx[0] = k_rope_new[(int64_t)b * DR + 2 * threadIdx.x];
+    kx[1] = k_rope_new[(int64_t)b * DR + 2 * threadIdx.x + 1];
+  }
+  const int pos = positions[b];
+  for (int i = threadIdx.x; i < half; i += blockDim.x) sincos_reduced((double)pos * freqs.theta[i], &cs[1][i], &cs[0][i]);
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < QP; ++u) {
+    const int idx = (int)threadIdx.x + u * (int)blockDim.x;
+    if (idx >= npairs) break;
+    const int hh = h0 + idx / half, i = idx % half;
+    const double x0 = load_d<T>(qx[u][0]), x1 = load_d<T>(qx[u][1]);
     const double c = cs[0][i], s = cs[1][i];
     T* dst = q_lat + ((int64_t)b * H + hh) * W + R + 2 * i;
     dst[0] = store_d<T>(x0 * c - x1 * s);
     dst[1] = store_d<T>(x0 * s + x1 * c);
   }
-  if (hb != 0) return;
+  if (!row_block) return;
   int64_t row = row_offsets[b] + pos;
   row = row < 0 ? 0 : (row >= total_rows ? total_rows - 1 : row);
   T* crow = cache + row * W;
   for (int k = threadIdx.x; k < R; k += blockDim.x) crow[k] = c_kv_new[(int64_t)b * R + k];
-  for (int i = threadIdx.x; i < half; i += blockDim.x) {
-    const T* src = k_rope_new + (int64_t)b * DR + 2 * i;
-    const double x0 = load_d<T>(src[0]), x1 = load_d<T>(src[1]);
+  if ((int)threadIdx.x < half) {
+    const int i = threadIdx.x;
+    const double x0 = load_d<T>(kx[0]), x1 = load_d<T>(kx[1]);
     const double c = cs[0][i], s = cs[1][i];
     crow[R + 2 * i] = store_d<T>(x0 * c - x1 * s);
     crow[R + 2 * i + 1] = store_d<T>(x0 * s + x1 * c);
@@ -1252,7 +1294,7 @@ mla_status mla_rope_append(const mla_dims* dims, const void* q_rope, const void*
   if (positions == nullptr || row_offsets == nullptr) return fail(MLA_ERR_INVALID_ARG, "positions/row_offsets NULL");
   if ((st = check_ptrs({q_rope, c_kv_new, k_rope_new, q_lat, kv_cache})) != MLA_OK) return st;
   if (total_rows < 1) return fail(MLA_ERR_INVALID_ARG, "total_rows must be >= 1");
-  if (dims->d_rope > 512) return fail(MLA_ERR_UNSUPPORTED, "d_rope above 512");
+  if (dims->d_rope > 64) return fail(MLA_ERR_UNSUPPORTED, "d_rope above 64");  // 16 heads x d_rope/2 pairs <= 2 per thread
   g_last_error.clear();
   hipStream_t s = (hipStream_t)stream;
   const double base = dims->rope_base > 0.f ? (double)dims->rope_base : 10000.0;

@@ -207,6 +207,18 @@ __device__ __forceinline__ float xor32(float v, F op) {
   return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// Sum and inclusive prefix sum of an int over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_prefix_sum(int v) {
+  const int lane = (int)(threadIdx.x & 63);
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int u = __shfl_up(v, d);
+    if (lane >= d) v += u;
+  }
+  return v;
+}
+__device__ __forceinline__ int wave_sum(int v) { return __shfl(wave_prefix_sum(v), 63); }
+
 // A 64-bit value known to be uniform across the wave, in SGPRs
 // (readfirstlane returns int: each half goes through uint32_t so that the low
 // half is not sign-extended into the high one).
@@ -313,33 +325,87 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (LDS DMA base)
   const int hf = lane >> 5, l32 = lane & 31;
-  // Work-groups are dealt to the 8 XCDs round-robin (blockIdx % 8).  Work
-  // item L = (b*num_splits + s)*GROUPS + g goes to XCD L / per, so that the
-  // splits of one sequence share an XCD and its L2 serves their common q_lat;
-  // the grid is padded to 8*per and the padding work-groups exit at once.
-  const int items = batch * num_splits * S::GROUPS;
-  const int per = (items + kXcds - 1) / kXcds;
-  int bid = ((int)blockIdx.x % kXcds) * per + (int)blockIdx.x / kXcds;
-  if (bid >= items) return;
-  const int g = bid % S::GROUPS;
-  bid /= S::GROUPS;
-  const int s = bid % num_splits;
-  const int b = bid / num_splits;
+  // Work items are the non-empty splits (b, s < n_b), n_b = ceil(seq_len_b /
+  // chunk) clamped to [1, num_splits], taken in sequence order (times GROUPS head
+  // groups).  Work-groups are dealt to the 8 XCDs round-robin (blockIdx % 8);
+  // item L goes to XCD L / per, so that the splits of one sequence share an
+  // XCD (its L2 serves their common q_lat) and each XCD gets the same number
+  // of items whatever the lengths.  The grid (host: 8 * ceil(B*num_splits*
+  // GROUPS / 8)) bounds the item count; work-groups without an item exit.
+  // The work-group of split 0 marks the sequence's empty splits (lse -inf).
+  // Each lane looks at one sequence per step of 64; the first 64 lengths and
+  // row offsets are loaded once and serve both passes, so that with B <= 64
+  // the item's metadata costs a single round of loads.
+  auto splits_of = [&](int len) { return max(1, min(num_splits, (len + chunk - 1) / chunk)); };
+  int b = 0, s = 0, n_b = 0, seq_len = 0;
+  int64_t row_off = 0;
+  {
+    const int bid = (int)blockIdx.x;
+    const bool in0 = lane < batch;
+    const int len0 = in0 ? seq_lens[lane] : 0;
+    const int64_t off0 = in0 ? row_offsets[lane] : 0;
+    // pass 1: item count
+    int items = wave_sum(in0 ? splits_of(len0) : 0);
+    for (int c0 = 64; c0 < batch; c0 += 64) {
+      const int bb = c0 + lane;
+      items += wave_sum(bb < batch ? splits_of(seq_lens[bb]) : 0);
+    }
+    items *= S::GROUPS;
+    const int per = (items + kXcds - 1) / kXcds;
+    const int item = (bid % kXcds) * per + bid / kXcds;
+    // an XCD's work-groups past its `per` items would repeat the next XCD's
+    if (bid / kXcds >= per || item >= items) return;
+    // pass 2: the sequence holding the item (inclusive prefix sums per step)
+    const int want = item / S::GROUPS;
+    int base = 0;
+    for (int c0 = 0; c0 < batch; c0 += 64) {
+      const int bb = c0 + lane;
+      int len = len0;
+      int64_t off = off0;
+      if (c0 > 0) {
+        len = bb < batch ? seq_lens[bb] : 0;
+        off = bb < batch ? row_offsets[bb] : 0;
+      }
+      const int n = bb < batch ? splits_of(len) : 0;
+      const int incl = wave_prefix_sum(n) + base;
+      const uint64_t hit = __ballot(incl > want);
+      if (hit != 0) {
+        const int first = __builtin_ctzll(hit);
+        b = c0 + first;
+        n_b = __shfl(n, first);
+        s = want - (__shfl(incl, first) - n_b);
+        seq_len = __shfl(len, first);
+        row_off = __shfl(off, first);
+        break;
+      }
+      base = __shfl(incl, 63);
+    }
+    b = __builtin_amdgcn_readfirstlane(b);
+    s = __builtin_amdgcn_readfirstlane(s);
+    n_b = __builtin_amdgcn_readfirstlane(n_b);
+    seq_len = __builtin_amdgcn_readfirstlane(seq_len);
+    row_off = (int64_t)uniform_u64((uint64_t)row_off);
+  }
+  const int g = 0;  // one head group per work item (GROUPS == 1 here)
+  static_assert(S::GROUPS == 1, "one work-group covers all heads");
   const int head = g * S::HEADS_PER_GROUP + wave * 32 + l32;
   const bool head_ok = head < H;
 
-  const int seq_len = seq_lens[b];
   const int r0 = s * chunk;
   const int r1 = min(r0 + chunk, seq_len);
   float* lse_out = lse_part + ((int64_t)b * num_splits + s) * H;
-  if (r0 >= r1) {  // empty split (block-uniform)
+  if (s == 0) {
+    for (int e = n_b * H + (int)threadIdx.x; e < num_splits * H; e += NW * 64)
+      lse_part[(int64_t)b * num_splits * H + e] = -INFINITY;
+  }
+  if (r0 >= r1) {  // only with seq_lens[b] < 1 (inconsistent metadata): nothing to attend
     if (hf == 0 && head_ok) lse_out[head] = -INFINITY;
     return;
   }
   const int ntiles = (r1 - r0 + TILE - 1) / TILE;
   // Absolute cache rows of this split, clamped into the cache: inconsistent
   // metadata can then only produce wrong numbers, never a stray access.
-  int64_t row_lo = row_offsets[b] + r0, row_hi = row_offsets[b] + r1 - 1;
+  int64_t row_lo = row_off + r0, row_hi = row_off + r1 - 1;
   row_lo = row_lo < 0 ? 0 : (row_lo > total_rows - 1 ? total_rows - 1 : row_lo);
   row_hi = row_hi < row_lo ? row_lo : (row_hi > total_rows - 1 ? total_rows - 1 : row_hi);
   const char* split_base = (const char*)cache + row_lo * ROWB;
@@ -1408,13 +1474,29 @@ int32_t mla_plan_splits(const mla_dims* dims, int32_t max_seq_len, int64_t total
     if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess) return 0;
     num_cus = prop.multiProcessorCount;
   }
-  // One work-group per compute unit: split rows so that (splits in use) fit
-  // the CUs, keeping room for the partial last split of every sequence.
-  const int64_t slots = std::max<int64_t>(1, (int64_t)num_cus - dims->batch / 2);
-  int64_t chunk = (total_rows + slots - 1) / slots;
-  chunk = std::max<int64_t>(32, ((chunk + 31) / 32) * 32);
-  int64_t splits = ((int64_t)max_seq_len + chunk - 1) / chunk;
-  if (splits > kMaxSplits) splits = kMaxSplits;
+  // Pick the split count with the smallest estimated decode time.  A split is
+  // one work-group and a compute unit runs one at a time, dealt evenly over
+  // the 8 XCDs, so the time is (rounds of work-groups per CU) x (tiles per
+  // split + a fixed per-split cost for the prologue and the partial's store,
+  // about kSplitCost tiles).  Only the total and the longest length are known
+  // here: the non-empty splits are at most B * ceil(max / chunk), and for
+  // mixed lengths about total / chunk plus the partial last split of every
+  // sequence (counted as 0.6 of a split each, a little above the mean).
+  // Ties go to fewer splits (less partial traffic for the combine).
+  constexpr int64_t kSplitCost = 8;
+  const int64_t B = dims->batch, cus_per_xcd = std::max<int64_t>(1, num_cus / 8);
+  const int64_t s_max = std::min<int64_t>(kMaxSplits, ((int64_t)max_seq_len + 31) / 32);
+  int64_t best = 1, best_cost = INT64_MAX;
+  for (int64_t sp = 1; sp <= s_max; ++sp) {
+    const int64_t chunk = chunk_rows(max_seq_len, (int32_t)sp);
+    const int64_t full = B * (((int64_t)max_seq_len + chunk - 1) / chunk);
+    const int64_t est = std::min(full, (total_rows + chunk - 1) / chunk + (6 * B + 9) / 10);
+    const int64_t per_xcd = (est + 7) / 8;
+    const int64_t rounds = (per_xcd + cus_per_xcd - 1) / cus_per_xcd;
+    const int64_t cost = rounds * (chunk / 32 + kSplitCost);
+    if (cost < best_cost) best_cost = cost, best = sp;
+  }
+  const int64_t splits = best;
   return (int32_t)std::max<int64_t>(1, splits);
 }
 

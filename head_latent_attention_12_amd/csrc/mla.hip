@@ -1,7 +1,8 @@
 // Absorbed Multi-head Latent Attention decode for MI355X (gfx950 / CDNA4).
 //
 // Five kernels behind the C ABI declared in include/mla.h:
-//   absorb_q_kernel       q~ = W_UK^T q_nope                (32x32 MFMA, W_UK staged in LDS)
+//   absorb_q_kernel       q~ = W_UK^T q_nope                (32x32 MFMA, W_UK staged in LDS; fp32)
+//   absorb_q_bf16_kernel  the same for bf16, weight tile and queries copied to LDS by DMA
 //   rope_append_kernel    RoPE(q_rope), append [c_kv_new | RoPE(k_rope_new)]
 //   decode_latent_kernel  split-KV flash decode over the latent cache (32x32 MFMA)
 //   combine_kernel        log-sum-exp merge of the splits
@@ -943,30 +944,54 @@ __global__ __launch_bounds__(NW * 64) void absorb_q_kernel(const T* __restrict__
   __shared__ __attribute__((aligned(16))) char smem[DH * ROWB];
 
   const int nblk = R / COLS;
-  const int h = blockIdx.x / nblk;
-  const int j0 = (blockIdx.x - h * nblk) * COLS;
+  // The nblk column blocks of a head run on one XCD (work-groups are dealt to
+  // the 8 XCDs round-robin), so that the head's q_nope rows come from HBM into
+  // one L2 once.  The grid covers whole groups of 8 heads.
+  int h, blk;
+  {
+    const int bid = (int)blockIdx.x;
+    const int grp = bid / (kXcds * nblk);
+    const int rem = bid - grp * (kXcds * nblk);
+    h = grp * kXcds + rem % kXcds;
+    blk = rem / kXcds;
+  }
+  if (h >= H) return;
+  const int j0 = blk * COLS;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int hf = lane >> 5, l32 = lane & 31;
-  // the first 32 queries' fragments are requested before the weight tile, so
-  // the two loads overlap
-  typename M::Frag bq[KS];
-  auto load_q = [&](int b0) {
+  // query fragments of 32 sequences (rows past B read sequence 0 and are
+  // zeroed before use)
+  typedef typename M::Frag QF[KS];
+  auto load_q = [&](QF& f, int b0) {
     const int bb = b0 + l32;
     const T* qrow = q_nope + ((int64_t)(bb < B ? bb : 0) * H + h) * DH;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       if constexpr (ES == 2) {
-        bq[kk] = *(const i16x8*)(qrow + 16 * kk + 8 * hf);
+        f[kk] = *(const i16x8*)(qrow + 16 * kk + 8 * hf);
       } else {
-        bq[kk] = qrow[2 * kk + hf];
+        f[kk] = qrow[2 * kk + hf];
       }
     }
   };
-  load_q(0);
-  for (int idx = threadIdx.x; idx < DH * NCH; idx += NW * 64) {
+  // The first 32 queries and the whole weight tile (W_UK[h][:, j0:j0+COLS],
+  // PER 16-byte chunks per thread) are all requested before the first wait.
+  QF bq;
+  load_q(bq, 0);
+  constexpr int PER = DH * NCH / (NW * 64);
+  static_assert(PER * NW * 64 == DH * NCH, "tile chunks split evenly over the threads");
+  int4 wv[PER];
+#pragma unroll
+  for (int it = 0; it < PER; ++it) {
+    const int idx = (int)threadIdx.x + it * NW * 64;
     const int d = idx / NCH, c = idx - (idx / NCH) * NCH;
-    const int4 v = *(const int4*)((const char*)(w_uk + ((int64_t)h * DH + d) * R + j0) + 16 * c);
-    *(int4*)(smem + d * ROWB + 16 * swz_chunk<NCH>(d, c)) = v;
+    wv[it] = *(const int4*)((const char*)(w_uk + ((int64_t)h * DH + d) * R + j0) + 16 * c);
+  }
+#pragma unroll
+  for (int it = 0; it < PER; ++it) {
+    const int idx = (int)threadIdx.x + it * NW * 64;
+    const int d = idx / NCH, c = idx - (idx / NCH) * NCH;
+    *(int4*)(smem + d * ROWB + 16 * swz_chunk<NCH>(d, c)) = wv[it];
   }
   __syncthreads();
 
@@ -983,7 +1008,10 @@ __global__ __launch_bounds__(NW * 64) void absorb_q_kernel(const T* __restrict__
   for (int b0 = 0; b0 < B; b0 += 32) {
     const int bb = b0 + l32;
     const bool bok = bb < B;
-    if (b0 > 0) load_q(b0);
+    if (b0 > 0) {
+      load_q(bq, b0);
+      __builtin_amdgcn_sched_barrier(0);  // all KS loads in flight before the first MFMA waits
+    }
     f32x16 acc = zero16();
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
@@ -1011,6 +1039,101 @@ __global__ __launch_bounds__(NW * 64) void absorb_q_kernel(const T* __restrict__
   }
 }
 
+// bf16: the weight tile and the queries of 64 sequences at a time are copied
+// into LDS by DMA (1 KB per wave instruction, no register staging), all issued
+// before the one wait, so a work-group pays a single HBM round trip up front.
+// Query rows are stored with their 16-byte chunks XOR-swizzled by row, which
+// makes the fragment reads (lane = sequence) conflict-free.
+template <int DH>
+__global__ __launch_bounds__(128) void absorb_q_bf16_kernel(const u16* __restrict__ q_nope,
+                                                            const u16* __restrict__ w_uk, int B, int H, int R,
+                                                            u16* __restrict__ q_lat, int W) {
+  using M = Mma<u16>;
+  constexpr int COLS = 64, ROWB = 2 * COLS, NCH = ROWB / 16, KS = DH / M::KSTEP;
+  constexpr int QROWS = 64, QROWB = 2 * DH, QCH = QROWB / 16;
+  constexpr int WCOP = DH * ROWB / 1024 / 2;      // weight DMA copies per wave
+  constexpr int QCOP = QROWS * QROWB / 1024 / 2;  // query DMA copies per wave
+  static_assert(WCOP >= 1 && QCOP >= 1 && (QCH & (QCH - 1)) == 0, "shape");
+  __shared__ __attribute__((aligned(1024))) char wt[DH * ROWB];
+  __shared__ __attribute__((aligned(1024))) char qs[QROWS * QROWB];
+
+  const int nblk = R / COLS;
+  // the nblk column blocks of a head run on one XCD (its L2 then serves the
+  // head's queries to all of them); the grid covers whole groups of 8 heads
+  int h, blk;
+  {
+    const int bid = (int)blockIdx.x;
+    const int grp = bid / (kXcds * nblk);
+    const int rem = bid - grp * (kXcds * nblk);
+    h = grp * kXcds + rem % kXcds;
+    blk = rem / kXcds;
+  }
+  if (h >= H) return;
+  const int j0 = blk * COLS;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hf = lane >> 5, l32 = lane & 31;
+
+  // LDS chunk p of the query block holds row p / QCH, chunk (p % QCH) ^ (row % QCH)
+  auto issue_q = [&](int b0) {
+#pragma unroll
+    for (int n = 0; n < QCOP; ++n) {
+      if ((wave * QCOP + n) * 64 / QCH >= B - b0) break;  // the copy's rows are all past B
+      const int p = (wave * QCOP + n) * 64 + lane;
+      const int row = p / QCH, c = (p % QCH) ^ (row & (QCH - 1));
+      const int bb = b0 + row;
+      const char* src = (const char*)(q_nope + ((int64_t)(bb < B ? bb : 0) * H + h) * DH) + 16 * c;
+      __builtin_amdgcn_global_load_lds(src, (LDS_AS char*)qs + (wave * QCOP + n) * 1024, 16, 0, 0);
+    }
+  };
+  issue_q(0);
+  // weight tile W_UK[h][:, j0:j0+64]: LDS chunk p holds row d = p / NCH, chunk
+  // swz(d, p % NCH) (the swizzle is an XOR, its own inverse)
+#pragma unroll
+  for (int n = 0; n < WCOP; ++n) {
+    const int p = (wave * WCOP + n) * 64 + lane;
+    const int d = p / NCH, c = swz_chunk<NCH>(d, p % NCH);
+    const char* src = (const char*)(w_uk + ((int64_t)h * DH + d) * R + j0) + 16 * c;
+    __builtin_amdgcn_global_load_lds(src, (LDS_AS char*)wt + (wave * WCOP + n) * 1024, 16, 0, 0);
+  }
+  __syncthreads();  // (waits for this work-group's DMA)
+
+  typename M::Frag af[KS];
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk)
+    af[kk] = load_col8_tr<ROWB, NCH>(wt, 32 * wave, 16 * kk + 8 * hf, 16 * kk + 8 * hf + 4, lane);
+  const int jw = j0 + 32 * wave;
+  for (int b0 = 0; b0 < B; b0 += QROWS) {
+    if (b0 > 0) {
+      __syncthreads();  // every wave is done with the previous block
+      issue_q(b0);
+      __syncthreads();
+    }
+#pragma unroll
+    for (int sub = 0; sub < QROWS / 32; ++sub) {
+      const int row = 32 * sub + l32, bb = b0 + row;
+      if (b0 + 32 * sub >= B) break;
+      const bool bok = bb < B;
+      f32x16 acc = zero16();
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        i16x8 b = *(const i16x8*)(qs + row * QROWB + 16 * ((2 * kk + hf) ^ (row & (QCH - 1))));
+        if (!bok) b = i16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        acc = M::mma(af[kk], b, acc);
+      }
+      if (bok) {
+        u16* dst = q_lat + ((int64_t)bb * H + h) * W + jw;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+          *(u32x2*)(dst + 8 * q + 4 * hf) =
+              u32x2{pack2bf(acc[4 * q], acc[4 * q + 1]), pack2bf(acc[4 * q + 2], acc[4 * q + 3])};
+        }
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // K5: out^T[d][b] = sum_j W_UV[h][d][j] o_lat[b][h][j].
 // bf16: one work-group per (head, 32 output rows).  The weight tile (32 rows of
@@ -1019,7 +1142,8 @@ __global__ __launch_bounds__(NW * 64) void absorb_q_kernel(const T* __restrict__
 // XOR-swizzled by row so that fragment reads are conflict-free.  The 4 waves
 // split the j range and sum their 32x32 partial tiles through LDS, each wave
 // finishing one quarter of the rows.  The fp32 o_lat enters as hi + lo bf16
-// parts (two MFMAs per step), keeping it exact to about 2^-16.
+// parts (two MFMAs per step), keeping it exact to about 2^-16.  The row blocks
+// of one head run on one XCD.
 // fp32: one wave per (head, 32 rows), fp32 MFMA over the whole j range.
 // ---------------------------------------------------------------------------
 
@@ -1040,8 +1164,17 @@ __global__ __launch_bounds__(256) void up_v_bf16_kernel(const float* __restrict_
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hf = lane >> 5, l32 = lane & 31;
   const int nblk = DV / 32;
-  const int h = blockIdx.x / nblk;
-  const int d0 = (blockIdx.x - h * nblk) * 32;
+  // the nblk row blocks of a head run on one XCD, whose L2 then serves them
+  // the head's o_lat rows; the grid covers whole groups of 8 heads
+  int h, d0;
+  {
+    const int bid = (int)blockIdx.x;
+    const int grp = bid / (kXcds * nblk);
+    const int rem = bid - grp * (kXcds * nblk);
+    h = grp * kXcds + rem % kXcds;
+    d0 = (rem / kXcds) * 32;
+  }
+  if (h >= H) return;
 
   // weight rows 8*wave .. 8*wave+7: LDS chunk l of row n holds source chunk l ^ (n & 15)
   {
@@ -1297,20 +1430,40 @@ mla_status launch_decode(const mla_dims& d, const void* q_lat, const void* cache
 template <typename T, int NW, int DH>
 mla_status launch_absorb(const mla_dims& d, const void* q_nope, const void* w_uk, void* q_lat, hipStream_t stream) {
   if (d.rank % (32 * NW) != 0) return fail(MLA_ERR_UNSUPPORTED, "rank must be a multiple of the column block");
-  const int blocks = d.heads * (d.rank / (32 * NW));
+  const int blocks = (d.heads + kXcds - 1) / kXcds * kXcds * (d.rank / (32 * NW));  // whole groups of 8 heads
   hipLaunchKernelGGL((absorb_q_kernel<T, NW, DH>), dim3(blocks), dim3(NW * 64), 0, stream, (const T*)q_nope,
                      (const T*)w_uk, d.batch, d.heads, d.rank, (T*)q_lat, d.rank + d.d_rope);
   return launch_result("mla_absorb_q");
 }
 
+template <int DH>
+mla_status launch_absorb_bf16(const mla_dims& d, const void* q_nope, const void* w_uk, void* q_lat,
+                              hipStream_t stream) {
+  if (d.rank % 64 != 0) return fail(MLA_ERR_UNSUPPORTED, "rank must be a multiple of 64");
+  const int blocks = (d.heads + kXcds - 1) / kXcds * kXcds * (d.rank / 64);  // whole groups of 8 heads
+  hipLaunchKernelGGL((absorb_q_bf16_kernel<DH>), dim3(blocks), dim3(128), 0, stream, (const u16*)q_nope,
+                     (const u16*)w_uk, d.batch, d.heads, d.rank, (u16*)q_lat, d.rank + d.d_rope);
+  return launch_result("mla_absorb_q");
+}
+
 template <typename T, int NW>
 mla_status launch_absorb_dh(const mla_dims& d, const void* q_nope, const void* w_uk, void* q_lat, hipStream_t stream) {
-  switch (d.d_head) {
-    case 32: return launch_absorb<T, NW, 32>(d, q_nope, w_uk, q_lat, stream);
-    case 64: return launch_absorb<T, NW, 64>(d, q_nope, w_uk, q_lat, stream);
-    case 128: return launch_absorb<T, NW, 128>(d, q_nope, w_uk, q_lat, stream);
-    case 256: return launch_absorb<T, NW, 256>(d, q_nope, w_uk, q_lat, stream);
-    default: return fail(MLA_ERR_UNSUPPORTED, "d_head");
+  if constexpr (sizeof(T) == 2) {
+    switch (d.d_head) {
+      case 32: return launch_absorb_bf16<32>(d, q_nope, w_uk, q_lat, stream);
+      case 64: return launch_absorb_bf16<64>(d, q_nope, w_uk, q_lat, stream);
+      case 128: return launch_absorb_bf16<128>(d, q_nope, w_uk, q_lat, stream);
+      case 256: return launch_absorb_bf16<256>(d, q_nope, w_uk, q_lat, stream);
+      default: return fail(MLA_ERR_UNSUPPORTED, "d_head");
+    }
+  } else {
+    switch (d.d_head) {
+      case 32: return launch_absorb<T, NW, 32>(d, q_nope, w_uk, q_lat, stream);
+      case 64: return launch_absorb<T, NW, 64>(d, q_nope, w_uk, q_lat, stream);
+      case 128: return launch_absorb<T, NW, 128>(d, q_nope, w_uk, q_lat, stream);
+      case 256: return launch_absorb<T, NW, 256>(d, q_nope, w_uk, q_lat, stream);
+      default: return fail(MLA_ERR_UNSUPPORTED, "d_head");
+    }
   }
 }
 
@@ -1444,7 +1597,8 @@ mla_status mla_up_v(const mla_dims* dims, const float* o_lat, const void* w_uv, 
   hipStream_t s = (hipStream_t)stream;
   if (dims->dtype == MLA_BF16) {
     if (dims->rank != 512) return fail(MLA_ERR_UNSUPPORTED, "bf16 up_v is built for rank 512");
-    hipLaunchKernelGGL((up_v_bf16_kernel<512>), dim3(dims->heads * (dims->d_v / 32)), dim3(256), 0, s, o_lat,
+    const int blocks = (dims->heads + kXcds - 1) / kXcds * kXcds * (dims->d_v / 32);  // whole groups of 8 heads
+    hipLaunchKernelGGL((up_v_bf16_kernel<512>), dim3(blocks), dim3(256), 0, s, o_lat,
                        (const u16*)w_uv, dims->batch, dims->heads, dims->d_v, out);
   } else {
     hipLaunchKernelGGL(up_v_f32_kernel, dim3(dims->heads * (dims->d_v / 32)), dim3(64), 0, s, o_lat,

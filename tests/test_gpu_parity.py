@@ -125,6 +125,19 @@ def test_step_matches_oracle(name, override):
     check_step(inp, ds, ref, tag=f"{name} {override} splits={ds.num_splits}")
 
 
+@pytest.mark.parametrize("override", [
+    dict(B=3, T=200, d_head=32, d_v=32),
+    dict(B=5, T=300, d_head=64, d_v=96),
+    dict(B=40, T=150, d_head=256, d_v=256),   # two query blocks in W_UK's pass, 8 output row blocks
+])
+def test_head_widths(override):
+    """Other content-head and value widths of the bf16 instantiation (the
+    absorption and W_UV kernels are templated on them)."""
+    inp = syn.make_inputs("dsv2", **override)
+    ds = _run(inp)
+    check_step(inp, ds, oracle_step(inp), tag=f"dsv2 {override}")
+
+
 @pytest.mark.parametrize("name,lens", [
     ("tiny", [0]),                       # empty cache: only the appended row
     ("tiny", [31]), ("tiny", [32]), ("tiny", [33]),

@@ -650,37 +650,17 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
         pf[0] = __builtin_bit_cast(i16x8, u32x4{w[0], w[1], w[2], w[3]});
         pf[1] = __builtin_bit_cast(i16x8, u32x4{w[4], w[5], w[6], w[7]});
       }
-      for (int i = 0; i < ntiles; ++i) {
-        // tile i+1 has landed (tile i+2 may still be in flight) and every wave
-        // has finished iteration i-1
-        if (i + 2 < ntiles) wait_vm_then_barrier<DPW>();
-        else wait_vm_then_barrier<0>();
-        // tile i+3 into the stage of tile i-1: a full tile is copied by the
-        // asm block below (spread over its score MFMAs), a partial one here
-        const int t3 = i + STAGES - 1;
-        int dma = 0, ldst = 0;
-        uint64_t tbase = (uint64_t)split_base;
-        if (t3 < ntiles) {
-          if (t3 * TILE + TILE - 1 <= last_rel) {
-            dma = 1;
-            tbase += (uint64_t)t3 * TILE * ROWB;
-            ldst = lds_base + stg(t3) * TB + wave * DPW * 1024;
-          } else {
-            issue_tile(t3, stg(t3));
-          }
-        }
-        dma = __builtin_amdgcn_readfirstlane(dma);
-        ldst = __builtin_amdgcn_readfirstlane(ldst);
-        const uint64_t tb_s = uniform_u64(tbase);
-        // iteration i: scores and softmax of tile i+1 (skipped at the last
-        // tile: nx = 0, every row masked, weights 0, max -inf), P*V of tile i
-        const int nx = __builtin_amdgcn_readfirstlane((i + 1 < ntiles) ? 1 : 0);
+      // One pipelined iteration: scores and softmax of tile i+1 (skipped when
+      // nx = 0, the last tile: every row masked, weights 0, max -inf), P*V of
+      // tile i, and (dma = 1) the copy of the full tile at tb_s into the LDS
+      // bytes at ldst, spread over the score MFMAs.  valid = rows of tile i+1
+      // before the split end (the mask inside the block acts below 32).
+      float mx_run = -INFINITY;  // largest tile max seen in this pass (overflow check after the loop)
+      auto iterate = [&](int i, int dma, int ldst, uint64_t tb_s, int nx, int valid) {
         const int cur = lds_base + stg(i) * TB;
         const int nxt = lds_base + stg(i + 1) * TB;
         const int tb0 = cur + tr_base[0], tb1 = cur + tr_base[1], tb2 = cur + tr_base[2], tb3 = cur + tr_base[3];
         const int sb0 = nxt + s_base[0], sb1 = nxt + s_base[1], sb2 = nxt + s_base[2], sb3 = nxt + s_base[3];
-        // rows of the next tile before the split end (the mask inside the block)
-        const int valid = __builtin_amdgcn_readfirstlane(nx ? r1 - (r0 + (i + 1) * TILE) : 0);
         uint32_t w0, w1, w2, w3, w4, w5, w6, w7, m0save;
         float mx;
         asm volatile(MLA_ASM_FUSED_BLOCK
@@ -708,11 +688,48 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
                        "v217", "v218", "v219", "v220", "v221", "v222", "v223", "v240", "v241", "v242", "v243",
                        "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254",
                        "v255", "vcc", "scc", "memory");
-        ovf = ovf || __any(mx > m_ref + kRefSlack);
+        mx_run = fmaxf(mx_run, mx);
         typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
         pf[0] = __builtin_bit_cast(i16x8, u32x4{w0, w1, w2, w3});
         pf[1] = __builtin_bit_cast(i16x8, u32x4{w4, w5, w6, w7});
+      };
+      // Steady state, free of per-tile branches: tiles i+1 .. i+3 exist and
+      // are full (nfull counts the split's full tiles).
+      const int nfull = (last_rel + 1) / TILE;
+      const uint64_t split_s = uniform_u64((uint64_t)split_base);
+      const int ldst_w = lds_base + wave * DPW * 1024;
+      int i = 0;
+      for (; i + STAGES - 1 < nfull; ++i) {
+        wait_vm_then_barrier<DPW>();  // tile i+1 has landed, every wave has finished iteration i-1
+        const int t3 = i + STAGES - 1;
+        iterate(i, 1, ldst_w + stg(t3) * TB, split_s + (uint64_t)t3 * (TILE * ROWB), 1, TILE);
       }
+      // the last STAGES - 1 iterations (and every iteration of a short split)
+      for (; i < ntiles; ++i) {
+        // tile i+1 has landed (tile i+2 may still be in flight) and every wave
+        // has finished iteration i-1
+        if (i + 2 < ntiles) wait_vm_then_barrier<DPW>();
+        else wait_vm_then_barrier<0>();
+        // tile i+3 into the stage of tile i-1: a full tile is copied inside
+        // the block, a partial one here
+        const int t3 = i + STAGES - 1;
+        int dma = 0, ldst = 0;
+        uint64_t tbase = (uint64_t)split_base;
+        if (t3 < ntiles) {
+          if (t3 * TILE + TILE - 1 <= last_rel) {
+            dma = 1;
+            tbase += (uint64_t)t3 * TILE * ROWB;
+            ldst = ldst_w + stg(t3) * TB;
+          } else {
+            issue_tile(t3, stg(t3));
+          }
+        }
+        const int nx = (i + 1 < ntiles) ? 1 : 0;
+        iterate(i, __builtin_amdgcn_readfirstlane(dma), __builtin_amdgcn_readfirstlane(ldst), uniform_u64(tbase),
+                __builtin_amdgcn_readfirstlane(nx),
+                __builtin_amdgcn_readfirstlane(nx ? r1 - (r0 + (i + 1) * TILE) : 0));
+      }
+      ovf = __any(mx_run > m_ref + kRefSlack);
       if (pass == 0) {  // redo if any wave overflowed
         if (ovf && lane == 0) redo_flag = 1;
         wait_vm_then_barrier<0>();

@@ -8,7 +8,8 @@ wave, 512 latent columns.  Blocks:
   score block (18 k-steps): S^T[t][h] += cache[t][k..k+16) . q^T, A fragments
     streamed from LDS with ds_read_b128 through a 4-deep rolling window held in
     v[240:255]; B fragments (q) and the accumulator are asm operands.
-  fused block: the scores of the next tile (36 k-steps into v[208:223]), then
+  fused block (and its branch-free steady-state form): the scores of the
+    next tile (36 k-steps into v[208:223]), then
     the P*V product of the current tile, O^T[c][h] += cache^T P^T (16 column
     blocks x 2 k-halves; cache^T fragments from pairs of ds_read_b64_tr_b16
     through the same kind of 4-deep rolling window; accumulators are AGPR
@@ -137,10 +138,12 @@ def _pv_lines(valu=None, first_valu_after=0, prelude=None):
     return out
 
 
-def _mask_block():
+def _mask_block(steady=False):
     """Rows past the split end get -inf (only when %[valid] < 32, a tile that
     is the split's last or past it): register r holds row c + 4*(lane/32) with
     c = 8*(r/4) + r%4, valid iff c < %[valid] - 4*(lane/32)."""
+    if steady:  # every row of the next tile is valid
+        return []
     s = [f"v{SACC + r}" for r in range(16)]
     vl, ninf = f"v{VLIM}", f"v{TMP + 1}"
     out = ["s_cmp_ge_i32 %[valid], 32", "s_cbranch_scc1 .Lmla_full_%=",
@@ -191,32 +194,38 @@ def _softmax_ops():
 DMA_PER_WAVE = 9     # 16-byte-per-lane LDS DMA instructions per wave and tile
 
 
-def _dma_lines(n):
-    """LDS DMA n of a later tile (skipped when %[dma] = 0): lane l copies 16
-    bytes from %[tbase] + %[d<n>] to LDS %[ldst] + 1024*n + 16*l."""
-    return ["s_cmp_eq_u32 %[dma], 0", f"s_cbranch_scc1 .Lmla_nodma{n}_%=",
-            f"s_add_u32 m0, %[ldst], {1024 * n}", "s_nop 0",
-            f"global_load_lds_dwordx4 %[d{n}], %[tbase]", f".Lmla_nodma{n}_%=:"]
+def _dma_lines(n, steady=False):
+    """LDS DMA n of a later tile (skipped when %[dma] = 0; always issued in the
+    steady-state block): lane l copies 16 bytes from %[tbase] + %[d<n>] to LDS
+    %[ldst] + 1024*n + 16*l."""
+    copy = [f"s_add_u32 m0, %[ldst], {1024 * n}", "s_nop 0", f"global_load_lds_dwordx4 %[d{n}], %[tbase]"]
+    if steady:
+        return copy
+    return ["s_cmp_eq_u32 %[dma], 0", f"s_cbranch_scc1 .Lmla_nodma{n}_%="] + copy + [f".Lmla_nodma{n}_%=:"]
 
 
-def fused_block() -> str:
+def fused_block(steady=False) -> str:
     # %[nx] = 0 at the last tile of a split: no next tile, the scores are
     # skipped and %[valid] = 0 masks every row, so the softmax part yields
     # weights 0, sum += 0 and max = -inf.  The DMA of a later tile is spread
-    # over the score MFMAs so that its issue never queues up.
+    # over the score MFMAs so that its issue never queues up.  The steady-state
+    # variant (a next tile that is full, a copy always issued) has no branches.
     # m0 (which the DMA uses) is saved and restored: the compiler reserves it
-    out = ["s_mov_b32 %[m0save], m0", "s_waitcnt lgkmcnt(0)", "s_cmp_eq_u32 %[nx], 0", "s_cbranch_scc1 .Lmla_pv_%="]
+    out = ["s_mov_b32 %[m0save], m0", "s_waitcnt lgkmcnt(0)"]
+    if not steady:
+        out += ["s_cmp_eq_u32 %[nx], 0", "s_cbranch_scc1 .Lmla_pv_%="]
     score = _score_lines(0, KS, True, f"v[{SACC}:{SACC + 15}]", lambda j: f"%[q{j}]")
     mfma_at = [k for k, line in enumerate(score) if line.startswith("v_mfma")]
     after = {mfma_at[3 + 4 * n]: n for n in range(DMA_PER_WAVE)}
     for k, line in enumerate(score):
         out.append(line)
         if k in after:
-            out += _dma_lines(after[k])
-    out.append(".Lmla_pv_%=:")
+            out += _dma_lines(after[k], steady)
+    if not steady:
+        out.append(".Lmla_pv_%=:")
     # P*V of the current tile; the first VALU read of the scores comes at
     # least MFMA_TO_VALU wait states after the last score MFMA
-    out += _pv_lines(_softmax_ops(), MFMA_TO_VALU, _mask_block())
+    out += _pv_lines(_softmax_ops(), MFMA_TO_VALU, _mask_block(steady))
     out.append("s_mov_b32 m0, %[m0save]")
     return "\\n\\t".join(out)
 
@@ -227,7 +236,8 @@ def main():
     w("// Inner blocks of the bf16 decode kernel (32-row tile, 32 heads per wave).\n\n")
     w(f'#define MLA_ASM_SCORE_BLOCK0 "{score_block(0, 18, True, False)}"\n\n')
     w(f'#define MLA_ASM_SCORE_BLOCK1 "{score_block(18, 18, False, True)}"\n\n')
-    w(f'#define MLA_ASM_FUSED_BLOCK "{fused_block()}"\n')
+    w(f'#define MLA_ASM_FUSED_BLOCK "{fused_block()}"\n\n')
+    w(f'#define MLA_ASM_FUSED_BLOCK_STEADY "{fused_block(True)}"\n')
 
 
 if __name__ == "__main__":

@@ -30,6 +30,7 @@
 #include <cstdint>
 #include <cstring>
 #include <string>
+#include <type_traits>
 
 #include "mla.h"
 
@@ -650,44 +651,50 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
         pf[0] = __builtin_bit_cast(i16x8, u32x4{w[0], w[1], w[2], w[3]});
         pf[1] = __builtin_bit_cast(i16x8, u32x4{w[4], w[5], w[6], w[7]});
       }
+// operands of the fused block (both forms)
+#define MLA_FUSED_OPERANDS \
+                     : [o0] "+a"(o[0]), [o1] "+a"(o[1]), [o2] "+a"(o[2]), [o3] "+a"(o[3]), [o4] "+a"(o[4]), \
+                       [o5] "+a"(o[5]), [o6] "+a"(o[6]), [o7] "+a"(o[7]), [o8] "+a"(o[8]), [o9] "+a"(o[9]), \
+                       [o10] "+a"(o[10]), [o11] "+a"(o[11]), [o12] "+a"(o[12]), [o13] "+a"(o[13]), \
+                       [o14] "+a"(o[14]), [o15] "+a"(o[15]), [w0] "=&v"(w0), [w1] "=&v"(w1), [w2] "=&v"(w2), \
+                       [w3] "=&v"(w3), [w4] "=&v"(w4), [w5] "=&v"(w5), [w6] "=&v"(w6), [w7] "=&v"(w7), \
+                       [mx] "=&v"(mx), [l] "+v"(l_sum), [m0save] "=&s"(m0save) \
+                     : [q0] "v"(qf[0]), [q1] "v"(qf[1]), [q2] "v"(qf[2]), [q3] "v"(qf[3]), [q4] "v"(qf[4]), \
+                       [q5] "v"(qf[5]), [q6] "v"(qf[6]), [q7] "v"(qf[7]), [q8] "v"(qf[8]), [q9] "v"(qf[9]), \
+                       [q10] "v"(qf[10]), [q11] "v"(qf[11]), [q12] "v"(qf[12]), [q13] "v"(qf[13]), \
+                       [q14] "v"(qf[14]), [q15] "v"(qf[15]), [q16] "v"(qf[16]), [q17] "v"(qf[17]), \
+                       [q18] "v"(qf[18]), [q19] "v"(qf[19]), [q20] "v"(qf[20]), [q21] "v"(qf[21]), \
+                       [q22] "v"(qf[22]), [q23] "v"(qf[23]), [q24] "v"(qf[24]), [q25] "v"(qf[25]), \
+                       [q26] "v"(qf[26]), [q27] "v"(qf[27]), [q28] "v"(qf[28]), [q29] "v"(qf[29]), \
+                       [q30] "v"(qf[30]), [q31] "v"(qf[31]), [q32] "v"(qf[32]), [q33] "v"(qf[33]), \
+                       [q34] "v"(qf[34]), [q35] "v"(qf[35]), [p0] "v"(pf[0]), [p1] "v"(pf[1]), [b0] "v"(sb0), \
+                       [b1] "v"(sb1), [b2] "v"(sb2), [b3] "v"(sb3), [t0] "v"(tb0), [t1] "v"(tb1), \
+                       [t2] "v"(tb2), [t3] "v"(tb3), [mref] "v"(m_ref), [sc] "s"(scale_log2), [valid] "s"(valid), [nx] "s"(nx), \
+                       [dma] "s"(dma), [ldst] "s"(ldst), [tbase] "s"(tb_s), [d0] "v"(dma_off[0]), \
+                       [d1] "v"(dma_off[1]), [d2] "v"(dma_off[2]), [d3] "v"(dma_off[3]), [d4] "v"(dma_off[4]), \
+                       [d5] "v"(dma_off[5]), [d6] "v"(dma_off[6]), [d7] "v"(dma_off[7]), [d8] "v"(dma_off[8]) \
+                     : "v204", "v205", "v206", "v208", "v209", "v210", "v211", "v212", "v213", "v214", "v215", "v216", \
+                       "v217", "v218", "v219", "v220", "v221", "v222", "v223", "v240", "v241", "v242", "v243", \
+                       "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", \
+                       "v255", "vcc", "scc", "memory"
       // One pipelined iteration: scores and softmax of tile i+1 (skipped when
       // nx = 0, the last tile: every row masked, weights 0, max -inf), P*V of
       // tile i, and (dma = 1) the copy of the full tile at tb_s into the LDS
       // bytes at ldst, spread over the score MFMAs.  valid = rows of tile i+1
       // before the split end (the mask inside the block acts below 32).
       float mx_run = -INFINITY;  // largest tile max seen in this pass (overflow check after the loop)
-      auto iterate = [&](int i, int dma, int ldst, uint64_t tb_s, int nx, int valid) {
+      auto iterate = [&](auto steady, int i, int dma, int ldst, uint64_t tb_s, int nx, int valid) {
         const int cur = lds_base + stg(i) * TB;
         const int nxt = lds_base + stg(i + 1) * TB;
         const int tb0 = cur + tr_base[0], tb1 = cur + tr_base[1], tb2 = cur + tr_base[2], tb3 = cur + tr_base[3];
         const int sb0 = nxt + s_base[0], sb1 = nxt + s_base[1], sb2 = nxt + s_base[2], sb3 = nxt + s_base[3];
         uint32_t w0, w1, w2, w3, w4, w5, w6, w7, m0save;
         float mx;
-        asm volatile(MLA_ASM_FUSED_BLOCK
-                     : [o0] "+a"(o[0]), [o1] "+a"(o[1]), [o2] "+a"(o[2]), [o3] "+a"(o[3]), [o4] "+a"(o[4]),
-                       [o5] "+a"(o[5]), [o6] "+a"(o[6]), [o7] "+a"(o[7]), [o8] "+a"(o[8]), [o9] "+a"(o[9]),
-                       [o10] "+a"(o[10]), [o11] "+a"(o[11]), [o12] "+a"(o[12]), [o13] "+a"(o[13]),
-                       [o14] "+a"(o[14]), [o15] "+a"(o[15]), [w0] "=&v"(w0), [w1] "=&v"(w1), [w2] "=&v"(w2),
-                       [w3] "=&v"(w3), [w4] "=&v"(w4), [w5] "=&v"(w5), [w6] "=&v"(w6), [w7] "=&v"(w7),
-                       [mx] "=&v"(mx), [l] "+v"(l_sum), [m0save] "=&s"(m0save)
-                     : [q0] "v"(qf[0]), [q1] "v"(qf[1]), [q2] "v"(qf[2]), [q3] "v"(qf[3]), [q4] "v"(qf[4]),
-                       [q5] "v"(qf[5]), [q6] "v"(qf[6]), [q7] "v"(qf[7]), [q8] "v"(qf[8]), [q9] "v"(qf[9]),
-                       [q10] "v"(qf[10]), [q11] "v"(qf[11]), [q12] "v"(qf[12]), [q13] "v"(qf[13]),
-                       [q14] "v"(qf[14]), [q15] "v"(qf[15]), [q16] "v"(qf[16]), [q17] "v"(qf[17]),
-                       [q18] "v"(qf[18]), [q19] "v"(qf[19]), [q20] "v"(qf[20]), [q21] "v"(qf[21]),
-                       [q22] "v"(qf[22]), [q23] "v"(qf[23]), [q24] "v"(qf[24]), [q25] "v"(qf[25]),
-                       [q26] "v"(qf[26]), [q27] "v"(qf[27]), [q28] "v"(qf[28]), [q29] "v"(qf[29]),
-                       [q30] "v"(qf[30]), [q31] "v"(qf[31]), [q32] "v"(qf[32]), [q33] "v"(qf[33]),
-                       [q34] "v"(qf[34]), [q35] "v"(qf[35]), [p0] "v"(pf[0]), [p1] "v"(pf[1]), [b0] "v"(sb0),
-                       [b1] "v"(sb1), [b2] "v"(sb2), [b3] "v"(sb3), [t0] "v"(tb0), [t1] "v"(tb1),
-                       [t2] "v"(tb2), [t3] "v"(tb3), [mref] "v"(m_ref), [sc] "s"(scale_log2), [valid] "s"(valid), [nx] "s"(nx),
-                       [dma] "s"(dma), [ldst] "s"(ldst), [tbase] "s"(tb_s), [d0] "v"(dma_off[0]),
-                       [d1] "v"(dma_off[1]), [d2] "v"(dma_off[2]), [d3] "v"(dma_off[3]), [d4] "v"(dma_off[4]),
-                       [d5] "v"(dma_off[5]), [d6] "v"(dma_off[6]), [d7] "v"(dma_off[7]), [d8] "v"(dma_off[8])
-                     : "v204", "v205", "v206", "v208", "v209", "v210", "v211", "v212", "v213", "v214", "v215", "v216",
-                       "v217", "v218", "v219", "v220", "v221", "v222", "v223", "v240", "v241", "v242", "v243",
-                       "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254",
-                       "v255", "vcc", "scc", "memory");
+        if constexpr (decltype(steady)::value) {
+          asm volatile(MLA_ASM_FUSED_BLOCK_STEADY MLA_FUSED_OPERANDS);
+        } else {
+          asm volatile(MLA_ASM_FUSED_BLOCK MLA_FUSED_OPERANDS);
+        }
         mx_run = fmaxf(mx_run, mx);
         typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
         pf[0] = __builtin_bit_cast(i16x8, u32x4{w0, w1, w2, w3});
@@ -702,7 +709,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
       for (; i + STAGES - 1 < nfull; ++i) {
         wait_vm_then_barrier<DPW>();  // tile i+1 has landed, every wave has finished iteration i-1
         const int t3 = i + STAGES - 1;
-        iterate(i, 1, ldst_w + stg(t3) * TB, split_s + (uint64_t)t3 * (TILE * ROWB), 1, TILE);
+        iterate(std::true_type{}, i, 1, ldst_w + stg(t3) * TB, split_s + (uint64_t)t3 * (TILE * ROWB), 1, TILE);
       }
       // the last STAGES - 1 iterations (and every iteration of a short split)
       for (; i < ntiles; ++i) {
@@ -725,11 +732,12 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
           }
         }
         const int nx = (i + 1 < ntiles) ? 1 : 0;
-        iterate(i, __builtin_amdgcn_readfirstlane(dma), __builtin_amdgcn_readfirstlane(ldst), uniform_u64(tbase),
+        iterate(std::false_type{}, i, __builtin_amdgcn_readfirstlane(dma), __builtin_amdgcn_readfirstlane(ldst), uniform_u64(tbase),
                 __builtin_amdgcn_readfirstlane(nx),
                 __builtin_amdgcn_readfirstlane(nx ? r1 - (r0 + (i + 1) * TILE) : 0));
       }
       ovf = __any(mx_run > m_ref + kRefSlack);
+#undef MLA_FUSED_OPERANDS
       if (pass == 0) {  // redo if any wave overflowed
         if (ovf && lane == 0) redo_flag = 1;
         wait_vm_then_barrier<0>();
@@ -831,17 +839,28 @@ constexpr int kCombineThreads = 256;
 constexpr int kCombineMaxGroups = 16;
 
 // four (two) consecutive values of a partial in its storage dtype, as fp32
+// A quad pair of one split's partial: 8 values as stored (raw bits), then
+// unpacked to two fp32 quads.  The raw load is kept apart from the unpacking
+// so that all of a step's loads are in flight before the first is used.
 template <typename PT> struct Pair8;
 template <> struct Pair8<float> {
-  static __device__ __forceinline__ void load(const float* p, f32x4& a, f32x4& b) {
-    a = *(const f32x4*)p;
-    b = *(const f32x4*)(p + 4);
+  typedef f32x4 Raw[2];
+  static __device__ __forceinline__ void zero(Raw& r) { r[0] = r[1] = f32x4{0.f, 0.f, 0.f, 0.f}; }
+  static __device__ __forceinline__ void load(const float* p, Raw& r) {
+    r[0] = *(const f32x4*)p;
+    r[1] = *(const f32x4*)(p + 4);
+  }
+  static __device__ __forceinline__ void unpack(const Raw& r, f32x4& a, f32x4& b) {
+    a = r[0];
+    b = r[1];
   }
 };
 template <> struct Pair8<u16> {
-  static __device__ __forceinline__ void load(const u16* p, f32x4& a, f32x4& b) {
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    const u32x4 v = *(const u32x4*)p;
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  typedef u32x4 Raw;
+  static __device__ __forceinline__ void zero(Raw& r) { r = u32x4{0u, 0u, 0u, 0u}; }
+  static __device__ __forceinline__ void load(const u16* p, Raw& r) { r = *(const u32x4*)p; }
+  static __device__ __forceinline__ void unpack(const Raw& v, f32x4& a, f32x4& b) {
     a = f32x4{__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xffff0000u), __uint_as_float(v[1] << 16),
               __uint_as_float(v[1] & 0xffff0000u)};
     b = f32x4{__uint_as_float(v[2] << 16), __uint_as_float(v[2] & 0xffff0000u), __uint_as_float(v[3] << 16),
@@ -880,16 +899,16 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const PT* __re
       l0[u] = ok ? lp[(int64_t)s * H] : -INFINITY;
       l1[u] = ok ? lp[(int64_t)s * H + 1] : -INFINITY;
     }
+    typename Pair8<PT>::Raw raw[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int s = s0 + u * SG;
       // an empty split (lse -inf for every head) never wrote its partial
-      if (s < num_splits && l0[u] != -INFINITY) {
-        Pair8<PT>::load(op + s * sstride, va[u], vb[u]);
-      } else {
-        va[u] = vb[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
+      Pair8<PT>::zero(raw[u]);
+      if (s < num_splits && l0[u] != -INFINITY) Pair8<PT>::load(op + s * sstride, raw[u]);
     }
+#pragma unroll
+    for (int u = 0; u < U; ++u) Pair8<PT>::unpack(raw[u], va[u], vb[u]);
     float n0 = m0, n1 = m1;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -1290,8 +1309,9 @@ __global__ __launch_bounds__(64) void up_v_f32_kernel(const float* __restrict__ 
 // in double precision.
 // ---------------------------------------------------------------------------
 
+constexpr int kMaxRopePairs = 32;  // d_rope <= 64
 struct RopeFreqs {
-  double theta[256];  // theta_i = base^(-2i/d_rope), i < d_rope/2
+  double theta[kMaxRopePairs];  // theta_i = base^(-2i/d_rope), i < d_rope/2
 };
 
 __device__ __forceinline__ void sincos_reduced(double ang, double* s, double* c) {
@@ -1314,7 +1334,9 @@ __global__ __launch_bounds__(256) void rope_append_kernel(const T* __restrict__ 
                                                           int H, int R, int DR, RopeFreqs freqs,
                                                           T* __restrict__ q_lat, T* __restrict__ cache) {
   constexpr int QP = 2;  // q_rope pairs per thread (16 heads x d_rope/2 <= 256 * QP)
-  __shared__ double cs[2][256];
+  constexpr int CV = 4;  // c_kv_new values per thread (R <= 1024)
+  typedef T T2 __attribute__((ext_vector_type(2)));
+  __shared__ double cs[2][kMaxRopePairs];
   const int hblocks = (H + 15) / 16;
   const int b = blockIdx.x / hblocks;
   const int hb = blockIdx.x - b * hblocks;
@@ -1322,47 +1344,52 @@ __global__ __launch_bounds__(256) void rope_append_kernel(const T* __restrict__ 
   const int W = R + DR;
   const int h0 = hb * 16, h1 = min(H, h0 + 16);
   const int npairs = (h1 - h0) * half;
-  // every global load is issued before the sincos work that waits on positions
-  T qx[QP][2];
+  const int tid = (int)threadIdx.x;
+  const bool row_block = hb == 0;
+  // Every global load is issued up front, unconditionally (indices clamped
+  // into range), so that they all share one round trip: the position, this
+  // thread's angle frequency, q_rope pairs, and (used by the work-group of
+  // head block 0 only) the new key pair, c_kv_new values and the row offset.
+  const int pos = positions[b];
+  const int ti = min(tid, half - 1);
+  const double theta = freqs.theta[ti];
+  T2 qx[QP];
 #pragma unroll
   for (int u = 0; u < QP; ++u) {
-    const int idx = (int)threadIdx.x + u * (int)blockDim.x;
+    const int idx = tid + u * (int)blockDim.x;
     const int hh = h0 + idx / half, i = idx % half;
-    const T* src = q_rope + ((int64_t)b * H + (idx < npairs ? hh : h0)) * DR + 2 * i;
-    qx[u][0] = src[0];
-    qx[u][1] = src[1];
+    qx[u] = *(const T2*)(q_rope + ((int64_t)b * H + (idx < npairs ? hh : h0)) * DR + 2 * i);
   }
-  const bool row_block = hb == 0;
-  T kx[2] = {T(0), T(0)};
-  if (row_block && (int)threadIdx.x < half) {
-    kx[0] = k_rope_new[(int64_t)b * DR + 2 * threadIdx.x];
-    kx[1] = k_rope_new[(int64_t)b * DR + 2 * threadIdx.x + 1];
-  }
-  const int pos = positions[b];
-  for (int i = threadIdx.x; i < half; i += blockDim.x) sincos_reduced((double)pos * freqs.theta[i], &cs[1][i], &cs[0][i]);
+  const T2 kx = *(const T2*)(k_rope_new + (int64_t)b * DR + 2 * ti);
+  T cv[CV];
+#pragma unroll
+  for (int u = 0; u < CV; ++u) cv[u] = c_kv_new[(int64_t)b * R + min(tid + u * (int)blockDim.x, R - 1)];
+  const int64_t row_off = row_offsets[b];
+
+  if (tid < half) sincos_reduced((double)pos * theta, &cs[1][tid], &cs[0][tid]);
   __syncthreads();
 #pragma unroll
   for (int u = 0; u < QP; ++u) {
-    const int idx = (int)threadIdx.x + u * (int)blockDim.x;
+    const int idx = tid + u * (int)blockDim.x;
     if (idx >= npairs) break;
     const int hh = h0 + idx / half, i = idx % half;
     const double x0 = load_d<T>(qx[u][0]), x1 = load_d<T>(qx[u][1]);
     const double c = cs[0][i], s = cs[1][i];
-    T* dst = q_lat + ((int64_t)b * H + hh) * W + R + 2 * i;
-    dst[0] = store_d<T>(x0 * c - x1 * s);
-    dst[1] = store_d<T>(x0 * s + x1 * c);
+    *(T2*)(q_lat + ((int64_t)b * H + hh) * W + R + 2 * i) = T2{store_d<T>(x0 * c - x1 * s), store_d<T>(x0 * s + x1 * c)};
   }
   if (!row_block) return;
-  int64_t row = row_offsets[b] + pos;
+  int64_t row = row_off + pos;
   row = row < 0 ? 0 : (row >= total_rows ? total_rows - 1 : row);
   T* crow = cache + row * W;
-  for (int k = threadIdx.x; k < R; k += blockDim.x) crow[k] = c_kv_new[(int64_t)b * R + k];
-  if ((int)threadIdx.x < half) {
-    const int i = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < CV; ++u) {
+    const int k = tid + u * (int)blockDim.x;
+    if (k < R) crow[k] = cv[u];
+  }
+  if (tid < half) {
     const double x0 = load_d<T>(kx[0]), x1 = load_d<T>(kx[1]);
-    const double c = cs[0][i], s = cs[1][i];
-    crow[R + 2 * i] = store_d<T>(x0 * c - x1 * s);
-    crow[R + 2 * i + 1] = store_d<T>(x0 * s + x1 * c);
+    const double c = cs[0][tid], s = cs[1][tid];
+    *(T2*)(crow + R + 2 * tid) = T2{store_d<T>(x0 * c - x1 * s), store_d<T>(x0 * s + x1 * c)};
   }
 }
 
@@ -1530,7 +1557,8 @@ mla_status mla_rope_append(const mla_dims* dims, const void* q_rope, const void*
   if (positions == nullptr || row_offsets == nullptr) return fail(MLA_ERR_INVALID_ARG, "positions/row_offsets NULL");
   if ((st = check_ptrs({q_rope, c_kv_new, k_rope_new, q_lat, kv_cache})) != MLA_OK) return st;
   if (total_rows < 1) return fail(MLA_ERR_INVALID_ARG, "total_rows must be >= 1");
-  if (dims->d_rope > 64) return fail(MLA_ERR_UNSUPPORTED, "d_rope above 64");  // 16 heads x d_rope/2 pairs <= 2 per thread
+  if (dims->d_rope > 2 * kMaxRopePairs) return fail(MLA_ERR_UNSUPPORTED, "d_rope above 64");  // 16 heads x d_rope/2 pairs <= 2 per thread
+  if (dims->rank > 1024) return fail(MLA_ERR_UNSUPPORTED, "rank above 1024");  // c_kv_new values <= 4 per thread
   g_last_error.clear();
   hipStream_t s = (hipStream_t)stream;
   const double base = dims->rope_base > 0.f ? (double)dims->rope_base : 10000.0;

@@ -38,24 +38,49 @@ VLIM = 206           # per-lane row limit of the mask, then a softmax temporary
 MFMA_TO_VALU = 20    # wait states between the last score MFMA and a VALU read of it
 
 
-def _score_lines(k0, steps, first, acc, qname):
-    """LDS-fed score MFMAs for k-steps k0..k0+steps-1 (4 bases b0..b3)."""
+class _Lds:
+    """In-order model of this wave's LDS reads: the wait for read r is
+    lgkmcnt(reads issued after r), capped at 15 (a smaller count only waits
+    longer, as LDS reads complete in order)."""
+
+    def __init__(self):
+        self.n = 0
+
+    def issue(self):
+        self.n += 1
+        return self.n - 1
+
+    def wait(self, r):
+        return f"s_waitcnt lgkmcnt({min(15, self.n - r - 1)})"
+
+
+def _score_lines(k0, steps, first, acc, qname, extra=None, lds=None):
+    """LDS-fed score MFMAs for k-steps k0..k0+steps-1 (4 bases b0..b3).
+    `extra` maps an MFMA index to lines of other LDS reads issued right after
+    it (their count is taken into the waits)."""
     buf = [f"v[{240 + 4 * j}:{243 + 4 * j}]" for j in range(S_DEPTH)]
+    extra = extra or {}
+    lds = lds or _Lds()
     out = ["s_waitcnt lgkmcnt(0)"]
+    rid = {}
 
     def read(j):
         kk = k0 + j
-        return f"ds_read_b128 {buf[j % S_DEPTH]}, %[b{kk & 3}] offset:{128 * (kk >> 2)}"
+        rid[j] = lds.issue()
+        out.append(f"ds_read_b128 {buf[j % S_DEPTH]}, %[b{kk & 3}] offset:{128 * (kk >> 2)}")
 
     for j in range(min(S_DEPTH, steps)):
-        out.append(read(j))
+        read(j)
     for j in range(steps):
-        issued = min(steps, j + S_DEPTH)
-        out.append(f"s_waitcnt lgkmcnt({issued - j - 1})")
+        out.append(lds.wait(rid[j]))
         src_c = "0" if (first and j == 0) else acc
         out.append(f"v_mfma_f32_32x32x16_bf16 {acc}, {buf[j % S_DEPTH]}, {qname(j)}, {src_c}")
         if j + S_DEPTH < steps:
-            out.append(read(j + S_DEPTH))
+            read(j + S_DEPTH)
+        for line in extra.get(j, []):
+            if line.startswith("ds_read"):
+                lds.issue()
+            out.append(line)
     return out
 
 
@@ -70,11 +95,14 @@ PV_FRAGS = [(2 * g + dc, ks) for g in range(8) for dc, ks in ((0, 0), (1, 0), (0
 PV_DEPTH = 4         # P*V fragments in flight (rolling window v[240:255], as for the scores)
 
 
-def _pv_reads(n):
+PRE_BASE = 232       # first VGPR of the P*V fragments prefetched during the score phase
+
+
+def _pv_reads(n, slot=None, base=None):
     """The two transpose reads of P*V fragment n (column block cb, k-half ks)
-    into window slot n % PV_DEPTH."""
+    into window slot `slot` (default n % PV_DEPTH) or into v[base:base+3]."""
     cb, ks = PV_FRAGS[n]
-    r = 256 - 4 * PV_DEPTH + 4 * (n % PV_DEPTH)
+    r = base if base is not None else 256 - 4 * PV_DEPTH + 4 * ((n if slot is None else slot) % PV_DEPTH)
     off = 128 * (cb >> 1) + 16 * ks * ROWB
     # rows 16*ks + j (base t0/t1) and 16*ks + 8 + j (base t2/t3: rows 8 on
     # have their own swizzle), j = 4*(lane/32) + (lane%16)/4
@@ -82,15 +110,22 @@ def _pv_reads(n):
             f"ds_read_b64_tr_b16 v[{r + 2}:{r + 3}], %[t{2 + (cb & 1)}] offset:{off}"]
 
 
-def _pv_lines(valu=None, first_valu_after=0, prelude=None):
-    """P*V MFMAs over the 32 fragments (16 column blocks x 2 k-halves), fed
-    through a rolling window: the reads of fragment n + PV_DEPTH go into the
-    slot of fragment n right after its MFMA has been issued.  `valu` (list of
+def _pv_lines(valu=None, first_valu_after=0, prelude=None, lds=None, pre=None):
+    """P*V MFMAs over the 32 fragments (16 column blocks x 2 k-halves).
+    Fragments in `pre` (n -> (first VGPR, id of its second read)) were read
+    earlier into their own registers; the others are fed through a rolling
+    window: the reads of the window's fragment k + PV_DEPTH go into the slot
+    of fragment k right after its MFMA has been issued.  `valu` (list of
     instructions) is spread between the MFMAs, starting once
     `first_valu_after` wait states have passed since the block start;
     `prelude` (a list of lines) is emitted whole at that point."""
     valu = list(valu or [])
+    pre = pre or {}
+    lds = lds or _Lds()
     nfr = len(PV_FRAGS)
+    win = [n for n in range(nfr) if n not in pre]
+    pos = {n: k for k, n in enumerate(win)}
+    rid = {}
     out = []
     waited = 0  # wait states since the block start
 
@@ -98,6 +133,11 @@ def _pv_lines(valu=None, first_valu_after=0, prelude=None):
         nonlocal waited
         out.append(line)
         waited += int(line.split()[1]) + 1 if line.startswith("s_nop") else 1
+
+    def issue(k):
+        for line in _pv_reads(win[k], slot=k):
+            rid[win[k]] = lds.issue()
+            emit(line)
 
     last_trans = [None]
 
@@ -108,20 +148,21 @@ def _pv_lines(valu=None, first_valu_after=0, prelude=None):
         emit(op)
         last_trans[0] = op.split()[1].rstrip(",") if op.startswith("v_exp_f32") else None
 
-    for n in range(min(PV_DEPTH, nfr)):
-        for line in _pv_reads(n):
-            emit(line)
+    for k in range(min(PV_DEPTH, len(win))):
+        issue(k)
     per_slot = None
     for n in range(nfr):
-        issued = min(nfr, n + PV_DEPTH)
-        emit(f"s_waitcnt lgkmcnt({2 * (issued - n - 1)})")
         cb, ks = PV_FRAGS[n]
-        r = 256 - 4 * PV_DEPTH + 4 * (n % PV_DEPTH)
+        if n in pre:
+            r, last_read = pre[n]
+            emit(lds.wait(last_read))
+        else:
+            r = 256 - 4 * PV_DEPTH + 4 * (pos[n] % PV_DEPTH)
+            emit(lds.wait(rid[n]))
         emit(f"v_mfma_f32_32x32x16_bf16 %[o{cb}], v[{r}:{r + 3}], %[p{ks}], %[o{cb}]")
         last_trans[0] = None
-        if n + PV_DEPTH < nfr:
-            for line in _pv_reads(n + PV_DEPTH):
-                emit(line)
+        if n not in pre and pos[n] + PV_DEPTH < len(win):
+            issue(pos[n] + PV_DEPTH)
         if valu:
             if waited < first_valu_after:
                 emit(f"s_nop {first_valu_after - waited - 1}")
@@ -204,17 +245,47 @@ def _dma_lines(n, steady=False):
     return ["s_cmp_eq_u32 %[dma], 0", f"s_cbranch_scc1 .Lmla_nodma{n}_%="] + copy + [f".Lmla_nodma{n}_%=:"]
 
 
+PV_PRE = 2           # P*V fragments the steady-state block reads during the score phase
+
+
 def fused_block(steady=False) -> str:
     # %[nx] = 0 at the last tile of a split: no next tile, the scores are
     # skipped and %[valid] = 0 masks every row, so the softmax part yields
     # weights 0, sum += 0 and max = -inf.  The DMA of a later tile is spread
     # over the score MFMAs so that its issue never queues up.  The steady-state
-    # variant (a next tile that is full, a copy always issued) has no branches.
+    # variant (a next tile that is full, a copy always issued) has no branches
+    # and moves the transpose reads of the first PV_PRE P*V fragments into the
+    # score phase: there the four waves' b128 reads leave LDS bandwidth spare,
+    # while in the P*V phase the transpose reads alone would saturate it.
     # m0 (which the DMA uses) is saved and restored: the compiler reserves it
     out = ["s_mov_b32 %[m0save], m0", "s_waitcnt lgkmcnt(0)"]
     if not steady:
         out += ["s_cmp_eq_u32 %[nx], 0", "s_cbranch_scc1 .Lmla_pv_%="]
-    score = _score_lines(0, KS, True, f"v[{SACC}:{SACC + 15}]", lambda j: f"%[q{j}]")
+    lds = _Lds()
+    extra, pre = {}, {}
+    npre = PV_PRE if steady else 0
+    for f in range(npre):
+        at = 4 + f * (KS - 8) // max(1, npre)
+        lines = _pv_reads(f, base=PRE_BASE + 4 * f)
+        extra.setdefault(at, []).extend(lines)
+        # the id of the fragment's second read: counted as the score emitter issues it
+        pre[f] = PRE_BASE + 4 * f
+    # the score emitter issues the extra reads through `lds`; record their ids
+    issued_ids = []
+    orig_issue = lds.issue
+
+    def tracking_issue():
+        r = orig_issue()
+        issued_ids.append(r)
+        return r
+
+    lds.issue = tracking_issue
+    score = _score_lines(0, KS, True, f"v[{SACC}:{SACC + 15}]", lambda j: f"%[q{j}]", extra, lds)
+    lds.issue = orig_issue
+    # ids of the extra reads, in order: the score reads are the ds_read_b128 ones
+    kinds = [l for l in score if l.startswith("ds_read")]
+    extra_ids = [rid for rid, l in zip(issued_ids, kinds) if l.startswith("ds_read_b64_tr")]
+    pre = {f: (pre[f], extra_ids[2 * f + 1]) for f in range(npre)}
     mfma_at = [k for k, line in enumerate(score) if line.startswith("v_mfma")]
     after = {mfma_at[3 + 4 * n]: n for n in range(DMA_PER_WAVE)}
     for k, line in enumerate(score):
@@ -223,9 +294,10 @@ def fused_block(steady=False) -> str:
             out += _dma_lines(after[k], steady)
     if not steady:
         out.append(".Lmla_pv_%=:")
+        lds = _Lds()  # (the score phase may have been skipped)
     # P*V of the current tile; the first VALU read of the scores comes at
     # least MFMA_TO_VALU wait states after the last score MFMA
-    out += _pv_lines(_softmax_ops(), MFMA_TO_VALU, _mask_block(steady))
+    out += _pv_lines(_softmax_ops(), MFMA_TO_VALU, _mask_block(steady), lds, pre)
     out.append("s_mov_b32 m0, %[m0save]")
     return "\\n\\t".join(out)
 

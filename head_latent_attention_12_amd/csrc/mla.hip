@@ -674,7 +674,8 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
                        [d1] "v"(dma_off[1]), [d2] "v"(dma_off[2]), [d3] "v"(dma_off[3]), [d4] "v"(dma_off[4]), \
                        [d5] "v"(dma_off[5]), [d6] "v"(dma_off[6]), [d7] "v"(dma_off[7]), [d8] "v"(dma_off[8]) \
                      : "v204", "v205", "v206", "v208", "v209", "v210", "v211", "v212", "v213", "v214", "v215", "v216", \
-                       "v217", "v218", "v219", "v220", "v221", "v222", "v223", "v240", "v241", "v242", "v243", \
+                       "v217", "v218", "v219", "v220", "v221", "v222", "v223", \
+                       "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", \
                        "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", \
                        "v255", "vcc", "scc", "memory"
       // One pipelined iteration: scores and softmax of tile i+1 (skipped when

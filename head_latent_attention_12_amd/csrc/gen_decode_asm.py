@@ -14,7 +14,7 @@ wave, 512 latent columns.  Blocks:
     blocks x 2 k-halves; cache^T fragments from pairs of ds_read_b64_tr_b16
     through the same kind of 4-deep rolling window; accumulators are AGPR
     operands), with the next tile's softmax (mask of rows past the split end,
-    tile max, exponentials, bf16 packing, running sum) interleaved between
+    exponentials, bf16 packing, running sum) interleaved between
     the P*V MFMAs so that it runs while the matrix core is busy; the LDS DMA
     of a later tile is spread over the score MFMAs.
 
@@ -33,8 +33,8 @@ ROWB = 1152          # bytes per cache row
 S_DEPTH = 4          # score-phase fragments in flight
 KS = 36              # k-steps of 16 over the 576-wide row
 SACC = 208           # first VGPR of the next tile's score accumulator (16 regs)
-TMP = 204            # softmax temporaries v204, v205
-VLIM = 206           # per-lane row limit of the mask, then a softmax temporary
+TMP = 204            # mask temporaries (v205 holds -inf)
+VLIM = 206           # per-lane row limit of the mask
 MFMA_TO_VALU = 20    # wait states between the last score MFMA and a VALU read of it
 
 
@@ -202,29 +202,13 @@ def _mask_block(steady=False):
 def _softmax_ops():
     """Softmax of the next tile on v[208:223] (accumulator register r holds
     row 8*(r/4) + 4*(lane/32) + r%4 of the tile, head = lane%32):
-    outputs %[mx] (tile max per head, log2 units), %[w0..w7] (bf16 pairs of
-    2^(s*scale - mref)) and %[l] += the sum of those rounded weights.
-    Ordered so that no instruction waits on a recent result: two interleaved
-    max chains, the exponent arguments (in place, after the max has read the
-    scores), the exponentials, then the packing and the running sum."""
+    outputs %[w0..w7] (bf16 pairs of 2^(s*scale - mref)) and %[l] += the sum
+    of those rounded weights.  (No tile maximum: the overflow test runs once
+    per pass on the sum, outside.)  Ordered so that no instruction waits on a
+    recent result: the exponent arguments (in place), the exponentials, then
+    the packing and the running sum."""
     s = [f"v{SACC + r}" for r in range(16)]
-    m, m2, t = f"v{TMP}", f"v{TMP + 1}", f"v{VLIM}"
-
-    def fma(r):
-        return f"v_fma_f32 {s[r]}, {s[r]}, %[sc], -%[mref]"
-
-    ops = [f"v_max3_f32 {m}, {s[0]}, {s[1]}, {s[2]}", f"v_max3_f32 {m2}, {s[8]}, {s[9]}, {s[10]}",
-           f"v_max3_f32 {m}, {m}, {s[3]}, {s[4]}", f"v_max3_f32 {m2}, {m2}, {s[11]}, {s[12]}",
-           f"v_max3_f32 {m}, {m}, {s[5]}, {s[6]}", f"v_max3_f32 {m2}, {m2}, {s[13]}, {s[14]}",
-           f"v_max_f32_e32 {m}, {m}, {s[7]}", f"v_max_f32_e32 {m2}, {m2}, {s[15]}",
-           f"v_max_f32_e32 {m}, {m}, {m2}",
-           # max with lane ^ 32: swap the upper half of m with the lower half of
-           # a copy (two wait states after the VALU writes it reads)
-           f"v_mov_b32_e32 {t}, {m}", fma(0), fma(1),
-           f"v_permlane32_swap_b32_e32 {m}, {t}", fma(2),
-           f"v_max_f32_e32 {m}, {m}, {t}", fma(3),
-           f"v_mul_f32_e32 %[mx], %[sc], {m}"]
-    ops += [fma(r) for r in range(4, 16)]
+    ops = [f"v_fma_f32 {s[r]}, {s[r]}, %[sc], -%[mref]" for r in range(16)]
     ops += [f"v_exp_f32_e32 {s[r]}, {s[r]}" for r in range(16)]
     # round pairs to bf16 (the weights P*V uses), then add them to the sum
     ops += [f"v_cvt_pk_bf16_f32 %[w{j}], {s[2 * j]}, {s[2 * j + 1]}" for j in range(8)]

@@ -54,6 +54,11 @@ constexpr float kLog2e = 1.44269504088896340736f;
 // the work-group runs a scores-only pass over the split to find each head's
 // exact maximum and then redoes the split with that reference (p <= 1), so the
 // accumulators are never rescaled inside the loop and at most one redo happens.
+// The bf16 pipelined loop checks this once per pass on the sum of the weights
+// instead of per tile on the scores: every weight is non-negative, so a sum
+// below 2^kRefSlack means every weight was, and a weight at or above it (or an
+// infinite one) makes the sum fail the test (a few weights just under the bound
+// may also trigger a redo, which is only slower).
 constexpr float kRefSlack = 64.0f;
 // MI355X: 8 accelerator complex dies (XCDs), each with its own L2
 constexpr int kXcds = 8;
@@ -631,7 +636,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
       else if (ntiles == 2) wait_vm_then_barrier<DPW>();
       else wait_vm_then_barrier<0>();
       i16x8 pf[2];
-      bool ovf = false;  // wave-uniform: a score above m_ref + kRefSlack was seen
+      bool ovf = false;  // wave-uniform: some weight of the pass reached 2^kRefSlack
       {
         f32x16 sacc = score_tile(stg(0) * TB);
         const float mx = tile_max(sacc, r1 - r0);
@@ -658,7 +663,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
                        [o10] "+a"(o[10]), [o11] "+a"(o[11]), [o12] "+a"(o[12]), [o13] "+a"(o[13]), \
                        [o14] "+a"(o[14]), [o15] "+a"(o[15]), [w0] "=&v"(w0), [w1] "=&v"(w1), [w2] "=&v"(w2), \
                        [w3] "=&v"(w3), [w4] "=&v"(w4), [w5] "=&v"(w5), [w6] "=&v"(w6), [w7] "=&v"(w7), \
-                       [mx] "=&v"(mx), [l] "+v"(l_sum), [m0save] "=&s"(m0save) \
+                       [l] "+v"(l_sum), [m0save] "=&s"(m0save) \
                      : [q0] "v"(qf[0]), [q1] "v"(qf[1]), [q2] "v"(qf[2]), [q3] "v"(qf[3]), [q4] "v"(qf[4]), \
                        [q5] "v"(qf[5]), [q6] "v"(qf[6]), [q7] "v"(qf[7]), [q8] "v"(qf[8]), [q9] "v"(qf[9]), \
                        [q10] "v"(qf[10]), [q11] "v"(qf[11]), [q12] "v"(qf[12]), [q13] "v"(qf[13]), \
@@ -683,20 +688,17 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
       // tile i, and (dma = 1) the copy of the full tile at tb_s into the LDS
       // bytes at ldst, spread over the score MFMAs.  valid = rows of tile i+1
       // before the split end (the mask inside the block acts below 32).
-      float mx_run = -INFINITY;  // largest tile max seen in this pass (overflow check after the loop)
       auto iterate = [&](auto steady, int i, int dma, int ldst, uint64_t tb_s, int nx, int valid) {
         const int cur = lds_base + stg(i) * TB;
         const int nxt = lds_base + stg(i + 1) * TB;
         const int tb0 = cur + tr_base[0], tb1 = cur + tr_base[1], tb2 = cur + tr_base[2], tb3 = cur + tr_base[3];
         const int sb0 = nxt + s_base[0], sb1 = nxt + s_base[1], sb2 = nxt + s_base[2], sb3 = nxt + s_base[3];
         uint32_t w0, w1, w2, w3, w4, w5, w6, w7, m0save;
-        float mx;
         if constexpr (decltype(steady)::value) {
           asm volatile(MLA_ASM_FUSED_BLOCK_STEADY MLA_FUSED_OPERANDS);
         } else {
           asm volatile(MLA_ASM_FUSED_BLOCK MLA_FUSED_OPERANDS);
         }
-        mx_run = fmaxf(mx_run, mx);
         typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
         pf[0] = __builtin_bit_cast(i16x8, u32x4{w0, w1, w2, w3});
         pf[1] = __builtin_bit_cast(i16x8, u32x4{w4, w5, w6, w7});
@@ -737,7 +739,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
                 __builtin_amdgcn_readfirstlane(nx),
                 __builtin_amdgcn_readfirstlane(nx ? r1 - (r0 + (i + 1) * TILE) : 0));
       }
-      ovf = __any(mx_run > m_ref + kRefSlack);
+      ovf = __any(!(l_sum < 0x1p64f));  // 2^kRefSlack
 #undef MLA_FUSED_OPERANDS
       if (pass == 0) {  // redo if any wave overflowed
         if (ovf && lane == 0) redo_flag = 1;

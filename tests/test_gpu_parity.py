@@ -238,3 +238,66 @@ def test_graph_replay_matches_eager(name, override):
         for k, v in eager.items():
             assert torch.equal(getattr(ds, k), v), f"replay {rep}: {k} differs from the eager run"
     check_out(inp, ds.out.cpu().numpy().astype(np.float64), oracle_step(inp)["out"], tag=f"{name} graph")
+
+
+@pytest.mark.parametrize("name,lens,splits", [
+    ("dsv2", [40, 300, 1, 700, 150], 4),        # sequences with 1, 2 and 4 non-empty splits
+    ("dsv2", [0, 2000, 31, 64, 1000, 5], 7),
+    ("small", [10, 500, 1023, 0, 77], 5),
+])
+def test_split_partials(name, lens, splits):
+    """mla_decode_latent on its own, split by split: each non-empty split's
+    partial (mean of c_kv under the softmax within the split) and log-sum-exp
+    against an fp64 reference built from the oracle's softmax and log-sum-exp
+    over the split's rows, with the kernel's own inputs (q_lat and the cache
+    after the append); the splits past a sequence's end leave o_part untouched
+    (a sentinel survives) and set lse_part to -inf."""
+    from head_latent_attention_12_amd import mla
+    from head_latent_attention_12_amd.step import DeviceStep
+    inp = syn.make_inputs(name, lens=lens)
+    ds = DeviceStep(inp, num_splits=splits)
+    ds.absorb_q()
+    ds.rope_append()
+    ds.o_part.fill_(0x5A5A5A5A)
+    ds.lse_part.fill_(float("nan"))
+    ds.decode_latent()
+    torch.cuda.synchronize()
+    B, H, r, S = inp.B, inp.H, inp.r, splits
+    chunk = -(-inp.max_seq_len // S)
+    chunk = -(-chunk // 32) * 32
+    q_lat = ds.q_lat_f64()
+    cache = ds.cache_f64()
+    lse = ds.lse_part.cpu().numpy().astype(np.float64)
+    raw = ds.o_part.cpu().numpy()
+    if inp.dtype == syn.BF16:
+        bits = raw.view(np.uint16)
+        parts = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        sentinel = np.uint16(0x5A5A)
+    else:
+        bits = raw.view(np.uint32)
+        parts = bits.view(np.float32).astype(np.float64)
+        sentinel = np.uint32(0x5A5A5A5A)
+    # element (b, s, h, c) at ((b*S + s)*(r/4) + c/4)*H*4 + h*4 + c%4
+    parts = parts.reshape(B, S, r // 4, H, 4).transpose(0, 1, 3, 2, 4).reshape(B, S, H, r)
+    bits = bits.reshape(B, S, r // 4, H, 4).transpose(0, 1, 3, 2, 4).reshape(B, S, H, r)
+    tol_o = 1e-2 if inp.dtype == syn.BF16 else 1e-5
+    tol_l = 2e-2 if inp.dtype == syn.BF16 else 1e-5
+    checked = 0
+    for b in range(B):
+        n_rows = int(inp.seq_lens[b])
+        off = int(inp.row_offsets[b])
+        rows = cache[off:off + n_rows]
+        scores = inp.softmax_scale * (q_lat[b] @ rows.T)          # [H, rows]
+        for s in range(S):
+            lo, hi = s * chunk, min((s + 1) * chunk, n_rows)
+            if lo >= hi:
+                assert np.all(bits[b, s] == sentinel), f"b={b} s={s}: empty split wrote its partial"
+                assert np.all(np.isneginf(lse[b, s])), f"b={b} s={s}: empty split lse"
+                continue
+            ref_o = orc.softmax(scores[:, lo:hi]) @ rows[lo:hi, :r]  # [H, r]
+            ref_l = orc.logsumexp(scores[:, lo:hi])
+            err = np.abs(parts[b, s] - ref_o).max() / max(1e-30, np.abs(ref_o).max())
+            assert err <= tol_o, f"b={b} s={s}: partial rel err {err:.3e}"
+            np.testing.assert_allclose(lse[b, s], ref_l, rtol=0, atol=tol_l * max(1.0, np.abs(ref_l).max()))
+            checked += 1
+    print(f"[{name} splits={S}] {checked} non-empty splits checked", flush=True)

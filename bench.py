@@ -312,7 +312,7 @@ def main():
     traffic = counter_traffic(main_res["name"])
     achieved = main_res["decode_kernel_GBps"]
     line = {
-        "metric": "MLA decode cached-tokens/s (absorbed decode step, 1 GPU)",
+        "metric": "MLA decode cached-tokens/s + achieved HBM GB/s & MFMA util vs roofline (1 GPU)",
         "value": round(main_res["value"], 1),
         "unit": "cached-tokens/s",
         "n_gpus": 1,

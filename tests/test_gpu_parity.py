@@ -145,6 +145,8 @@ def test_head_widths(override):
     ("dsv2", [0]),
     ("dsv2", [1, 30, 31, 32, 95, 96, 97, 500]),
     ("dsv2", [5] * 33),                  # batch not a multiple of 32 (q~ and W_UV blocks)
+    ("dsv2", [3] * 65),                  # the decode's work count spans two steps of 64 sequences
+    ("dsv2", [(37 * i) % 401 for i in range(130)]),  # three steps, mixed split counts
 ])
 def test_edge_lengths(name, lens):
     inp = syn.make_inputs(name, lens=lens)

@@ -132,3 +132,29 @@ def test_plan_splits_rejects_bad_args():
     d = dsv2()
     with pytest.raises(mla.MlaError):
         mla.mla_plan_splits(d, 0, 10, 256)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_plan_splits_ragged_one_round(seed):
+    """Ragged batches (64 sequences, 512..8192 cached tokens): the planned split
+    count gives at most one work-group per CU (the non-empty splits fit the
+    256 CUs), and never fewer than a quarter of the CUs' worth of work items."""
+    import numpy as np
+    lens = np.random.default_rng(100 + seed).integers(512, 8192, size=64, endpoint=True) + 1
+    T, total = int(lens.max()), int(lens.sum())
+    d = mla.make_dims(64, 128, 128, 128, 512, 64, mla.MLA_BF16)
+    s = mla.mla_plan_splits(d, T, total, 256)
+    chunk = -(-T // s)
+    chunk = -(-chunk // 32) * 32
+    items = int(sum(min(s, -(-int(l) // chunk)) for l in lens))
+    assert 64 <= items <= 256, (s, chunk, items)
+
+
+def test_plan_splits_prefers_one_round_over_finer_splits():
+    """A uniform batch whose finer split would need two rounds of work-groups
+    stays at the coarser split (B = 16, T = 4097: 15 splits, 240 work items)."""
+    d = mla.make_dims(16, 128, 128, 128, 512, 64, mla.MLA_BF16)
+    s = mla.mla_plan_splits(d, 4097, 16 * 4097, 256)
+    chunk = -(-(-(-4097 // s)) // 32) * 32
+    assert 16 * -(-4097 // chunk) <= 256
+    assert s >= 8

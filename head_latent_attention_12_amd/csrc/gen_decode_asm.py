@@ -9,14 +9,16 @@ wave, 512 latent columns.  Blocks:
     streamed from LDS with ds_read_b128 through a 4-deep rolling window held in
     v[240:255]; B fragments (q) and the accumulator are asm operands.
   fused block (and its branch-free steady-state form): the scores of the
-    next tile (36 k-steps into v[208:223]), then
-    the P*V product of the current tile, O^T[c][h] += cache^T P^T (16 column
-    blocks x 2 k-halves; cache^T fragments from pairs of ds_read_b64_tr_b16
-    through the same kind of 4-deep rolling window; accumulators are AGPR
-    operands), with the next tile's softmax (mask of rows past the split end,
-    exponentials, bf16 packing, running sum) interleaved between
-    the P*V MFMAs so that it runs while the matrix core is busy; the LDS DMA
-    of a later tile is spread over the score MFMAs.
+    next tile (36 k-steps into v[208:223]) with the current tile's softmax
+    (mask of rows past the split end, exponentials, bf16 packing into
+    v[196:203], running sum) interleaved between the first score MFMAs, so
+    that it runs while the matrix core is busy; then the P*V product of the
+    current tile, O^T[c][h] += cache^T P^T (16 column blocks x 2 k-halves;
+    cache^T fragments from pairs of ds_read_b64_tr_b16 through the same kind
+    of 4-deep rolling window; accumulators are AGPR operands), during which
+    the next tile's scores move into the score operands that the following
+    block's softmax reads.  The LDS DMA of a later tile is spread over the
+    score MFMAs.
 
 Every LDS read issued by a block is waited for inside that block, so no load
 is in flight when the asm statement ends.  The dependency rules observed in
@@ -32,10 +34,8 @@ import sys
 ROWB = 1152          # bytes per cache row
 S_DEPTH = 4          # score-phase fragments in flight
 KS = 36              # k-steps of 16 over the 576-wide row
-SACC = 208           # first VGPR of the next tile's score accumulator (16 regs)
 TMP = 204            # mask temporaries (v205 holds -inf)
 VLIM = 206           # per-lane row limit of the mask
-MFMA_TO_VALU = 20    # wait states between the last score MFMA and a VALU read of it
 
 
 class _Lds:
@@ -95,9 +95,6 @@ PV_FRAGS = [(2 * g + dc, ks) for g in range(8) for dc, ks in ((0, 0), (1, 0), (0
 PV_DEPTH = 4         # P*V fragments in flight (rolling window v[240:255], as for the scores)
 
 
-PRE_BASE = 232       # first VGPR of the P*V fragments prefetched during the score phase
-
-
 def _pv_reads(n, slot=None, base=None):
     """The two transpose reads of P*V fragment n (column block cb, k-half ks)
     into window slot `slot` (default n % PV_DEPTH) or into v[base:base+3]."""
@@ -110,82 +107,17 @@ def _pv_reads(n, slot=None, base=None):
             f"ds_read_b64_tr_b16 v[{r + 2}:{r + 3}], %[t{2 + (cb & 1)}] offset:{off}"]
 
 
-def _pv_lines(valu=None, first_valu_after=0, prelude=None, lds=None, pre=None):
-    """P*V MFMAs over the 32 fragments (16 column blocks x 2 k-halves).
-    Fragments in `pre` (n -> (first VGPR, id of its second read)) were read
-    earlier into their own registers; the others are fed through a rolling
-    window: the reads of the window's fragment k + PV_DEPTH go into the slot
-    of fragment k right after its MFMA has been issued.  `valu` (list of
-    instructions) is spread between the MFMAs, starting once
-    `first_valu_after` wait states have passed since the block start;
-    `prelude` (a list of lines) is emitted whole at that point."""
-    valu = list(valu or [])
-    pre = pre or {}
-    lds = lds or _Lds()
-    nfr = len(PV_FRAGS)
-    win = [n for n in range(nfr) if n not in pre]
-    pos = {n: k for k, n in enumerate(win)}
-    rid = {}
-    out = []
-    waited = 0  # wait states since the block start
-
-    def emit(line):
-        nonlocal waited
-        out.append(line)
-        waited += int(line.split()[1]) + 1 if line.startswith("s_nop") else 1
-
-    def issue(k):
-        for line in _pv_reads(win[k], slot=k):
-            rid[win[k]] = lds.issue()
-            emit(line)
-
-    last_trans = [None]
-
-    def emit_valu(op):
-        # one instruction between a transcendental and a VALU read of its result
-        if last_trans[0] is not None and last_trans[0] in op.split(",", 1)[-1]:
-            emit("s_nop 0")
-        emit(op)
-        last_trans[0] = op.split()[1].rstrip(",") if op.startswith("v_exp_f32") else None
-
-    for k in range(min(PV_DEPTH, len(win))):
-        issue(k)
-    per_slot = None
-    for n in range(nfr):
-        cb, ks = PV_FRAGS[n]
-        if n in pre:
-            r, last_read = pre[n]
-            emit(lds.wait(last_read))
-        else:
-            r = 256 - 4 * PV_DEPTH + 4 * (pos[n] % PV_DEPTH)
-            emit(lds.wait(rid[n]))
-        emit(f"v_mfma_f32_32x32x16_bf16 %[o{cb}], v[{r}:{r + 3}], %[p{ks}], %[o{cb}]")
-        last_trans[0] = None
-        if n not in pre and pos[n] + PV_DEPTH < len(win):
-            issue(pos[n] + PV_DEPTH)
-        if valu:
-            if waited < first_valu_after:
-                emit(f"s_nop {first_valu_after - waited - 1}")
-            if prelude:
-                for line in prelude:
-                    emit(line)
-                prelude = None
-            if per_slot is None:
-                per_slot = -(-len(valu) // (nfr - n))
-            for _ in range(min(per_slot, len(valu))):
-                emit_valu(valu.pop(0))
-    while valu:  # (not reached with the shapes generated here)
-        emit_valu(valu.pop(0))
-    return out
+SACC = 208           # the next tile's score accumulator (16 VGPRs)
+MFMA_TO_VALU = 20    # instructions between the last score MFMA and a VALU read of its result
+PREG = 196           # P of the tile being multiplied: v[196:199] (k-half 0), v[200:203] (k-half 1)
+VALU_TAIL = 4        # score MFMAs at the end of the score phase with no softmax work after them
 
 
-def _mask_block(steady=False):
+def _mask_lines():
     """Rows past the split end get -inf (only when %[valid] < 32, a tile that
-    is the split's last or past it): register r holds row c + 4*(lane/32) with
+    is the split's last): register r holds row c + 4*(lane/32) with
     c = 8*(r/4) + r%4, valid iff c < %[valid] - 4*(lane/32)."""
-    if steady:  # every row of the next tile is valid
-        return []
-    s = [f"v{SACC + r}" for r in range(16)]
+    s = [f"%[s{r}]" for r in range(16)]
     vl, ninf = f"v{VLIM}", f"v{TMP + 1}"
     out = ["s_cmp_ge_i32 %[valid], 32", "s_cbranch_scc1 .Lmla_full_%=",
            f"v_mbcnt_lo_u32_b32 {vl}, -1, 0", f"v_mbcnt_hi_u32_b32 {vl}, -1, {vl}",
@@ -200,20 +132,38 @@ def _mask_block(steady=False):
 
 
 def _softmax_ops():
-    """Softmax of the next tile on v[208:223] (accumulator register r holds
-    row 8*(r/4) + 4*(lane/32) + r%4 of the tile, head = lane%32):
-    outputs %[w0..w7] (bf16 pairs of 2^(s*scale - mref)) and %[l] += the sum
-    of those rounded weights.  (No tile maximum: the overflow test runs once
-    per pass on the sum, outside.)  Ordered so that no instruction waits on a
-    recent result: the exponent arguments (in place), the exponentials, then
-    the packing and the running sum."""
-    s = [f"v{SACC + r}" for r in range(16)]
+    """Softmax of a tile's scores in %[s0..s15] (score r holds row
+    8*(r/4) + 4*(lane/32) + r%4 of the tile, head = lane%32): the
+    bf16 pairs of 2^(s*scale - mref) into v[PREG:PREG+7] (the P fragments of
+    the tile's P*V product) and %[l] += the sum of those rounded weights.  (No
+    tile maximum: the overflow test runs once per pass on the sum, outside.)
+    Ordered so that no instruction waits on a recent result: the exponent
+    arguments (in place), the exponentials, the packing, then the sum."""
+    s = [f"%[s{r}]" for r in range(16)]
     ops = [f"v_fma_f32 {s[r]}, {s[r]}, %[sc], -%[mref]" for r in range(16)]
     ops += [f"v_exp_f32_e32 {s[r]}, {s[r]}" for r in range(16)]
-    # round pairs to bf16 (the weights P*V uses), then add them to the sum
-    ops += [f"v_cvt_pk_bf16_f32 %[w{j}], {s[2 * j]}, {s[2 * j + 1]}" for j in range(8)]
-    ops += [f"v_dot2c_f32_bf16_e32 %[l], 0x3f803f80, %[w{j}]" for j in range(8)]
+    ops += [f"v_cvt_pk_bf16_f32 v{PREG + j}, {s[2 * j]}, {s[2 * j + 1]}" for j in range(8)]
+    ops += [f"v_dot2c_f32_bf16_e32 %[l], 0x3f803f80, v{PREG + j}" for j in range(8)]
     return ops
+
+
+class _Valu:
+    """Emits VALU ops with one instruction between a transcendental and a VALU
+    read of its result (any other instruction in between counts)."""
+
+    def __init__(self, out):
+        self.out = out
+        self.last_trans = None
+
+    def other(self, line):
+        self.out.append(line)
+        self.last_trans = None
+
+    def valu(self, op):
+        if self.last_trans is not None and self.last_trans in op.split(",", 1)[-1]:
+            self.out.append("s_nop 0")
+        self.out.append(op)
+        self.last_trans = op.split()[1].rstrip(",") if op.startswith("v_exp_f32") else None
 
 
 DMA_PER_WAVE = 9     # 16-byte-per-lane LDS DMA instructions per wave and tile
@@ -229,59 +179,101 @@ def _dma_lines(n, steady=False):
     return ["s_cmp_eq_u32 %[dma], 0", f"s_cbranch_scc1 .Lmla_nodma{n}_%="] + copy + [f".Lmla_nodma{n}_%=:"]
 
 
-PV_PRE = 2           # P*V fragments the steady-state block reads during the score phase
+def _score_phase(acc_out, valu_ops, steady, lds):
+    """Scores of the next tile into v[acc_out:acc_out+15] (36 LDS-fed MFMAs,
+    the first starting from zero), with the DMA of a later tile after MFMAs
+    3, 7, ... and `valu_ops` spread over the MFMAs, the last VALU_TAIL MFMAs
+    left free so that the P fragments are written well before the P*V MFMAs
+    read them."""
+    buf = [f"v[{256 - 4 * S_DEPTH + 4 * j}:{259 - 4 * S_DEPTH + 4 * j}]" for j in range(S_DEPTH)]
+    out = ["s_waitcnt lgkmcnt(0)"]
+    em = _Valu(out)
+    rid = {}
+
+    def read(j):
+        rid[j] = lds.issue()
+        em.other(f"ds_read_b128 {buf[j % S_DEPTH]}, %[b{j & 3}] offset:{128 * (j >> 2)}")
+
+    for j in range(S_DEPTH):
+        read(j)
+    valu = list(valu_ops)
+    slots = KS - VALU_TAIL
+    dma_at = {3 + 4 * n: n for n in range(DMA_PER_WAVE)}
+    for j in range(KS):
+        em.other(lds.wait(rid[j]))
+        src_c = "0" if j == 0 else f"v[{acc_out}:{acc_out + 15}]"
+        em.other(f"v_mfma_f32_32x32x16_bf16 v[{acc_out}:{acc_out + 15}], {buf[j % S_DEPTH]}, %[q{j}], {src_c}")
+        if j + S_DEPTH < KS:
+            read(j + S_DEPTH)
+        if j in dma_at:
+            for line in _dma_lines(dma_at[j], steady):
+                em.other(line)
+        if j < slots and valu:
+            take = -(-len(valu) // (slots - j))
+            for _ in range(take):
+                em.valu(valu.pop(0))
+    assert not valu
+    return out
+
+
+def _pv_phase(lds, moves=()):
+    """P*V MFMAs over the 32 fragments (16 column blocks x 2 k-halves) with P
+    in v[PREG:PREG+7], cache^T fragments fed through a rolling window: the
+    reads of fragment n + PV_DEPTH go into the slot of fragment n right after
+    its MFMA has been issued.  `moves` (VALU copies of the new scores) go one
+    per MFMA once MFMA_TO_VALU instructions have passed since the phase start."""
+    nfr = len(PV_FRAGS)
+    out, rid = [], {}
+    moves = list(moves)
+
+    def issue(n):
+        for line in _pv_reads(n):
+            rid[n] = lds.issue()
+            out.append(line)
+
+    for n in range(min(PV_DEPTH, nfr)):
+        issue(n)
+    for n in range(nfr):
+        cb, ks = PV_FRAGS[n]
+        r = 256 - 4 * PV_DEPTH + 4 * (n % PV_DEPTH)
+        out.append(lds.wait(rid[n]))
+        out.append(f"v_mfma_f32_32x32x16_bf16 %[o{cb}], v[{r}:{r + 3}], v[{PREG + 4 * ks}:{PREG + 4 * ks + 3}], %[o{cb}]")
+        if n + PV_DEPTH < nfr:
+            issue(n + PV_DEPTH)
+        if moves and len(out) >= MFMA_TO_VALU:
+            out.append(moves.pop(0))
+    assert not moves
+    return out
 
 
 def fused_block(steady=False) -> str:
-    # %[nx] = 0 at the last tile of a split: no next tile, the scores are
-    # skipped and %[valid] = 0 masks every row, so the softmax part yields
-    # weights 0, sum += 0 and max = -inf.  The DMA of a later tile is spread
-    # over the score MFMAs so that its issue never queues up.  The steady-state
-    # variant (a next tile that is full, a copy always issued) has no branches
-    # and moves the transpose reads of the first PV_PRE P*V fragments into the
-    # score phase: there the four waves' b128 reads leave LDS bandwidth spare,
-    # while in the P*V phase the transpose reads alone would saturate it.
-    # m0 (which the DMA uses) is saved and restored: the compiler reserves it
+    """Iteration i of the tile loop: the scores of tile i+1 into v[SACC:SACC+15]
+    with the softmax of tile i (scores in %[s0..s15], computed one iteration
+    earlier) interleaved between the score MFMAs, then the P*V product of
+    tile i with no other VALU work than copying the new scores into %[s*] for
+    the next iteration; the LDS DMA of tile i+3 spread over the score MFMAs.
+    The steady-state form (a full tile i, a next tile, a copy always issued)
+    has no branches.  The general form masks the rows of tile i past the split
+    end (%[valid] < 32), and at the split's last tile (%[nx] = 0) runs the
+    softmax alone.  m0 (which the DMA uses) is saved and restored: the
+    compiler reserves it."""
     out = ["s_mov_b32 %[m0save], m0", "s_waitcnt lgkmcnt(0)"]
-    if not steady:
-        out += ["s_cmp_eq_u32 %[nx], 0", "s_cbranch_scc1 .Lmla_pv_%="]
     lds = _Lds()
-    extra, pre = {}, {}
-    npre = PV_PRE if steady else 0
-    for f in range(npre):
-        at = 4 + f * (KS - 8) // max(1, npre)
-        lines = _pv_reads(f, base=PRE_BASE + 4 * f)
-        extra.setdefault(at, []).extend(lines)
-        # the id of the fragment's second read: counted as the score emitter issues it
-        pre[f] = PRE_BASE + 4 * f
-    # the score emitter issues the extra reads through `lds`; record their ids
-    issued_ids = []
-    orig_issue = lds.issue
-
-    def tracking_issue():
-        r = orig_issue()
-        issued_ids.append(r)
-        return r
-
-    lds.issue = tracking_issue
-    score = _score_lines(0, KS, True, f"v[{SACC}:{SACC + 15}]", lambda j: f"%[q{j}]", extra, lds)
-    lds.issue = orig_issue
-    # ids of the extra reads, in order: the score reads are the ds_read_b128 ones
-    kinds = [l for l in score if l.startswith("ds_read")]
-    extra_ids = [rid for rid, l in zip(issued_ids, kinds) if l.startswith("ds_read_b64_tr")]
-    pre = {f: (pre[f], extra_ids[2 * f + 1]) for f in range(npre)}
-    mfma_at = [k for k, line in enumerate(score) if line.startswith("v_mfma")]
-    after = {mfma_at[3 + 4 * n]: n for n in range(DMA_PER_WAVE)}
-    for k, line in enumerate(score):
-        out.append(line)
-        if k in after:
-            out += _dma_lines(after[k], steady)
-    if not steady:
+    sm = _softmax_ops()
+    if steady:
+        out += _score_phase(SACC, sm, True, lds)
+    else:
+        out += _mask_lines()
+        out += ["s_cmp_eq_u32 %[nx], 0", "s_cbranch_scc1 .Lmla_smonly_%="]
+        out += _score_phase(SACC, sm, False, lds)
+        out += ["s_branch .Lmla_pv_%=", ".Lmla_smonly_%=:"]
+        em = _Valu(out)
+        for op in sm:
+            em.valu(op)
         out.append(".Lmla_pv_%=:")
-        lds = _Lds()  # (the score phase may have been skipped)
-    # P*V of the current tile; the first VALU read of the scores comes at
-    # least MFMA_TO_VALU wait states after the last score MFMA
-    out += _pv_lines(_softmax_ops(), MFMA_TO_VALU, _mask_block(steady), lds, pre)
+        lds = _Lds()  # (one of the two paths ran)
+    moves = [f"v_mov_b32_e32 %[s{r}], v{SACC + r}" for r in range(16)]
+    out += _pv_phase(lds, moves)
     out.append("s_mov_b32 m0, %[m0save]")
     return "\\n\\t".join(out)
 

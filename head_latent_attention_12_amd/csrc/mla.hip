@@ -625,126 +625,124 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
     }
     bool redo = false;
     if (BF16 && pass != 1) {
-      // Software-pipelined tile loop.  Iteration i computes the scores of tile
-      // i+1 and then P*V of tile i, with the softmax of tile i+1 running on the
-      // VALU between the P*V MFMAs (one asm block).  Tile 0's scores and
-      // softmax come first.  A stage is refilled (tile i+3 into the stage of
-      // tile i-1) once every wave has passed the barrier of iteration i.  An
-      // overflow (pass 0) is only recorded; the pass runs to its end and the
-      // work-group then decides on a redo.
-      if (ntiles >= 3) wait_vm_then_barrier<2 * DPW>();
-      else if (ntiles == 2) wait_vm_then_barrier<DPW>();
-      else wait_vm_then_barrier<0>();
-      i16x8 pf[2];
-      bool ovf = false;  // wave-uniform: some weight of the pass reached 2^kRefSlack
-      {
-        f32x16 sacc = score_tile(stg(0) * TB);
-        const float mx = tile_max(sacc, r1 - r0);
-        if (m_ref == -INFINITY) m_ref = mx;
-        // p = 2^(s*scale - ref), rounded to the bf16 that P*V sees.  In a pass
-        // that overflows (a score above ref + kRefSlack) p may be huge or
-        // infinite; that pass is discarded.
-        uint32_t w[8];
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[r], scale_log2, -m_ref));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[r + 1], scale_log2, -m_ref));
-          w[r / 2] = cvt_pk_bf16(p0, p1);
-          l_sum += __uint_as_float(w[r / 2] << 16) + __uint_as_float(w[r / 2] & 0xffff0000u);
-        }
-        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-        pf[0] = __builtin_bit_cast(i16x8, u32x4{w[0], w[1], w[2], w[3]});
-        pf[1] = __builtin_bit_cast(i16x8, u32x4{w[4], w[5], w[6], w[7]});
-      }
-// operands of the fused block (both forms)
-#define MLA_FUSED_OPERANDS \
-                     : [o0] "+a"(o[0]), [o1] "+a"(o[1]), [o2] "+a"(o[2]), [o3] "+a"(o[3]), [o4] "+a"(o[4]), \
-                       [o5] "+a"(o[5]), [o6] "+a"(o[6]), [o7] "+a"(o[7]), [o8] "+a"(o[8]), [o9] "+a"(o[9]), \
-                       [o10] "+a"(o[10]), [o11] "+a"(o[11]), [o12] "+a"(o[12]), [o13] "+a"(o[13]), \
-                       [o14] "+a"(o[14]), [o15] "+a"(o[15]), [w0] "=&v"(w0), [w1] "=&v"(w1), [w2] "=&v"(w2), \
-                       [w3] "=&v"(w3), [w4] "=&v"(w4), [w5] "=&v"(w5), [w6] "=&v"(w6), [w7] "=&v"(w7), \
-                       [l] "+v"(l_sum), [m0save] "=&s"(m0save) \
-                     : [q0] "v"(qf[0]), [q1] "v"(qf[1]), [q2] "v"(qf[2]), [q3] "v"(qf[3]), [q4] "v"(qf[4]), \
-                       [q5] "v"(qf[5]), [q6] "v"(qf[6]), [q7] "v"(qf[7]), [q8] "v"(qf[8]), [q9] "v"(qf[9]), \
-                       [q10] "v"(qf[10]), [q11] "v"(qf[11]), [q12] "v"(qf[12]), [q13] "v"(qf[13]), \
-                       [q14] "v"(qf[14]), [q15] "v"(qf[15]), [q16] "v"(qf[16]), [q17] "v"(qf[17]), \
-                       [q18] "v"(qf[18]), [q19] "v"(qf[19]), [q20] "v"(qf[20]), [q21] "v"(qf[21]), \
-                       [q22] "v"(qf[22]), [q23] "v"(qf[23]), [q24] "v"(qf[24]), [q25] "v"(qf[25]), \
-                       [q26] "v"(qf[26]), [q27] "v"(qf[27]), [q28] "v"(qf[28]), [q29] "v"(qf[29]), \
-                       [q30] "v"(qf[30]), [q31] "v"(qf[31]), [q32] "v"(qf[32]), [q33] "v"(qf[33]), \
-                       [q34] "v"(qf[34]), [q35] "v"(qf[35]), [p0] "v"(pf[0]), [p1] "v"(pf[1]), [b0] "v"(sb0), \
-                       [b1] "v"(sb1), [b2] "v"(sb2), [b3] "v"(sb3), [t0] "v"(tb0), [t1] "v"(tb1), \
-                       [t2] "v"(tb2), [t3] "v"(tb3), [mref] "v"(m_ref), [sc] "s"(scale_log2), [valid] "s"(valid), [nx] "s"(nx), \
-                       [dma] "s"(dma), [ldst] "s"(ldst), [tbase] "s"(tb_s), [d0] "v"(dma_off[0]), \
-                       [d1] "v"(dma_off[1]), [d2] "v"(dma_off[2]), [d3] "v"(dma_off[3]), [d4] "v"(dma_off[4]), \
-                       [d5] "v"(dma_off[5]), [d6] "v"(dma_off[6]), [d7] "v"(dma_off[7]), [d8] "v"(dma_off[8]) \
-                     : "v204", "v205", "v206", "v208", "v209", "v210", "v211", "v212", "v213", "v214", "v215", "v216", \
-                       "v217", "v218", "v219", "v220", "v221", "v222", "v223", \
-                       "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", \
-                       "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", \
-                       "v255", "vcc", "scc", "memory"
-      // One pipelined iteration: scores and softmax of tile i+1 (skipped when
-      // nx = 0, the last tile: every row masked, weights 0, max -inf), P*V of
-      // tile i, and (dma = 1) the copy of the full tile at tb_s into the LDS
-      // bytes at ldst, spread over the score MFMAs.  valid = rows of tile i+1
-      // before the split end (the mask inside the block acts below 32).
-      auto iterate = [&](auto steady, int i, int dma, int ldst, uint64_t tb_s, int nx, int valid) {
-        const int cur = lds_base + stg(i) * TB;
-        const int nxt = lds_base + stg(i + 1) * TB;
-        const int tb0 = cur + tr_base[0], tb1 = cur + tr_base[1], tb2 = cur + tr_base[2], tb3 = cur + tr_base[3];
-        const int sb0 = nxt + s_base[0], sb1 = nxt + s_base[1], sb2 = nxt + s_base[2], sb3 = nxt + s_base[3];
-        uint32_t w0, w1, w2, w3, w4, w5, w6, w7, m0save;
-        if constexpr (decltype(steady)::value) {
-          asm volatile(MLA_ASM_FUSED_BLOCK_STEADY MLA_FUSED_OPERANDS);
-        } else {
-          asm volatile(MLA_ASM_FUSED_BLOCK MLA_FUSED_OPERANDS);
-        }
-        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-        pf[0] = __builtin_bit_cast(i16x8, u32x4{w0, w1, w2, w3});
-        pf[1] = __builtin_bit_cast(i16x8, u32x4{w4, w5, w6, w7});
-      };
-      // Steady state, free of per-tile branches: tiles i+1 .. i+3 exist and
-      // are full (nfull counts the split's full tiles).
-      const int nfull = (last_rel + 1) / TILE;
-      const uint64_t split_s = uniform_u64((uint64_t)split_base);
-      const int ldst_w = lds_base + wave * DPW * 1024;
-      int i = 0;
-      for (; i + STAGES - 1 < nfull; ++i) {
-        wait_vm_then_barrier<DPW>();  // tile i+1 has landed, every wave has finished iteration i-1
-        const int t3 = i + STAGES - 1;
-        iterate(std::true_type{}, i, 1, ldst_w + stg(t3) * TB, split_s + (uint64_t)t3 * (TILE * ROWB), 1, TILE);
-      }
-      // the last STAGES - 1 iterations (and every iteration of a short split)
-      for (; i < ntiles; ++i) {
-        // tile i+1 has landed (tile i+2 may still be in flight) and every wave
-        // has finished iteration i-1
-        if (i + 2 < ntiles) wait_vm_then_barrier<DPW>();
+      if constexpr (BF16) {  // (only the bf16 instance has the pipelined loop)
+        // Software-pipelined tile loop.  Iteration i is one asm block: the
+        // softmax of tile i (its scores held in sv) runs on the VALU between
+        // the score MFMAs of tile i+1, then P*V of tile i, whose weights the
+        // block keeps in fixed registers.  Tile 0's scores come first.  A stage
+        // is refilled (tile i+3 into the stage of tile i-1) once every wave has
+        // passed the barrier of iteration i.  An overflow (pass 0) is only
+        // recorded; the pass runs to its end and the work-group then decides
+        // on a redo.
+        if (ntiles >= 3) wait_vm_then_barrier<2 * DPW>();
+        else if (ntiles == 2) wait_vm_then_barrier<DPW>();
         else wait_vm_then_barrier<0>();
-        // tile i+3 into the stage of tile i-1: a full tile is copied inside
-        // the block, a partial one here
-        const int t3 = i + STAGES - 1;
-        int dma = 0, ldst = 0;
-        uint64_t tbase = (uint64_t)split_base;
-        if (t3 < ntiles) {
-          if (t3 * TILE + TILE - 1 <= last_rel) {
-            dma = 1;
-            tbase += (uint64_t)t3 * TILE * ROWB;
-            ldst = ldst_w + stg(t3) * TB;
-          } else {
-            issue_tile(t3, stg(t3));
-          }
+        bool ovf = false;  // wave-uniform: some weight of the pass reached 2^kRefSlack
+        // scores of the tile whose softmax the next block computes (register r of
+        // the tile's score accumulator)
+        float sv0, sv1, sv2, sv3, sv4, sv5, sv6, sv7, sv8, sv9, sv10, sv11, sv12, sv13, sv14, sv15;
+        {
+          // tile 0's scores (masked past the split end) set the exponent
+          // reference and are the first block's softmax input
+          f32x16 sacc = score_tile(stg(0) * TB);
+          const float mx = tile_max(sacc, r1 - r0);
+          if (m_ref == -INFINITY) m_ref = mx;
+          sv0 = sacc[0], sv1 = sacc[1], sv2 = sacc[2], sv3 = sacc[3], sv4 = sacc[4], sv5 = sacc[5];
+          sv6 = sacc[6], sv7 = sacc[7], sv8 = sacc[8], sv9 = sacc[9], sv10 = sacc[10], sv11 = sacc[11];
+          sv12 = sacc[12], sv13 = sacc[13], sv14 = sacc[14], sv15 = sacc[15];
         }
-        const int nx = (i + 1 < ntiles) ? 1 : 0;
-        iterate(std::false_type{}, i, __builtin_amdgcn_readfirstlane(dma), __builtin_amdgcn_readfirstlane(ldst), uniform_u64(tbase),
-                __builtin_amdgcn_readfirstlane(nx),
-                __builtin_amdgcn_readfirstlane(nx ? r1 - (r0 + (i + 1) * TILE) : 0));
-      }
-      ovf = __any(!(l_sum < 0x1p64f));  // 2^kRefSlack
+  // operands of the fused block (both forms)
+#define MLA_FUSED_OPERANDS \
+                       : [o0] "+a"(o[0]), [o1] "+a"(o[1]), [o2] "+a"(o[2]), [o3] "+a"(o[3]), [o4] "+a"(o[4]), \
+                         [o5] "+a"(o[5]), [o6] "+a"(o[6]), [o7] "+a"(o[7]), [o8] "+a"(o[8]), [o9] "+a"(o[9]), \
+                         [o10] "+a"(o[10]), [o11] "+a"(o[11]), [o12] "+a"(o[12]), [o13] "+a"(o[13]), \
+                         [o14] "+a"(o[14]), [o15] "+a"(o[15]), \
+                         [l] "+v"(l_sum), [m0save] "=&s"(m0save), [s0] "+v"(sv0), [s1] "+v"(sv1), \
+                         [s2] "+v"(sv2), [s3] "+v"(sv3), [s4] "+v"(sv4), [s5] "+v"(sv5), [s6] "+v"(sv6), \
+                         [s7] "+v"(sv7), [s8] "+v"(sv8), [s9] "+v"(sv9), [s10] "+v"(sv10), [s11] "+v"(sv11), \
+                         [s12] "+v"(sv12), [s13] "+v"(sv13), [s14] "+v"(sv14), [s15] "+v"(sv15) \
+                       : [q0] "v"(qf[0]), [q1] "v"(qf[1]), [q2] "v"(qf[2]), [q3] "v"(qf[3]), [q4] "v"(qf[4]), \
+                         [q5] "v"(qf[5]), [q6] "v"(qf[6]), [q7] "v"(qf[7]), [q8] "v"(qf[8]), [q9] "v"(qf[9]), \
+                         [q10] "v"(qf[10]), [q11] "v"(qf[11]), [q12] "v"(qf[12]), [q13] "v"(qf[13]), \
+                         [q14] "v"(qf[14]), [q15] "v"(qf[15]), [q16] "v"(qf[16]), [q17] "v"(qf[17]), \
+                         [q18] "v"(qf[18]), [q19] "v"(qf[19]), [q20] "v"(qf[20]), [q21] "v"(qf[21]), \
+                         [q22] "v"(qf[22]), [q23] "v"(qf[23]), [q24] "v"(qf[24]), [q25] "v"(qf[25]), \
+                         [q26] "v"(qf[26]), [q27] "v"(qf[27]), [q28] "v"(qf[28]), [q29] "v"(qf[29]), \
+                         [q30] "v"(qf[30]), [q31] "v"(qf[31]), [q32] "v"(qf[32]), [q33] "v"(qf[33]), \
+                         [q34] "v"(qf[34]), [q35] "v"(qf[35]), [b0] "v"(sb0), \
+                         [b1] "v"(sb1), [b2] "v"(sb2), [b3] "v"(sb3), [t0] "v"(tb0), [t1] "v"(tb1), \
+                         [t2] "v"(tb2), [t3] "v"(tb3), [mref] "v"(m_ref), [sc] "s"(scale_log2), [valid] "s"(valid), [nx] "s"(nx), \
+                         [dma] "s"(dma), [ldst] "s"(ldst), [tbase] "s"(tb_s), [d0] "v"(dma_off[0]), \
+                         [d1] "v"(dma_off[1]), [d2] "v"(dma_off[2]), [d3] "v"(dma_off[3]), [d4] "v"(dma_off[4]), \
+                         [d5] "v"(dma_off[5]), [d6] "v"(dma_off[6]), [d7] "v"(dma_off[7]), [d8] "v"(dma_off[8]) \
+                       : "v196", "v197", "v198", "v199", "v200", "v201", "v202", "v203", "v204", "v205", "v206", \
+                         "v208", "v209", "v210", "v211", "v212", "v213", "v214", "v215", "v216", "v217", "v218", "v219", \
+                         "v220", "v221", "v222", "v223", "v240", "v241", "v242", "v243", \
+                         "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", \
+                         "v255", "vcc", "scc", "memory"
+        // One pipelined iteration: the scores of tile i+1 (skipped when nx = 0,
+        // at the split's last tile) with the softmax of tile i (scores in sv)
+        // interleaved, then P*V of tile i; (dma = 1) the copy
+        // of the full tile at tb_s into the LDS bytes at ldst, spread over the
+        // score MFMAs.  valid = rows of tile i before the split end (the general
+        // block masks the rest when it is below 32).
+        auto iterate = [&](bool steady, int i, int dma, int ldst, uint64_t tb_s, int nx, int valid) {
+          const int cur = lds_base + stg(i) * TB;
+          const int nxt = lds_base + stg(i + 1) * TB;
+          const int tb0 = cur + tr_base[0], tb1 = cur + tr_base[1], tb2 = cur + tr_base[2], tb3 = cur + tr_base[3];
+          const int sb0 = nxt + s_base[0], sb1 = nxt + s_base[1], sb2 = nxt + s_base[2], sb3 = nxt + s_base[3];
+          uint32_t m0save;
+          if (steady) {
+            asm volatile(MLA_ASM_FUSED_BLOCK_STEADY MLA_FUSED_OPERANDS);
+          } else {
+            asm volatile(MLA_ASM_FUSED_BLOCK MLA_FUSED_OPERANDS);
+          }
+        };
+        // Steady state, free of per-tile branches: tiles i .. i+3 exist and are
+        // full (nfull counts the split's full tiles).
+        const int nfull = (last_rel + 1) / TILE;
+        const uint64_t split_s = uniform_u64((uint64_t)split_base);
+        const int ldst_w = lds_base + wave * DPW * 1024;
+        int i = 0;
+        for (; i + STAGES - 1 < nfull; ++i) {
+          wait_vm_then_barrier<DPW>();  // tile i+1 has landed, every wave has finished iteration i-1
+          const int t3 = i + STAGES - 1;
+          iterate(true, i, 1, ldst_w + stg(t3) * TB, split_s + (uint64_t)t3 * (TILE * ROWB), 1, TILE);
+        }
+        // the last STAGES - 1 iterations (and every iteration of a short split)
+        for (; i < ntiles; ++i) {
+          // tile i+1 has landed (tile i+2 may still be in flight) and every wave
+          // has finished iteration i-1
+          if (i + 2 < ntiles) wait_vm_then_barrier<DPW>();
+          else wait_vm_then_barrier<0>();
+          // tile i+3 into the stage of tile i-1: a full tile is copied inside
+          // the block, a partial one here
+          const int t3 = i + STAGES - 1;
+          int dma = 0, ldst = 0;
+          uint64_t tbase = (uint64_t)split_base;
+          if (t3 < ntiles) {
+            if (t3 * TILE + TILE - 1 <= last_rel) {
+              dma = 1;
+              tbase += (uint64_t)t3 * TILE * ROWB;
+              ldst = ldst_w + stg(t3) * TB;
+            } else {
+              issue_tile(t3, stg(t3));
+            }
+          }
+          const int nx = __builtin_amdgcn_readfirstlane((i + 1 < ntiles) ? 1 : 0);
+          const int valid = __builtin_amdgcn_readfirstlane(r1 - (r0 + i * TILE));
+          dma = __builtin_amdgcn_readfirstlane(dma);
+          ldst = __builtin_amdgcn_readfirstlane(ldst);
+          const uint64_t tb_s = uniform_u64(tbase);
+          iterate(false, i, dma, ldst, tb_s, nx, valid);
+        }
+        ovf = __any(!(l_sum < 0x1p64f));  // 2^kRefSlack
 #undef MLA_FUSED_OPERANDS
-      if (pass == 0) {  // redo if any wave overflowed
-        if (ovf && lane == 0) redo_flag = 1;
-        wait_vm_then_barrier<0>();
-        redo = redo_flag != 0;
+        if (pass == 0) {  // redo if any wave overflowed
+          if (ovf && lane == 0) redo_flag = 1;
+          wait_vm_then_barrier<0>();
+          redo = redo_flag != 0;
+        }
       }
     } else {
       // One tile per iteration: scores, softmax, P*V (fp32), or scores only

@@ -798,53 +798,71 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
     if (pass == 1) m_ref = m_seen;  // exact max of the split: p <= 1 in the final pass
   }
 
-  // o_part of split (b, s) is [R/4][H][4] in the storage dtype: column quad
-  // cq = 8*cb + 2*q + hf of this lane's head sits at (cq*H + head)*4, so the 32
-  // lanes of a half-wave store contiguous bytes.  bf16 partials are the fp32
-  // softmax-weighted means rounded once (relative error <= 2^-9 of each value).
+  // o_part of split (b, s) is [H][R] in the storage dtype: one contiguous row
+  // per head, which its consumers read whole.  A lane holds columns
+  // 32*cb + 8*q + 4*hf + (0..3) of its head, so the bf16 block goes through
+  // LDS (the ring is free now): each wave writes its 32 heads x R as rows of
+  // R*2 bytes, 16-byte chunk k of row t at slot k ^ (t & 15), then stores the
+  // rows with one coalesced 16-byte access per lane.  bf16 partials are the
+  // fp32 softmax-weighted means rounded once (relative error <= 2^-9).
   const float l_tot = xor32(l_sum, [](float a, float b) { return a + b; });
-  if (head_ok) {
-    const float inv = 1.f / l_tot;
-    T* op = o_part + ((int64_t)b * num_splits + s) * H * R + (int64_t)(hf * H + head) * 4;
+  const float inv = 1.f / l_tot;
+  if constexpr (BF16) {
+    static_assert(R * 2 == 1024 && 4 * 32 * R * 2 <= STAGES * TB, "one 1 KB row per lane-chunk, 4 waves in the ring");
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    __syncthreads();  // every wave is done with the ring
+    LDS_AS char* wrows = (LDS_AS char*)smem + wave * 32 * (R * 2);
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        T* dst = op + (int64_t)(8 * cb + 2 * q) * H * 4;
-        if constexpr (BF16) {
-          typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-          *(u32x2*)dst = u32x2{cvt_pk_bf16(o[cb][4 * q] * inv, o[cb][4 * q + 1] * inv),
-                               cvt_pk_bf16(o[cb][4 * q + 2] * inv, o[cb][4 * q + 3] * inv)};
-        } else {
-          *(f32x4*)dst = f32x4{o[cb][4 * q] * inv, o[cb][4 * q + 1] * inv, o[cb][4 * q + 2] * inv,
-                               o[cb][4 * q + 3] * inv};
-        }
+        const int k = 4 * cb + q;  // 16-byte chunk of the row; this lane's half is hf
+        *(LDS_AS u32x2*)(wrows + l32 * (R * 2) + 16 * (k ^ (l32 & 15)) + 8 * hf) =
+            u32x2{cvt_pk_bf16(o[cb][4 * q] * inv, o[cb][4 * q + 1] * inv),
+                  cvt_pk_bf16(o[cb][4 * q + 2] * inv, o[cb][4 * q + 3] * inv)};
       }
+    }
+    __syncthreads();  // (the rows of a wave are written and read by that wave only)
+    T* op = o_part + (((int64_t)b * num_splits + s) * H + wave * 32) * R + 8 * lane;
+#pragma unroll 8
+    for (int t = 0; t < 32; ++t) {
+      const u32x4 v = *(const LDS_AS u32x4*)(wrows + t * (R * 2) + 16 * (lane ^ (t & 15)));
+      *(u32x4*)(op + (int64_t)t * R) = v;
+    }
+    if (hf == 0) lse_out[head] = (m_ref + __log2f(l_tot)) * kLn2;
+  } else if (head_ok) {
+    T* op = o_part + (((int64_t)b * num_splits + s) * H + head) * R + 4 * hf;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *(f32x4*)(op + 32 * cb + 8 * q) = f32x4{o[cb][4 * q] * inv, o[cb][4 * q + 1] * inv,
+                                                 o[cb][4 * q + 2] * inv, o[cb][4 * q + 3] * inv};
     }
     if (hf == 0) lse_out[head] = (m_ref + __log2f(l_tot)) * kLn2;
   }
 }
 
 // ---------------------------------------------------------------------------
-// K4: merge the splits.  The partials of split (b, s) are [R/4][H][4]
-// (column quads, heads, 4 columns), so quad pair P (quads 2P, 2P+1: heads h,
-// h+1 of one column quad, H even) is 8 contiguous values.  A work-group of 256
-// threads is SG split groups x TQ = 256/SG threads; thread t of a group takes
-// quad pair (block*TQ + t) of every SG-th split, eight splits per step with
-// the loads issued together, keeping a running maximum of the log-sum-exps
-// (sums rescaled when it grows).  The groups are merged through LDS the same
-// way.  SG grows with the split count so that a thread sees about eight.
+// K4: merge the splits.  The partials of split (b, s) are [H][R], so octet P
+// (8 contiguous values: columns 8*(P % (R/8)) .. +7 of head P / (R/8)) is one
+// 16-byte (bf16) or 32-byte (fp32) load.  A work-group of 256 threads is SG
+// split groups x TQ = 256/SG threads; thread t of a group takes octet
+// (block*TQ + t) of every SG-th split, eight splits per step with the loads
+// issued together, keeping a running maximum of the log-sum-exps (sums
+// rescaled when it grows).  The groups are merged through LDS the same way.
+// SG grows with the split count so that a thread sees about eight.
 // ---------------------------------------------------------------------------
 
 constexpr int kCombineThreads = 256;
 constexpr int kCombineMaxGroups = 16;
 
-// four (two) consecutive values of a partial in its storage dtype, as fp32
-// A quad pair of one split's partial: 8 values as stored (raw bits), then
-// unpacked to two fp32 quads.  The raw load is kept apart from the unpacking
-// so that all of a step's loads are in flight before the first is used.
-template <typename PT> struct Pair8;
-template <> struct Pair8<float> {
+// Eight consecutive values of a partial: the raw load is kept apart from the
+// unpacking to two fp32 quads, so that all of a step's loads are in flight
+// before the first is used.
+template <typename PT> struct Oct;
+template <> struct Oct<float> {
   typedef f32x4 Raw[2];
   static __device__ __forceinline__ void zero(Raw& r) { r[0] = r[1] = f32x4{0.f, 0.f, 0.f, 0.f}; }
   static __device__ __forceinline__ void load(const float* p, Raw& r) {
@@ -856,7 +874,7 @@ template <> struct Pair8<float> {
     b = r[1];
   }
 };
-template <> struct Pair8<u16> {
+template <> struct Oct<u16> {
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   typedef u32x4 Raw;
   static __device__ __forceinline__ void zero(Raw& r) { r = u32x4{0u, 0u, 0u, 0u}; }
@@ -877,87 +895,77 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const PT* __re
                                                                   float* __restrict__ lse_out) {
   constexpr int U = 8;
   __shared__ f32x4 part[kCombineThreads][2];
-  __shared__ float wpart[kCombineThreads][2], mpart[kCombineThreads][2];
+  __shared__ float wpart[kCombineThreads], mpart[kCombineThreads];
   const int TQ = (int)blockDim.x / SG;
-  const int pairs = (R / 4) * H / 2;            // quad pairs per split
-  const int blocks_per_b = pairs / TQ;
+  const int octs = (R / 8) * H;                 // octets per split
+  const int blocks_per_b = octs / TQ;
   const int b = (int)blockIdx.x / blocks_per_b;
   const int t = (int)threadIdx.x % TQ, sg = (int)threadIdx.x / TQ;
-  const int pair = ((int)blockIdx.x - b * blocks_per_b) * TQ + t;
-  const int q0 = 2 * pair, cq = q0 / H, h = q0 - cq * H;  // heads h, h+1 of column quad cq
+  const int oct = ((int)blockIdx.x - b * blocks_per_b) * TQ + t;
+  const int h = oct / (R / 8), c0 = 8 * (oct - h * (R / 8));
   const float* lp = lse_part + (int64_t)b * num_splits * H + h;
   const int64_t sstride = (int64_t)H * R;
-  const PT* op = o_part + (int64_t)b * num_splits * sstride + (int64_t)q0 * 4;
+  const PT* op = o_part + (int64_t)b * num_splits * sstride + (int64_t)oct * 8;
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
-  float w0 = 0.f, w1 = 0.f, m0 = -INFINITY, m1 = -INFINITY;
+  float w = 0.f, m = -INFINITY;
   for (int s0 = sg; s0 < num_splits; s0 += U * SG) {
-    float l0[U], l1[U];
+    float l[U];
     f32x4 va[U], vb[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int s = s0 + u * SG;
-      const bool ok = s < num_splits;
-      l0[u] = ok ? lp[(int64_t)s * H] : -INFINITY;
-      l1[u] = ok ? lp[(int64_t)s * H + 1] : -INFINITY;
+      l[u] = s < num_splits ? lp[(int64_t)s * H] : -INFINITY;
     }
-    typename Pair8<PT>::Raw raw[U];
+    typename Oct<PT>::Raw raw[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int s = s0 + u * SG;
-      // an empty split (lse -inf for every head) never wrote its partial
-      Pair8<PT>::zero(raw[u]);
-      if (s < num_splits && l0[u] != -INFINITY) Pair8<PT>::load(op + s * sstride, raw[u]);
+      // an empty split (lse -inf) never wrote its partial
+      Oct<PT>::zero(raw[u]);
+      if (s < num_splits && l[u] != -INFINITY) Oct<PT>::load(op + s * sstride, raw[u]);
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) Pair8<PT>::unpack(raw[u], va[u], vb[u]);
-    float n0 = m0, n1 = m1;
+    for (int u = 0; u < U; ++u) Oct<PT>::unpack(raw[u], va[u], vb[u]);
+    float n = m;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      n0 = fmaxf(n0, l0[u]);
-      n1 = fmaxf(n1, l1[u]);
-    }
-    if (n0 == -INFINITY) continue;  // only empty splits so far (then n1 is -inf too)
-    const float c0 = __expf(m0 - n0), c1 = __expf(m1 - n1);  // 0 while m = -inf
-    acc0 *= c0;
-    w0 *= c0;
-    acc1 *= c1;
-    w1 *= c1;
+    for (int u = 0; u < U; ++u) n = fmaxf(n, l[u]);
+    if (n == -INFINITY) continue;  // only empty splits so far
+    const float c = __expf(m - n);  // 0 while m = -inf
+    acc0 *= c;
+    acc1 *= c;
+    w *= c;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float e0 = __expf(l0[u] - n0), e1 = __expf(l1[u] - n1);
-      w0 += e0;
-      w1 += e1;
-      acc0 += e0 * va[u];
-      acc1 += e1 * vb[u];
+      const float e = __expf(l[u] - n);
+      w += e;
+      acc0 += e * va[u];
+      acc1 += e * vb[u];
     }
-    m0 = n0;
-    m1 = n1;
+    m = n;
   }
   part[threadIdx.x][0] = acc0;
   part[threadIdx.x][1] = acc1;
-  wpart[threadIdx.x][0] = w0;
-  wpart[threadIdx.x][1] = w1;
-  mpart[threadIdx.x][0] = m0;
-  mpart[threadIdx.x][1] = m1;
+  wpart[threadIdx.x] = w;
+  mpart[threadIdx.x] = m;
   __syncthreads();
   if (sg == 0) {
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      float mt = -INFINITY;
-      for (int g = 0; g < SG; ++g) mt = fmaxf(mt, mpart[g * TQ + t][k]);
-      f32x4 tot = {0.f, 0.f, 0.f, 0.f};
-      float wt = 0.f;
-      for (int g = 0; g < SG; ++g) {
-        const float mg = mpart[g * TQ + t][k];
-        if (mg == -INFINITY) continue;  // a group that saw only empty splits
-        const float c = __expf(mg - mt);
-        tot += c * part[g * TQ + t][k];
-        wt += c * wpart[g * TQ + t][k];
-      }
-      const int64_t row = (int64_t)b * H + h + k;
-      *(f32x4*)(o_lat + row * R + 4 * cq) = tot * (1.f / wt);
-      if (lse_out != nullptr && cq == 0) lse_out[row] = mt + __logf(wt);
+    float mt = -INFINITY;
+    for (int g = 0; g < SG; ++g) mt = fmaxf(mt, mpart[g * TQ + t]);
+    f32x4 tot0 = {0.f, 0.f, 0.f, 0.f}, tot1 = tot0;
+    float wt = 0.f;
+    for (int g = 0; g < SG; ++g) {
+      const float mg = mpart[g * TQ + t];
+      if (mg == -INFINITY) continue;  // a group that saw only empty splits
+      const float c = __expf(mg - mt);
+      tot0 += c * part[g * TQ + t][0];
+      tot1 += c * part[g * TQ + t][1];
+      wt += c * wpart[g * TQ + t];
     }
+    const int64_t row = (int64_t)b * H + h;
+    float* dst = o_lat + row * R + c0;
+    *(f32x4*)dst = tot0 * (1.f / wt);
+    *(f32x4*)(dst + 4) = tot1 * (1.f / wt);
+    if (lse_out != nullptr && c0 == 0) lse_out[row] = mt + __logf(wt);
   }
 }
 
@@ -1302,6 +1310,328 @@ __global__ __launch_bounds__(64) void up_v_f32_kernel(const float* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
+// K4 + K5 in one kernel: out[b][h][d] = sum_j W_UV[h][d][j] o[b][h][j], where
+// o is the merge of the splits (as K4), formed where it is consumed instead of
+// going through memory.
+// bf16: one work-group (8 waves) per (head, block of DB = 32*NH output rows);
+// the blocks of a head run on one XCD, whose L2 then serves them the head's
+// partials.  The DB weight rows are copied into LDS by DMA at the start.  Per
+// chunk of up to 32 sequences:
+//   merge: a unit is a (sequence, part) pair covering the splits s = part
+//     (mod WPR) of that sequence; WPR is the largest power of two with
+//     rows * WPR <= 8 (1 from 5 rows up), so that short chunks still use
+//     every wave, and then each wave holds at most one unit.  A wave takes up to UPW units and issues the loads of all their
+//     splits (one contiguous 1 KB partial row each, 16 bytes per lane)
+//     together with the log-sum-exp reads, so one round trip serves them.
+//     Units of one sequence add their sums through LDS.  The merged fp32 row
+//     enters LDS as a hi and a lo bf16 row (16-byte chunk k of row t at slot
+//     k ^ (t & 15)).
+//   product: wave w takes output rows 32*(w/4) .. +31 of the block and the j
+//     quarter w % 4 (two MFMAs per k step, hi and lo); the four quarters are
+//     summed through LDS (which then reuses the merged rows' bytes).
+// fp32: one wave per (sequence, head): lane c merges column c, then lane d
+// forms out[d] with fp32 FMAs over j from the merged row in LDS.
+// ---------------------------------------------------------------------------
+
+constexpr int kCuvWaves = 8;
+constexpr int kCuvRows = 32;      // sequences per chunk (the MFMA's N)
+constexpr int kCuvMaxRankF32 = 256;
+
+__device__ __forceinline__ float wave_max_f(float v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d));
+  return v;
+}
+__device__ __forceinline__ float wave_sum_f(float v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d);
+  return v;
+}
+
+// Log-sum-exp statistics of one (sequence, head) over its S splits (lse at
+// lp[s * H]): mx = max_s lse, wsum = sum_s exp(lse - mx); -inf and 0 when
+// every split is empty.  Every lane returns the same values.
+__device__ __forceinline__ void lse_stats(const float* __restrict__ lp, int S, int H, int lane, float& mx,
+                                          float& wsum) {
+  float ml = -INFINITY, wl = 0.f;
+  for (int s = lane; s < S; s += 64) {
+    const float l = lp[(int64_t)s * H];
+    if (l > ml) {
+      wl = wl * __expf(ml - l) + 1.f;  // (0 while ml = -inf)
+      ml = l;
+    } else if (l != -INFINITY) {
+      wl += __expf(l - ml);
+    }
+  }
+  mx = wave_max_f(ml);
+  wsum = wave_sum_f(ml == -INFINITY ? 0.f : wl * __expf(ml - mx));
+}
+
+// hi + lo bf16 parts of a merged row's 8 columns of this lane into LDS row t
+__device__ __forceinline__ void cuv_put_row(char* ot, int t, int lane, const float (&o)[8]) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 hi, lo;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    hi[e] = cvt_pk_bf16(o[2 * e], o[2 * e + 1]);
+    lo[e] = cvt_pk_bf16(o[2 * e] - __uint_as_float(hi[e] << 16), o[2 * e + 1] - __uint_as_float(hi[e] & 0xffff0000u));
+  }
+  LDS_AS char* row = (LDS_AS char*)ot + t * 2048 + 16 * (lane ^ (t & 15));
+  *(LDS_AS u32x4*)row = hi;
+  *(LDS_AS u32x4*)(row + 1024) = lo;
+}
+
+// The merge of one chunk (see above), UPW units per wave with NB splits of
+// each in flight.  The splits of a unit are taken 64 at a time: lane i holds
+// the log-sum-exp of the group's split i (one load), the group raises the
+// unit's running maximum (the sums so far rescaled), and split i's weight is
+// read from lane i.  Only splits that exist are loaded, and an empty split's
+// bytes are never used.  Leaves the merged rows in ot and, if lse_out is not
+// null, the merged log-sum-exps there.
+template <int UPW, int NB>
+__device__ __forceinline__ void cuv_merge(const u16* __restrict__ o_part, const float* __restrict__ lse_part,
+                                          int S, int H, int h, int b0, int nb, int WPR, int wave, int lane,
+                                          char* ot, float (*xs)[64][8], float* xm, float* xw,
+                                          float* __restrict__ lse_out) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  constexpr int R = 512;
+  const int units = nb * WPR;
+  const int part = wave % WPR;                                // the same for all units of a wave
+  const int spu = part < S ? (S - part + WPR - 1) / WPR : 0;  // splits of this part: s = part + WPR*i
+  bool uok[UPW];
+  int trow[UPW];
+  int64_t base[UPW];  // (b*S + part)*H + h: split i of the unit is row base + i*WPR*H of o_part / lse_part
+  // The partial rows are read through a buffer resource over the sequence's
+  // S*H*R values (at most 512 MB): a split that does not exist gets an offset
+  // past the end, which returns zeros without a memory access, so every load
+  // of a batch is issued unconditionally.
+  __amdgpu_buffer_rsrc_t rsrc[UPW];
+  const uint32_t nrec = (uint32_t)S * (uint32_t)H * (R * 2);
+#pragma unroll
+  for (int k = 0; k < UPW; ++k) {
+    const int u = wave + kCuvWaves * k;
+    uok[k] = u < units;
+    trow[k] = uok[k] ? u / WPR : 0;
+    base[k] = ((int64_t)(b0 + trow[k]) * S + part) * H + h;
+    rsrc[k] = __builtin_amdgcn_make_buffer_rsrc((void*)(o_part + (int64_t)(b0 + trow[k]) * S * H * R), (short)0,
+                                                (int)nrec, 0x00020000);
+  }
+  const int64_t istride = (int64_t)WPR * H;
+  float acc[UPW][8], mx[UPW], wsum[UPW];
+#pragma unroll
+  for (int k = 0; k < UPW; ++k) {
+    mx[k] = -INFINITY;
+    wsum[k] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[k][e] = 0.f;
+  }
+  for (int g0 = 0; g0 < spu; g0 += 64) {
+    const int gn = min(64, spu - g0);  // splits of this group (per unit)
+    float lv[UPW], ev[UPW];
+#pragma unroll
+    for (int k = 0; k < UPW; ++k) {
+      lv[k] = -INFINITY;
+      if (uok[k] && lane < gn) lv[k] = lse_part[base[k] + (int64_t)(g0 + lane) * istride];
+    }
+    for (int u0 = 0; u0 < gn; u0 += NB) {
+      u32x4 raw[UPW][NB];
+#pragma unroll
+      for (int k = 0; k < UPW; ++k)
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+          const uint32_t off = (uok[k] && u0 + u < gn)
+                                   ? (uint32_t)((part + WPR * (g0 + u0 + u)) * H + h) * (R * 2) + 16 * lane
+                                   : nrec;
+          raw[k][u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc[k], off, 0, 0));
+        }
+      if (u0 == 0) {  // the group's log-sum-exps (loaded before these rows) update the maxima
+#pragma unroll
+        for (int k = 0; k < UPW; ++k) {
+          const float mn = fmaxf(mx[k], wave_max_f(lv[k]));
+          ev[k] = 0.f;
+          if (mn != -INFINITY) {
+            const float c = __expf(mx[k] - mn);  // 0 while mx = -inf
+            wsum[k] *= c;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[k][e] *= c;
+            mx[k] = mn;
+            ev[k] = lv[k] == -INFINITY ? 0.f : __expf(lv[k] - mn);
+            wsum[k] += wave_sum_f(ev[k]);
+          }
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < UPW; ++k)
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+          if (!(uok[k] && u0 + u < gn)) continue;
+          // the split's weight (0 for an empty split, whose bytes are not used)
+          const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ev[k]), u0 + u));
+          if (c == 0.f) continue;
+          const u32x4 v = raw[k][u];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[k][2 * e] = fmaf(c, __uint_as_float(v[e] << 16), acc[k][2 * e]);
+            acc[k][2 * e + 1] = fmaf(c, __uint_as_float(v[e] & 0xffff0000u), acc[k][2 * e + 1]);
+          }
+        }
+    }
+  }
+  if (WPR == 1) {
+#pragma unroll
+    for (int k = 0; k < UPW; ++k) {
+      if (!uok[k]) continue;
+      const float inv = wsum[k] > 0.f ? 1.f / wsum[k] : 0.f;  // 0: every split empty
+      float o[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = acc[k][e] * inv;
+      cuv_put_row(ot, trow[k], lane, o);
+      if (lse_out != nullptr && lane == 0) lse_out[(int64_t)(b0 + trow[k]) * H + h] = mx[k] + __logf(wsum[k]);
+    }
+  } else {  // one unit per wave (units <= 8): the parts of a sequence are waves t*WPR .. t*WPR + WPR-1
+    if (uok[0]) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xs[wave][lane][e] = acc[0][e];
+      if (lane == 0) {
+        xm[wave] = mx[0];
+        xw[wave] = wsum[0];
+      }
+    }
+    __syncthreads();
+    if (uok[0] && part == 0) {
+      float mt = -INFINITY;
+      for (int p = 0; p < WPR; ++p) mt = fmaxf(mt, xm[wave + p]);
+      float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      float wt = 0.f;
+      if (mt != -INFINITY) {
+        for (int p = 0; p < WPR; ++p) {
+          if (xm[wave + p] == -INFINITY) continue;  // a part with only empty splits
+          const float c = __expf(xm[wave + p] - mt);
+          wt += c * xw[wave + p];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] = fmaf(c, xs[wave + p][lane][e], o[e]);
+        }
+        const float inv = 1.f / wt;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] *= inv;
+      }
+      cuv_put_row(ot, trow[0], lane, o);
+      if (lse_out != nullptr && lane == 0) lse_out[(int64_t)(b0 + trow[0]) * H + h] = mt + __logf(wt);
+    }
+  }
+}
+
+template <int NH>
+__global__ __launch_bounds__(kCuvWaves * 64) void combine_up_v_bf16_kernel(
+    const u16* __restrict__ o_part, const float* __restrict__ lse_part, int num_splits,
+    const u16* __restrict__ w_uv, int B, int H, int DV, float* __restrict__ out, float* __restrict__ lse_out) {
+  using M = Mma<u16>;
+  constexpr int R = 512, WROW = R * 2, DB = 32 * NH;
+  __shared__ __attribute__((aligned(16))) char wt[DB * WROW];             // weight rows d0 .. d0+DB-1
+  __shared__ __attribute__((aligned(16))) char ot[kCuvRows * 2 * WROW];   // merged rows (hi | lo)
+  __shared__ float xs[kCuvWaves][64][8];                                   // unit sums of shared sequences
+  __shared__ float xm[kCuvWaves], xw[kCuvWaves];                           // their maxima and weight sums
+  static_assert(kCuvWaves * 4 * 64 * 16 <= kCuvRows * 2 * WROW, "the reduction fits in the merged rows' bytes");
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hf = lane >> 5, l32 = lane & 31;
+  const int nblk = DV / DB;
+  int h, d0;
+  {
+    const int bid = (int)blockIdx.x;
+    const int grp = bid / (kXcds * nblk);
+    const int rem = bid - grp * (kXcds * nblk);
+    h = grp * kXcds + rem % kXcds;
+    d0 = (rem / kXcds) * DB;
+  }
+  if (h >= H) return;
+  // weight row n (1 KB) into LDS: chunk l of the row at slot l ^ (n & 15)
+  {
+    const char* wbase = (const char*)(w_uv + ((int64_t)h * DV + d0) * R);
+#pragma unroll
+    for (int i = 0; i < DB / kCuvWaves; ++i) {
+      const int n = wave + kCuvWaves * i;
+      __builtin_amdgcn_global_load_lds(wbase + (int64_t)n * WROW + 16 * (lane ^ (n & 15)),
+                                       (LDS_AS char*)wt + n * WROW, 16, 0, 0);
+    }
+  }
+  float* lse_w = d0 == 0 ? lse_out : nullptr;
+  const int dh = wave >> 2, jq = wave & 3;
+  for (int b0 = 0; b0 < B; b0 += kCuvRows) {
+    const int nb = min(kCuvRows, B - b0);
+    // waves per sequence: the largest power of two with nb * WPR <= 8 (1 from 5 rows up)
+    const int WPR = nb >= 5 ? 1 : (nb >= 3 ? 2 : (nb == 2 ? 4 : 8));
+    const int upw = (nb * WPR + kCuvWaves - 1) / kCuvWaves;
+    if (upw == 1) {
+      cuv_merge<1, 32>(o_part, lse_part, num_splits, H, h, b0, nb, WPR, wave, lane, ot, xs, xm, xw, lse_w);
+    } else if (upw == 2) {
+      cuv_merge<2, 16>(o_part, lse_part, num_splits, H, h, b0, nb, WPR, wave, lane, ot, xs, xm, xw, lse_w);
+    } else {
+      cuv_merge<4, 8>(o_part, lse_part, num_splits, H, h, b0, nb, WPR, wave, lane, ot, xs, xm, xw, lse_w);
+    }
+    __syncthreads();  // merged rows written (and, the first time, the weight DMA landed)
+    f32x16 acc = zero16();
+    if (dh < NH) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int ch = 16 * jq + 2 * u + hf;  // 16-byte chunk: k = 128*jq + 16*u + 8*hf .. +7
+        const int sl = 16 * (ch ^ (l32 & 15));
+        const i16x8 a = *(const LDS_AS i16x8*)((LDS_AS char*)wt + (32 * dh + l32) * WROW + sl);
+        const i16x8 bh = *(const LDS_AS i16x8*)((LDS_AS char*)ot + l32 * 2 * WROW + sl);
+        const i16x8 bl = *(const LDS_AS i16x8*)((LDS_AS char*)ot + l32 * 2 * WROW + WROW + sl);
+        acc = M::mma(a, bh, acc);
+        acc = M::mma(a, bl, acc);
+      }
+    }
+    __syncthreads();  // every wave has read the merged rows: their bytes take the partial tiles
+    LDS_AS f32x4* red = (LDS_AS f32x4*)(LDS_AS char*)ot;  // [wave][row quarter][lane]
+    if (dh < NH) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        red[(wave * 4 + q) * 64 + lane] = f32x4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+    }
+    __syncthreads();
+    if (dh < NH && l32 < nb) {
+      const int q = wave & 3;  // rows 8q + 4hf .. +3 of the 32-row half dh
+      const f32x4 sum = red[((4 * dh + 0) * 4 + q) * 64 + lane] + red[((4 * dh + 1) * 4 + q) * 64 + lane] +
+                        red[((4 * dh + 2) * 4 + q) * 64 + lane] + red[((4 * dh + 3) * 4 + q) * 64 + lane];
+      *(f32x4*)(out + ((int64_t)(b0 + l32) * H + h) * DV + d0 + 32 * dh + 8 * q + 4 * hf) = sum;
+    }
+    __syncthreads();  // the next chunk rewrites these bytes
+  }
+}
+
+__global__ __launch_bounds__(64) void combine_up_v_f32_kernel(const float* __restrict__ o_part,
+                                                              const float* __restrict__ lse_part, int S,
+                                                              const float* __restrict__ w_uv, int H, int DV, int R,
+                                                              float* __restrict__ out, float* __restrict__ lse_out) {
+  __shared__ float orow[kCuvMaxRankF32];
+  const int lane = threadIdx.x & 63;
+  const int b = (int)blockIdx.x / H, h = (int)blockIdx.x - b * H;
+  const int64_t base = (int64_t)b * S * H + h;
+  float mx, wsum;
+  lse_stats(lse_part + base, S, H, lane, mx, wsum);
+  const float sc = 1.f / wsum;
+  for (int c = lane; c < R; c += 64) {
+    float acc = 0.f;
+    for (int s = 0; s < S; ++s) {
+      const float l = lse_part[base + (int64_t)s * H];
+      if (l == -INFINITY) continue;  // an empty split never wrote its partial
+      acc = fmaf(__expf(l - mx) * sc, o_part[(base + (int64_t)s * H) * R + c], acc);
+    }
+    orow[c] = acc;
+  }
+  __syncthreads();
+  for (int d = lane; d < DV; d += 64) {
+    const float* wr = w_uv + ((int64_t)h * DV + d) * R;
+    float acc = 0.f;
+    for (int j = 0; j < R; ++j) acc = fmaf(wr[j], orow[j], acc);
+    out[((int64_t)b * H + h) * DV + d] = acc;
+  }
+  if (lse_out != nullptr && lane == 0) lse_out[(int64_t)b * H + h] = mx + __logf(wsum);
+}
+
+// ---------------------------------------------------------------------------
 // K2: RoPE on q_rope and on the new token's shared key; append the new row.
 // One work-group per (sequence, block of 16 heads); the work-group of head
 // block 0 also writes the cache row.  Pair frequencies come from the host (in
@@ -1616,11 +1946,10 @@ mla_status mla_combine(const mla_dims* dims, const void* o_part, const float* ls
   // split groups: about eight splits per thread, 1 to 16 groups
   int groups = 1;
   while (groups < kCombineMaxGroups && groups * 8 < num_splits) groups *= 2;
-  const int64_t pairs = (int64_t)(dims->rank / 4) * dims->heads / 2;  // quad pairs per split
-  const int tq = (int)std::min<int64_t>(kCombineThreads / groups, pairs);
-  if (dims->heads % 2 != 0 || pairs % tq != 0)
-    return fail(MLA_ERR_UNSUPPORTED, "heads must be even and rank/8 * heads a power-of-two multiple");
-  const dim3 grid((unsigned)(dims->batch * (pairs / tq)));
+  const int64_t octs = (int64_t)(dims->rank / 8) * dims->heads;  // octets per split
+  const int tq = (int)std::min<int64_t>(kCombineThreads / groups, octs);
+  if (octs % tq != 0) return fail(MLA_ERR_UNSUPPORTED, "rank/8 * heads must be a multiple of the thread count");
+  const dim3 grid((unsigned)(dims->batch * (octs / tq)));
   const dim3 block((unsigned)(tq * groups));
   // partials are stored in the dtype of the cache (see the decode kernel)
   if (dims->dtype == MLA_BF16 && dims->rank == 512) {
@@ -1653,6 +1982,37 @@ mla_status mla_up_v(const mla_dims* dims, const float* o_lat, const void* w_uv, 
   return launch_result("mla_up_v");
 }
 
+mla_status mla_combine_up_v(const mla_dims* dims, const void* o_part, const float* lse_part, int32_t num_splits,
+                            const void* w_uv, float* out, float* lse, void* stream) {
+  mla_status st = check_dims_impl(dims);
+  if (st != MLA_OK) return st;
+  if ((st = check_ptrs({o_part, lse_part, w_uv, out})) != MLA_OK) return st;
+  if (num_splits < 1) return fail(MLA_ERR_INVALID_ARG, "num_splits must be >= 1");
+  if (num_splits > kMaxSplits) return fail(MLA_ERR_WORKSPACE, "num_splits above 4096");
+  g_last_error.clear();
+  hipStream_t s = (hipStream_t)stream;
+  if (dims->dtype == MLA_BF16) {
+    if (dims->rank != 512) return fail(MLA_ERR_UNSUPPORTED, "bf16 combine_up_v is built for rank 512");
+    if ((int64_t)num_splits * dims->heads * dims->rank * 2 >= ((int64_t)1 << 31))
+      return fail(MLA_ERR_UNSUPPORTED, "one sequence's partials must stay under 2 GB");
+    const int nh = dims->d_v % 64 == 0 ? 2 : 1;
+    const int blocks = (dims->heads + kXcds - 1) / kXcds * kXcds * (dims->d_v / (32 * nh));  // whole groups of 8 heads
+    if (nh == 2) {
+      hipLaunchKernelGGL((combine_up_v_bf16_kernel<2>), dim3(blocks), dim3(kCuvWaves * 64), 0, s, (const u16*)o_part,
+                         lse_part, num_splits, (const u16*)w_uv, dims->batch, dims->heads, dims->d_v, out, lse);
+    } else {
+      hipLaunchKernelGGL((combine_up_v_bf16_kernel<1>), dim3(blocks), dim3(kCuvWaves * 64), 0, s, (const u16*)o_part,
+                         lse_part, num_splits, (const u16*)w_uv, dims->batch, dims->heads, dims->d_v, out, lse);
+    }
+  } else {
+    if (dims->rank > kCuvMaxRankF32) return fail(MLA_ERR_UNSUPPORTED, "fp32 combine_up_v takes rank <= 256");
+    hipLaunchKernelGGL(combine_up_v_f32_kernel, dim3(dims->batch * dims->heads), dim3(64), 0, s,
+                       (const float*)o_part, lse_part, num_splits, (const float*)w_uv, dims->heads, dims->d_v,
+                       dims->rank, out, lse);
+  }
+  return launch_result("mla_combine_up_v");
+}
+
 mla_status mla_partials_size(const mla_dims* dims, int32_t num_splits, size_t* o_part_bytes, size_t* lse_part_bytes) {
   mla_status st = check_dims_impl(dims);
   if (st != MLA_OK) return st;
@@ -1674,16 +2034,18 @@ int32_t mla_plan_splits(const mla_dims* dims, int32_t max_seq_len, int64_t total
     if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess) return 0;
     num_cus = prop.multiProcessorCount;
   }
-  // Pick the split count with the smallest estimated decode time.  A split is
+  // Pick the split count with the smallest estimated step time.  A split is
   // one work-group and a compute unit runs one at a time, dealt evenly over
-  // the 8 XCDs, so the time is (rounds of work-groups per CU) x (tiles per
-  // split + a fixed per-split cost for the prologue and the partial's store,
-  // about kSplitCost tiles).  Only the total and the longest length are known
-  // here: the non-empty splits are at most B * ceil(max / chunk), and for
-  // mixed lengths about total / chunk plus the partial last split of every
-  // sequence (counted as 0.6 of a split each, a little above the mean).
-  // Ties go to fewer splits (less partial traffic for the combine).
-  constexpr int64_t kSplitCost = 8;
+  // the 8 XCDs, so the decode time is (rounds of work-groups per CU) x (tiles
+  // per split + a fixed per-split cost for the prologue and the partial's
+  // store, about kSplitCost tiles).  Every non-empty split also adds its
+  // partial to what all work-groups start by loading at once and to what the
+  // merge reads back: about kItemCost tiles per CU's worth of splits.  Only
+  // the total and the longest length are known here: the non-empty splits are
+  // at most B * ceil(max / chunk), and for mixed lengths about total / chunk
+  // plus the partial last split of every sequence (counted as 0.6 of a split
+  // each, a little above the mean).  Ties go to fewer splits.
+  constexpr int64_t kSplitCost = 8, kItemCost = 12;
   const int64_t B = dims->batch, cus_per_xcd = std::max<int64_t>(1, num_cus / 8);
   const int64_t s_max = std::min<int64_t>(kMaxSplits, ((int64_t)max_seq_len + 31) / 32);
   int64_t best = 1, best_cost = INT64_MAX;
@@ -1693,7 +2055,8 @@ int32_t mla_plan_splits(const mla_dims* dims, int32_t max_seq_len, int64_t total
     const int64_t est = std::min(full, (total_rows + chunk - 1) / chunk + (6 * B + 9) / 10);
     const int64_t per_xcd = (est + 7) / 8;
     const int64_t rounds = (per_xcd + cus_per_xcd - 1) / cus_per_xcd;
-    const int64_t cost = rounds * (chunk / 32 + kSplitCost);
+    // in units of tiles / num_cus
+    const int64_t cost = rounds * (chunk / 32 + kSplitCost) * num_cus + kItemCost * est;
     if (cost < best_cost) best_cost = cost, best = sp;
   }
   const int64_t splits = best;

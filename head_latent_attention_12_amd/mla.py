@@ -21,7 +21,7 @@ STATUS = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARG", 2: "MLA_ERR_UNSUPPORTED", 3: "M
           4: "MLA_ERR_WORKSPACE", 5: "MLA_ERR_HIP"}
 
 EXPORTS = ("mla_absorb_q", "mla_rope_append", "mla_decode_latent", "mla_combine", "mla_up_v",
-           "mla_partials_size", "mla_plan_splits", "mla_check_dims", "mla_status_string", "mla_last_error")
+           "mla_combine_up_v", "mla_partials_size", "mla_plan_splits", "mla_check_dims", "mla_status_string", "mla_last_error")
 
 
 class MlaDims(ctypes.Structure):
@@ -55,6 +55,7 @@ def lib() -> ctypes.CDLL:
             "mla_decode_latent": (i32, [D, P, P, P, P, i64, i32, i32, P, P, P]),
             "mla_combine": (i32, [D, P, P, i32, P, P, P]),
             "mla_up_v": (i32, [D, P, P, P, P]),
+            "mla_combine_up_v": (i32, [D, P, P, i32, P, P, P, P]),
             "mla_partials_size": (i32, [D, i32, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]),
             "mla_plan_splits": (i32, [D, i32, i64, i32]),
             "mla_check_dims": (i32, [D]),
@@ -121,6 +122,11 @@ def mla_combine(dims, o_part, lse_part, num_splits, o_lat, lse=None, stream=None
 
 def mla_up_v(dims, o_lat, w_uv, out, stream=None):
     _check("mla_up_v", lib().mla_up_v(ctypes.byref(dims), _p(o_lat), _p(w_uv), _p(out), _s(stream)))
+
+
+def mla_combine_up_v(dims, o_part, lse_part, num_splits, w_uv, out, lse=None, stream=None):
+    _check("mla_combine_up_v", lib().mla_combine_up_v(ctypes.byref(dims), _p(o_part), _p(lse_part),
+                                                      int(num_splits), _p(w_uv), _p(out), _p(lse), _s(stream)))
 
 
 def mla_partials_size(dims, num_splits):

@@ -1,4 +1,4 @@
-"""One decode step on the GPU: upload seeded inputs, run the five C-ABI calls.
+"""One decode step on the GPU: upload seeded inputs, run the C-ABI calls.
 
 Marshalling only: buffers are torch tensors (device memory), every step of
 the computation runs in libmla.so.
@@ -27,7 +27,9 @@ def bits_to_f64(t: torch.Tensor, dtype: str) -> np.ndarray:
 
 
 class DeviceStep:
-    """Device buffers of one step and the five calls that compute it."""
+    """Device buffers of one step and the calls that compute it: absorb_q,
+    rope_append, decode_latent, then combine and up_v, which ``run`` issues as
+    the one fused call combine_up_v (the separate calls stay available)."""
 
     def __init__(self, inp: StepInputs, num_splits: int | None = None, device: str = "cuda:0",
                  weights: "DeviceStep | None" = None, scratch: "DeviceStep | None" = None):
@@ -73,7 +75,7 @@ class DeviceStep:
         self.o_part = torch.empty((o_bytes // 4,), dtype=torch.int32, device=self.device)  # raw partials buffer
         self.lse_part = torch.empty((inp.B, self.num_splits, inp.H), dtype=torch.float32, device=self.device)
 
-    # the five calls -------------------------------------------------------
+    # the calls ----------------------------------------------------------------
     def absorb_q(self, stream=None):
         mla.mla_absorb_q(self.dims, self.q_nope, self.w_uk, self.q_lat, stream)
 
@@ -92,15 +94,19 @@ class DeviceStep:
     def up_v(self, stream=None):
         mla.mla_up_v(self.dims, self.o_lat, self.w_uv, self.out, stream)
 
+    def combine_up_v(self, stream=None):
+        mla.mla_combine_up_v(self.dims, self.o_part, self.lse_part, self.num_splits, self.w_uv, self.out,
+                             self.lse, stream)
+
     def run(self, stream=None):
+        """One step: out and lse (o_lat is only written by ``combine``)."""
         self.absorb_q(stream)
         self.rope_append(stream)
         self.decode_latent(stream)
-        self.combine(stream)
-        self.up_v(stream)
+        self.combine_up_v(stream)
 
     def capture(self) -> "torch.cuda.CUDAGraph":
-        """The five calls recorded once as a HIP graph (the library launches
+        """The calls of ``run`` recorded once as a HIP graph (the library launches
         kernels only: no allocation, copy or memset), replayed with
         ``graph.replay()`` on the current stream."""
         graph = torch.cuda.CUDAGraph()

@@ -13,6 +13,8 @@
  *                     sum of the latents, one partial result per split
  *   mla_combine       log-sum-exp merge of the splits into o_lat
  *   mla_up_v          out = W_UV o_lat per head
+ *   mla_combine_up_v  the last two in one call: the merge is formed where
+ *                     W_UV consumes it and o_lat never goes to memory
  *
  * Sources (page title, section):
  *   [P1] "DeepSeek MLA, Built From the Paper": section 1 (the cache holds
@@ -52,14 +54,11 @@
  *                            token's position and its row index in the sequence
  *   row_offsets [B] int64    first cache row of sequence b
  *   seq_lens    [B] int32    rows attended = L_b + 1 (after the append)
- *   o_part   [B][num_splits][r/4][H][4] in the storage dtype (float32 for
- *            MLA_F32, bf16 for MLA_BF16): the split partials with the columns
- *            taken four at a time and the heads interleaved, i.e.
- *            o_part(b, s, h, c) is element
- *            ((b*num_splits + s)*(r/4) + c/4)*H*4 + h*4 + c%4, so that the
- *            heads of one column quad are contiguous (coalesced stores from
- *            the decode kernel, whose lanes hold one head each).  A bf16
- *            partial is the fp32 result rounded once to nearest even.
+ *   o_part   [B][num_splits][H][r] in the storage dtype (float32 for
+ *            MLA_F32, bf16 for MLA_BF16): the partial of split s of
+ *            sequence b for head h is the contiguous row (b*num_splits + s)*H
+ *            + h.  A bf16 partial is the fp32 result rounded once to nearest
+ *            even.
  *   lse_part [B][num_splits][H] float32
  *   o_lat    [B][H][r] float32, lse [B][H] float32, out [B][H][d_v] float32
  *   Sequence b owns cache rows [row_offsets[b], row_offsets[b] + seq_lens[b]).
@@ -163,6 +162,18 @@ mla_status mla_combine(const mla_dims* dims, const void* o_part, const float* ls
  * of two bf16 terms (high and low part), which keeps it exact to ~2^-16. */
 mla_status mla_up_v(const mla_dims* dims, const float* o_lat, const void* w_uv, float* out,
                     void* stream);
+
+/* mla_combine followed by mla_up_v, without o_lat ([P2] absorbing
+ * projections: the weighted sum of the latents, then W_UV):
+ *   out[b][h][d] = sum_j w_uv[h][d][j] * o_lat[b][h][j]
+ * with o_lat[b][h] the merge of the splits defined under mla_combine, and
+ * lse[b][h] as there (lse may be NULL).  The merged row is formed in fp32 and,
+ * with bf16 weights, enters the product as the sum of two bf16 terms (as in
+ * mla_up_v).  A sequence whose splits are all empty gets out = 0 and
+ * lse = -inf. */
+mla_status mla_combine_up_v(const mla_dims* dims, const void* o_part, const float* lse_part,
+                            int32_t num_splits, const void* w_uv, float* out, float* lse,
+                            void* stream);
 
 /* Bytes of o_part and lse_part for `num_splits` splits. */
 mla_status mla_partials_size(const mla_dims* dims, int32_t num_splits, size_t* o_part_bytes,

@@ -88,6 +88,9 @@ def test_entry_points_reject_null_and_misaligned_pointers():
     _expect(1, mla.mla_combine, d, P16, P16, 1, 0, None, 0)
     _expect(1, mla.mla_up_v, d, P16, 0, P16, 0)
     _expect(3, mla.mla_up_v, d, P16, P16, P16 + 12, 0)
+    _expect(1, mla.mla_combine_up_v, d, P16, P16, 1, 0, P16, None, 0)               # w_uv NULL
+    _expect(1, mla.mla_combine_up_v, d, P16, 0, 1, P16, P16, None, 0)               # lse_part NULL
+    _expect(3, mla.mla_combine_up_v, d, P16, P16, 1, P16, P16 + 4, None, 0)
 
 
 def test_split_count_limits():
@@ -97,6 +100,8 @@ def test_split_count_limits():
     _expect(1, mla.mla_decode_latent, d, P16, P16, P16, P16, 10, 0, 1, P16, P16, 0)   # max_seq_len 0
     _expect(1, mla.mla_combine, d, P16, P16, 0, P16, None, 0)
     _expect(4, mla.mla_combine, d, P16, P16, 5000, P16, None, 0)
+    _expect(1, mla.mla_combine_up_v, d, P16, P16, 0, P16, P16, None, 0)
+    _expect(4, mla.mla_combine_up_v, d, P16, P16, 4097, P16, P16, None, 0)
     _expect(4, mla.mla_partials_size, d, 4097)
 
 
@@ -152,7 +157,7 @@ def test_plan_splits_ragged_one_round(seed):
 
 def test_plan_splits_prefers_one_round_over_finer_splits():
     """A uniform batch whose finer split would need two rounds of work-groups
-    stays at the coarser split (B = 16, T = 4097: 15 splits, 240 work items)."""
+    stays at a coarser split (B = 16, T = 4097: at most 256 work items)."""
     d = mla.make_dims(16, 128, 128, 128, 512, 64, mla.MLA_BF16)
     s = mla.mla_plan_splits(d, 4097, 16 * 4097, 256)
     chunk = -(-(-(-4097 // s)) // 32) * 32

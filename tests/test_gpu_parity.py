@@ -86,19 +86,30 @@ def check_step(step_inp, ds, ref, tag=""):
     keep = np.ones(step_inp.total_rows, bool)
     keep[slots] = False
     np.testing.assert_array_equal(cache[keep], step_inp.kv_cache[keep])   # other rows untouched
-    # the latent-space result and its log-sum-exp
+    # out and lse of the step (the fused combine_up_v call), then the separate
+    # combine and up_v calls on the same partials: o_lat, lse and out again
+    out_fused = ds.out.cpu().numpy().astype(np.float64)
+    lse_fused = ds.lse.cpu().numpy().astype(np.float64)
+    ds.out.fill_(float("nan"))
+    ds.lse.fill_(float("nan"))
+    ds.combine()
+    ds.up_v()
+    torch.cuda.synchronize()
     o_lat = ds.o_lat.cpu().numpy().astype(np.float64)
     lse = ds.lse.cpu().numpy().astype(np.float64)
     if step_inp.dtype == syn.F32:
         assert normwise_rel(o_lat, ref["o_lat"]) <= 1e-5, tag
-        np.testing.assert_allclose(lse, ref["lse"], rtol=0, atol=1e-5 * max(1.0, np.abs(ref["lse"]).max()))
+        for l in (lse, lse_fused):
+            np.testing.assert_allclose(l, ref["lse"], rtol=0, atol=1e-5 * max(1.0, np.abs(ref["lse"]).max()))
     else:
         o_err = np.abs(o_lat - ref["o_lat"])
         o_scale = np.abs(ref["o_lat"]).max()
         print(f"[{tag}] o_lat max abs {o_err.max():.3e} mean abs {o_err.mean():.3e} (scale {o_scale:.3f})", flush=True)
         assert o_err.max() <= BF16_TIGHT_MAX_REL * o_scale and o_err.mean() <= BF16_TIGHT_MEAN_REL * o_scale, tag
-        np.testing.assert_allclose(lse, ref["lse"], rtol=0, atol=2e-2)
-    check_out(step_inp, ds.out.cpu().numpy().astype(np.float64), ref["out"], tag)
+        for l in (lse, lse_fused):
+            np.testing.assert_allclose(l, ref["lse"], rtol=0, atol=2e-2)
+    check_out(step_inp, out_fused, ref["out"], tag + " combine_up_v")
+    check_out(step_inp, ds.out.cpu().numpy().astype(np.float64), ref["out"], tag + " combine, up_v")
 
 
 # ---------------------------------------------------------------------------
@@ -152,6 +163,19 @@ def test_edge_lengths(name, lens):
     inp = syn.make_inputs(name, lens=lens)
     ds = _run(inp)
     check_step(inp, ds, oracle_step(inp), tag=f"{name} lens={lens[:8]}")
+
+
+@pytest.mark.parametrize("B", [1, 2, 3, 4, 5, 6, 7, 8, 9, 31, 32, 33, 40, 64, 65])
+@pytest.mark.parametrize("splits", [1, 3, 40])
+def test_combine_up_v_batch_shapes(B, splits):
+    """The fused merge + W_UV call over the batch sizes where its work layout
+    changes (waves per sequence 8, 4, 2, 1; up to four sequences per wave;
+    chunks of 32 sequences with a short last chunk) and split counts from
+    one to more than one load batch, against the oracle and against the
+    separate combine and up_v calls on the same partials."""
+    inp = syn.make_inputs("dsv2", B=B, T=(1, 400))
+    ds = _run(inp, num_splits=splits)
+    check_step(inp, ds, oracle_step(inp), tag=f"dsv2 B={B} splits={splits}")
 
 
 @pytest.mark.parametrize("name,override", [("small", {}), ("dsv2", dict(B=3, T=1000)),
@@ -226,11 +250,11 @@ def test_graph_replay_matches_eager(name, override):
     synchronisation between replays, reproduces the eager result bit for bit."""
     inp = syn.make_inputs(name, **override)
     ds = _run(inp)
-    eager = {k: getattr(ds, k).clone() for k in ("out", "o_lat", "lse", "q_lat", "kv_cache")}
+    eager = {k: getattr(ds, k).clone() for k in ("out", "lse", "q_lat", "kv_cache")}
     graph = ds.capture()
     torch.cuda.synchronize()
     for rep in range(3):
-        for k in ("out", "o_lat", "lse"):
+        for k in ("out", "lse"):
             getattr(ds, k).fill_(float("nan"))  # eager work on the buffers the graph writes
         junk = torch.randn(1 << 20, device=ds.out.device).sum()
         torch.cuda.synchronize()
@@ -279,9 +303,9 @@ def test_split_partials(name, lens, splits):
         bits = raw.view(np.uint32)
         parts = bits.view(np.float32).astype(np.float64)
         sentinel = np.uint32(0x5A5A5A5A)
-    # element (b, s, h, c) at ((b*S + s)*(r/4) + c/4)*H*4 + h*4 + c%4
-    parts = parts.reshape(B, S, r // 4, H, 4).transpose(0, 1, 3, 2, 4).reshape(B, S, H, r)
-    bits = bits.reshape(B, S, r // 4, H, 4).transpose(0, 1, 3, 2, 4).reshape(B, S, H, r)
+    # element (b, s, h, c) at ((b*S + s)*H + h)*r + c
+    parts = parts.reshape(B, S, H, r)
+    bits = bits.reshape(B, S, H, r)
     tol_o = 1e-2 if inp.dtype == syn.BF16 else 1e-5
     tol_l = 2e-2 if inp.dtype == syn.BF16 else 1e-5
     checked = 0

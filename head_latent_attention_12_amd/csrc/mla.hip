@@ -1084,30 +1084,65 @@ __global__ __launch_bounds__(NW * 64) void absorb_q_kernel(const T* __restrict__
   }
 }
 
+constexpr int kMaxRopePairs = 32;  // d_rope <= 64
+struct RopeFreqs {
+  double theta[kMaxRopePairs];  // theta_i = base^(-2i/d_rope), i < d_rope/2
+};
+
+__device__ __forceinline__ void sincos_reduced(double ang, double* s, double* c) {
+  // 2*pi = P1 + P2 (P1 the double nearest 2*pi); fma keeps each k*Pn exact
+  // inside its subtraction, so |r| <= pi with an error of a few 1e-16
+  constexpr double kInv2Pi = 0.15915494309189533577;
+  constexpr double P1 = 6.28318530717958623200e+00;
+  constexpr double P2 = 2.44929359829470635445e-16;
+  const double k = rint(ang * kInv2Pi);
+  double r = fma(-k, P1, ang);
+  r = fma(-k, P2, r);
+  sincos(r, s, c);
+}
+
+// RoPE work that the fused bf16 launch hands to the absorption blocks
+struct RopeArgs {
+  const u16* q_rope;
+  const u16* c_kv_new;
+  const u16* k_rope_new;
+  const int32_t* positions;
+  const int64_t* row_offsets;
+  int64_t total_rows;
+  int DR;
+  u16* cache;
+};
+
+// RoPE of pair i of a bf16 pair (x0, x1) at position pos, rounded once
+__device__ __forceinline__ uint32_t rope_pair_bf16(uint32_t x, int pos, double theta) {
+  double sn, cn;
+  sincos_reduced((double)pos * theta, &sn, &cn);
+  const double x0 = (double)bf2f((u16)(x & 0xffffu)), x1 = (double)bf2f((u16)(x >> 16));
+  return (uint32_t)d2bf(x0 * cn - x1 * sn) | ((uint32_t)d2bf(x0 * sn + x1 * cn) << 16);
+}
+
 // bf16: the weight tile and the queries of 64 sequences at a time are copied
 // into LDS by DMA (1 KB per wave instruction, no register staging), all issued
 // before the one wait, so a work-group pays a single HBM round trip up front.
 // Query rows are stored with their 16-byte chunks XOR-swizzled by row, which
 // makes the fragment reads (lane = sequence) conflict-free.
-template <int DH>
-__global__ __launch_bounds__(128) void absorb_q_bf16_kernel(const u16* __restrict__ q_nope,
-                                                            const u16* __restrict__ w_uk, int B, int H, int R,
-                                                            u16* __restrict__ q_lat, int W) {
+template <int DH, bool ROPE>
+__device__ __forceinline__ void absorb_bf16_block(int bid, const u16* __restrict__ q_nope,
+                                                  const u16* __restrict__ w_uk, int B, int H, int R,
+                                                  u16* __restrict__ q_lat, int W, char* wt, char* qs,
+                                                  const RopeArgs& ra, const RopeFreqs& freqs) {
   using M = Mma<u16>;
   constexpr int COLS = 64, ROWB = 2 * COLS, NCH = ROWB / 16, KS = DH / M::KSTEP;
   constexpr int QROWS = 64, QROWB = 2 * DH, QCH = QROWB / 16;
   constexpr int WCOP = DH * ROWB / 1024 / 2;      // weight DMA copies per wave
   constexpr int QCOP = QROWS * QROWB / 1024 / 2;  // query DMA copies per wave
   static_assert(WCOP >= 1 && QCOP >= 1 && (QCH & (QCH - 1)) == 0, "shape");
-  __shared__ __attribute__((aligned(1024))) char wt[DH * ROWB];
-  __shared__ __attribute__((aligned(1024))) char qs[QROWS * QROWB];
 
   const int nblk = R / COLS;
   // the nblk column blocks of a head run on one XCD (its L2 then serves the
   // head's queries to all of them); the grid covers whole groups of 8 heads
   int h, blk;
   {
-    const int bid = (int)blockIdx.x;
     const int grp = bid / (kXcds * nblk);
     const int rem = bid - grp * (kXcds * nblk);
     h = grp * kXcds + rem % kXcds;
@@ -1119,6 +1154,39 @@ __global__ __launch_bounds__(128) void absorb_q_bf16_kernel(const u16* __restric
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hf = lane >> 5, l32 = lane & 31;
 
+  // RoPE (fused launch): block (h, blk) rotates head h's query pairs of the
+  // sequences b = blk (mod nblk), and block h*nblk + blk appends the cache row
+  // of sequence h*nblk + blk (mod H*nblk).  The first UQ pairs per thread and
+  // the first appended row are loaded before the DMA below is issued (so they
+  // land while it is in flight) and computed after the wait for it.
+  constexpr int UQ = 2, CVA = 2;  // pairs per thread; c_kv_new quads per thread (R <= 1024)
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const int half = ROPE ? ra.DR / 2 : 1;
+  const int tid = (int)threadIdx.x;
+  const int nq = blk < B ? (B - blk + nblk - 1) / nblk * half : 0;  // this block's query pairs
+  const int ab0 = h * nblk + blk;                                   // first sequence whose row it appends
+  uint32_t qx[UQ], kx = 0;
+  int qpos[UQ], apos = 0;
+  double qth[UQ], ath = 0.0;
+  int64_t aoff = 0;
+  u32x2 cvv[CVA];
+  if constexpr (ROPE) {
+#pragma unroll
+    for (int u = 0; u < UQ; ++u) {
+      const int pidx = min(tid + 128 * u, max(nq - 1, 0));
+      const int bb = min(blk + nblk * (pidx / half), B - 1), i = pidx % half;
+      qx[u] = *(const uint32_t*)(ra.q_rope + ((int64_t)bb * H + h) * ra.DR + 2 * i);
+      qpos[u] = ra.positions[bb];
+      qth[u] = freqs.theta[i];
+    }
+    const int ab = min(ab0, B - 1), ti = min(tid, half - 1);
+    apos = ra.positions[ab];
+    aoff = ra.row_offsets[ab];
+    kx = *(const uint32_t*)(ra.k_rope_new + (int64_t)ab * ra.DR + 2 * ti);
+    ath = freqs.theta[ti];
+#pragma unroll
+    for (int u = 0; u < CVA; ++u) cvv[u] = *(const u32x2*)(ra.c_kv_new + (int64_t)ab * R + min(4 * (tid + 128 * u), R - 4));
+  }
   // LDS chunk p of the query block holds row p / QCH, chunk (p % QCH) ^ (row % QCH)
   auto issue_q = [&](int b0) {
 #pragma unroll
@@ -1142,6 +1210,40 @@ __global__ __launch_bounds__(128) void absorb_q_bf16_kernel(const u16* __restric
     __builtin_amdgcn_global_load_lds(src, (LDS_AS char*)wt + (wave * WCOP + n) * 1024, 16, 0, 0);
   }
   __syncthreads();  // (waits for this work-group's DMA)
+  if constexpr (ROPE) {
+    const int W2 = R + ra.DR;
+    auto qstore = [&](int pidx, uint32_t x, int pos, double th) {
+      const int bb = blk + nblk * (pidx / half), i = pidx % half;
+      *(uint32_t*)(q_lat + ((int64_t)bb * H + h) * W2 + R + 2 * i) = rope_pair_bf16(x, pos, th);
+    };
+#pragma unroll
+    for (int u = 0; u < UQ; ++u)
+      if (tid + 128 * u < nq) qstore(tid + 128 * u, qx[u], qpos[u], qth[u]);
+    for (int pidx = tid + 128 * UQ; pidx < nq; pidx += 128) {  // beyond UQ*128 pairs (B > 8*UQ*128/d_rope)
+      const int bb = blk + nblk * (pidx / half), i = pidx % half;
+      qstore(pidx, *(const uint32_t*)(ra.q_rope + ((int64_t)bb * H + h) * ra.DR + 2 * i), ra.positions[bb],
+             freqs.theta[i]);
+    }
+    // the appended rows: [c_kv_new | RoPE(k_rope_new)] (c_kv_new bit for bit)
+    auto append = [&](int bb, int pos, int64_t off, const u32x2 (&cv)[CVA], uint32_t k, double th) {
+      int64_t row = off + pos;
+      row = row < 0 ? 0 : (row >= ra.total_rows ? ra.total_rows - 1 : row);
+      u16* crow = ra.cache + row * W2;
+#pragma unroll
+      for (int u = 0; u < CVA; ++u)
+        if (4 * (tid + 128 * u) < R) *(u32x2*)(crow + 4 * (tid + 128 * u)) = cv[u];
+      if (tid < half) *(uint32_t*)(crow + R + 2 * tid) = rope_pair_bf16(k, pos, th);
+    };
+    if (ab0 < B) append(ab0, apos, aoff, cvv, kx, ath);
+    for (int bb = ab0 + H * nblk; bb < B; bb += H * nblk) {  // more than H*nblk sequences
+      const int ti = min(tid, half - 1);
+      u32x2 cv[CVA];
+#pragma unroll
+      for (int u = 0; u < CVA; ++u) cv[u] = *(const u32x2*)(ra.c_kv_new + (int64_t)bb * R + min(4 * (tid + 128 * u), R - 4));
+      append(bb, ra.positions[bb], ra.row_offsets[bb], cv, *(const uint32_t*)(ra.k_rope_new + (int64_t)bb * ra.DR + 2 * ti),
+             freqs.theta[ti]);
+    }
+  }
 
   typename M::Frag af[KS];
 #pragma unroll
@@ -1177,6 +1279,20 @@ __global__ __launch_bounds__(128) void absorb_q_bf16_kernel(const u16* __restric
       }
     }
   }
+}
+
+// LDS of one absorption block: the weight tile and 64 query rows
+template <int DH> struct AbsorbLds {
+  static constexpr int WT = DH * 128, QS = 64 * 2 * DH;
+};
+
+template <int DH>
+__global__ __launch_bounds__(128) void absorb_q_bf16_kernel(const u16* __restrict__ q_nope,
+                                                            const u16* __restrict__ w_uk, int B, int H, int R,
+                                                            u16* __restrict__ q_lat, int W) {
+  __shared__ __attribute__((aligned(1024))) char wt[AbsorbLds<DH>::WT];
+  __shared__ __attribute__((aligned(1024))) char qs[AbsorbLds<DH>::QS];
+  absorb_bf16_block<DH, false>((int)blockIdx.x, q_nope, w_uk, B, H, R, q_lat, W, wt, qs, RopeArgs{}, RopeFreqs{});
 }
 
 // ---------------------------------------------------------------------------
@@ -1633,47 +1749,28 @@ __global__ __launch_bounds__(64) void combine_up_v_f32_kernel(const float* __res
 
 // ---------------------------------------------------------------------------
 // K2: RoPE on q_rope and on the new token's shared key; append the new row.
-// One work-group per (sequence, block of 16 heads); the work-group of head
-// block 0 also writes the cache row.  Pair frequencies come from the host (in
+// One work-group per (sequence, block of HB heads: 16 in this kernel); the
+// work-group of head block 0 also writes the cache row.  Pair frequencies come from the host (in
 // double); each angle pos * theta_i is reduced modulo 2*pi in double (two-
 // part constant) before sincos, and rotations and the final rounding are done
 // in double precision.
 // ---------------------------------------------------------------------------
 
-constexpr int kMaxRopePairs = 32;  // d_rope <= 64
-struct RopeFreqs {
-  double theta[kMaxRopePairs];  // theta_i = base^(-2i/d_rope), i < d_rope/2
-};
-
-__device__ __forceinline__ void sincos_reduced(double ang, double* s, double* c) {
-  // 2*pi = P1 + P2 (P1 the double nearest 2*pi); fma keeps each k*Pn exact
-  // inside its subtraction, so |r| <= pi with an error of a few 1e-16
-  constexpr double kInv2Pi = 0.15915494309189533577;
-  constexpr double P1 = 6.28318530717958623200e+00;
-  constexpr double P2 = 2.44929359829470635445e-16;
-  const double k = rint(ang * kInv2Pi);
-  double r = fma(-k, P1, ang);
-  r = fma(-k, P2, r);
-  sincos(r, s, c);
-}
-
-template <typename T>
-__global__ __launch_bounds__(256) void rope_append_kernel(const T* __restrict__ q_rope, const T* __restrict__ c_kv_new,
-                                                          const T* __restrict__ k_rope_new,
-                                                          const int32_t* __restrict__ positions,
-                                                          const int64_t* __restrict__ row_offsets, int64_t total_rows,
-                                                          int H, int R, int DR, RopeFreqs freqs,
-                                                          T* __restrict__ q_lat, T* __restrict__ cache) {
-  constexpr int QP = 2;  // q_rope pairs per thread (16 heads x d_rope/2 <= 256 * QP)
-  constexpr int CV = 4;  // c_kv_new values per thread (R <= 1024)
+template <typename T, int NT, int HB>
+__device__ __forceinline__ void rope_block(int blk, const T* __restrict__ q_rope, const T* __restrict__ c_kv_new,
+                                           const T* __restrict__ k_rope_new, const int32_t* __restrict__ positions,
+                                           const int64_t* __restrict__ row_offsets, int64_t total_rows, int H, int R,
+                                           int DR, const RopeFreqs& freqs, T* __restrict__ q_lat,
+                                           T* __restrict__ cache, double* cs /* LDS, 2 * kMaxRopePairs */) {
+  constexpr int QP = HB * kMaxRopePairs / NT;  // q_rope pairs per thread (HB heads x d_rope/2)
+  constexpr int CV = 1024 / NT;                // c_kv_new values per thread (R <= 1024)
   typedef T T2 __attribute__((ext_vector_type(2)));
-  __shared__ double cs[2][kMaxRopePairs];
-  const int hblocks = (H + 15) / 16;
-  const int b = blockIdx.x / hblocks;
-  const int hb = blockIdx.x - b * hblocks;
+  const int hblocks = (H + HB - 1) / HB;
+  const int b = blk / hblocks;
+  const int hb = blk - b * hblocks;
   const int half = DR / 2;
   const int W = R + DR;
-  const int h0 = hb * 16, h1 = min(H, h0 + 16);
+  const int h0 = hb * HB, h1 = min(H, h0 + HB);
   const int npairs = (h1 - h0) * half;
   const int tid = (int)threadIdx.x;
   const bool row_block = hb == 0;
@@ -1687,25 +1784,25 @@ __global__ __launch_bounds__(256) void rope_append_kernel(const T* __restrict__ 
   T2 qx[QP];
 #pragma unroll
   for (int u = 0; u < QP; ++u) {
-    const int idx = tid + u * (int)blockDim.x;
+    const int idx = tid + u * NT;
     const int hh = h0 + idx / half, i = idx % half;
     qx[u] = *(const T2*)(q_rope + ((int64_t)b * H + (idx < npairs ? hh : h0)) * DR + 2 * i);
   }
   const T2 kx = *(const T2*)(k_rope_new + (int64_t)b * DR + 2 * ti);
   T cv[CV];
 #pragma unroll
-  for (int u = 0; u < CV; ++u) cv[u] = c_kv_new[(int64_t)b * R + min(tid + u * (int)blockDim.x, R - 1)];
+  for (int u = 0; u < CV; ++u) cv[u] = c_kv_new[(int64_t)b * R + min(tid + u * NT, R - 1)];
   const int64_t row_off = row_offsets[b];
 
-  if (tid < half) sincos_reduced((double)pos * theta, &cs[1][tid], &cs[0][tid]);
+  if (tid < half) sincos_reduced((double)pos * theta, &cs[kMaxRopePairs + tid], &cs[tid]);
   __syncthreads();
 #pragma unroll
   for (int u = 0; u < QP; ++u) {
-    const int idx = tid + u * (int)blockDim.x;
+    const int idx = tid + u * NT;
     if (idx >= npairs) break;
     const int hh = h0 + idx / half, i = idx % half;
     const double x0 = load_d<T>(qx[u][0]), x1 = load_d<T>(qx[u][1]);
-    const double c = cs[0][i], s = cs[1][i];
+    const double c = cs[i], s = cs[kMaxRopePairs + i];
     *(T2*)(q_lat + ((int64_t)b * H + hh) * W + R + 2 * i) = T2{store_d<T>(x0 * c - x1 * s), store_d<T>(x0 * s + x1 * c)};
   }
   if (!row_block) return;
@@ -1714,14 +1811,38 @@ __global__ __launch_bounds__(256) void rope_append_kernel(const T* __restrict__ 
   T* crow = cache + row * W;
 #pragma unroll
   for (int u = 0; u < CV; ++u) {
-    const int k = tid + u * (int)blockDim.x;
+    const int k = tid + u * NT;
     if (k < R) crow[k] = cv[u];
   }
   if (tid < half) {
     const double x0 = load_d<T>(kx[0]), x1 = load_d<T>(kx[1]);
-    const double c = cs[0][tid], s = cs[1][tid];
+    const double c = cs[tid], s = cs[kMaxRopePairs + tid];
     *(T2*)(crow + R + 2 * tid) = T2{store_d<T>(x0 * c - x1 * s), store_d<T>(x0 * s + x1 * c)};
   }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void rope_append_kernel(const T* __restrict__ q_rope, const T* __restrict__ c_kv_new,
+                                                          const T* __restrict__ k_rope_new,
+                                                          const int32_t* __restrict__ positions,
+                                                          const int64_t* __restrict__ row_offsets, int64_t total_rows,
+                                                          int H, int R, int DR, RopeFreqs freqs,
+                                                          T* __restrict__ q_lat, T* __restrict__ cache) {
+  __shared__ double cs[2 * kMaxRopePairs];
+  rope_block<T, 256, 16>((int)blockIdx.x, q_rope, c_kv_new, k_rope_new, positions, row_offsets, total_rows, H, R, DR,
+                         freqs, q_lat, cache, cs);
+}
+
+// K1 + K2 in one bf16 launch: the absorption blocks also do the RoPE work
+// (see absorb_bf16_block); q~ and the rotated RoPE part are disjoint columns
+// of q_lat.
+template <int DH>
+__global__ __launch_bounds__(128) void absorb_rope_bf16_kernel(const u16* __restrict__ q_nope,
+                                                               const u16* __restrict__ w_uk, int B, int H, int R,
+                                                               RopeArgs ra, RopeFreqs freqs, u16* __restrict__ q_lat) {
+  __shared__ __attribute__((aligned(1024))) char wt[AbsorbLds<DH>::WT];
+  __shared__ __attribute__((aligned(1024))) char qs[AbsorbLds<DH>::QS];
+  absorb_bf16_block<DH, true>((int)blockIdx.x, q_nope, w_uk, B, H, R, q_lat, R + ra.DR, wt, qs, ra, freqs);
 }
 
 // ---------------------------------------------------------------------------
@@ -1821,6 +1942,20 @@ mla_status launch_absorb_bf16(const mla_dims& d, const void* q_nope, const void*
   return launch_result("mla_absorb_q");
 }
 
+template <int DH>
+mla_status launch_absorb_rope_bf16(const mla_dims& d, const void* q_nope, const void* w_uk, const void* q_rope,
+                                   const void* c_kv_new, const void* k_rope_new, const int32_t* positions,
+                                   const int64_t* row_offsets, int64_t total_rows, const RopeFreqs& freqs,
+                                   void* q_lat, void* kv_cache, hipStream_t stream) {
+  if (d.rank % 64 != 0) return fail(MLA_ERR_UNSUPPORTED, "rank must be a multiple of 64");
+  const int blocks = (d.heads + kXcds - 1) / kXcds * kXcds * (d.rank / 64);  // whole groups of 8 heads
+  const RopeArgs ra{(const u16*)q_rope, (const u16*)c_kv_new, (const u16*)k_rope_new, positions, row_offsets,
+                    total_rows, d.d_rope, (u16*)kv_cache};
+  hipLaunchKernelGGL((absorb_rope_bf16_kernel<DH>), dim3(blocks), dim3(128), 0, stream, (const u16*)q_nope,
+                     (const u16*)w_uk, d.batch, d.heads, d.rank, ra, freqs, (u16*)q_lat);
+  return launch_result("mla_absorb_rope");
+}
+
 template <typename T, int NW>
 mla_status launch_absorb_dh(const mla_dims& d, const void* q_nope, const void* w_uk, void* q_lat, hipStream_t stream) {
   if constexpr (sizeof(T) == 2) {
@@ -1880,21 +2015,43 @@ mla_status mla_absorb_q(const mla_dims* dims, const void* q_nope, const void* w_
   return fail(MLA_ERR_UNSUPPORTED, "no instantiation");
 }
 
-mla_status mla_rope_append(const mla_dims* dims, const void* q_rope, const void* c_kv_new, const void* k_rope_new,
+}  // extern "C"
+
+namespace {
+
+mla_status check_rope_args(const mla_dims* dims, const void* q_rope, const void* c_kv_new, const void* k_rope_new,
                            const int32_t* positions, const int64_t* row_offsets, int64_t total_rows, void* q_lat,
-                           void* kv_cache, void* stream) {
+                           void* kv_cache) {
   mla_status st = check_dims_impl(dims);
   if (st != MLA_OK) return st;
   if (positions == nullptr || row_offsets == nullptr) return fail(MLA_ERR_INVALID_ARG, "positions/row_offsets NULL");
   if ((st = check_ptrs({q_rope, c_kv_new, k_rope_new, q_lat, kv_cache})) != MLA_OK) return st;
   if (total_rows < 1) return fail(MLA_ERR_INVALID_ARG, "total_rows must be >= 1");
-  if (dims->d_rope > 2 * kMaxRopePairs) return fail(MLA_ERR_UNSUPPORTED, "d_rope above 64");  // 16 heads x d_rope/2 pairs <= 2 per thread
-  if (dims->rank > 1024) return fail(MLA_ERR_UNSUPPORTED, "rank above 1024");  // c_kv_new values <= 4 per thread
-  g_last_error.clear();
-  hipStream_t s = (hipStream_t)stream;
+  if (dims->d_rope > 2 * kMaxRopePairs) return fail(MLA_ERR_UNSUPPORTED, "d_rope above 64");  // 16 heads x d_rope/2 pairs per block
+  if (dims->rank > 1024) return fail(MLA_ERR_UNSUPPORTED, "rank above 1024");  // c_kv_new values per thread
+  return MLA_OK;
+}
+
+RopeFreqs rope_freqs(const mla_dims* dims) {
   const double base = dims->rope_base > 0.f ? (double)dims->rope_base : 10000.0;
   RopeFreqs freqs;
   for (int i = 0; i < dims->d_rope / 2; ++i) freqs.theta[i] = std::pow(base, -2.0 * (double)i / (double)dims->d_rope);
+  return freqs;
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status mla_rope_append(const mla_dims* dims, const void* q_rope, const void* c_kv_new, const void* k_rope_new,
+                           const int32_t* positions, const int64_t* row_offsets, int64_t total_rows, void* q_lat,
+                           void* kv_cache, void* stream) {
+  mla_status st = check_rope_args(dims, q_rope, c_kv_new, k_rope_new, positions, row_offsets, total_rows, q_lat,
+                                  kv_cache);
+  if (st != MLA_OK) return st;
+  g_last_error.clear();
+  hipStream_t s = (hipStream_t)stream;
+  const RopeFreqs freqs = rope_freqs(dims);
   const int blocks = dims->batch * ((dims->heads + 15) / 16);
   if (dims->dtype == MLA_BF16) {
     hipLaunchKernelGGL((rope_append_kernel<u16>), dim3(blocks), dim3(256), 0, s, (const u16*)q_rope,
@@ -1906,6 +2063,35 @@ mla_status mla_rope_append(const mla_dims* dims, const void* q_rope, const void*
                        dims->heads, dims->rank, dims->d_rope, freqs, (float*)q_lat, (float*)kv_cache);
   }
   return launch_result("mla_rope_append");
+}
+
+mla_status mla_absorb_rope(const mla_dims* dims, const void* q_nope, const void* w_uk, const void* q_rope,
+                           const void* c_kv_new, const void* k_rope_new, const int32_t* positions,
+                           const int64_t* row_offsets, int64_t total_rows, void* q_lat, void* kv_cache,
+                           void* stream) {
+  mla_status st = check_rope_args(dims, q_rope, c_kv_new, k_rope_new, positions, row_offsets, total_rows, q_lat,
+                                  kv_cache);
+  if (st != MLA_OK) return st;
+  if ((st = check_ptrs({q_nope, w_uk})) != MLA_OK) return st;
+  g_last_error.clear();
+  hipStream_t s = (hipStream_t)stream;
+  if (find_inst(*dims) != kBf16H128R512D64) {  // fp32: the two launches, in order
+    if ((st = mla_absorb_q(dims, q_nope, w_uk, q_lat, stream)) != MLA_OK) return st;
+    return mla_rope_append(dims, q_rope, c_kv_new, k_rope_new, positions, row_offsets, total_rows, q_lat, kv_cache,
+                           stream);
+  }
+  const RopeFreqs freqs = rope_freqs(dims);
+  switch (dims->d_head) {
+    case 32: return launch_absorb_rope_bf16<32>(*dims, q_nope, w_uk, q_rope, c_kv_new, k_rope_new, positions,
+                                                row_offsets, total_rows, freqs, q_lat, kv_cache, s);
+    case 64: return launch_absorb_rope_bf16<64>(*dims, q_nope, w_uk, q_rope, c_kv_new, k_rope_new, positions,
+                                                row_offsets, total_rows, freqs, q_lat, kv_cache, s);
+    case 128: return launch_absorb_rope_bf16<128>(*dims, q_nope, w_uk, q_rope, c_kv_new, k_rope_new, positions,
+                                                  row_offsets, total_rows, freqs, q_lat, kv_cache, s);
+    case 256: return launch_absorb_rope_bf16<256>(*dims, q_nope, w_uk, q_rope, c_kv_new, k_rope_new, positions,
+                                                  row_offsets, total_rows, freqs, q_lat, kv_cache, s);
+  }
+  return fail(MLA_ERR_UNSUPPORTED, "d_head");
 }
 
 mla_status mla_decode_latent(const mla_dims* dims, const void* q_lat, const void* kv_cache, const int64_t* row_offsets,

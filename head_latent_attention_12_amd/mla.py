@@ -21,7 +21,7 @@ STATUS = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARG", 2: "MLA_ERR_UNSUPPORTED", 3: "M
           4: "MLA_ERR_WORKSPACE", 5: "MLA_ERR_HIP"}
 
 EXPORTS = ("mla_absorb_q", "mla_rope_append", "mla_decode_latent", "mla_combine", "mla_up_v",
-           "mla_combine_up_v", "mla_partials_size", "mla_plan_splits", "mla_check_dims", "mla_status_string", "mla_last_error")
+           "mla_combine_up_v", "mla_absorb_rope", "mla_partials_size", "mla_plan_splits", "mla_check_dims", "mla_status_string", "mla_last_error")
 
 
 class MlaDims(ctypes.Structure):
@@ -56,6 +56,7 @@ def lib() -> ctypes.CDLL:
             "mla_combine": (i32, [D, P, P, i32, P, P, P]),
             "mla_up_v": (i32, [D, P, P, P, P]),
             "mla_combine_up_v": (i32, [D, P, P, i32, P, P, P, P]),
+            "mla_absorb_rope": (i32, [D, P, P, P, P, P, P, P, i64, P, P, P]),
             "mla_partials_size": (i32, [D, i32, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]),
             "mla_plan_splits": (i32, [D, i32, i64, i32]),
             "mla_check_dims": (i32, [D]),
@@ -106,6 +107,13 @@ def mla_rope_append(dims, q_rope, c_kv_new, k_rope_new, positions, row_offsets, 
     _check("mla_rope_append", lib().mla_rope_append(
         ctypes.byref(dims), _p(q_rope), _p(c_kv_new), _p(k_rope_new), _p(positions), _p(row_offsets),
         int(total_rows), _p(q_lat), _p(kv_cache), _s(stream)))
+
+
+def mla_absorb_rope(dims, q_nope, w_uk, q_rope, c_kv_new, k_rope_new, positions, row_offsets, total_rows, q_lat,
+                    kv_cache, stream=None):
+    _check("mla_absorb_rope", lib().mla_absorb_rope(
+        ctypes.byref(dims), _p(q_nope), _p(w_uk), _p(q_rope), _p(c_kv_new), _p(k_rope_new), _p(positions),
+        _p(row_offsets), int(total_rows), _p(q_lat), _p(kv_cache), _s(stream)))
 
 
 def mla_decode_latent(dims, q_lat, kv_cache, row_offsets, seq_lens, total_rows, max_seq_len, num_splits, o_part,

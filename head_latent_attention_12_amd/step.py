@@ -28,8 +28,9 @@ def bits_to_f64(t: torch.Tensor, dtype: str) -> np.ndarray:
 
 class DeviceStep:
     """Device buffers of one step and the calls that compute it: absorb_q,
-    rope_append, decode_latent, then combine and up_v, which ``run`` issues as
-    the one fused call combine_up_v (the separate calls stay available)."""
+    rope_append, decode_latent, combine and up_v.  ``run`` issues them as
+    absorb_rope, decode_latent and combine_up_v (the fused entry points); the
+    separate calls stay available."""
 
     def __init__(self, inp: StepInputs, num_splits: int | None = None, device: str = "cuda:0",
                  weights: "DeviceStep | None" = None, scratch: "DeviceStep | None" = None):
@@ -83,6 +84,10 @@ class DeviceStep:
         mla.mla_rope_append(self.dims, self.q_rope, self.c_kv_new, self.k_rope_new, self.positions,
                             self.row_offsets, self.inp.total_rows, self.q_lat, self.kv_cache, stream)
 
+    def absorb_rope(self, stream=None):
+        mla.mla_absorb_rope(self.dims, self.q_nope, self.w_uk, self.q_rope, self.c_kv_new, self.k_rope_new,
+                            self.positions, self.row_offsets, self.inp.total_rows, self.q_lat, self.kv_cache, stream)
+
     def decode_latent(self, stream=None):
         mla.mla_decode_latent(self.dims, self.q_lat, self.kv_cache, self.row_offsets, self.seq_lens,
                               self.inp.total_rows, self.inp.max_seq_len, self.num_splits, self.o_part,
@@ -100,8 +105,7 @@ class DeviceStep:
 
     def run(self, stream=None):
         """One step: out and lse (o_lat is only written by ``combine``)."""
-        self.absorb_q(stream)
-        self.rope_append(stream)
+        self.absorb_rope(stream)
         self.decode_latent(stream)
         self.combine_up_v(stream)
 

@@ -13,6 +13,8 @@
  *                     sum of the latents, one partial result per split
  *   mla_combine       log-sum-exp merge of the splits into o_lat
  *   mla_up_v          out = W_UV o_lat per head
+ *   mla_absorb_rope   mla_absorb_q and mla_rope_append in one call (one launch
+ *                     for bf16)
  *   mla_combine_up_v  the last two in one call: the merge is formed where
  *                     W_UV consumes it and o_lat never goes to memory
  *
@@ -133,6 +135,15 @@ mla_status mla_rope_append(const mla_dims* dims, const void* q_rope, const void*
                            const void* k_rope_new, const int32_t* positions,
                            const int64_t* row_offsets, int64_t total_rows, void* q_lat,
                            void* kv_cache, void* stream);
+
+/* mla_absorb_q followed by mla_rope_append, with the arguments of both
+ * ([P1] section 3, [P2] cache management, [P5]): the two write disjoint
+ * columns of q_lat, so with bf16 storage they run as one kernel launch (fp32
+ * storage enqueues the two launches).  Results are those of the two calls. */
+mla_status mla_absorb_rope(const mla_dims* dims, const void* q_nope, const void* w_uk,
+                           const void* q_rope, const void* c_kv_new, const void* k_rope_new,
+                           const int32_t* positions, const int64_t* row_offsets, int64_t total_rows,
+                           void* q_lat, void* kv_cache, void* stream);
 
 /* Attention in the latent space ([P1] section 3, [P2] absorbing projections,
  * [P3] content score + position score): for every b, h and split s with rows

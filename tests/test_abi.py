@@ -88,6 +88,10 @@ def test_entry_points_reject_null_and_misaligned_pointers():
     _expect(1, mla.mla_combine, d, P16, P16, 1, 0, None, 0)
     _expect(1, mla.mla_up_v, d, P16, 0, P16, 0)
     _expect(3, mla.mla_up_v, d, P16, P16, P16 + 12, 0)
+    _expect(1, mla.mla_absorb_rope, d, P16, P16, P16, P16, P16, P16, P16, 0, P16, P16, 0)   # total_rows 0
+    _expect(1, mla.mla_absorb_rope, d, P16, P16, P16, P16, P16, 0, P16, 10, P16, P16, 0)    # positions NULL
+    _expect(1, mla.mla_absorb_rope, d, 0, P16, P16, P16, P16, P16, P16, 10, P16, P16, 0)    # q_nope NULL
+    _expect(3, mla.mla_absorb_rope, d, P16, P16 + 2, P16, P16, P16, P16, P16, 10, P16, P16, 0)
     _expect(1, mla.mla_combine_up_v, d, P16, P16, 1, 0, P16, None, 0)               # w_uv NULL
     _expect(1, mla.mla_combine_up_v, d, P16, 0, 1, P16, P16, None, 0)               # lse_part NULL
     _expect(3, mla.mla_combine_up_v, d, P16, P16, 1, P16, P16 + 4, None, 0)

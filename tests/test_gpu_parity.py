@@ -86,6 +86,14 @@ def check_step(step_inp, ds, ref, tag=""):
     keep = np.ones(step_inp.total_rows, bool)
     keep[slots] = False
     np.testing.assert_array_equal(cache[keep], step_inp.kv_cache[keep])   # other rows untouched
+    # the separate absorb_q and rope_append calls write the same bytes as the
+    # step's fused absorb_rope call
+    q_fused, cache_fused = ds.q_lat.clone(), ds.kv_cache.clone()
+    ds.q_lat.fill_(-1)
+    ds.absorb_q()
+    ds.rope_append()
+    torch.cuda.synchronize()
+    assert torch.equal(ds.q_lat, q_fused) and torch.equal(ds.kv_cache, cache_fused), tag
     # out and lse of the step (the fused combine_up_v call), then the separate
     # combine and up_v calls on the same partials: o_lat, lse and out again
     out_fused = ds.out.cpu().numpy().astype(np.float64)

@@ -247,8 +247,7 @@ def run_workload(name, steps, warmup, min_sets, verbose=True):
     t1 = time.perf_counter()
     for i in range(steps):
         ds = sets[i % n_sets]
-        ds.absorb_q()
-        ds.rope_append()
+        ds.absorb_rope()
         k3_start[i].record(stream)
         ds.decode_latent()
         k3_end[i].record(stream)

@@ -189,7 +189,7 @@ def capture_round(sets):
     return graph
 
 
-def run_workload(name, steps, warmup, min_sets, verbose=True):
+def run_workload(name, steps, warmup, min_sets, verbose=True, page_rows=None):
     import torch
 
     from head_latent_attention_12_amd import mla, synthetic as syn
@@ -202,8 +202,8 @@ def run_workload(name, steps, warmup, min_sets, verbose=True):
     # each set has its own cache and weights (like successive layers); the
     # per-step temporaries (q_lat, split partials, o_lat, out) are one shared
     # workspace, as a multi-layer decode would reuse them
-    sets = [DeviceStep(inp)]
-    sets += [DeviceStep(inp, scratch=sets[0]) for _ in range(n_sets - 1)]
+    sets = [DeviceStep(inp, page_rows=page_rows, page_seed=0)]
+    sets += [DeviceStep(inp, scratch=sets[0], page_rows=page_rows, page_seed=i) for i in range(1, n_sets)]
     stream = torch.cuda.current_stream()
     for i in range(warmup):
         sets[i % n_sets].run()
@@ -270,8 +270,9 @@ def run_workload(name, steps, warmup, min_sets, verbose=True):
 
     ms = wall * 1e3 / steps
     res = {
-        "name": name,
-        "workload": workload_label(inp),
+        "name": name if page_rows is None else f"{name}_paged{page_rows}",
+        "workload": workload_label(inp) + ("" if page_rows is None else
+                                           f", paged cache ({page_rows}-row pages, shuffled block table)"),
         "cached_tokens_per_step": rows,
         "ms_per_step": ms,
         "device_ms_per_step": dev_ms,
@@ -292,7 +293,7 @@ def run_workload(name, steps, warmup, min_sets, verbose=True):
         "inp": inp,
     }
     if verbose:
-        print(f"# {name}: {ms * 1e3:.1f} us/step (device {dev_ms * 1e3:.1f}, eager {eager_ms * 1e3:.1f}), "
+        print(f"# {res['name']}: {ms * 1e3:.1f} us/step (device {dev_ms * 1e3:.1f}, eager {eager_ms * 1e3:.1f}), "
               f"decode kernel {k3_ms * 1e3:.1f} us "
               f"= {res['decode_kernel_GBps']:.0f} GB/s, {res['decode_kernel_TFLOPs']:.0f} TFLOP/s; "
               f"splits {res['num_splits']}, sets {n_sets}", file=sys.stderr, flush=True)
@@ -337,12 +338,13 @@ def main():
     main_res = run_workload(args.workload, args.steps, args.warmup, min_sets=5)
     others = {}
     if not args.no_others:
-        for name in ("dsv2_ragged", "dsv2_long"):
-            if name == args.workload:
+        for name, page_rows in (("dsv2_ragged", None), ("dsv2_long", None), ("dsv2_ragged", 64)):
+            if name == args.workload and page_rows is None:
                 continue
-            r = run_workload(name, max(20, args.steps // 4), max(5, args.warmup // 4), min_sets=2)
-            others[name] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items()
-                            if k not in ("inp", "k3_bytes", "k3_flops", "step_bytes", "step_flops")}
+            r = run_workload(name, max(20, args.steps // 4), max(5, args.warmup // 4), min_sets=2,
+                             page_rows=page_rows)
+            others[r["name"]] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items()
+                                 if k not in ("inp", "k3_bytes", "k3_flops", "step_bytes", "step_flops")}
 
     inp = main_res["inp"]
     bf16 = inp.dtype == "bf16"

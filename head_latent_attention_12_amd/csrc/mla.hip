@@ -294,6 +294,36 @@ __device__ __forceinline__ void wait_vm_then_barrier() {
 //                                                    from the S^T accumulators)
 // ---------------------------------------------------------------------------
 
+// Where the rows of a sequence live in the cache.  Packed: in-sequence row t
+// of sequence b is cache row row_offsets[b] + t.  Paged: the cache is pages
+// of 2^page_shift rows (at least 32, so a 32-row tile never straddles two),
+// and row t is row t & (page_rows - 1) of page block_table[b * bt_stride +
+// (t >> page_shift)].  Rows are clamped into the cache either way, so that
+// inconsistent metadata can only give wrong numbers, never a stray access.
+struct CacheMap {
+  const int64_t* row_offsets;  // packed (nullptr when paged)
+  const int32_t* block_table;  // paged (nullptr when packed)
+  int64_t total_rows;          // rows in the cache
+  int64_t total_pages;         // paged: pages in the cache
+  int32_t bt_stride;           // paged: entries per sequence in block_table
+  int32_t page_shift;          // paged: log2(page_rows)
+  // (bt: block_table, passed separately where a restrict-qualified pointer
+  // lets the compiler read it with scalar loads)
+  __device__ __forceinline__ int64_t paged_row(int b, int t, const int32_t* __restrict__ bt) const {
+    int pi = t >> page_shift;
+    pi = pi < 0 ? 0 : (pi >= bt_stride ? bt_stride - 1 : pi);
+    int64_t pg = bt[(int64_t)b * bt_stride + pi];
+    pg = pg < 0 ? 0 : (pg >= total_pages ? total_pages - 1 : pg);
+    return (pg << page_shift) + (t & ((1 << page_shift) - 1));
+  }
+  // row t of sequence b; off = row_offsets[b] (packed, loaded by the caller)
+  __device__ __forceinline__ int64_t row(int b, int t, int64_t off) const {
+    if (block_table != nullptr) return paged_row(b, t, block_table);
+    const int64_t r = off + t;
+    return r < 0 ? 0 : (r >= total_rows ? total_rows - 1 : r);
+  }
+};
+
 template <typename T, int H, int R, int DR, int NW>
 struct DecodeShape {
   static constexpr int W = R + DR;
@@ -316,11 +346,11 @@ struct DecodeShape {
   static_assert(STAGES * TILE_BYTES <= 160 * 1024, "LDS");
 };
 
-template <typename T, int H, int R, int DR, int NW>
+template <typename T, int H, int R, int DR, int NW, bool PAGED>
 __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
-    const T* __restrict__ q_lat, const T* __restrict__ cache, const int64_t* __restrict__ row_offsets,
-    const int32_t* __restrict__ seq_lens, int64_t total_rows, int32_t batch, int32_t num_splits, int32_t chunk,
-    T* __restrict__ o_part, float* __restrict__ lse_part, float scale_log2) {
+    const T* __restrict__ q_lat, const T* __restrict__ cache, CacheMap cm, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ seq_lens, int32_t batch, int32_t num_splits, int32_t chunk, T* __restrict__ o_part,
+    float* __restrict__ lse_part, float scale_log2) {
   using S = DecodeShape<T, H, R, DR, NW>;
   using M = Mma<T>;
   constexpr int W = S::W, ROWB = S::ROWB, NCH = S::NCH, TILE = S::TILE, STAGES = S::STAGES;
@@ -350,7 +380,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
     const int bid = (int)blockIdx.x;
     const bool in0 = lane < batch;
     const int len0 = in0 ? seq_lens[lane] : 0;
-    const int64_t off0 = in0 ? row_offsets[lane] : 0;
+    const int64_t off0 = (!PAGED && in0) ? cm.row_offsets[lane] : 0;
     // pass 1: item count
     int items = wave_sum(in0 ? splits_of(len0) : 0);
     for (int c0 = 64; c0 < batch; c0 += 64) {
@@ -371,7 +401,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
       int64_t off = off0;
       if (c0 > 0) {
         len = bb < batch ? seq_lens[bb] : 0;
-        off = bb < batch ? row_offsets[bb] : 0;
+        off = (!PAGED && bb < batch) ? cm.row_offsets[bb] : 0;
       }
       const int n = bb < batch ? splits_of(len) : 0;
       const int incl = wave_prefix_sum(n) + base;
@@ -410,13 +440,29 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
     return;
   }
   const int ntiles = (r1 - r0 + TILE - 1) / TILE;
-  // Absolute cache rows of this split, clamped into the cache: inconsistent
-  // metadata can then only produce wrong numbers, never a stray access.
-  int64_t row_lo = row_off + r0, row_hi = row_off + r1 - 1;
-  row_lo = row_lo < 0 ? 0 : (row_lo > total_rows - 1 ? total_rows - 1 : row_lo);
-  row_hi = row_hi < row_lo ? row_lo : (row_hi > total_rows - 1 ? total_rows - 1 : row_hi);
-  const char* split_base = (const char*)cache + row_lo * ROWB;
-  const int last_rel = (int)(row_hi - row_lo);  // last valid row relative to row_lo
+  // Packed: the split's absolute cache rows, clamped into the cache
+  // (inconsistent metadata can then only produce wrong numbers, never a stray
+  // access).  Paged: every 32-row tile lies in one page (chunk and page size
+  // are multiples of 32); its rows are looked up per tile.
+  const char* split_base = nullptr;
+  int last_rel;  // last valid row relative to the split's first
+  if constexpr (!PAGED) {
+    int64_t row_lo = row_off + r0, row_hi = row_off + r1 - 1;
+    row_lo = row_lo < 0 ? 0 : (row_lo > cm.total_rows - 1 ? cm.total_rows - 1 : row_lo);
+    row_hi = row_hi < row_lo ? row_lo : (row_hi > cm.total_rows - 1 ? cm.total_rows - 1 : row_hi);
+    split_base = (const char*)cache + row_lo * ROWB;
+    last_rel = (int)(row_hi - row_lo);
+  } else {
+    last_rel = r1 - 1 - r0;
+  }
+  // first byte of the split's tile `tile` (32 consecutive cache rows)
+  auto tile_ptr = [&](int tile) -> const char* {
+    if constexpr (PAGED) {
+      return (const char*)cache + cm.paged_row(b, r0 + tile * TILE, block_table) * ROWB;
+    } else {
+      return split_base + (int64_t)tile * TILE * ROWB;
+    }
+  };
 
   // DMA: wave instruction n of a tile fills LDS bytes [gi*1024, gi*1024 + 1024)
   // of the stage (gi = wave*DPW + n); lane l writes 16 bytes at gi*1024 + 16*l,
@@ -448,8 +494,9 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
   auto issue_tile = [&](int tile, int stage) {
     const int rel0 = tile * TILE;
     LDS_AS char* dst = (LDS_AS char*)smem + stage * TB + wave * DPW * 1024;
+    const char* tbase = tile_ptr(tile);
     if (rel0 + TILE - 1 <= last_rel) {
-      issue_rows(split_base + (int64_t)rel0 * ROWB, stage);
+      issue_rows(tbase, stage);
     } else {
       int ln = lane;
       asm volatile("" : "+v"(ln));  // recomputed here, not kept live
@@ -460,7 +507,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
           const int p = (wave * DPW + n) * 64 + ln;
           const int t = p / NCH;
           const int rel = min(rel0 + t, last_rel);
-          addr[n] = (uint64_t)(split_base + (int64_t)rel * ROWB + 16 * swz_chunk<NCH>(t, p - t * NCH));
+          addr[n] = (uint64_t)(tbase + (int64_t)(rel - rel0) * ROWB + 16 * swz_chunk<NCH>(t, p - t * NCH));
         }
         lds_dma9((int)(uintptr_t)dst, addr);
       } else {
@@ -469,7 +516,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
           const int p = (wave * DPW + n) * 64 + ln;
           const int t = p / NCH;
           const int rel = min(rel0 + t, last_rel);
-          const char* src = split_base + (int64_t)rel * ROWB + 16 * swz_chunk<NCH>(t, p - t * NCH);
+          const char* src = tbase + (int64_t)(rel - rel0) * ROWB + 16 * swz_chunk<NCH>(t, p - t * NCH);
           __builtin_amdgcn_global_load_lds(src, dst + n * 1024, 16, 0, 0);
         }
       }
@@ -707,7 +754,10 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
         for (; i + STAGES - 1 < nfull; ++i) {
           wait_vm_then_barrier<DPW>();  // tile i+1 has landed, every wave has finished iteration i-1
           const int t3 = i + STAGES - 1;
-          iterate(true, i, 1, ldst_w + stg(t3) * TB, split_s + (uint64_t)t3 * (TILE * ROWB), 1, TILE);
+          // paged: one scalar read of the block table per tile (16 page ids
+          // share a scalar-cache line)
+          const uint64_t tb = PAGED ? uniform_u64((uint64_t)tile_ptr(t3)) : split_s + (uint64_t)t3 * (TILE * ROWB);
+          iterate(true, i, 1, ldst_w + stg(t3) * TB, tb, 1, TILE);
         }
         // the last STAGES - 1 iterations (and every iteration of a short split)
         for (; i < ntiles; ++i) {
@@ -723,7 +773,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
           if (t3 < ntiles) {
             if (t3 * TILE + TILE - 1 <= last_rel) {
               dma = 1;
-              tbase += (uint64_t)t3 * TILE * ROWB;
+              tbase = (uint64_t)tile_ptr(t3);
               ldst = ldst_w + stg(t3) * TB;
             } else {
               issue_tile(t3, stg(t3));
@@ -1107,8 +1157,7 @@ struct RopeArgs {
   const u16* c_kv_new;
   const u16* k_rope_new;
   const int32_t* positions;
-  const int64_t* row_offsets;
-  int64_t total_rows;
+  CacheMap cm;  // where the appended rows go
   int DR;
   u16* cache;
 };
@@ -1126,7 +1175,7 @@ __device__ __forceinline__ uint32_t rope_pair_bf16(uint32_t x, int pos, double t
 // before the one wait, so a work-group pays a single HBM round trip up front.
 // Query rows are stored with their 16-byte chunks XOR-swizzled by row, which
 // makes the fragment reads (lane = sequence) conflict-free.
-template <int DH, bool ROPE>
+template <int DH, bool ROPE, bool PAGED>
 __device__ __forceinline__ void absorb_bf16_block(int bid, const u16* __restrict__ q_nope,
                                                   const u16* __restrict__ w_uk, int B, int H, int R,
                                                   u16* __restrict__ q_lat, int W, char* wt, char* qs,
@@ -1181,7 +1230,7 @@ __device__ __forceinline__ void absorb_bf16_block(int bid, const u16* __restrict
     }
     const int ab = min(ab0, B - 1), ti = min(tid, half - 1);
     apos = ra.positions[ab];
-    aoff = ra.row_offsets[ab];
+    if constexpr (!PAGED) aoff = ra.cm.row_offsets[ab];  // (paged: the page is read after the wait)
     kx = *(const uint32_t*)(ra.k_rope_new + (int64_t)ab * ra.DR + 2 * ti);
     ath = freqs.theta[ti];
 #pragma unroll
@@ -1226,9 +1275,7 @@ __device__ __forceinline__ void absorb_bf16_block(int bid, const u16* __restrict
     }
     // the appended rows: [c_kv_new | RoPE(k_rope_new)] (c_kv_new bit for bit)
     auto append = [&](int bb, int pos, int64_t off, const u32x2 (&cv)[CVA], uint32_t k, double th) {
-      int64_t row = off + pos;
-      row = row < 0 ? 0 : (row >= ra.total_rows ? ra.total_rows - 1 : row);
-      u16* crow = ra.cache + row * W2;
+      u16* crow = ra.cache + ra.cm.row(bb, pos, off) * W2;
 #pragma unroll
       for (int u = 0; u < CVA; ++u)
         if (4 * (tid + 128 * u) < R) *(u32x2*)(crow + 4 * (tid + 128 * u)) = cv[u];
@@ -1240,8 +1287,8 @@ __device__ __forceinline__ void absorb_bf16_block(int bid, const u16* __restrict
       u32x2 cv[CVA];
 #pragma unroll
       for (int u = 0; u < CVA; ++u) cv[u] = *(const u32x2*)(ra.c_kv_new + (int64_t)bb * R + min(4 * (tid + 128 * u), R - 4));
-      append(bb, ra.positions[bb], ra.row_offsets[bb], cv, *(const uint32_t*)(ra.k_rope_new + (int64_t)bb * ra.DR + 2 * ti),
-             freqs.theta[ti]);
+      append(bb, ra.positions[bb], PAGED ? 0 : ra.cm.row_offsets[bb], cv,
+             *(const uint32_t*)(ra.k_rope_new + (int64_t)bb * ra.DR + 2 * ti), freqs.theta[ti]);
     }
   }
 
@@ -1292,7 +1339,7 @@ __global__ __launch_bounds__(128) void absorb_q_bf16_kernel(const u16* __restric
                                                             u16* __restrict__ q_lat, int W) {
   __shared__ __attribute__((aligned(1024))) char wt[AbsorbLds<DH>::WT];
   __shared__ __attribute__((aligned(1024))) char qs[AbsorbLds<DH>::QS];
-  absorb_bf16_block<DH, false>((int)blockIdx.x, q_nope, w_uk, B, H, R, q_lat, W, wt, qs, RopeArgs{}, RopeFreqs{});
+  absorb_bf16_block<DH, false, false>((int)blockIdx.x, q_nope, w_uk, B, H, R, q_lat, W, wt, qs, RopeArgs{}, RopeFreqs{});
 }
 
 // ---------------------------------------------------------------------------
@@ -1759,7 +1806,7 @@ __global__ __launch_bounds__(64) void combine_up_v_f32_kernel(const float* __res
 template <typename T, int NT, int HB>
 __device__ __forceinline__ void rope_block(int blk, const T* __restrict__ q_rope, const T* __restrict__ c_kv_new,
                                            const T* __restrict__ k_rope_new, const int32_t* __restrict__ positions,
-                                           const int64_t* __restrict__ row_offsets, int64_t total_rows, int H, int R,
+                                           const CacheMap& cm, int H, int R,
                                            int DR, const RopeFreqs& freqs, T* __restrict__ q_lat,
                                            T* __restrict__ cache, double* cs /* LDS, 2 * kMaxRopePairs */) {
   constexpr int QP = HB * kMaxRopePairs / NT;  // q_rope pairs per thread (HB heads x d_rope/2)
@@ -1792,7 +1839,7 @@ __device__ __forceinline__ void rope_block(int blk, const T* __restrict__ q_rope
   T cv[CV];
 #pragma unroll
   for (int u = 0; u < CV; ++u) cv[u] = c_kv_new[(int64_t)b * R + min(tid + u * NT, R - 1)];
-  const int64_t row_off = row_offsets[b];
+  const int64_t row_off = cm.block_table == nullptr ? cm.row_offsets[b] : 0;  // (paged: looked up below)
 
   if (tid < half) sincos_reduced((double)pos * theta, &cs[kMaxRopePairs + tid], &cs[tid]);
   __syncthreads();
@@ -1806,9 +1853,7 @@ __device__ __forceinline__ void rope_block(int blk, const T* __restrict__ q_rope
     *(T2*)(q_lat + ((int64_t)b * H + hh) * W + R + 2 * i) = T2{store_d<T>(x0 * c - x1 * s), store_d<T>(x0 * s + x1 * c)};
   }
   if (!row_block) return;
-  int64_t row = row_off + pos;
-  row = row < 0 ? 0 : (row >= total_rows ? total_rows - 1 : row);
-  T* crow = cache + row * W;
+  T* crow = cache + cm.row(b, pos, row_off) * W;
 #pragma unroll
   for (int u = 0; u < CV; ++u) {
     const int k = tid + u * NT;
@@ -1824,25 +1869,24 @@ __device__ __forceinline__ void rope_block(int blk, const T* __restrict__ q_rope
 template <typename T>
 __global__ __launch_bounds__(256) void rope_append_kernel(const T* __restrict__ q_rope, const T* __restrict__ c_kv_new,
                                                           const T* __restrict__ k_rope_new,
-                                                          const int32_t* __restrict__ positions,
-                                                          const int64_t* __restrict__ row_offsets, int64_t total_rows,
+                                                          const int32_t* __restrict__ positions, CacheMap cm,
                                                           int H, int R, int DR, RopeFreqs freqs,
                                                           T* __restrict__ q_lat, T* __restrict__ cache) {
   __shared__ double cs[2 * kMaxRopePairs];
-  rope_block<T, 256, 16>((int)blockIdx.x, q_rope, c_kv_new, k_rope_new, positions, row_offsets, total_rows, H, R, DR,
-                         freqs, q_lat, cache, cs);
+  rope_block<T, 256, 16>((int)blockIdx.x, q_rope, c_kv_new, k_rope_new, positions, cm, H, R, DR, freqs, q_lat,
+                         cache, cs);
 }
 
 // K1 + K2 in one bf16 launch: the absorption blocks also do the RoPE work
 // (see absorb_bf16_block); q~ and the rotated RoPE part are disjoint columns
 // of q_lat.
-template <int DH>
+template <int DH, bool PAGED>
 __global__ __launch_bounds__(128) void absorb_rope_bf16_kernel(const u16* __restrict__ q_nope,
                                                                const u16* __restrict__ w_uk, int B, int H, int R,
                                                                RopeArgs ra, RopeFreqs freqs, u16* __restrict__ q_lat) {
   __shared__ __attribute__((aligned(1024))) char wt[AbsorbLds<DH>::WT];
   __shared__ __attribute__((aligned(1024))) char qs[AbsorbLds<DH>::QS];
-  absorb_bf16_block<DH, true>((int)blockIdx.x, q_nope, w_uk, B, H, R, q_lat, R + ra.DR, wt, qs, ra, freqs);
+  absorb_bf16_block<DH, true, PAGED>((int)blockIdx.x, q_nope, w_uk, B, H, R, q_lat, R + ra.DR, wt, qs, ra, freqs);
 }
 
 // ---------------------------------------------------------------------------
@@ -1909,16 +1953,22 @@ int32_t chunk_rows(int32_t max_seq_len, int32_t num_splits) {
 constexpr int kMaxSplits = 4096;
 
 template <typename T, int H, int R, int DR, int NW>
-mla_status launch_decode(const mla_dims& d, const void* q_lat, const void* cache, const int64_t* row_offsets,
-                         const int32_t* seq_lens, int64_t total_rows, int32_t max_seq_len, int32_t num_splits,
-                         void* o_part, float* lse_part, hipStream_t stream) {
+mla_status launch_decode(const mla_dims& d, const void* q_lat, const void* cache, const CacheMap& cm,
+                         const int32_t* seq_lens, int32_t max_seq_len, int32_t num_splits, void* o_part,
+                         float* lse_part, hipStream_t stream) {
   using S = DecodeShape<T, H, R, DR, NW>;
   const int64_t items = (int64_t)d.batch * num_splits * S::GROUPS;
   const int64_t blocks = (items + kXcds - 1) / kXcds * kXcds;  // padded to whole rounds over the XCDs
   if (blocks > 0x7fffffff) return fail(MLA_ERR_UNSUPPORTED, "grid too large");
   const float scale_log2 = scale_of(d) * kLog2e;
-  hipLaunchKernelGGL((decode_latent_kernel<T, H, R, DR, NW>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream,
-                     (const T*)q_lat, (const T*)cache, row_offsets, seq_lens, total_rows, d.batch, num_splits,
+  if (cm.block_table != nullptr) {
+    hipLaunchKernelGGL((decode_latent_kernel<T, H, R, DR, NW, true>), dim3((unsigned)blocks), dim3(NW * 64), 0,
+                       stream, (const T*)q_lat, (const T*)cache, cm, cm.block_table, seq_lens, d.batch, num_splits,
+                       chunk_rows(max_seq_len, num_splits), (T*)o_part, lse_part, scale_log2);
+    return launch_result("mla_decode_latent_paged");
+  }
+  hipLaunchKernelGGL((decode_latent_kernel<T, H, R, DR, NW, false>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream,
+                     (const T*)q_lat, (const T*)cache, cm, nullptr, seq_lens, d.batch, num_splits,
                      chunk_rows(max_seq_len, num_splits), (T*)o_part, lse_part, scale_log2);
   return launch_result("mla_decode_latent");
 }
@@ -1945,13 +1995,18 @@ mla_status launch_absorb_bf16(const mla_dims& d, const void* q_nope, const void*
 template <int DH>
 mla_status launch_absorb_rope_bf16(const mla_dims& d, const void* q_nope, const void* w_uk, const void* q_rope,
                                    const void* c_kv_new, const void* k_rope_new, const int32_t* positions,
-                                   const int64_t* row_offsets, int64_t total_rows, const RopeFreqs& freqs,
-                                   void* q_lat, void* kv_cache, hipStream_t stream) {
+                                   const CacheMap& cm, const RopeFreqs& freqs, void* q_lat, void* kv_cache,
+                                   hipStream_t stream) {
   if (d.rank % 64 != 0) return fail(MLA_ERR_UNSUPPORTED, "rank must be a multiple of 64");
   const int blocks = (d.heads + kXcds - 1) / kXcds * kXcds * (d.rank / 64);  // whole groups of 8 heads
-  const RopeArgs ra{(const u16*)q_rope, (const u16*)c_kv_new, (const u16*)k_rope_new, positions, row_offsets,
-                    total_rows, d.d_rope, (u16*)kv_cache};
-  hipLaunchKernelGGL((absorb_rope_bf16_kernel<DH>), dim3(blocks), dim3(128), 0, stream, (const u16*)q_nope,
+  const RopeArgs ra{(const u16*)q_rope, (const u16*)c_kv_new, (const u16*)k_rope_new, positions, cm, d.d_rope,
+                    (u16*)kv_cache};
+  if (cm.block_table != nullptr) {
+    hipLaunchKernelGGL((absorb_rope_bf16_kernel<DH, true>), dim3(blocks), dim3(128), 0, stream, (const u16*)q_nope,
+                       (const u16*)w_uk, d.batch, d.heads, d.rank, ra, freqs, (u16*)q_lat);
+    return launch_result("mla_absorb_rope_paged");
+  }
+  hipLaunchKernelGGL((absorb_rope_bf16_kernel<DH, false>), dim3(blocks), dim3(128), 0, stream, (const u16*)q_nope,
                      (const u16*)w_uk, d.batch, d.heads, d.rank, ra, freqs, (u16*)q_lat);
   return launch_result("mla_absorb_rope");
 }
@@ -2019,16 +2074,36 @@ mla_status mla_absorb_q(const mla_dims* dims, const void* q_nope, const void* w_
 
 namespace {
 
+// A paged cache description: block table, pages of page_rows (a power of two
+// from 32 to 65536) rows, total_pages pages.
+mla_status paged_map(const int32_t* block_table, int32_t bt_stride, int32_t page_rows, int64_t total_pages,
+                     CacheMap* cm) {
+  if (block_table == nullptr) return fail(MLA_ERR_INVALID_ARG, "block_table NULL");
+  if (bt_stride < 1) return fail(MLA_ERR_INVALID_ARG, "bt_stride must be >= 1");
+  if (page_rows < 32 || page_rows > 65536 || (page_rows & (page_rows - 1)) != 0)
+    return fail(MLA_ERR_INVALID_ARG, "page_rows must be a power of two from 32 to 65536");
+  if (total_pages < 1 || total_pages > ((int64_t)1 << 40)) return fail(MLA_ERR_INVALID_ARG, "total_pages out of range");
+  int shift = 0;
+  while ((1 << shift) < page_rows) ++shift;
+  *cm = CacheMap{nullptr, block_table, total_pages * page_rows, total_pages, bt_stride, shift};
+  return MLA_OK;
+}
+
 mla_status check_rope_args(const mla_dims* dims, const void* q_rope, const void* c_kv_new, const void* k_rope_new,
-                           const int32_t* positions, const int64_t* row_offsets, int64_t total_rows, void* q_lat,
-                           void* kv_cache) {
+                           const int32_t* positions, void* q_lat, void* kv_cache) {
   mla_status st = check_dims_impl(dims);
   if (st != MLA_OK) return st;
-  if (positions == nullptr || row_offsets == nullptr) return fail(MLA_ERR_INVALID_ARG, "positions/row_offsets NULL");
+  if (positions == nullptr) return fail(MLA_ERR_INVALID_ARG, "positions NULL");
   if ((st = check_ptrs({q_rope, c_kv_new, k_rope_new, q_lat, kv_cache})) != MLA_OK) return st;
-  if (total_rows < 1) return fail(MLA_ERR_INVALID_ARG, "total_rows must be >= 1");
   if (dims->d_rope > 2 * kMaxRopePairs) return fail(MLA_ERR_UNSUPPORTED, "d_rope above 64");  // 16 heads x d_rope/2 pairs per block
   if (dims->rank > 1024) return fail(MLA_ERR_UNSUPPORTED, "rank above 1024");  // c_kv_new values per thread
+  return MLA_OK;
+}
+
+mla_status packed_map(const int64_t* row_offsets, int64_t total_rows, CacheMap* cm) {
+  if (row_offsets == nullptr) return fail(MLA_ERR_INVALID_ARG, "row_offsets NULL");
+  if (total_rows < 1) return fail(MLA_ERR_INVALID_ARG, "total_rows must be >= 1");
+  *cm = CacheMap{row_offsets, nullptr, total_rows, 0, 0, 0};
   return MLA_OK;
 }
 
@@ -2039,6 +2114,48 @@ RopeFreqs rope_freqs(const mla_dims* dims) {
   return freqs;
 }
 
+mla_status rope_append_impl(const mla_dims* dims, const void* q_rope, const void* c_kv_new, const void* k_rope_new,
+                            const int32_t* positions, const CacheMap& cm, void* q_lat, void* kv_cache,
+                            void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  const RopeFreqs freqs = rope_freqs(dims);
+  const int blocks = dims->batch * ((dims->heads + 15) / 16);
+  if (dims->dtype == MLA_BF16) {
+    hipLaunchKernelGGL((rope_append_kernel<u16>), dim3(blocks), dim3(256), 0, s, (const u16*)q_rope,
+                       (const u16*)c_kv_new, (const u16*)k_rope_new, positions, cm, dims->heads, dims->rank,
+                       dims->d_rope, freqs, (u16*)q_lat, (u16*)kv_cache);
+  } else {
+    hipLaunchKernelGGL((rope_append_kernel<float>), dim3(blocks), dim3(256), 0, s, (const float*)q_rope,
+                       (const float*)c_kv_new, (const float*)k_rope_new, positions, cm, dims->heads, dims->rank,
+                       dims->d_rope, freqs, (float*)q_lat, (float*)kv_cache);
+  }
+  return launch_result(cm.block_table != nullptr ? "mla_rope_append_paged" : "mla_rope_append");
+}
+
+mla_status absorb_rope_impl(const mla_dims* dims, const void* q_nope, const void* w_uk, const void* q_rope,
+                            const void* c_kv_new, const void* k_rope_new, const int32_t* positions,
+                            const CacheMap& cm, void* q_lat, void* kv_cache, void* stream) {
+  mla_status st;
+  if ((st = check_ptrs({q_nope, w_uk})) != MLA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (find_inst(*dims) != kBf16H128R512D64) {  // fp32: the two launches, in order
+    if ((st = mla_absorb_q(dims, q_nope, w_uk, q_lat, stream)) != MLA_OK) return st;
+    return rope_append_impl(dims, q_rope, c_kv_new, k_rope_new, positions, cm, q_lat, kv_cache, stream);
+  }
+  const RopeFreqs freqs = rope_freqs(dims);
+  switch (dims->d_head) {
+    case 32: return launch_absorb_rope_bf16<32>(*dims, q_nope, w_uk, q_rope, c_kv_new, k_rope_new, positions, cm,
+                                                freqs, q_lat, kv_cache, s);
+    case 64: return launch_absorb_rope_bf16<64>(*dims, q_nope, w_uk, q_rope, c_kv_new, k_rope_new, positions, cm,
+                                                freqs, q_lat, kv_cache, s);
+    case 128: return launch_absorb_rope_bf16<128>(*dims, q_nope, w_uk, q_rope, c_kv_new, k_rope_new, positions, cm,
+                                                  freqs, q_lat, kv_cache, s);
+    case 256: return launch_absorb_rope_bf16<256>(*dims, q_nope, w_uk, q_rope, c_kv_new, k_rope_new, positions, cm,
+                                                  freqs, q_lat, kv_cache, s);
+  }
+  return fail(MLA_ERR_UNSUPPORTED, "d_head");
+}
+
 }  // namespace
 
 extern "C" {
@@ -2046,78 +2163,110 @@ extern "C" {
 mla_status mla_rope_append(const mla_dims* dims, const void* q_rope, const void* c_kv_new, const void* k_rope_new,
                            const int32_t* positions, const int64_t* row_offsets, int64_t total_rows, void* q_lat,
                            void* kv_cache, void* stream) {
-  mla_status st = check_rope_args(dims, q_rope, c_kv_new, k_rope_new, positions, row_offsets, total_rows, q_lat,
-                                  kv_cache);
+  mla_status st = check_rope_args(dims, q_rope, c_kv_new, k_rope_new, positions, q_lat, kv_cache);
   if (st != MLA_OK) return st;
+  CacheMap cm;
+  if ((st = packed_map(row_offsets, total_rows, &cm)) != MLA_OK) return st;
   g_last_error.clear();
-  hipStream_t s = (hipStream_t)stream;
-  const RopeFreqs freqs = rope_freqs(dims);
-  const int blocks = dims->batch * ((dims->heads + 15) / 16);
-  if (dims->dtype == MLA_BF16) {
-    hipLaunchKernelGGL((rope_append_kernel<u16>), dim3(blocks), dim3(256), 0, s, (const u16*)q_rope,
-                       (const u16*)c_kv_new, (const u16*)k_rope_new, positions, row_offsets, total_rows,
-                       dims->heads, dims->rank, dims->d_rope, freqs, (u16*)q_lat, (u16*)kv_cache);
-  } else {
-    hipLaunchKernelGGL((rope_append_kernel<float>), dim3(blocks), dim3(256), 0, s, (const float*)q_rope,
-                       (const float*)c_kv_new, (const float*)k_rope_new, positions, row_offsets, total_rows,
-                       dims->heads, dims->rank, dims->d_rope, freqs, (float*)q_lat, (float*)kv_cache);
-  }
-  return launch_result("mla_rope_append");
+  return rope_append_impl(dims, q_rope, c_kv_new, k_rope_new, positions, cm, q_lat, kv_cache, stream);
+}
+
+mla_status mla_rope_append_paged(const mla_dims* dims, const void* q_rope, const void* c_kv_new,
+                                 const void* k_rope_new, const int32_t* positions, const int32_t* block_table,
+                                 int32_t bt_stride, int32_t page_rows, int64_t total_pages, void* q_lat,
+                                 void* kv_cache, void* stream) {
+  mla_status st = check_rope_args(dims, q_rope, c_kv_new, k_rope_new, positions, q_lat, kv_cache);
+  if (st != MLA_OK) return st;
+  CacheMap cm;
+  if ((st = paged_map(block_table, bt_stride, page_rows, total_pages, &cm)) != MLA_OK) return st;
+  g_last_error.clear();
+  return rope_append_impl(dims, q_rope, c_kv_new, k_rope_new, positions, cm, q_lat, kv_cache, stream);
 }
 
 mla_status mla_absorb_rope(const mla_dims* dims, const void* q_nope, const void* w_uk, const void* q_rope,
                            const void* c_kv_new, const void* k_rope_new, const int32_t* positions,
                            const int64_t* row_offsets, int64_t total_rows, void* q_lat, void* kv_cache,
                            void* stream) {
-  mla_status st = check_rope_args(dims, q_rope, c_kv_new, k_rope_new, positions, row_offsets, total_rows, q_lat,
-                                  kv_cache);
+  mla_status st = check_rope_args(dims, q_rope, c_kv_new, k_rope_new, positions, q_lat, kv_cache);
   if (st != MLA_OK) return st;
-  if ((st = check_ptrs({q_nope, w_uk})) != MLA_OK) return st;
+  CacheMap cm;
+  if ((st = packed_map(row_offsets, total_rows, &cm)) != MLA_OK) return st;
   g_last_error.clear();
-  hipStream_t s = (hipStream_t)stream;
-  if (find_inst(*dims) != kBf16H128R512D64) {  // fp32: the two launches, in order
-    if ((st = mla_absorb_q(dims, q_nope, w_uk, q_lat, stream)) != MLA_OK) return st;
-    return mla_rope_append(dims, q_rope, c_kv_new, k_rope_new, positions, row_offsets, total_rows, q_lat, kv_cache,
-                           stream);
-  }
-  const RopeFreqs freqs = rope_freqs(dims);
-  switch (dims->d_head) {
-    case 32: return launch_absorb_rope_bf16<32>(*dims, q_nope, w_uk, q_rope, c_kv_new, k_rope_new, positions,
-                                                row_offsets, total_rows, freqs, q_lat, kv_cache, s);
-    case 64: return launch_absorb_rope_bf16<64>(*dims, q_nope, w_uk, q_rope, c_kv_new, k_rope_new, positions,
-                                                row_offsets, total_rows, freqs, q_lat, kv_cache, s);
-    case 128: return launch_absorb_rope_bf16<128>(*dims, q_nope, w_uk, q_rope, c_kv_new, k_rope_new, positions,
-                                                  row_offsets, total_rows, freqs, q_lat, kv_cache, s);
-    case 256: return launch_absorb_rope_bf16<256>(*dims, q_nope, w_uk, q_rope, c_kv_new, k_rope_new, positions,
-                                                  row_offsets, total_rows, freqs, q_lat, kv_cache, s);
-  }
-  return fail(MLA_ERR_UNSUPPORTED, "d_head");
+  return absorb_rope_impl(dims, q_nope, w_uk, q_rope, c_kv_new, k_rope_new, positions, cm, q_lat, kv_cache, stream);
 }
+
+mla_status mla_absorb_rope_paged(const mla_dims* dims, const void* q_nope, const void* w_uk, const void* q_rope,
+                                 const void* c_kv_new, const void* k_rope_new, const int32_t* positions,
+                                 const int32_t* block_table, int32_t bt_stride, int32_t page_rows,
+                                 int64_t total_pages, void* q_lat, void* kv_cache, void* stream) {
+  mla_status st = check_rope_args(dims, q_rope, c_kv_new, k_rope_new, positions, q_lat, kv_cache);
+  if (st != MLA_OK) return st;
+  CacheMap cm;
+  if ((st = paged_map(block_table, bt_stride, page_rows, total_pages, &cm)) != MLA_OK) return st;
+  g_last_error.clear();
+  return absorb_rope_impl(dims, q_nope, w_uk, q_rope, c_kv_new, k_rope_new, positions, cm, q_lat, kv_cache, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+mla_status decode_dispatch(const mla_dims* dims, const void* q_lat, const void* kv_cache, const CacheMap& cm,
+                           const int32_t* seq_lens, int32_t max_seq_len, int32_t num_splits, void* o_part,
+                           float* lse_part, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  switch (find_inst(*dims)) {
+    case kF32H8R64D16:
+      return launch_decode<float, 8, 64, 16, 1>(*dims, q_lat, kv_cache, cm, seq_lens, max_seq_len, num_splits,
+                                                o_part, lse_part, s);
+    case kF32H16R64D32:
+      return launch_decode<float, 16, 64, 32, 1>(*dims, q_lat, kv_cache, cm, seq_lens, max_seq_len, num_splits,
+                                                 o_part, lse_part, s);
+    case kBf16H128R512D64:
+      return launch_decode<u16, 128, 512, 64, 4>(*dims, q_lat, kv_cache, cm, seq_lens, max_seq_len, num_splits,
+                                                 o_part, lse_part, s);
+  }
+  return fail(MLA_ERR_UNSUPPORTED, "no instantiation");
+}
+
+mla_status check_decode_args(const mla_dims* dims, const void* q_lat, const void* kv_cache, const int32_t* seq_lens,
+                             int32_t max_seq_len, int32_t num_splits, void* o_part, float* lse_part) {
+  mla_status st = check_dims_impl(dims);
+  if (st != MLA_OK) return st;
+  if (seq_lens == nullptr) return fail(MLA_ERR_INVALID_ARG, "seq_lens NULL");
+  if ((st = check_ptrs({q_lat, kv_cache, o_part, lse_part})) != MLA_OK) return st;
+  if (max_seq_len < 1) return fail(MLA_ERR_INVALID_ARG, "max_seq_len must be >= 1");
+  if (num_splits < 1) return fail(MLA_ERR_INVALID_ARG, "num_splits must be >= 1");
+  if (num_splits > kMaxSplits) return fail(MLA_ERR_WORKSPACE, "num_splits above 4096");
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
 
 mla_status mla_decode_latent(const mla_dims* dims, const void* q_lat, const void* kv_cache, const int64_t* row_offsets,
                              const int32_t* seq_lens, int64_t total_rows, int32_t max_seq_len, int32_t num_splits,
                              void* o_part, float* lse_part, void* stream) {
-  mla_status st = check_dims_impl(dims);
+  mla_status st = check_decode_args(dims, q_lat, kv_cache, seq_lens, max_seq_len, num_splits, o_part, lse_part);
   if (st != MLA_OK) return st;
-  if (row_offsets == nullptr || seq_lens == nullptr) return fail(MLA_ERR_INVALID_ARG, "row_offsets/seq_lens NULL");
-  if ((st = check_ptrs({q_lat, kv_cache, o_part, lse_part})) != MLA_OK) return st;
-  if (total_rows < 1 || max_seq_len < 1) return fail(MLA_ERR_INVALID_ARG, "total_rows and max_seq_len must be >= 1");
-  if (num_splits < 1) return fail(MLA_ERR_INVALID_ARG, "num_splits must be >= 1");
-  if (num_splits > kMaxSplits) return fail(MLA_ERR_WORKSPACE, "num_splits above 4096");
+  if (row_offsets == nullptr) return fail(MLA_ERR_INVALID_ARG, "row_offsets NULL");
+  if (total_rows < 1) return fail(MLA_ERR_INVALID_ARG, "total_rows must be >= 1");
   g_last_error.clear();
-  hipStream_t s = (hipStream_t)stream;
-  switch (find_inst(*dims)) {
-    case kF32H8R64D16:
-      return launch_decode<float, 8, 64, 16, 1>(*dims, q_lat, kv_cache, row_offsets, seq_lens, total_rows,
-                                                max_seq_len, num_splits, o_part, lse_part, s);
-    case kF32H16R64D32:
-      return launch_decode<float, 16, 64, 32, 1>(*dims, q_lat, kv_cache, row_offsets, seq_lens, total_rows,
-                                                 max_seq_len, num_splits, o_part, lse_part, s);
-    case kBf16H128R512D64:
-      return launch_decode<u16, 128, 512, 64, 4>(*dims, q_lat, kv_cache, row_offsets, seq_lens, total_rows,
-                                                 max_seq_len, num_splits, o_part, lse_part, s);
-  }
-  return fail(MLA_ERR_UNSUPPORTED, "no instantiation");
+  const CacheMap cm{row_offsets, nullptr, total_rows, 0, 0, 0};
+  return decode_dispatch(dims, q_lat, kv_cache, cm, seq_lens, max_seq_len, num_splits, o_part, lse_part, stream);
+}
+
+mla_status mla_decode_latent_paged(const mla_dims* dims, const void* q_lat, const void* kv_cache,
+                                   const int32_t* block_table, int32_t bt_stride, int32_t page_rows,
+                                   int64_t total_pages, const int32_t* seq_lens, int32_t max_seq_len,
+                                   int32_t num_splits, void* o_part, float* lse_part, void* stream) {
+  mla_status st = check_decode_args(dims, q_lat, kv_cache, seq_lens, max_seq_len, num_splits, o_part, lse_part);
+  if (st != MLA_OK) return st;
+  CacheMap cm;
+  if ((st = paged_map(block_table, bt_stride, page_rows, total_pages, &cm)) != MLA_OK) return st;
+  g_last_error.clear();
+  return decode_dispatch(dims, q_lat, kv_cache, cm, seq_lens, max_seq_len, num_splits, o_part, lse_part, stream);
 }
 
 mla_status mla_combine(const mla_dims* dims, const void* o_part, const float* lse_part, int32_t num_splits,

@@ -21,7 +21,8 @@ STATUS = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARG", 2: "MLA_ERR_UNSUPPORTED", 3: "M
           4: "MLA_ERR_WORKSPACE", 5: "MLA_ERR_HIP"}
 
 EXPORTS = ("mla_absorb_q", "mla_rope_append", "mla_decode_latent", "mla_combine", "mla_up_v",
-           "mla_combine_up_v", "mla_absorb_rope", "mla_partials_size", "mla_plan_splits", "mla_check_dims", "mla_status_string", "mla_last_error")
+           "mla_combine_up_v", "mla_absorb_rope", "mla_decode_latent_paged", "mla_rope_append_paged",
+           "mla_absorb_rope_paged", "mla_partials_size", "mla_plan_splits", "mla_check_dims", "mla_status_string", "mla_last_error")
 
 
 class MlaDims(ctypes.Structure):
@@ -57,6 +58,9 @@ def lib() -> ctypes.CDLL:
             "mla_up_v": (i32, [D, P, P, P, P]),
             "mla_combine_up_v": (i32, [D, P, P, i32, P, P, P, P]),
             "mla_absorb_rope": (i32, [D, P, P, P, P, P, P, P, i64, P, P, P]),
+            "mla_decode_latent_paged": (i32, [D, P, P, P, i32, i32, i64, P, i32, i32, P, P, P]),
+            "mla_rope_append_paged": (i32, [D, P, P, P, P, P, i32, i32, i64, P, P, P]),
+            "mla_absorb_rope_paged": (i32, [D, P, P, P, P, P, P, P, i32, i32, i64, P, P, P]),
             "mla_partials_size": (i32, [D, i32, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]),
             "mla_plan_splits": (i32, [D, i32, i64, i32]),
             "mla_check_dims": (i32, [D]),
@@ -121,6 +125,27 @@ def mla_decode_latent(dims, q_lat, kv_cache, row_offsets, seq_lens, total_rows, 
     _check("mla_decode_latent", lib().mla_decode_latent(
         ctypes.byref(dims), _p(q_lat), _p(kv_cache), _p(row_offsets), _p(seq_lens), int(total_rows),
         int(max_seq_len), int(num_splits), _p(o_part), _p(lse_part), _s(stream)))
+
+
+def mla_decode_latent_paged(dims, q_lat, kv_cache, block_table, bt_stride, page_rows, total_pages, seq_lens,
+                            max_seq_len, num_splits, o_part, lse_part, stream=None):
+    _check("mla_decode_latent_paged", lib().mla_decode_latent_paged(
+        ctypes.byref(dims), _p(q_lat), _p(kv_cache), _p(block_table), int(bt_stride), int(page_rows),
+        int(total_pages), _p(seq_lens), int(max_seq_len), int(num_splits), _p(o_part), _p(lse_part), _s(stream)))
+
+
+def mla_rope_append_paged(dims, q_rope, c_kv_new, k_rope_new, positions, block_table, bt_stride, page_rows,
+                          total_pages, q_lat, kv_cache, stream=None):
+    _check("mla_rope_append_paged", lib().mla_rope_append_paged(
+        ctypes.byref(dims), _p(q_rope), _p(c_kv_new), _p(k_rope_new), _p(positions), _p(block_table),
+        int(bt_stride), int(page_rows), int(total_pages), _p(q_lat), _p(kv_cache), _s(stream)))
+
+
+def mla_absorb_rope_paged(dims, q_nope, w_uk, q_rope, c_kv_new, k_rope_new, positions, block_table, bt_stride,
+                          page_rows, total_pages, q_lat, kv_cache, stream=None):
+    _check("mla_absorb_rope_paged", lib().mla_absorb_rope_paged(
+        ctypes.byref(dims), _p(q_nope), _p(w_uk), _p(q_rope), _p(c_kv_new), _p(k_rope_new), _p(positions),
+        _p(block_table), int(bt_stride), int(page_rows), int(total_pages), _p(q_lat), _p(kv_cache), _s(stream)))
 
 
 def mla_combine(dims, o_part, lse_part, num_splits, o_lat, lse=None, stream=None):

@@ -9,7 +9,7 @@ import numpy as np
 import torch
 
 from . import mla
-from .synthetic import BF16, StepInputs
+from .synthetic import BF16, PagedCache, StepInputs, paginate
 
 
 def _dev(a: np.ndarray, device) -> torch.Tensor:
@@ -33,11 +33,13 @@ class DeviceStep:
     separate calls stay available."""
 
     def __init__(self, inp: StepInputs, num_splits: int | None = None, device: str = "cuda:0",
-                 weights: "DeviceStep | None" = None, scratch: "DeviceStep | None" = None):
+                 weights: "DeviceStep | None" = None, scratch: "DeviceStep | None" = None,
+                 page_rows: int | None = None, page_seed: int = 0):
         """``weights``: share W_UK/W_UV with another step (same layer).
         ``scratch``: share the per-step temporaries (q_lat, split partials,
         o_lat, lse, out) with another step of the same shape, as successive
-        layers of one decode step would."""
+        layers of one decode step would.  ``page_rows``: keep the cache in
+        pages of that many rows behind a block table (the paged calls)."""
         self.inp = inp
         self.device = device
         self.dims = mla.make_dims(inp.B, inp.H, inp.d_head, inp.d_v, inp.r, inp.d_rope,
@@ -51,7 +53,13 @@ class DeviceStep:
             self.w_uk, self.w_uv = weights.w_uk, weights.w_uv
         self.q_nope = _dev(inp.q_nope, device)
         self.q_rope = _dev(inp.q_rope, device)
-        self.kv_cache = _dev(inp.kv_cache, device)
+        self.paged: PagedCache | None = None
+        if page_rows is None:
+            self.kv_cache = _dev(inp.kv_cache, device)
+        else:
+            self.paged = paginate(inp, page_rows, seed=page_seed)
+            self.kv_cache = _dev(self.paged.cache, device)
+            self.block_table = _dev(self.paged.block_table, device)
         self.c_kv_new = _dev(inp.c_kv_new, device)
         self.k_rope_new = _dev(inp.k_rope_new, device)
         self.positions = _dev(inp.positions.astype(np.int32), device)
@@ -80,15 +88,32 @@ class DeviceStep:
     def absorb_q(self, stream=None):
         mla.mla_absorb_q(self.dims, self.q_nope, self.w_uk, self.q_lat, stream)
 
+    def _pages(self):
+        pc = self.paged
+        return self.block_table, pc.bt_stride, pc.page_rows, pc.total_pages
+
     def rope_append(self, stream=None):
+        if self.paged is not None:
+            mla.mla_rope_append_paged(self.dims, self.q_rope, self.c_kv_new, self.k_rope_new, self.positions,
+                                      *self._pages(), self.q_lat, self.kv_cache, stream)
+            return
         mla.mla_rope_append(self.dims, self.q_rope, self.c_kv_new, self.k_rope_new, self.positions,
                             self.row_offsets, self.inp.total_rows, self.q_lat, self.kv_cache, stream)
 
     def absorb_rope(self, stream=None):
+        if self.paged is not None:
+            mla.mla_absorb_rope_paged(self.dims, self.q_nope, self.w_uk, self.q_rope, self.c_kv_new,
+                                      self.k_rope_new, self.positions, *self._pages(), self.q_lat, self.kv_cache,
+                                      stream)
+            return
         mla.mla_absorb_rope(self.dims, self.q_nope, self.w_uk, self.q_rope, self.c_kv_new, self.k_rope_new,
                             self.positions, self.row_offsets, self.inp.total_rows, self.q_lat, self.kv_cache, stream)
 
     def decode_latent(self, stream=None):
+        if self.paged is not None:
+            mla.mla_decode_latent_paged(self.dims, self.q_lat, self.kv_cache, *self._pages(), self.seq_lens,
+                                        self.inp.max_seq_len, self.num_splits, self.o_part, self.lse_part, stream)
+            return
         mla.mla_decode_latent(self.dims, self.q_lat, self.kv_cache, self.row_offsets, self.seq_lens,
                               self.inp.total_rows, self.inp.max_seq_len, self.num_splits, self.o_part,
                               self.lse_part, stream)
@@ -131,5 +156,15 @@ class DeviceStep:
         return bits_to_f64(self.kv_cache, self.inp.dtype)
 
     def cache_raw(self) -> np.ndarray:
+        """The cache in storage form, in the packed order (a paged cache is
+        gathered back through its block table)."""
         a = self.kv_cache.cpu().numpy()
-        return a.view(np.uint16) if self.inp.dtype == BF16 else a
+        a = a.view(np.uint16) if self.inp.dtype == BF16 else a
+        if self.paged is None:
+            return a
+        out = self.inp.kv_cache.copy()
+        for b in range(self.inp.B):
+            n = int(self.inp.lens[b]) + 1
+            o = int(self.inp.row_offsets[b])
+            out[o:o + n] = a[self.paged.rows_of(b, n)]
+        return out

@@ -224,3 +224,55 @@ def make_inputs(name: str, seed: int | None = None, **override) -> StepInputs:
         q_nope=_store(q_nope, dtype), q_rope=_store(q_rope, dtype),
         kv_cache=cache, c_kv_new=_store(c_new, dtype), k_rope_new=_store(k_new, dtype),
     )
+
+
+@dataclasses.dataclass
+class PagedCache:
+    """The same cache rows laid out in pages: row t of sequence b is row
+    t % page_rows of page block_table[b, t // page_rows]."""
+
+    page_rows: int
+    block_table: np.ndarray   # [B, bt_stride] int32 physical page ids
+    cache: np.ndarray         # [total_pages * page_rows, r + d_rope], storage form
+
+    @property
+    def bt_stride(self) -> int:
+        return int(self.block_table.shape[1])
+
+    @property
+    def total_pages(self) -> int:
+        return self.cache.shape[0] // self.page_rows
+
+    def rows_of(self, b: int, n: int) -> np.ndarray:
+        """Physical cache rows of the first n in-sequence rows of sequence b."""
+        t = np.arange(n)
+        return self.block_table[b, t // self.page_rows].astype(np.int64) * self.page_rows + t % self.page_rows
+
+
+def paginate(step: StepInputs, page_rows: int, seed: int = 0, spare_pages: int = 3) -> PagedCache:
+    """Scatter the packed cache of ``step`` into pages of ``page_rows`` rows,
+    page ids shuffled with a seeded permutation (so the pages of different
+    sequences interleave), each sequence given the pages for its L_b + 1 rows
+    (the appended row included).  Unused page rows and the ``spare_pages``
+    never referenced hold NaN, so that a read through a wrong page cannot
+    pass."""
+    rng = np.random.default_rng(seed)
+    need = [(int(L) + 1 + page_rows - 1) // page_rows for L in step.lens]
+    bt_stride = max(need) + 1
+    total_pages = sum(need) + spare_pages
+    perm = rng.permutation(total_pages).astype(np.int32)
+    nan = np.uint16(0x7FC0) if step.dtype == BF16 else np.float32(np.nan)
+    cache = np.full((total_pages * page_rows, step.W), nan, dtype=step.kv_cache.dtype)
+    block_table = np.full((step.B, bt_stride), -1, dtype=np.int32)
+    k = 0
+    for b in range(step.B):
+        block_table[b, :need[b]] = perm[k:k + need[b]]
+        k += need[b]
+    paged = PagedCache(page_rows, block_table, cache)
+    for b in range(step.B):
+        n = int(step.lens[b]) + 1
+        src = int(step.row_offsets[b])
+        cache[paged.rows_of(b, n)] = step.kv_cache[src:src + n]
+    # unused entries point at a spare page (in range, never read for valid rows)
+    block_table[block_table < 0] = perm[-1]
+    return paged

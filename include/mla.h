@@ -15,6 +15,8 @@
  *   mla_up_v          out = W_UV o_lat per head
  *   mla_absorb_rope   mla_absorb_q and mla_rope_append in one call (one launch
  *                     for bf16)
+ *   mla_*_paged       the calls that touch the cache, for a cache kept in
+ *                     fixed-size pages behind a block table
  *   mla_combine_up_v  the last two in one call: the merge is formed where
  *                     W_UV consumes it and o_lat never goes to memory
  *
@@ -185,6 +187,31 @@ mla_status mla_up_v(const mla_dims* dims, const float* o_lat, const void* w_uv, 
 mla_status mla_combine_up_v(const mla_dims* dims, const void* o_part, const float* lse_part,
                             int32_t num_splits, const void* w_uv, float* out, float* lse,
                             void* stream);
+
+/* Paged cache ([P2] mentions vLLM-style page management for variable-length
+ * batches; this is the plainest form of it).  The cache is total_pages pages
+ * of page_rows rows (a power of two from 32 to 65536), row layout as above;
+ * in-sequence row t of sequence b is row t % page_rows of page
+ * block_table[b * bt_stride + t / page_rows] (int32 page ids, bt_stride >= 1
+ * entries per sequence).  The paging changes where rows live, not what is
+ * computed: each call below gives the same result as its packed counterpart
+ * on the same rows.  Page ids and page indices are clamped into range on the
+ * device (wrong numbers, never a stray access, for inconsistent tables). */
+mla_status mla_decode_latent_paged(const mla_dims* dims, const void* q_lat, const void* kv_cache,
+                                   const int32_t* block_table, int32_t bt_stride, int32_t page_rows,
+                                   int64_t total_pages, const int32_t* seq_lens, int32_t max_seq_len,
+                                   int32_t num_splits, void* o_part, float* lse_part, void* stream);
+
+mla_status mla_rope_append_paged(const mla_dims* dims, const void* q_rope, const void* c_kv_new,
+                                 const void* k_rope_new, const int32_t* positions,
+                                 const int32_t* block_table, int32_t bt_stride, int32_t page_rows,
+                                 int64_t total_pages, void* q_lat, void* kv_cache, void* stream);
+
+mla_status mla_absorb_rope_paged(const mla_dims* dims, const void* q_nope, const void* w_uk,
+                                 const void* q_rope, const void* c_kv_new, const void* k_rope_new,
+                                 const int32_t* positions, const int32_t* block_table,
+                                 int32_t bt_stride, int32_t page_rows, int64_t total_pages,
+                                 void* q_lat, void* kv_cache, void* stream);
 
 /* Bytes of o_part and lse_part for `num_splits` splits. */
 mla_status mla_partials_size(const mla_dims* dims, int32_t num_splits, size_t* o_part_bytes,

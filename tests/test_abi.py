@@ -167,3 +167,51 @@ def test_plan_splits_prefers_one_round_over_finer_splits():
     chunk = -(-(-(-4097 // s)) // 32) * 32
     assert 16 * -(-4097 // chunk) <= 256
     assert s >= 8
+
+
+def test_paged_argument_checks():
+    """Host-side checks of the paged calls: page size a power of two from 32
+    to 65536, a block table, at least one page and one entry per sequence."""
+    d = dsv2()
+    ok = dict(bt=P16, stride=4, page=64, pages=10)
+
+    def dec(bt=ok["bt"], stride=ok["stride"], page=ok["page"], pages=ok["pages"]):
+        mla.mla_decode_latent_paged(d, P16, P16, bt, stride, page, pages, P16, 100, 2, P16, P16, 0)
+
+    def rope(bt=ok["bt"], stride=ok["stride"], page=ok["page"], pages=ok["pages"]):
+        mla.mla_rope_append_paged(d, P16, P16, P16, P16, bt, stride, page, pages, P16, P16, 0)
+
+    def absorb(bt=ok["bt"], stride=ok["stride"], page=ok["page"], pages=ok["pages"]):
+        mla.mla_absorb_rope_paged(d, P16, P16, P16, P16, P16, P16, bt, stride, page, pages, P16, P16, 0)
+
+    for fn in (dec, rope, absorb):
+        for bad in (dict(bt=0), dict(stride=0), dict(page=16), dict(page=96), dict(page=1 << 17), dict(pages=0)):
+            _expect(1, lambda: fn(**bad))
+    _expect(1, mla.mla_decode_latent_paged, d, P16, P16, P16, 4, 64, 10, 0, 100, 2, P16, P16, 0)   # seq_lens NULL
+    _expect(4, mla.mla_decode_latent_paged, d, P16, P16, P16, 4, 64, 10, P16, 100, 4097, P16, P16, 0)
+    _expect(3, mla.mla_decode_latent_paged, d, P16, P16 + 8, P16, 4, 64, 10, P16, 100, 2, P16, P16, 0)
+
+
+def test_paginate_layout():
+    """The paged layout helper: every sequence's rows land on distinct pages of
+    its own, the gather through the block table gives the packed rows back,
+    and the rest of the paged cache is NaN."""
+    import numpy as np
+    from head_latent_attention_12_amd import synthetic as syn
+    inp = syn.make_inputs("small", lens=[0, 31, 32, 100, 64])
+    pc = syn.paginate(inp, 32, seed=3)
+    used = set()
+    for b in range(inp.B):
+        n = int(inp.lens[b]) + 1
+        pages = set(int(p) for p in pc.block_table[b, :(n + 31) // 32])
+        assert not (pages & used)
+        used |= pages
+        o = int(inp.row_offsets[b])
+        rows = pc.cache[pc.rows_of(b, n)]
+        same = (rows == inp.kv_cache[o:o + n]) | (np.isnan(rows) & np.isnan(inp.kv_cache[o:o + n]))
+        assert same.all()
+    mask = np.ones(pc.cache.shape[0], bool)
+    for b in range(inp.B):
+        mask[pc.rows_of(b, int(inp.lens[b]) + 1)] = False
+    assert np.isnan(pc.cache[mask]).all()
+    assert pc.block_table.min() >= 0 and pc.block_table.max() < pc.total_pages

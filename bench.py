@@ -172,6 +172,42 @@ def cpu_baseline(inp, budget_s: float):
                       f"sequences ({done_rows} attended rows) in {dt:.1f} s"}
 
 
+def run_kv_down(B=16, d_model=5120, launches=50):
+    """Latent KV production from the hidden state at the DeepSeek-V2 shape:
+    back-to-back launches between one pair of HIP events, over 8 weight sets
+    (5.9 MB each) so that they do not sit in the Infinity Cache together."""
+    import torch
+
+    from head_latent_attention_12_amd import mla, synthetic as syn
+    from head_latent_attention_12_amd.step import _dev
+
+    kin = syn.make_kv_down_inputs(B, d_model)
+    dims = mla.make_dims(B, 128, 128, 128, kin.r, kin.d_rope, mla.MLA_BF16)
+    n_sets = 8
+    ws = [{k: _dev(getattr(kin, k), "cuda") for k in ("h", "w_dkv", "w_kr", "norm_w")} for _ in range(n_sets)]
+    work = torch.empty(mla.mla_kv_down_workspace_size(dims, d_model) // 4, dtype=torch.float32, device="cuda")
+    c = torch.empty((B, kin.r), dtype=torch.int16, device="cuda")
+    k = torch.empty((B, kin.d_rope), dtype=torch.int16, device="cuda")
+    call = lambda w: mla.mla_kv_down(dims, d_model, w["h"], w["w_dkv"], w["w_kr"], w["norm_w"], kin.eps, work, c, k)
+    for i in range(10):
+        call(ws[i % n_sets])
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(launches):
+        call(ws[i % n_sets])
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / launches
+    nbytes = (kin.r + kin.d_rope) * d_model * 2 + B * d_model * 2 + B * (kin.r + kin.d_rope) * 2
+    print(f"# kv_down B={B} d_model={d_model}: {us:.2f} us per call (two launches), "
+          f"{nbytes / (us * 1e-6) / 1e9:.0f} GB/s of weights and activations", file=sys.stderr, flush=True)
+    return {"workload": f"latent KV production bf16 B={B} d_model={d_model} r={kin.r} d_rope={kin.d_rope}",
+            "us_per_call": round(us, 2), "algorithmic_bytes": nbytes,
+            "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "timing": "HIP events around back-to-back calls over 8 weight sets"}
+
+
 def capture_round(sets):
     """One HIP graph with one step of each input set, in order."""
     import torch
@@ -345,6 +381,7 @@ def main():
                              page_rows=page_rows)
             others[r["name"]] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items()
                                  if k not in ("inp", "k3_bytes", "k3_flops", "step_bytes", "step_flops")}
+        others["kv_down_dsv2"] = run_kv_down()
 
     inp = main_res["inp"]
     bf16 = inp.dtype == "bf16"

@@ -1795,6 +1795,98 @@ __global__ __launch_bounds__(64) void combine_up_v_f32_kernel(const float* __res
 }
 
 // ---------------------------------------------------------------------------
+// Latent KV production from the hidden state (the step before the path):
+// x = W_DKV h, c_kv_new = norm_w * x / sqrt(mean(x^2) + eps), k_rope_new =
+// W_KR h, for the R + DR = 576 output features of each sequence.  bf16.
+// Pass 1: one work-group per (32 features, 512 of the d_model inputs); wave
+// w takes 128 of the inputs (8 k-steps of the 32x32x16 MFMA, A = weight rows,
+// B = hidden-state rows, both straight from global memory, all loads issued
+// before the first MFMA), the four waves are summed through LDS, and the fp32
+// partial goes to the workspace [chunk][B][576].  Pass 2: one work-group per
+// sequence; a thread sums its features' chunks in order (deterministic, eight
+// loads in flight per feature), the sum of squares of the first R features
+// goes through LDS, and each output is rounded once after the RMSNorm.
+// ---------------------------------------------------------------------------
+
+constexpr int kKvChunk = 512;  // d_model inputs per pass-1 work-group
+
+__global__ __launch_bounds__(256) void kv_down_partial_kernel(const u16* __restrict__ h, const u16* __restrict__ w_dkv,
+                                                              const u16* __restrict__ w_kr, int B, int DM, int R,
+                                                              int DR, float* __restrict__ part) {
+  using M = Mma<u16>;
+  const int NF = R + DR;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hf = lane >> 5, l32 = lane & 31;
+  const int nfb = (NF + 31) / 32;
+  const int fb = (int)blockIdx.x % nfb, kc = (int)blockIdx.x / nfb;
+  const int f = fb * 32 + l32;  // this lane's A row (output feature)
+  const u16* wrow = f < R ? w_dkv + (int64_t)f * DM : w_kr + (int64_t)(min(f, NF - 1) - R) * DM;
+  const int kbase = kc * kKvChunk + wave * (kKvChunk / 4) + 8 * hf;
+  __shared__ f32x4 red[4][4][64];
+  i16x8 a[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) a[u] = *(const i16x8*)(wrow + kbase + 16 * u);
+  for (int b0 = 0; b0 < B; b0 += 32) {
+    const int bb = min(b0 + l32, B - 1);  // rows past B compute garbage columns that are not stored
+    i16x8 x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x[u] = *(const i16x8*)(h + (int64_t)bb * DM + kbase + 16 * u);
+    f32x16 acc = zero16();
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc = M::mma(a[u], x[u], acc);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) red[wave][q][lane] = f32x4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+    __syncthreads();
+    // wave w sums the four k-quarters of feature rows 8w + 4hf .. +3
+    const f32x4 sum = red[0][wave][lane] + red[1][wave][lane] + red[2][wave][lane] + red[3][wave][lane];
+    const int ff = fb * 32 + 8 * wave + 4 * hf;
+    if (b0 + l32 < B && ff < NF) *(f32x4*)(part + ((int64_t)kc * B + b0 + l32) * NF + ff) = sum;
+    __syncthreads();  // red is rewritten for the next batch block
+  }
+}
+
+__global__ __launch_bounds__(256) void kv_down_final_kernel(const float* __restrict__ part, int nchunks, int B, int R,
+                                                            int DR, const u16* __restrict__ norm_w, float eps,
+                                                            u16* __restrict__ c_kv_new, u16* __restrict__ k_rope_new) {
+  constexpr int FPT = 4, CG = 8;  // features per thread (R + DR <= 1024), chunk loads in flight per feature
+  const int NF = R + DR;
+  const int tid = (int)threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = (int)blockIdx.x;
+  __shared__ float wss[4];
+  float v[FPT] = {0.f, 0.f, 0.f, 0.f};
+  for (int c0 = 0; c0 < nchunks; c0 += CG) {
+    float x[FPT][CG];
+#pragma unroll
+    for (int j = 0; j < FPT; ++j)
+#pragma unroll
+      for (int u = 0; u < CG; ++u) {
+        const int f = min(tid + 256 * j, NF - 1), c = min(c0 + u, nchunks - 1);
+        x[j][u] = part[((int64_t)c * B + b) * NF + f];
+      }
+#pragma unroll
+    for (int j = 0; j < FPT; ++j)
+#pragma unroll
+      for (int u = 0; u < CG; ++u)
+        if (c0 + u < nchunks) v[j] += x[j][u];  // chunks in order
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < FPT; ++j)
+    if (tid + 256 * j < R) ss = fmaf(v[j], v[j], ss);
+  ss = wave_sum_f(ss);
+  if (lane == 0) wss[wave] = ss;
+  __syncthreads();
+  const float inv = 1.f / sqrtf((wss[0] + wss[1] + wss[2] + wss[3]) / (float)R + eps);
+#pragma unroll
+  for (int j = 0; j < FPT; ++j) {
+    const int f = tid + 256 * j;
+    if (f < R) c_kv_new[(int64_t)b * R + f] = f2bf(v[j] * inv * bf2f(norm_w[f]));
+    else if (f < NF) k_rope_new[(int64_t)b * DR + (f - R)] = f2bf(v[j]);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // K2: RoPE on q_rope and on the new token's shared key; append the new row.
 // One work-group per (sequence, block of HB heads: 16 in this kernel); the
 // work-group of head block 0 also writes the cache row.  Pair frequencies come from the host (in
@@ -2346,6 +2438,37 @@ mla_status mla_combine_up_v(const mla_dims* dims, const void* o_part, const floa
                        dims->rank, out, lse);
   }
   return launch_result("mla_combine_up_v");
+}
+
+mla_status mla_kv_down_workspace_size(const mla_dims* dims, int32_t d_model, size_t* bytes) {
+  mla_status st = check_dims_impl(dims);
+  if (st != MLA_OK) return st;
+  if (bytes == nullptr) return fail(MLA_ERR_INVALID_ARG, "bytes NULL");
+  if (d_model < kKvChunk || d_model % kKvChunk != 0) return fail(MLA_ERR_UNSUPPORTED, "d_model must be a multiple of 512");
+  *bytes = (size_t)(d_model / kKvChunk) * dims->batch * (dims->rank + dims->d_rope) * sizeof(float);
+  return MLA_OK;
+}
+
+mla_status mla_kv_down(const mla_dims* dims, int32_t d_model, const void* h, const void* w_dkv, const void* w_kr,
+                       const void* norm_w, float eps, void* workspace, void* c_kv_new, void* k_rope_new,
+                       void* stream) {
+  size_t ws = 0;
+  mla_status st = mla_kv_down_workspace_size(dims, d_model, &ws);
+  if (st != MLA_OK) return st;
+  if ((st = check_ptrs({h, w_dkv, w_kr, norm_w, workspace, c_kv_new, k_rope_new})) != MLA_OK) return st;
+  if (dims->dtype != MLA_BF16) return fail(MLA_ERR_UNSUPPORTED, "kv_down is built for bf16 storage");
+  if (dims->rank + dims->d_rope > 1024) return fail(MLA_ERR_UNSUPPORTED, "rank + d_rope above 1024");
+  if (!(eps >= 0.f)) return fail(MLA_ERR_INVALID_ARG, "eps must be >= 0");
+  g_last_error.clear();
+  hipStream_t s = (hipStream_t)stream;
+  const int nf = dims->rank + dims->d_rope, nchunks = d_model / kKvChunk;
+  hipLaunchKernelGGL(kv_down_partial_kernel, dim3(((nf + 31) / 32) * nchunks), dim3(256), 0, s, (const u16*)h,
+                     (const u16*)w_dkv, (const u16*)w_kr, dims->batch, d_model, dims->rank, dims->d_rope,
+                     (float*)workspace);
+  hipLaunchKernelGGL(kv_down_final_kernel, dim3(dims->batch), dim3(256), 0, s, (const float*)workspace, nchunks,
+                     dims->batch, dims->rank, dims->d_rope, (const u16*)norm_w, eps, (u16*)c_kv_new,
+                     (u16*)k_rope_new);
+  return launch_result("mla_kv_down");
 }
 
 mla_status mla_partials_size(const mla_dims* dims, int32_t num_splits, size_t* o_part_bytes, size_t* lse_part_bytes) {

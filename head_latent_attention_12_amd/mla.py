@@ -22,7 +22,7 @@ STATUS = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARG", 2: "MLA_ERR_UNSUPPORTED", 3: "M
 
 EXPORTS = ("mla_absorb_q", "mla_rope_append", "mla_decode_latent", "mla_combine", "mla_up_v",
            "mla_combine_up_v", "mla_absorb_rope", "mla_decode_latent_paged", "mla_rope_append_paged",
-           "mla_absorb_rope_paged", "mla_partials_size", "mla_plan_splits", "mla_check_dims", "mla_status_string", "mla_last_error")
+           "mla_absorb_rope_paged", "mla_kv_down", "mla_kv_down_workspace_size", "mla_partials_size", "mla_plan_splits", "mla_check_dims", "mla_status_string", "mla_last_error")
 
 
 class MlaDims(ctypes.Structure):
@@ -61,6 +61,8 @@ def lib() -> ctypes.CDLL:
             "mla_decode_latent_paged": (i32, [D, P, P, P, i32, i32, i64, P, i32, i32, P, P, P]),
             "mla_rope_append_paged": (i32, [D, P, P, P, P, P, i32, i32, i64, P, P, P]),
             "mla_absorb_rope_paged": (i32, [D, P, P, P, P, P, P, P, i32, i32, i64, P, P, P]),
+            "mla_kv_down": (i32, [D, i32, P, P, P, P, ctypes.c_float, P, P, P, P]),
+            "mla_kv_down_workspace_size": (i32, [D, i32, ctypes.POINTER(ctypes.c_size_t)]),
             "mla_partials_size": (i32, [D, i32, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]),
             "mla_plan_splits": (i32, [D, i32, i64, i32]),
             "mla_check_dims": (i32, [D]),
@@ -160,6 +162,18 @@ def mla_up_v(dims, o_lat, w_uv, out, stream=None):
 def mla_combine_up_v(dims, o_part, lse_part, num_splits, w_uv, out, lse=None, stream=None):
     _check("mla_combine_up_v", lib().mla_combine_up_v(ctypes.byref(dims), _p(o_part), _p(lse_part),
                                                       int(num_splits), _p(w_uv), _p(out), _p(lse), _s(stream)))
+
+
+def mla_kv_down_workspace_size(dims, d_model) -> int:
+    n = ctypes.c_size_t(0)
+    _check("mla_kv_down_workspace_size", lib().mla_kv_down_workspace_size(ctypes.byref(dims), int(d_model),
+                                                                          ctypes.byref(n)))
+    return n.value
+
+
+def mla_kv_down(dims, d_model, h, w_dkv, w_kr, norm_w, eps, workspace, c_kv_new, k_rope_new, stream=None):
+    _check("mla_kv_down", lib().mla_kv_down(ctypes.byref(dims), int(d_model), _p(h), _p(w_dkv), _p(w_kr), _p(norm_w),
+                                            float(eps), _p(workspace), _p(c_kv_new), _p(k_rope_new), _s(stream)))
 
 
 def mla_partials_size(dims, num_splits):

@@ -276,3 +276,35 @@ def paginate(step: StepInputs, page_rows: int, seed: int = 0, spare_pages: int =
     # unused entries point at a spare page (in range, never read for valid rows)
     block_table[block_table < 0] = perm[-1]
     return paged
+
+
+@dataclasses.dataclass
+class KvDownInputs:
+    """Inputs of the latent KV production from the hidden state (bf16 bits)."""
+
+    B: int
+    d_model: int
+    r: int
+    d_rope: int
+    eps: float
+    h: np.ndarray        # [B, d_model]
+    w_dkv: np.ndarray    # [r, d_model]
+    w_kr: np.ndarray     # [d_rope, d_model]
+    norm_w: np.ndarray   # [r]
+
+    def f64(self, field: str) -> np.ndarray:
+        return bf16_bits_to_f64(getattr(self, field))
+
+
+def make_kv_down_inputs(B: int, d_model: int, r: int = 512, d_rope: int = 64, seed: int = 11,
+                        eps: float = 1e-6) -> KvDownInputs:
+    """Seeded bf16 inputs: h ~ N(0, 1); W_DKV, W_KR ~ N(0, 1/d_model); the
+    RMSNorm gain ~ 1 + N(0, 0.1^2); eps 1e-6 (a common choice; the pages give
+    none)."""
+    rng = np.random.default_rng(seed)
+    h = rng.standard_normal((B, d_model))
+    w_dkv = rng.standard_normal((r, d_model)) / math.sqrt(d_model)
+    w_kr = rng.standard_normal((d_rope, d_model)) / math.sqrt(d_model)
+    g = 1.0 + 0.1 * rng.standard_normal(r)
+    return KvDownInputs(B, d_model, r, d_rope, eps, bf16_bits_from_f64(h), bf16_bits_from_f64(w_dkv),
+                        bf16_bits_from_f64(w_kr), bf16_bits_from_f64(g))

@@ -15,6 +15,8 @@
  *   mla_up_v          out = W_UV o_lat per head
  *   mla_absorb_rope   mla_absorb_q and mla_rope_append in one call (one launch
  *                     for bf16)
+ *   mla_kv_down       the appended row's latent and RoPE key from the hidden
+ *                     state (the step before the path)
  *   mla_*_paged       the calls that touch the cache, for a cache kept in
  *                     fixed-size pages behind a block table
  *   mla_combine_up_v  the last two in one call: the merge is formed where
@@ -212,6 +214,24 @@ mla_status mla_absorb_rope_paged(const mla_dims* dims, const void* q_nope, const
                                  const int32_t* positions, const int32_t* block_table,
                                  int32_t bt_stride, int32_t page_rows, int64_t total_pages,
                                  void* q_lat, void* kv_cache, void* stream);
+
+/* Latent KV production from the hidden state, the step before the append
+ * ([P2] module structure: W_DKV, then the RMSNorm norm_kv over the latent;
+ * [P1] section 2, [P5]: W_KR gives the one RoPE key shared by the heads):
+ *   x             = w_dkv h[b]                       w_dkv [r][d_model]
+ *   c_kv_new[b]   = norm_w * x / sqrt(mean(x^2) + eps)   norm_w [r]
+ *   k_rope_new[b] = w_kr h[b]                        w_kr [d_rope][d_model]
+ * h [B][d_model]; weights are Linear weights (out, in); outputs are the
+ * inputs of mla_rope_append / mla_absorb_rope (RoPE is applied there).  fp32
+ * accumulation, summed over d_model in a fixed order, each output rounded
+ * once.  bf16 storage only; d_model a multiple of 512; eps >= 0.  workspace:
+ * device memory of mla_kv_down_workspace_size bytes (fp32 partial sums),
+ * owned by the caller; calls that share one workspace must not overlap. */
+mla_status mla_kv_down(const mla_dims* dims, int32_t d_model, const void* h, const void* w_dkv,
+                       const void* w_kr, const void* norm_w, float eps, void* workspace,
+                       void* c_kv_new, void* k_rope_new, void* stream);
+
+mla_status mla_kv_down_workspace_size(const mla_dims* dims, int32_t d_model, size_t* bytes);
 
 /* Bytes of o_part and lse_part for `num_splits` splits. */
 mla_status mla_partials_size(const mla_dims* dims, int32_t num_splits, size_t* o_part_bytes,

@@ -232,3 +232,25 @@ def rope_through_projection_scores(q, w_uk, c, q_pos, k_pos, base):
     q_tilde = w_uk.T @ qr
     folded = c @ q_tilde
     return true, folded
+
+
+# ---------------------------------------------------------------------------
+# Latent KV production from the hidden state  [P2] module structure: W_DKV
+# (d_model -> d_c) then norm_kv (an RMSNorm over the latent); [P1] §2 and
+# [P5]: W_KR gives the one RoPE key shared by the heads (rotated later, by the
+# append).  The RMSNorm's epsilon is not on the pages; the caller passes it.
+# ---------------------------------------------------------------------------
+
+
+def rms_norm(x: np.ndarray, weight: np.ndarray, eps: float) -> np.ndarray:
+    """weight * x / sqrt(mean(x**2) + eps) over the last axis."""
+    return weight * x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+
+
+def kv_down(h: np.ndarray, w_dkv: np.ndarray, w_kr: np.ndarray, norm_w: np.ndarray,
+            eps: float) -> tuple[np.ndarray, np.ndarray]:
+    """(c_kv_new, k_rope_new) for hidden states h [B, d_model]; w_dkv [d_c,
+    d_model] and w_kr [d_rope, d_model] are Linear weights (out, in)."""
+    c_kv = rms_norm(h @ w_dkv.T, norm_w, eps)
+    k_rope = h @ w_kr.T
+    return c_kv, k_rope

@@ -215,3 +215,18 @@ def test_paginate_layout():
         mask[pc.rows_of(b, int(inp.lens[b]) + 1)] = False
     assert np.isnan(pc.cache[mask]).all()
     assert pc.block_table.min() >= 0 and pc.block_table.max() < pc.total_pages
+
+
+def test_kv_down_argument_checks():
+    """mla_kv_down: bf16 only, d_model a multiple of 512, eps >= 0, no NULLs;
+    the workspace holds one fp32 partial per (512-input chunk, sequence,
+    output feature)."""
+    d = dsv2()
+    assert mla.mla_kv_down_workspace_size(d, 5120) == 10 * 16 * 576 * 4
+    _expect(2, mla.mla_kv_down_workspace_size, d, 1000)
+    _expect(2, mla.mla_kv_down, d, 768, P16, P16, P16, P16, 1e-6, P16, P16, P16, 0)
+    _expect(1, mla.mla_kv_down, d, 512, 0, P16, P16, P16, 1e-6, P16, P16, P16, 0)
+    _expect(1, mla.mla_kv_down, d, 512, P16, P16, P16, P16, 1e-6, 0, P16, P16, 0)
+    _expect(1, mla.mla_kv_down, d, 512, P16, P16, P16, P16, -1.0, P16, P16, P16, 0)
+    f = mla.make_dims(8, 16, 64, 64, 64, 32, mla.MLA_F32)
+    _expect(2, mla.mla_kv_down, f, 512, P16, P16, P16, P16, 1e-6, P16, P16, P16, 0)

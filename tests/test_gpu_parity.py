@@ -372,3 +372,37 @@ def test_paged_step_matches_packed_and_oracle(name, override, page_rows):
     assert torch.equal(ds.out, packed.out) and torch.equal(ds.lse, packed.lse)
     np.testing.assert_array_equal(ds.cache_raw(), packed.cache_raw())
     check_step(inp, ds, oracle_step(inp), tag=f"{name} {override} paged {page_rows}")
+
+
+# ---------------------------------------------------------------------------
+# latent KV production from the hidden state
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("B,d_model", [(1, 512), (16, 5120), (33, 1536), (64, 5120)])
+def test_kv_down_matches_oracle(B, d_model):
+    """mla_kv_down against the fp64 oracle on the same bf16 inputs: every
+    output within one bf16 rounding of the exact value (the kernel sums in
+    fp32 and rounds once), and two runs bit for bit equal."""
+    from head_latent_attention_12_amd import mla
+    from head_latent_attention_12_amd.step import _dev
+    kin = syn.make_kv_down_inputs(B, d_model)
+    dims = mla.make_dims(B, 128, 128, 128, kin.r, kin.d_rope, mla.MLA_BF16)
+    dev = {k: _dev(getattr(kin, k), "cuda:0") for k in ("h", "w_dkv", "w_kr", "norm_w")}
+    ws = torch.empty(mla.mla_kv_down_workspace_size(dims, d_model) // 4, dtype=torch.float32, device="cuda:0")
+    outs = []
+    for _ in range(2):
+        c = torch.full((B, kin.r), -1, dtype=torch.int16, device="cuda:0")
+        k = torch.full((B, kin.d_rope), -1, dtype=torch.int16, device="cuda:0")
+        mla.mla_kv_down(dims, d_model, dev["h"], dev["w_dkv"], dev["w_kr"], dev["norm_w"], kin.eps, ws, c, k)
+        torch.cuda.synchronize()
+        outs.append((c.cpu().numpy().view(np.uint16), k.cpu().numpy().view(np.uint16)))
+    np.testing.assert_array_equal(outs[0][0], outs[1][0])
+    np.testing.assert_array_equal(outs[0][1], outs[1][1])
+    c_ref, k_ref = orc.kv_down(kin.f64("h"), kin.f64("w_dkv"), kin.f64("w_kr"), kin.f64("norm_w"), kin.eps)
+    for got_bits, ref, tag in ((outs[0][0], c_ref, "c_kv"), (outs[0][1], k_ref, "k_rope")):
+        got = syn.bf16_bits_to_f64(got_bits)
+        err = np.abs(got - ref)
+        bound = 2.0 ** -8 * np.abs(ref) + 1e-6 * np.abs(ref).max()
+        print(f"[kv_down B={B} d_model={d_model} {tag}] max abs {err.max():.3e}, "
+              f"max err / bound {np.max(err / bound):.3f}", flush=True)
+        assert np.all(err <= bound), tag

@@ -379,3 +379,43 @@ def test_generator_layout_and_determinism():
         assert np.all(slot == 0x7FC0)         # append slot holds NaN
         rows = a.cached_rows_f64(bi)[:, :a.r]
         np.testing.assert_allclose(np.sqrt(np.mean(rows ** 2, axis=1)), 1.0, atol=1e-2)
+
+
+# ---------------------------------------------------------------------------
+# latent KV production from the hidden state (W_DKV, RMSNorm, W_KR)
+# ---------------------------------------------------------------------------
+
+def test_kv_down_worked_by_hand():
+    """h = (1, 2); W_DKV rows (1, 0), (0, 1), (1, 1) give x = (1, 2, 3), whose
+    mean square is 14/3, so with unit gain and eps 0 the latent is
+    x / sqrt(14/3) (sqrt(14/3) = 2.1602468994692865...); W_KR = (1, -1) gives
+    the key -1."""
+    h = np.array([[1.0, 2.0]])
+    w_dkv = np.array([[1.0, 0.0], [0.0, 1.0], [1.0, 1.0]])
+    w_kr = np.array([[1.0, -1.0]])
+    c, k = orc.kv_down(h, w_dkv, w_kr, np.ones(3), 0.0)
+    np.testing.assert_allclose(c, [[0.46291004988627573, 0.92582009977255146, 1.38873014965882720]], rtol=1e-15)
+    np.testing.assert_allclose(k, [[-1.0]], rtol=0)
+
+
+def test_kv_down_invariants():
+    """With eps 0 the latent does not change when h is scaled (RMSNorm is
+    scale invariant) while the key scales with it (linear); with unit gain the
+    latent has unit mean square; with a gain g and eps > 0, (c/g) has mean
+    square ms / (ms + eps) for the row's mean square ms."""
+    rng = np.random.default_rng(5)
+    h = rng.standard_normal((3, 40))
+    w_dkv = rng.standard_normal((16, 40))
+    w_kr = rng.standard_normal((4, 40))
+    g = 1.0 + 0.2 * rng.standard_normal(16)
+    c1, k1 = orc.kv_down(h, w_dkv, w_kr, g, 0.0)
+    c3, k3 = orc.kv_down(3.0 * h, w_dkv, w_kr, g, 0.0)
+    np.testing.assert_allclose(c3, c1, rtol=1e-13)
+    np.testing.assert_allclose(k3, 3.0 * k1, rtol=1e-13)
+    cu, _ = orc.kv_down(h, w_dkv, w_kr, np.ones(16), 0.0)
+    np.testing.assert_allclose(np.mean(cu * cu, axis=-1), 1.0, rtol=1e-13)
+    eps = 0.7
+    ce, _ = orc.kv_down(h, w_dkv, w_kr, g, eps)
+    x = h @ w_dkv.T
+    ms = np.mean(x * x, axis=-1)
+    np.testing.assert_allclose(np.mean((ce / g) ** 2, axis=-1), ms / (ms + eps), rtol=1e-13)

@@ -343,19 +343,21 @@ def test_split_partials(name, lens, splits):
 # ---------------------------------------------------------------------------
 
 PAGED_CASES = [
-    ("tiny", {}, 32),
-    ("small", {}, 64),
-    ("dsv2", dict(B=3, T=300), 64),
-    ("dsv2", dict(lens=[0, 31, 32, 63, 64, 65, 127, 128]), 64),   # the new row opens a page, or not
-    ("dsv2", dict(B=2, T=3000), 32),                               # a new page every tile, steady loop
-    ("dsv2_ragged", dict(B=6, T=(1, 700)), 256),
-    ("dsv2_ragged", {}, 64),
+    ("tiny", {}, 32, None),
+    ("small", {}, 64, None),
+    ("dsv2", dict(B=3, T=300), 64, None),
+    ("dsv2", dict(lens=[0, 31, 32, 63, 64, 65, 127, 128]), 64, None),  # the new row opens a page, or not
+    ("dsv2", dict(B=2, T=3000), 32, None),
+    ("dsv2", dict(B=2, T=3000), 32, 2),      # long splits: a new page every tile of the steady loop
+    ("small", dict(B=3, T=1500), 128, 1),    # fp32 path, one split, pages of four tiles
+    ("dsv2_ragged", dict(B=6, T=(1, 700)), 256, None),
+    ("dsv2_ragged", {}, 64, None),
 ]
 
 
-@pytest.mark.parametrize("name,override,page_rows", PAGED_CASES,
-                         ids=[f"{n}-{o}-p{p}" for n, o, p in PAGED_CASES])
-def test_paged_step_matches_packed_and_oracle(name, override, page_rows):
+@pytest.mark.parametrize("name,override,page_rows,splits", PAGED_CASES,
+                         ids=[f"{n}-{o}-p{p}-s{q}" for n, o, p, q in PAGED_CASES])
+def test_paged_step_matches_packed_and_oracle(name, override, page_rows, splits):
     """The step over a paged cache (pages shuffled, unused page rows NaN):
     bit for bit the packed step's q_lat, appended row, split partials, out and
     lse (the same rows in the same order), and against the oracle like every
@@ -363,7 +365,7 @@ def test_paged_step_matches_packed_and_oracle(name, override, page_rows):
     W_UV calls included)."""
     from head_latent_attention_12_amd.step import DeviceStep
     inp = syn.make_inputs(name, **override)
-    packed = _run(inp)
+    packed = _run(inp, num_splits=splits)
     ds = DeviceStep(inp, num_splits=packed.num_splits, page_rows=page_rows, page_seed=7)
     ds.run()
     torch.cuda.synchronize()

@@ -1,8 +1,8 @@
 /*
  * mla.h - absorbed Multi-head Latent Attention (MLA) decode on AMD MI355X (gfx950).
  *
- * One decode step for a batch of sequences, split into five calls that run in
- * stream order:
+ * One decode step for a batch of sequences is five operations that run in
+ * stream order (the fused calls below run the same step in three launches):
  *
  *   mla_absorb_q      q~ = W_UK^T q_nope per head (the content query folded into
  *                     the latent space)

@@ -1768,6 +1768,84 @@ __global__ __launch_bounds__(kCuvWaves * 64) void combine_up_v_bf16_kernel(
   }
 }
 
+// d_v = 128 (the DeepSeek-V2 shape): one work-group per (head, half of the
+// sequences), so that each partial row is merged once; the head's W_UV (128
+// rows x 512, 128 KB) is held in registers over the 8 waves (wave w: rows
+// 32*(w%4) .. +31, latent half w/4: 16 k-steps, 64 VGPRs), read straight from
+// global memory (the two work-groups of a head run on one XCD, whose L2
+// serves the second).  The two latent halves are added through LDS.  The
+// merge keeps 16 partial rows in flight per lane here (the weights take the
+// registers of the other 16).
+__global__ __launch_bounds__(kCuvWaves * 64) void combine_up_v_bf16_d128_kernel(
+    const u16* __restrict__ o_part, const float* __restrict__ lse_part, int num_splits,
+    const u16* __restrict__ w_uv, int B, int H, float* __restrict__ out, float* __restrict__ lse_out) {
+  using M = Mma<u16>;
+  constexpr int R = 512, DV = 128, WROW = R * 2;
+  __shared__ __attribute__((aligned(16))) char ot[kCuvRows * 2 * WROW];  // merged rows (hi | lo)
+  __shared__ float xs[kCuvWaves][64][8];
+  __shared__ float xm[kCuvWaves], xw[kCuvWaves];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hf = lane >> 5, l32 = lane & 31;
+  int h, part;
+  {
+    const int bid = (int)blockIdx.x;
+    const int grp = bid / (kXcds * 2);
+    const int rem = bid - grp * (kXcds * 2);
+    h = grp * kXcds + rem % kXcds;
+    part = rem / kXcds;
+  }
+  if (h >= H) return;
+  const int half = (B + 1) / 2;
+  const int b_lo = part * half, b_hi = min(B, b_lo + half);
+  const int db = wave & 3, jh = wave >> 2;
+  i16x8 a[16];
+  {
+    const u16* wrow = w_uv + ((int64_t)h * DV + 32 * db + l32) * R + 256 * jh + 8 * hf;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) a[u] = *(const i16x8*)(wrow + 16 * u);
+  }
+  for (int b0 = b_lo; b0 < b_hi; b0 += kCuvRows) {
+    const int nb = min(kCuvRows, b_hi - b0);
+    // waves per sequence: the largest power of two with nb * WPR <= 8 (1 from 5 rows up)
+    const int WPR = nb >= 5 ? 1 : (nb >= 3 ? 2 : (nb == 2 ? 4 : 8));
+    const int upw = (nb * WPR + kCuvWaves - 1) / kCuvWaves;
+    if (upw == 1) {
+      cuv_merge<1, 16>(o_part, lse_part, num_splits, H, h, b0, nb, WPR, wave, lane, ot, xs, xm, xw, lse_out);
+    } else if (upw == 2) {
+      cuv_merge<2, 8>(o_part, lse_part, num_splits, H, h, b0, nb, WPR, wave, lane, ot, xs, xm, xw, lse_out);
+    } else {
+      cuv_merge<4, 4>(o_part, lse_part, num_splits, H, h, b0, nb, WPR, wave, lane, ot, xs, xm, xw, lse_out);
+    }
+    __syncthreads();  // merged rows written
+    f32x16 acc = zero16();
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int ch = 32 * jh + 2 * u + hf;  // 16-byte chunk: k = 256*jh + 16*u + 8*hf .. +7
+      const int sl = 16 * (ch ^ (l32 & 15));
+      const i16x8 bh = *(const LDS_AS i16x8*)((LDS_AS char*)ot + l32 * 2 * WROW + sl);
+      const i16x8 bl = *(const LDS_AS i16x8*)((LDS_AS char*)ot + l32 * 2 * WROW + WROW + sl);
+      acc = M::mma(a[u], bh, acc);
+      acc = M::mma(a[u], bl, acc);
+    }
+    __syncthreads();  // every wave has read the merged rows: their bytes take the partial tiles
+    LDS_AS f32x4* red = (LDS_AS f32x4*)(LDS_AS char*)ot;  // [wave][row quarter][lane]
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      red[(wave * 4 + q) * 64 + lane] = f32x4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+    __syncthreads();
+    if (l32 < nb) {
+#pragma unroll
+      for (int qq = 0; qq < 2; ++qq) {
+        const int q = 2 * jh + qq;  // wave w adds rows 8q + 4hf .. +3 of block db over the two latent halves
+        const f32x4 sum = red[(db * 4 + q) * 64 + lane] + red[((db + 4) * 4 + q) * 64 + lane];
+        *(f32x4*)(out + ((int64_t)(b0 + l32) * H + h) * DV + 32 * db + 8 * q + 4 * hf) = sum;
+      }
+    }
+    __syncthreads();  // the next chunk rewrites these bytes
+  }
+}
+
 __global__ __launch_bounds__(64) void combine_up_v_f32_kernel(const float* __restrict__ o_part,
                                                               const float* __restrict__ lse_part, int S,
                                                               const float* __restrict__ w_uv, int H, int DV, int R,
@@ -2426,6 +2504,13 @@ mla_status mla_combine_up_v(const mla_dims* dims, const void* o_part, const floa
     if (dims->rank != 512) return fail(MLA_ERR_UNSUPPORTED, "bf16 combine_up_v is built for rank 512");
     if ((int64_t)num_splits * dims->heads * dims->rank * 2 >= ((int64_t)1 << 31))
       return fail(MLA_ERR_UNSUPPORTED, "one sequence's partials must stay under 2 GB");
+    if (dims->d_v == 128) {
+      const int blocks = (dims->heads + kXcds - 1) / kXcds * kXcds * 2;  // whole groups of 8 heads, two halves
+      hipLaunchKernelGGL(combine_up_v_bf16_d128_kernel, dim3(blocks), dim3(kCuvWaves * 64), 0, s,
+                         (const u16*)o_part, lse_part, num_splits, (const u16*)w_uv, dims->batch, dims->heads, out,
+                         lse);
+      return launch_result("mla_combine_up_v");
+    }
     const int nh = dims->d_v % 64 == 0 ? 2 : 1;
     const int blocks = (dims->heads + kXcds - 1) / kXcds * kXcds * (dims->d_v / (32 * nh));  // whole groups of 8 heads
     if (nh == 2) {

@@ -2504,7 +2504,10 @@ mla_status mla_combine_up_v(const mla_dims* dims, const void* o_part, const floa
     if (dims->rank != 512) return fail(MLA_ERR_UNSUPPORTED, "bf16 combine_up_v is built for rank 512");
     if ((int64_t)num_splits * dims->heads * dims->rank * 2 >= ((int64_t)1 << 31))
       return fail(MLA_ERR_UNSUPPORTED, "one sequence's partials must stay under 2 GB");
-    if (dims->d_v == 128) {
+    // d_v 128 from three sequences up: split by sequences (each partial merged
+    // once).  With one or two sequences there is no repeated merge to save, and
+    // the per-block kernel measured faster (B 2: 15.1 against 16.0 us).
+    if (dims->d_v == 128 && dims->batch > 2) {
       const int blocks = (dims->heads + kXcds - 1) / kXcds * kXcds * 2;  // whole groups of 8 heads, two halves
       hipLaunchKernelGGL(combine_up_v_bf16_d128_kernel, dim3(blocks), dim3(kCuvWaves * 64), 0, s,
                          (const u16*)o_part, lse_part, num_splits, (const u16*)w_uv, dims->batch, dims->heads, out,

@@ -408,3 +408,31 @@ def test_kv_down_matches_oracle(B, d_model):
         print(f"[kv_down B={B} d_model={d_model} {tag}] max abs {err.max():.3e}, "
               f"max err / bound {np.max(err / bound):.3f}", flush=True)
         assert np.all(err <= bound), tag
+
+
+def test_inconsistent_metadata_stays_in_bounds():
+    """Device metadata the host cannot check (row offsets, page ids, lengths
+    past the cache or the block table) is clamped inside the kernels: the
+    calls complete with wrong numbers, never a stray access, and a correct
+    step afterwards still matches the oracle."""
+    from head_latent_attention_12_amd.step import DeviceStep
+    inp = syn.make_inputs("dsv2", B=3, T=200)
+    # packed: offsets before and past the cache, a length far past max_seq_len
+    ds = DeviceStep(inp, num_splits=4)
+    ds.row_offsets.copy_(torch.tensor([-(10 ** 9), inp.total_rows + 7, 10 ** 12], dtype=torch.int64))
+    ds.seq_lens.copy_(torch.tensor([10 ** 6, -3, int(inp.seq_lens[2])], dtype=torch.int32))
+    ds.positions.copy_(torch.tensor([10 ** 6, -9, 2 ** 30], dtype=torch.int32))
+    ds.run()
+    torch.cuda.synchronize()
+    # paged: page ids below zero and past the last page, lengths past the block table
+    dp = DeviceStep(inp, num_splits=4, page_rows=64)
+    bt = dp.block_table.clone()
+    bt[:, 0] = -7
+    bt[:, -1] = dp.paged.total_pages + 100
+    dp.block_table.copy_(bt)
+    dp.seq_lens.copy_(torch.tensor([10 ** 6, 1, 64 * dp.paged.bt_stride + 500], dtype=torch.int32))
+    dp.run()
+    torch.cuda.synchronize()
+    # the device is still healthy: a clean step matches the oracle
+    clean = _run(inp)
+    check_out(inp, clean.out.cpu().numpy().astype(np.float64), oracle_step(inp)["out"], tag="after bad metadata")

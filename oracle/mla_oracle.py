@@ -254,3 +254,73 @@ def kv_down(h: np.ndarray, w_dkv: np.ndarray, w_kr: np.ndarray, norm_w: np.ndarr
     c_kv = rms_norm(h @ w_dkv.T, norm_w, eps)
     k_rope = h @ w_kr.T
     return c_kv, k_rope
+
+
+# ---------------------------------------------------------------------------
+# FP8 latent cache  [P2] "what's not in this implementation": the latent cache
+# can be quantised to FP8 for a further memory reduction.  The pages fix no
+# format or scaling; the readings taken here (listed in the design notes):
+#   * codes are OCP E4M3FN: sign, 4 exponent bits (bias 7), 3 mantissa bits;
+#     exponent field 0 is subnormal (m/8 * 2^-6), 0x7f / 0xff are NaN, no
+#     infinities, 448 is the largest finite value;
+#   * one power-of-two scale per cached row: 2^e with e the smallest integer in
+#     [-116, 63] such that max|c_kv| <= 448 * 2^e;
+#   * codes round to the nearest value, ties to the even code, and saturate at
+#     448; the rotated RoPE key of the row stays bf16.
+# ---------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+FP8_MIN_EXP, FP8_MAX_EXP = -116, 63
+
+
+def e4m3_value(code: int) -> float:
+    """Value of one E4M3FN code, from the format's definition."""
+    sign = -1.0 if code & 0x80 else 1.0
+    e, m = (code >> 3) & 0xF, code & 0x7
+    if e == 0xF and m == 0x7:
+        return math.nan
+    if e == 0:
+        return sign * (m / 8.0) * 2.0 ** -6
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+_E4M3 = np.array([e4m3_value(c) for c in range(256)])
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    return _E4M3[np.asarray(codes, dtype=np.uint8)]
+
+
+def e4m3_encode(y: np.ndarray) -> np.ndarray:
+    """Nearest E4M3FN code of each finite y: the closest of the 127 finite
+    non-negative values to |y| (ties to the even code, above 448: 448), with
+    the sign bit of y (also for a result of zero)."""
+    y = np.asarray(y, dtype=np.float64)
+    pos = _E4M3[:0x7F]                       # codes 0 .. 0x7e, increasing
+    a = np.minimum(np.abs(y), E4M3_MAX)
+    hi = np.clip(np.searchsorted(pos, a), 1, 0x7E)   # pos[hi - 1] <= a <= pos[hi]
+    lo = hi - 1
+    d_lo, d_hi = a - pos[lo], pos[hi] - a
+    code = np.where(d_lo < d_hi, lo, np.where(d_hi < d_lo, hi, np.where(lo % 2 == 0, lo, hi)))
+    code = np.where(a <= 0.0, 0, code)
+    return (code | np.where(np.signbit(y), 0x80, 0)).astype(np.uint8)
+
+
+def fp8_row_exponent(amax: float) -> int:
+    """Smallest e in [FP8_MIN_EXP, FP8_MAX_EXP] with amax <= 448 * 2^e."""
+    for e in range(FP8_MIN_EXP, FP8_MAX_EXP + 1):
+        if amax <= E4M3_MAX * 2.0 ** e:
+            return e
+    return FP8_MAX_EXP
+
+
+def fp8_quantize_row(c: np.ndarray):
+    """(codes [r] uint8, scale) of one latent row."""
+    c = np.asarray(c, dtype=np.float64)
+    e = fp8_row_exponent(float(np.max(np.abs(c))))
+    return e4m3_encode(c / 2.0 ** e), 2.0 ** e
+
+
+def fp8_dequantize_rows(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Latent values code * scale of rows [n, r] with scales [n]."""
+    return e4m3_decode(codes) * np.asarray(scales, dtype=np.float64)[:, None]

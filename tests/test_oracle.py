@@ -419,3 +419,64 @@ def test_kv_down_invariants():
     x = h @ w_dkv.T
     ms = np.mean(x * x, axis=-1)
     np.testing.assert_allclose(np.mean((ce / g) ** 2, axis=-1), ms / (ms + eps), rtol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# FP8 latent cache: the E4M3FN format and the row quantisation
+# ---------------------------------------------------------------------------
+
+def test_e4m3_values_from_the_format_definition():
+    # exponent bias 7, 3 mantissa bits: a few values fixed by the definition
+    known = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0, 0x3C: 1.5,
+             0x40: 2.0, 0x7E: 448.0, 0x77: 240.0, 0xB8: -1.0, 0xFE: -448.0}
+    for code, v in known.items():
+        assert orc.e4m3_value(code) == v, hex(code)
+    assert math.isnan(orc.e4m3_value(0x7F)) and math.isnan(orc.e4m3_value(0xFF))
+    assert orc.e4m3_value(0x80) == 0.0 and math.copysign(1.0, orc.e4m3_value(0x80)) == -1.0
+    pos = np.array([orc.e4m3_value(c) for c in range(0x7F)])
+    assert np.all(np.diff(pos) > 0)                       # 127 distinct, increasing
+    assert np.all(np.diff(pos[:9]) == 2.0 ** -9)          # subnormals and the first normal evenly spaced
+    neg = np.array([orc.e4m3_value(c | 0x80) for c in range(0x7F)])
+    np.testing.assert_array_equal(neg, -pos)
+
+
+def test_e4m3_encode_round_trip_ties_and_saturation():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    np.testing.assert_array_equal(orc.e4m3_encode(orc.e4m3_decode(codes)), codes)
+    # ties go to the even code
+    cases = {1.0625: 0x38, 1.1875: 0x3A, 1.5 * 2.0 ** -9: 0x02, 0.5 * 2.0 ** -9: 0x00, 2.5 * 2.0 ** -9: 0x02,
+             -1.0625: 0xB8, 464.0: 0x7E, 500.0: 0x7E, 1e30: 0x7E, -1e30: 0xFE, 0.25 * 2.0 ** -9: 0x00}
+    for y, code in cases.items():
+        assert int(orc.e4m3_encode(np.array([y]))[0]) == code, y
+
+
+def test_e4m3_encode_is_the_nearest_code():
+    rng = np.random.default_rng(5)
+    y = np.concatenate([rng.standard_normal(4000) * 10.0 ** rng.uniform(-4, 2.5, 4000),
+                        rng.uniform(-448, 448, 1000)])
+    got = orc.e4m3_decode(orc.e4m3_encode(y))
+    finite = np.array([orc.e4m3_value(c) for c in range(256) if c not in (0x7F, 0xFF)])
+    best = np.min(np.abs(y[:, None] - finite[None, :]), axis=1)  # brute force over every code
+    np.testing.assert_array_equal(np.abs(got - y), best)
+    assert np.all(np.sign(got) * np.sign(y) >= 0)
+
+
+def test_fp8_row_exponent_and_quantised_row():
+    assert orc.fp8_row_exponent(448.0) == 0
+    assert orc.fp8_row_exponent(np.nextafter(448.0, 1e9)) == 1
+    assert orc.fp8_row_exponent(224.0) == -1
+    assert orc.fp8_row_exponent(1.0) == -8                  # 448 / 256 = 1.75 >= 1 > 448 / 512
+    assert orc.fp8_row_exponent(0.0) == orc.FP8_MIN_EXP
+    assert orc.fp8_row_exponent(1e300) == orc.FP8_MAX_EXP
+    rng = np.random.default_rng(6)
+    for amax in 10.0 ** rng.uniform(-30, 20, 200):
+        e = orc.fp8_row_exponent(amax)
+        assert amax <= 448.0 * 2.0 ** e and (e == orc.FP8_MIN_EXP or amax > 448.0 * 2.0 ** (e - 1))
+    c = rng.standard_normal(512)
+    codes, s = orc.fp8_quantize_row(c)
+    deq = orc.fp8_dequantize_rows(codes[None, :], np.array([s]))[0]
+    assert np.max(np.abs(deq)) <= 448.0 * s and np.max(np.abs(c)) > 224.0 * s   # the scale is tight
+    # every element is its nearest code times s; normal-range errors are within half a step (2^-4 relative)
+    np.testing.assert_array_equal(deq, orc.e4m3_decode(orc.e4m3_encode(c / s)) * s)
+    normal = np.abs(c) >= 2.0 ** -6 * s
+    assert np.all(np.abs(deq - c)[normal] <= 2.0 ** -4 * np.abs(c)[normal])

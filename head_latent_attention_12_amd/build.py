@@ -9,19 +9,24 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "mla.hip")
+CSRC = os.path.join(PKG, "csrc")
+SRC = os.path.join(CSRC, "mla.hip")
+SRC_FP8 = os.path.join(CSRC, "decode_fp8.hip")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmla.so")
 
-HIPCC_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+COMMON_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # keep the compiler from emitting packed fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # MFMA accumulators in VGPR form: lets the allocator keep the decode
-    # kernel's 32x512 fp32 accumulator block and its q fragments without scratch
-    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wall", "-Wno-unused-function",
 ]
+# mla.hip: MFMA accumulators in VGPR form, which lets the allocator keep the
+# bf16 decode kernel's 32x512 fp32 accumulator block (AGPR operands of its asm
+# blocks) and its q fragments without scratch.  decode_fp8.hip is compiler
+# scheduled and needs the default form (accumulators in AGPRs).
+MLA_FLAGS = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+HIPCC_FLAGS = COMMON_FLAGS + MLA_FLAGS  # (kept for callers that compile mla.hip alone)
 
 
 def hipcc() -> str:
@@ -31,14 +36,28 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-I", INCLUDE, SRC, "-o", tmp]
+def _run(cmd, verbose):
     res = subprocess.run(cmd, capture_output=True, text=True)
     if verbose or res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}): {' '.join(cmd)}")
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    """Compile both translation units (each with its own flags) and link them."""
+    tmp = LIB + ".tmp"
+    objs = []
+    for src, flags in ((SRC, COMMON_FLAGS + MLA_FLAGS), (SRC_FP8, COMMON_FLAGS)):
+        obj = os.path.join(CSRC, os.path.basename(src) + ".o")
+        _run([hipcc(), *flags, *extra, "-I", INCLUDE, "-c", src, "-o", obj], verbose)
+        objs.append(obj)
+    try:
+        _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+    finally:
+        for obj in objs:
+            if os.path.exists(obj):
+                os.remove(obj)
     _check_kernel_stubs(tmp)
     os.replace(tmp, LIB)
     return LIB

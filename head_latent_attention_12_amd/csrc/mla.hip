@@ -39,118 +39,9 @@
 #include "mla.h"
 
 #include "decode_asm.inc"  // hand-scheduled inner blocks of the bf16 decode tile
+#include "mla_common.h"
 
 namespace {
-
-using u16 = uint16_t;
-typedef short i16x8 __attribute__((ext_vector_type(8)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-#define LDS_AS __attribute__((address_space(3)))
-
-constexpr float kLn2 = 0.69314718055994530942f;
-constexpr float kLog2e = 1.44269504088896340736f;
-// Softmax reference: each head's exponent reference is fixed at the first tile
-// of a split, and p = 2^(s - ref) is accepted up to 2^kRefSlack (finite in fp32
-// and bf16, no overflow of the sums).  If a later score exceeds ref + kRefSlack,
-// the work-group runs a scores-only pass over the split to find each head's
-// exact maximum and then redoes the split with that reference (p <= 1), so the
-// accumulators are never rescaled inside the loop and at most one redo happens.
-// The bf16 pipelined loop checks this once per pass on the sum of the weights
-// instead of per tile on the scores: every weight is non-negative, so a sum
-// below 2^kRefSlack means every weight was, and a weight at or above it (or an
-// infinite one) makes the sum fail the test (a few weights just under the bound
-// may also trigger a redo, which is only slower).
-constexpr float kRefSlack = 64.0f;
-// MI355X: 8 accelerator complex dies (XCDs), each with its own L2
-constexpr int kXcds = 8;
-
-// ---------------------------------------------------------------------------
-// bf16 helpers (storage type u16 holds bf16 bits)
-// ---------------------------------------------------------------------------
-
-__device__ __forceinline__ float bf2f(u16 b) { return __uint_as_float((uint32_t)b << 16); }
-
-__device__ __forceinline__ u16 f2bf(float f) {  // round to nearest even
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u16)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (u16)(u >> 16);
-}
-
-__device__ __forceinline__ uint32_t pack2bf(float a, float b) {
-  return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
-}
-
-// Round a finite fp32 value to the nearest bf16 (ties to even), kept as fp32.
-__device__ __forceinline__ float round_bf16_finite(float a) {
-  uint32_t u = __float_as_uint(a);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return __uint_as_float(u & 0xffff0000u);
-}
-
-// Two fp32 values rounded to bf16 (nearest even, v_cvt_pk_bf16_f32), packed.
-__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
-}
-
-// Pack two fp32 values that are already bf16-representable into bf16x2.
-__device__ __forceinline__ uint32_t pack_hi16(float a, float b) {
-  return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
-}
-
-// double -> bf16 with a single rounding: round to odd into fp32, then nearest
-// even into bf16 (fp32 keeps more than two extra bits, so the result is the
-// correctly rounded bf16).
-__device__ __forceinline__ u16 d2bf(double x) {
-  float f = (float)x;
-  double fd = (double)f;
-  uint32_t u = __float_as_uint(f);
-  if (fd != x) {
-    if (fabs(fd) > fabs(x)) u -= 1u;  // step toward zero (same sign)
-    u |= 1u;
-  }
-  return f2bf(__uint_as_float(u));
-}
-
-template <typename T> __device__ __forceinline__ double load_d(T v);
-template <> __device__ __forceinline__ double load_d<u16>(u16 v) { return (double)bf2f(v); }
-template <> __device__ __forceinline__ double load_d<float>(float v) { return (double)v; }
-template <typename T> __device__ __forceinline__ T store_d(double v);
-template <> __device__ __forceinline__ u16 store_d<u16>(double v) { return d2bf(v); }
-template <> __device__ __forceinline__ float store_d<float>(double v) { return (float)v; }
-
-// ---------------------------------------------------------------------------
-// MFMA traits
-// ---------------------------------------------------------------------------
-
-template <typename T> struct Mma;
-template <> struct Mma<u16> {
-  static constexpr int KSTEP = 16;  // k per instruction (8 per lane)
-  using Frag = i16x8;
-  __device__ static __forceinline__ f32x16 mma(Frag a, Frag b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-  }
-};
-template <> struct Mma<float> {
-  static constexpr int KSTEP = 2;  // k per instruction (1 per lane)
-  using Frag = float;
-  __device__ static __forceinline__ f32x16 mma(Frag a, Frag b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
-  }
-};
-
-__device__ __forceinline__ f32x16 zero16() {
-  f32x16 z;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) z[r] = 0.f;
-  return z;
-}
 
 // ---------------------------------------------------------------------------
 // Row-major LDS tiles with 16-byte chunks XOR-swizzled within groups of 8.
@@ -209,34 +100,6 @@ __device__ __forceinline__ void acc_fence(f32x16 (&o)[CB]) {
                  "+a"(o[14]), "+a"(o[15]));
 }
 
-// Combine a value with the one held by lane ^ 32 (v_permlane32_swap: the two
-// results together hold both halves' values in every lane).
-template <typename F>
-__device__ __forceinline__ float xor32(float v, F op) {
-  const uint32_t u = __float_as_uint(v);
-  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-// Sum and inclusive prefix sum of an int over the 64 lanes of a wave.
-__device__ __forceinline__ int wave_prefix_sum(int v) {
-  const int lane = (int)(threadIdx.x & 63);
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int u = __shfl_up(v, d);
-    if (lane >= d) v += u;
-  }
-  return v;
-}
-__device__ __forceinline__ int wave_sum(int v) { return __shfl(wave_prefix_sum(v), 63); }
-
-// A 64-bit value known to be uniform across the wave, in SGPRs
-// (readfirstlane returns int: each half goes through uint32_t so that the low
-// half is not sign-extended into the high one).
-__device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
-  return ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32)) << 32) |
-         (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
-}
 
 // Nine 1 KB LDS DMA copies (16 bytes per lane): lane l of copy n moves 16
 // bytes from sbase + off[n] to LDS byte ldst + 1024*n + 16*l.  Issued from
@@ -278,10 +141,6 @@ __device__ __forceinline__ void lds_dma9(int ldst, const uint64_t (&addr)[9]) {
                : "memory", "scc");
 }
 
-template <int N>
-__device__ __forceinline__ void wait_vm_then_barrier() {
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
-}
 
 // ---------------------------------------------------------------------------
 // K3: split-KV attention over the latent cache.
@@ -297,36 +156,6 @@ __device__ __forceinline__ void wait_vm_then_barrier() {
 //                                                    reads, B = P^T straight
 //                                                    from the S^T accumulators)
 // ---------------------------------------------------------------------------
-
-// Where the rows of a sequence live in the cache.  Packed: in-sequence row t
-// of sequence b is cache row row_offsets[b] + t.  Paged: the cache is pages
-// of 2^page_shift rows (at least 32, so a 32-row tile never straddles two),
-// and row t is row t & (page_rows - 1) of page block_table[b * bt_stride +
-// (t >> page_shift)].  Rows are clamped into the cache either way, so that
-// inconsistent metadata can only give wrong numbers, never a stray access.
-struct CacheMap {
-  const int64_t* row_offsets;  // packed (nullptr when paged)
-  const int32_t* block_table;  // paged (nullptr when packed)
-  int64_t total_rows;          // rows in the cache
-  int64_t total_pages;         // paged: pages in the cache
-  int32_t bt_stride;           // paged: entries per sequence in block_table
-  int32_t page_shift;          // paged: log2(page_rows)
-  // (bt: block_table, passed separately where a restrict-qualified pointer
-  // lets the compiler read it with scalar loads)
-  __device__ __forceinline__ int64_t paged_row(int b, int t, const int32_t* __restrict__ bt) const {
-    int pi = t >> page_shift;
-    pi = pi < 0 ? 0 : (pi >= bt_stride ? bt_stride - 1 : pi);
-    int64_t pg = bt[(int64_t)b * bt_stride + pi];
-    pg = pg < 0 ? 0 : (pg >= total_pages ? total_pages - 1 : pg);
-    return (pg << page_shift) + (t & ((1 << page_shift) - 1));
-  }
-  // row t of sequence b; off = row_offsets[b] (packed, loaded by the caller)
-  __device__ __forceinline__ int64_t row(int b, int t, int64_t off) const {
-    if (block_table != nullptr) return paged_row(b, t, block_table);
-    const int64_t r = off + t;
-    return r < 0 ? 0 : (r >= total_rows ? total_rows - 1 : r);
-  }
-};
 
 template <typename T, int H, int R, int DR, int NW>
 struct DecodeShape {
@@ -366,67 +195,10 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (LDS DMA base)
   const int hf = lane >> 5, l32 = lane & 31;
-  // Work items are the non-empty splits (b, s < n_b), n_b = ceil(seq_len_b /
-  // chunk) clamped to [1, num_splits], taken in sequence order (times GROUPS head
-  // groups).  Work-groups are dealt to the 8 XCDs round-robin (blockIdx % 8);
-  // item L goes to XCD L / per, so that the splits of one sequence share an
-  // XCD (its L2 serves their common q_lat) and each XCD gets the same number
-  // of items whatever the lengths.  The grid (host: 8 * ceil(B*num_splits*
-  // GROUPS / 8)) bounds the item count; work-groups without an item exit.
-  // The work-group of split 0 marks the sequence's empty splits (lse -inf).
-  // Each lane looks at one sequence per step of 64; the first 64 lengths and
-  // row offsets are loaded once and serve both passes, so that with B <= 64
-  // the item's metadata costs a single round of loads.
-  auto splits_of = [&](int len) { return max(1, min(num_splits, (len + chunk - 1) / chunk)); };
-  int b = 0, s = 0, n_b = 0, seq_len = 0;
-  int64_t row_off = 0;
-  {
-    const int bid = (int)blockIdx.x;
-    const bool in0 = lane < batch;
-    const int len0 = in0 ? seq_lens[lane] : 0;
-    const int64_t off0 = (!PAGED && in0) ? cm.row_offsets[lane] : 0;
-    // pass 1: item count
-    int items = wave_sum(in0 ? splits_of(len0) : 0);
-    for (int c0 = 64; c0 < batch; c0 += 64) {
-      const int bb = c0 + lane;
-      items += wave_sum(bb < batch ? splits_of(seq_lens[bb]) : 0);
-    }
-    items *= S::GROUPS;
-    const int per = (items + kXcds - 1) / kXcds;
-    const int item = (bid % kXcds) * per + bid / kXcds;
-    // an XCD's work-groups past its `per` items would repeat the next XCD's
-    if (bid / kXcds >= per || item >= items) return;
-    // pass 2: the sequence holding the item (inclusive prefix sums per step)
-    const int want = item / S::GROUPS;
-    int base = 0;
-    for (int c0 = 0; c0 < batch; c0 += 64) {
-      const int bb = c0 + lane;
-      int len = len0;
-      int64_t off = off0;
-      if (c0 > 0) {
-        len = bb < batch ? seq_lens[bb] : 0;
-        off = (!PAGED && bb < batch) ? cm.row_offsets[bb] : 0;
-      }
-      const int n = bb < batch ? splits_of(len) : 0;
-      const int incl = wave_prefix_sum(n) + base;
-      const uint64_t hit = __ballot(incl > want);
-      if (hit != 0) {
-        const int first = __builtin_ctzll(hit);
-        b = c0 + first;
-        n_b = __shfl(n, first);
-        s = want - (__shfl(incl, first) - n_b);
-        seq_len = __shfl(len, first);
-        row_off = __shfl(off, first);
-        break;
-      }
-      base = __shfl(incl, 63);
-    }
-    b = __builtin_amdgcn_readfirstlane(b);
-    s = __builtin_amdgcn_readfirstlane(s);
-    n_b = __builtin_amdgcn_readfirstlane(n_b);
-    seq_len = __builtin_amdgcn_readfirstlane(seq_len);
-    row_off = (int64_t)uniform_u64((uint64_t)row_off);
-  }
+  DecodeItem it;
+  if (!decode_item<PAGED, S::GROUPS>(seq_lens, cm, batch, num_splits, chunk, it)) return;
+  const int b = it.b, s = it.s, n_b = it.n_b, seq_len = it.seq_len;
+  const int64_t row_off = it.row_off;
   const int g = 0;  // one head group per work item (GROUPS == 1 here)
   static_assert(S::GROUPS == 1, "one work-group covers all heads");
   const int head = g * S::HEADS_PER_GROUP + wave * 32 + l32;
@@ -1163,8 +935,47 @@ struct RopeArgs {
   const int32_t* positions;
   CacheMap cm;  // where the appended rows go
   int DR;
-  u16* cache;
+  u16* cache;      // bf16 cache rows [c_kv | k_rope] (nullptr with an fp8 cache)
+  uint8_t* cache8;  // fp8 cache rows [codes of c_kv | bf16 k_rope], or nullptr
+  float* scale8;    // their power-of-two row scales
 };
+
+// fp8 latent cache rows.  The pages name FP8 storage for the latent cache
+// ("MLA from scratch", what a production implementation adds) and fix nothing
+// else; this library stores c_kv as OCP E4M3FN codes of c_kv / 2^e with one
+// exponent per row, e the smallest integer with max|c_kv| <= 448 * 2^e,
+// clamped to [kFp8MinExp, kFp8MaxExp] (dequantised values are then exact in
+// bf16, and a weight of at most 2^64 times a scale stays finite).
+constexpr int kFp8MinExp = -116, kFp8MaxExp = 63;
+
+__device__ __forceinline__ int fp8_row_exponent(float amax) {
+  if (!(amax > 0.f)) return kFp8MinExp;
+  int x;
+  const float m = frexpf(amax, &x);  // amax = m 2^x, m in [0.5, 1); 448 = 0.875 * 2^9
+  const int e = m <= 0.875f ? x - 9 : x - 8;
+  return e < kFp8MinExp ? kFp8MinExp : (e > kFp8MaxExp ? kFp8MaxExp : e);
+}
+
+// E4M3FN code of y (finite): nearest value, ties to even, magnitudes above
+// 448 saturate to 448; the sign bit is kept (also for a zero result).
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+  const float a = fabsf(y);
+  uint32_t code;
+  if (a >= 448.f) {
+    code = 0x7eu;
+  } else if (a < 0x1p-6f) {  // subnormal range: multiples of 2^-9 (8 * 2^-9 is the first normal)
+    code = (uint32_t)rintf(a * 512.f);
+  } else {
+    int x;
+    frexpf(a, &x);  // a = 1.f * 2^(x - 1)
+    const int E = x - 1;
+    const uint32_t m = (uint32_t)rintf(ldexpf(a, 3 - E));  // 8 .. 16 (16 carries into the exponent)
+    code = ((uint32_t)(E + 7) << 3) + (m - 8u);
+    if (code > 0x7eu) code = 0x7eu;
+  }
+  return sign | code;
+}
 
 // RoPE of pair i of a bf16 pair (x0, x1) at position pos, rounded once
 __device__ __forceinline__ uint32_t rope_pair_bf16(uint32_t x, int pos, double theta) {
@@ -1285,14 +1096,41 @@ __device__ __forceinline__ void absorb_bf16_block(int bid, const u16* __restrict
         if (4 * (tid + 128 * u) < R) *(u32x2*)(crow + 4 * (tid + 128 * u)) = cv[u];
       if (tid < half) *(uint32_t*)(crow + R + 2 * tid) = rope_pair_bf16(k, pos, th);
     };
-    if (ab0 < B) append(ab0, apos, aoff, cvv, kx, ath);
+    // fp8 cache (R == 512: one quad of c_kv_new per thread): the row's
+    // exponent from the block-wide max |c_kv_new|, then the codes
+    auto append8 = [&](int bb, int pos, int64_t off, const u32x2 (&cv)[CVA], uint32_t k, double th) {
+      __shared__ float wmax[2];
+      const int64_t row = ra.cm.row(bb, pos, off);
+      uint8_t* crow = ra.cache8 + row * (R + 2 * ra.DR);
+      const float v0 = bf2f((u16)(cv[0].x & 0xffffu)), v1 = bf2f((u16)(cv[0].x >> 16));
+      const float v2 = bf2f((u16)(cv[0].y & 0xffffu)), v3 = bf2f((u16)(cv[0].y >> 16));
+      float mx = fmaxf(fmaxf(fabsf(v0), fabsf(v1)), fmaxf(fabsf(v2), fabsf(v3)));
+#pragma unroll
+      for (int d = 32; d >= 1; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d));
+      __syncthreads();  // (a block may append several rows) the previous maxima are read
+      if ((tid & 63) == 0) wmax[tid >> 6] = mx;
+      __syncthreads();
+      const int e = fp8_row_exponent(fmaxf(wmax[0], wmax[1]));
+      const float inv = ldexpf(1.f, -e);
+      *(uint32_t*)(crow + 4 * tid) = e4m3_code(v0 * inv) | (e4m3_code(v1 * inv) << 8) |
+                                     (e4m3_code(v2 * inv) << 16) | (e4m3_code(v3 * inv) << 24);
+      if (tid < half) *(uint32_t*)(crow + R + 4 * tid) = rope_pair_bf16(k, pos, th);
+      if (tid == 0) ra.scale8[row] = ldexpf(1.f, e);
+    };
+    const bool fp8 = ra.cache8 != nullptr;
+    if (ab0 < B) {
+      if (fp8) append8(ab0, apos, aoff, cvv, kx, ath);
+      else append(ab0, apos, aoff, cvv, kx, ath);
+    }
     for (int bb = ab0 + H * nblk; bb < B; bb += H * nblk) {  // more than H*nblk sequences
       const int ti = min(tid, half - 1);
       u32x2 cv[CVA];
 #pragma unroll
       for (int u = 0; u < CVA; ++u) cv[u] = *(const u32x2*)(ra.c_kv_new + (int64_t)bb * R + min(4 * (tid + 128 * u), R - 4));
-      append(bb, ra.positions[bb], PAGED ? 0 : ra.cm.row_offsets[bb], cv,
-             *(const uint32_t*)(ra.k_rope_new + (int64_t)bb * ra.DR + 2 * ti), freqs.theta[ti]);
+      const int64_t off = PAGED ? 0 : ra.cm.row_offsets[bb];
+      const uint32_t k = *(const uint32_t*)(ra.k_rope_new + (int64_t)bb * ra.DR + 2 * ti);
+      if (fp8) append8(bb, ra.positions[bb], off, cv, k, freqs.theta[ti]);
+      else append(bb, ra.positions[bb], off, cv, k, freqs.theta[ti]);
     }
   }
 
@@ -2170,11 +2008,11 @@ template <int DH>
 mla_status launch_absorb_rope_bf16(const mla_dims& d, const void* q_nope, const void* w_uk, const void* q_rope,
                                    const void* c_kv_new, const void* k_rope_new, const int32_t* positions,
                                    const CacheMap& cm, const RopeFreqs& freqs, void* q_lat, void* kv_cache,
-                                   hipStream_t stream) {
+                                   hipStream_t stream, uint8_t* cache8 = nullptr, float* scale8 = nullptr) {
   if (d.rank % 64 != 0) return fail(MLA_ERR_UNSUPPORTED, "rank must be a multiple of 64");
   const int blocks = (d.heads + kXcds - 1) / kXcds * kXcds * (d.rank / 64);  // whole groups of 8 heads
   const RopeArgs ra{(const u16*)q_rope, (const u16*)c_kv_new, (const u16*)k_rope_new, positions, cm, d.d_rope,
-                    (u16*)kv_cache};
+                    (u16*)kv_cache, cache8, scale8};
   if (cm.block_table != nullptr) {
     hipLaunchKernelGGL((absorb_rope_bf16_kernel<DH, true>), dim3(blocks), dim3(128), 0, stream, (const u16*)q_nope,
                        (const u16*)w_uk, d.batch, d.heads, d.rank, ra, freqs, (u16*)q_lat);
@@ -2441,6 +2279,108 @@ mla_status mla_decode_latent_paged(const mla_dims* dims, const void* q_lat, cons
   if ((st = paged_map(block_table, bt_stride, page_rows, total_pages, &cm)) != MLA_OK) return st;
   g_last_error.clear();
   return decode_dispatch(dims, q_lat, kv_cache, cm, seq_lens, max_seq_len, num_splits, o_part, lse_part, stream);
+}
+
+// ---- fp8 latent cache (rows of 512 E4M3 codes + 64 bf16 RoPE values, one
+// power-of-two scale per row; the bf16 instance H 128, r 512, d_rope 64)
+
+static mla_status check_fp8_dims(const mla_dims* dims, const float* kv_scale) {
+  if (find_inst(*dims) != kBf16H128R512D64)
+    return fail(MLA_ERR_UNSUPPORTED, "the fp8 cache is supported for (BF16, heads 128, rank 512, d_rope 64)");
+  if (kv_scale == nullptr) return fail(MLA_ERR_INVALID_ARG, "kv_scale NULL");
+  if (((uintptr_t)kv_scale & 15u) != 0) return fail(MLA_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
+  return MLA_OK;
+}
+
+static mla_status decode_fp8_impl(const mla_dims* dims, const void* q_lat, const void* kv_cache,
+                                  const float* kv_scale, const CacheMap& cm, const int32_t* seq_lens,
+                                  int32_t max_seq_len, int32_t num_splits, void* o_part, float* lse_part,
+                                  void* stream) {
+  const hipError_t e = mla_launch_decode_fp8(q_lat, kv_cache, kv_scale, cm, seq_lens, dims->batch, num_splits,
+                                             chunk_rows(max_seq_len, num_splits), o_part, lse_part,
+                                             scale_of(*dims) * kLog2e, (hipStream_t)stream);
+  if (e == hipErrorInvalidConfiguration) return fail(MLA_ERR_UNSUPPORTED, "grid too large");
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, std::string("mla_decode_latent_fp8: ") + hipGetErrorString(e));
+  return MLA_OK;
+}
+
+mla_status mla_decode_latent_fp8(const mla_dims* dims, const void* q_lat, const void* kv_cache,
+                                 const float* kv_scale, const int64_t* row_offsets, const int32_t* seq_lens,
+                                 int64_t total_rows, int32_t max_seq_len, int32_t num_splits, void* o_part,
+                                 float* lse_part, void* stream) {
+  mla_status st = check_decode_args(dims, q_lat, kv_cache, seq_lens, max_seq_len, num_splits, o_part, lse_part);
+  if (st != MLA_OK) return st;
+  if ((st = check_fp8_dims(dims, kv_scale)) != MLA_OK) return st;
+  CacheMap cm;
+  if ((st = packed_map(row_offsets, total_rows, &cm)) != MLA_OK) return st;
+  g_last_error.clear();
+  return decode_fp8_impl(dims, q_lat, kv_cache, kv_scale, cm, seq_lens, max_seq_len, num_splits, o_part, lse_part,
+                         stream);
+}
+
+mla_status mla_decode_latent_fp8_paged(const mla_dims* dims, const void* q_lat, const void* kv_cache,
+                                       const float* kv_scale, const int32_t* block_table, int32_t bt_stride,
+                                       int32_t page_rows, int64_t total_pages, const int32_t* seq_lens,
+                                       int32_t max_seq_len, int32_t num_splits, void* o_part, float* lse_part,
+                                       void* stream) {
+  mla_status st = check_decode_args(dims, q_lat, kv_cache, seq_lens, max_seq_len, num_splits, o_part, lse_part);
+  if (st != MLA_OK) return st;
+  if ((st = check_fp8_dims(dims, kv_scale)) != MLA_OK) return st;
+  CacheMap cm;
+  if ((st = paged_map(block_table, bt_stride, page_rows, total_pages, &cm)) != MLA_OK) return st;
+  g_last_error.clear();
+  return decode_fp8_impl(dims, q_lat, kv_cache, kv_scale, cm, seq_lens, max_seq_len, num_splits, o_part, lse_part,
+                         stream);
+}
+
+static mla_status absorb_rope_fp8_impl(const mla_dims* dims, const void* q_nope, const void* w_uk, const void* q_rope,
+                                       const void* c_kv_new, const void* k_rope_new, const int32_t* positions,
+                                       const CacheMap& cm, void* q_lat, void* kv_cache, float* kv_scale,
+                                       void* stream) {
+  mla_status st;
+  if ((st = check_ptrs({q_nope, w_uk})) != MLA_OK) return st;
+  const RopeFreqs freqs = rope_freqs(dims);
+  hipStream_t s = (hipStream_t)stream;
+  switch (dims->d_head) {
+    case 32: return launch_absorb_rope_bf16<32>(*dims, q_nope, w_uk, q_rope, c_kv_new, k_rope_new, positions, cm,
+                                                freqs, q_lat, nullptr, s, (uint8_t*)kv_cache, kv_scale);
+    case 64: return launch_absorb_rope_bf16<64>(*dims, q_nope, w_uk, q_rope, c_kv_new, k_rope_new, positions, cm,
+                                                freqs, q_lat, nullptr, s, (uint8_t*)kv_cache, kv_scale);
+    case 128: return launch_absorb_rope_bf16<128>(*dims, q_nope, w_uk, q_rope, c_kv_new, k_rope_new, positions, cm,
+                                                  freqs, q_lat, nullptr, s, (uint8_t*)kv_cache, kv_scale);
+    case 256: return launch_absorb_rope_bf16<256>(*dims, q_nope, w_uk, q_rope, c_kv_new, k_rope_new, positions, cm,
+                                                  freqs, q_lat, nullptr, s, (uint8_t*)kv_cache, kv_scale);
+  }
+  return fail(MLA_ERR_UNSUPPORTED, "d_head");
+}
+
+mla_status mla_absorb_rope_fp8(const mla_dims* dims, const void* q_nope, const void* w_uk, const void* q_rope,
+                               const void* c_kv_new, const void* k_rope_new, const int32_t* positions,
+                               const int64_t* row_offsets, int64_t total_rows, void* q_lat, void* kv_cache,
+                               float* kv_scale, void* stream) {
+  mla_status st = check_rope_args(dims, q_rope, c_kv_new, k_rope_new, positions, q_lat, kv_cache);
+  if (st != MLA_OK) return st;
+  if ((st = check_fp8_dims(dims, kv_scale)) != MLA_OK) return st;
+  CacheMap cm;
+  if ((st = packed_map(row_offsets, total_rows, &cm)) != MLA_OK) return st;
+  g_last_error.clear();
+  return absorb_rope_fp8_impl(dims, q_nope, w_uk, q_rope, c_kv_new, k_rope_new, positions, cm, q_lat, kv_cache,
+                              kv_scale, stream);
+}
+
+mla_status mla_absorb_rope_fp8_paged(const mla_dims* dims, const void* q_nope, const void* w_uk, const void* q_rope,
+                                     const void* c_kv_new, const void* k_rope_new, const int32_t* positions,
+                                     const int32_t* block_table, int32_t bt_stride, int32_t page_rows,
+                                     int64_t total_pages, void* q_lat, void* kv_cache, float* kv_scale,
+                                     void* stream) {
+  mla_status st = check_rope_args(dims, q_rope, c_kv_new, k_rope_new, positions, q_lat, kv_cache);
+  if (st != MLA_OK) return st;
+  if ((st = check_fp8_dims(dims, kv_scale)) != MLA_OK) return st;
+  CacheMap cm;
+  if ((st = paged_map(block_table, bt_stride, page_rows, total_pages, &cm)) != MLA_OK) return st;
+  g_last_error.clear();
+  return absorb_rope_fp8_impl(dims, q_nope, w_uk, q_rope, c_kv_new, k_rope_new, positions, cm, q_lat, kv_cache,
+                              kv_scale, stream);
 }
 
 mla_status mla_combine(const mla_dims* dims, const void* o_part, const float* lse_part, int32_t num_splits,

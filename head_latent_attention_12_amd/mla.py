@@ -22,7 +22,8 @@ STATUS = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARG", 2: "MLA_ERR_UNSUPPORTED", 3: "M
 
 EXPORTS = ("mla_absorb_q", "mla_rope_append", "mla_decode_latent", "mla_combine", "mla_up_v",
            "mla_combine_up_v", "mla_absorb_rope", "mla_decode_latent_paged", "mla_rope_append_paged",
-           "mla_absorb_rope_paged", "mla_kv_down", "mla_kv_down_workspace_size", "mla_partials_size", "mla_plan_splits", "mla_check_dims", "mla_status_string", "mla_last_error")
+           "mla_absorb_rope_paged", "mla_decode_latent_fp8", "mla_decode_latent_fp8_paged",
+           "mla_absorb_rope_fp8", "mla_absorb_rope_fp8_paged", "mla_kv_down", "mla_kv_down_workspace_size", "mla_partials_size", "mla_plan_splits", "mla_check_dims", "mla_status_string", "mla_last_error")
 
 
 class MlaDims(ctypes.Structure):
@@ -61,6 +62,10 @@ def lib() -> ctypes.CDLL:
             "mla_decode_latent_paged": (i32, [D, P, P, P, i32, i32, i64, P, i32, i32, P, P, P]),
             "mla_rope_append_paged": (i32, [D, P, P, P, P, P, i32, i32, i64, P, P, P]),
             "mla_absorb_rope_paged": (i32, [D, P, P, P, P, P, P, P, i32, i32, i64, P, P, P]),
+            "mla_decode_latent_fp8": (i32, [D, P, P, P, P, P, i64, i32, i32, P, P, P]),
+            "mla_decode_latent_fp8_paged": (i32, [D, P, P, P, P, i32, i32, i64, P, i32, i32, P, P, P]),
+            "mla_absorb_rope_fp8": (i32, [D, P, P, P, P, P, P, P, i64, P, P, P, P]),
+            "mla_absorb_rope_fp8_paged": (i32, [D, P, P, P, P, P, P, P, i32, i32, i64, P, P, P, P]),
             "mla_kv_down": (i32, [D, i32, P, P, P, P, ctypes.c_float, P, P, P, P]),
             "mla_kv_down_workspace_size": (i32, [D, i32, ctypes.POINTER(ctypes.c_size_t)]),
             "mla_partials_size": (i32, [D, i32, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]),
@@ -148,6 +153,36 @@ def mla_absorb_rope_paged(dims, q_nope, w_uk, q_rope, c_kv_new, k_rope_new, posi
     _check("mla_absorb_rope_paged", lib().mla_absorb_rope_paged(
         ctypes.byref(dims), _p(q_nope), _p(w_uk), _p(q_rope), _p(c_kv_new), _p(k_rope_new), _p(positions),
         _p(block_table), int(bt_stride), int(page_rows), int(total_pages), _p(q_lat), _p(kv_cache), _s(stream)))
+
+
+def mla_decode_latent_fp8(dims, q_lat, kv_cache, kv_scale, row_offsets, seq_lens, total_rows, max_seq_len,
+                          num_splits, o_part, lse_part, stream=None):
+    _check("mla_decode_latent_fp8", lib().mla_decode_latent_fp8(
+        ctypes.byref(dims), _p(q_lat), _p(kv_cache), _p(kv_scale), _p(row_offsets), _p(seq_lens), int(total_rows),
+        int(max_seq_len), int(num_splits), _p(o_part), _p(lse_part), _s(stream)))
+
+
+def mla_decode_latent_fp8_paged(dims, q_lat, kv_cache, kv_scale, block_table, bt_stride, page_rows, total_pages,
+                                seq_lens, max_seq_len, num_splits, o_part, lse_part, stream=None):
+    _check("mla_decode_latent_fp8_paged", lib().mla_decode_latent_fp8_paged(
+        ctypes.byref(dims), _p(q_lat), _p(kv_cache), _p(kv_scale), _p(block_table), int(bt_stride),
+        int(page_rows), int(total_pages), _p(seq_lens), int(max_seq_len), int(num_splits), _p(o_part),
+        _p(lse_part), _s(stream)))
+
+
+def mla_absorb_rope_fp8(dims, q_nope, w_uk, q_rope, c_kv_new, k_rope_new, positions, row_offsets, total_rows,
+                        q_lat, kv_cache, kv_scale, stream=None):
+    _check("mla_absorb_rope_fp8", lib().mla_absorb_rope_fp8(
+        ctypes.byref(dims), _p(q_nope), _p(w_uk), _p(q_rope), _p(c_kv_new), _p(k_rope_new), _p(positions),
+        _p(row_offsets), int(total_rows), _p(q_lat), _p(kv_cache), _p(kv_scale), _s(stream)))
+
+
+def mla_absorb_rope_fp8_paged(dims, q_nope, w_uk, q_rope, c_kv_new, k_rope_new, positions, block_table, bt_stride,
+                              page_rows, total_pages, q_lat, kv_cache, kv_scale, stream=None):
+    _check("mla_absorb_rope_fp8_paged", lib().mla_absorb_rope_fp8_paged(
+        ctypes.byref(dims), _p(q_nope), _p(w_uk), _p(q_rope), _p(c_kv_new), _p(k_rope_new), _p(positions),
+        _p(block_table), int(bt_stride), int(page_rows), int(total_pages), _p(q_lat), _p(kv_cache), _p(kv_scale),
+        _s(stream)))
 
 
 def mla_combine(dims, o_part, lse_part, num_splits, o_lat, lse=None, stream=None):

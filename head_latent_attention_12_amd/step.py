@@ -9,7 +9,7 @@ import numpy as np
 import torch
 
 from . import mla
-from .synthetic import BF16, PagedCache, StepInputs, paginate
+from .synthetic import BF16, Fp8Cache, PagedCache, StepInputs, make_fp8_cache, paginate
 
 
 def _dev(a: np.ndarray, device) -> torch.Tensor:
@@ -34,12 +34,14 @@ class DeviceStep:
 
     def __init__(self, inp: StepInputs, num_splits: int | None = None, device: str = "cuda:0",
                  weights: "DeviceStep | None" = None, scratch: "DeviceStep | None" = None,
-                 page_rows: int | None = None, page_seed: int = 0):
+                 page_rows: int | None = None, page_seed: int = 0, fp8: bool = False, fp8_seed: int = 3):
         """``weights``: share W_UK/W_UV with another step (same layer).
         ``scratch``: share the per-step temporaries (q_lat, split partials,
         o_lat, lse, out) with another step of the same shape, as successive
         layers of one decode step would.  ``page_rows``: keep the cache in
-        pages of that many rows behind a block table (the paged calls)."""
+        pages of that many rows behind a block table (the paged calls).
+        ``fp8``: keep the cache in the fp8 row layout (codes drawn with
+        ``fp8_seed``, the fp8 calls)."""
         self.inp = inp
         self.device = device
         self.dims = mla.make_dims(inp.B, inp.H, inp.d_head, inp.d_v, inp.r, inp.d_rope,
@@ -54,12 +56,17 @@ class DeviceStep:
         self.q_nope = _dev(inp.q_nope, device)
         self.q_rope = _dev(inp.q_rope, device)
         self.paged: PagedCache | None = None
+        self.fp8: Fp8Cache | None = make_fp8_cache(inp, fp8_seed) if fp8 else None
         if page_rows is None:
-            self.kv_cache = _dev(inp.kv_cache, device)
+            self.kv_cache = _dev(self.fp8.rows if fp8 else inp.kv_cache, device)
+            if fp8:
+                self.kv_scale = _dev(self.fp8.scale, device)
         else:
-            self.paged = paginate(inp, page_rows, seed=page_seed)
+            self.paged = paginate(inp, page_rows, seed=page_seed, fp8=self.fp8)
             self.kv_cache = _dev(self.paged.cache, device)
             self.block_table = _dev(self.paged.block_table, device)
+            if fp8:
+                self.kv_scale = _dev(self.paged.scale, device)
         self.c_kv_new = _dev(inp.c_kv_new, device)
         self.k_rope_new = _dev(inp.k_rope_new, device)
         self.positions = _dev(inp.positions.astype(np.int32), device)
@@ -86,13 +93,19 @@ class DeviceStep:
 
     # the calls ----------------------------------------------------------------
     def absorb_q(self, stream=None):
+        self._no_fp8("absorb_q")
         mla.mla_absorb_q(self.dims, self.q_nope, self.w_uk, self.q_lat, stream)
 
     def _pages(self):
         pc = self.paged
         return self.block_table, pc.bt_stride, pc.page_rows, pc.total_pages
 
+    def _no_fp8(self, call):
+        if self.fp8 is not None:
+            raise RuntimeError(f"{call}: the fp8 cache is written by absorb_rope (mla_absorb_rope_fp8*)")
+
     def rope_append(self, stream=None):
+        self._no_fp8("rope_append")
         if self.paged is not None:
             mla.mla_rope_append_paged(self.dims, self.q_rope, self.c_kv_new, self.k_rope_new, self.positions,
                                       *self._pages(), self.q_lat, self.kv_cache, stream)
@@ -101,6 +114,16 @@ class DeviceStep:
                             self.row_offsets, self.inp.total_rows, self.q_lat, self.kv_cache, stream)
 
     def absorb_rope(self, stream=None):
+        if self.fp8 is not None:
+            if self.paged is not None:
+                mla.mla_absorb_rope_fp8_paged(self.dims, self.q_nope, self.w_uk, self.q_rope, self.c_kv_new,
+                                              self.k_rope_new, self.positions, *self._pages(), self.q_lat,
+                                              self.kv_cache, self.kv_scale, stream)
+            else:
+                mla.mla_absorb_rope_fp8(self.dims, self.q_nope, self.w_uk, self.q_rope, self.c_kv_new,
+                                        self.k_rope_new, self.positions, self.row_offsets, self.inp.total_rows,
+                                        self.q_lat, self.kv_cache, self.kv_scale, stream)
+            return
         if self.paged is not None:
             mla.mla_absorb_rope_paged(self.dims, self.q_nope, self.w_uk, self.q_rope, self.c_kv_new,
                                       self.k_rope_new, self.positions, *self._pages(), self.q_lat, self.kv_cache,
@@ -110,6 +133,16 @@ class DeviceStep:
                             self.positions, self.row_offsets, self.inp.total_rows, self.q_lat, self.kv_cache, stream)
 
     def decode_latent(self, stream=None):
+        if self.fp8 is not None:
+            if self.paged is not None:
+                mla.mla_decode_latent_fp8_paged(self.dims, self.q_lat, self.kv_cache, self.kv_scale, *self._pages(),
+                                                self.seq_lens, self.inp.max_seq_len, self.num_splits, self.o_part,
+                                                self.lse_part, stream)
+            else:
+                mla.mla_decode_latent_fp8(self.dims, self.q_lat, self.kv_cache, self.kv_scale, self.row_offsets,
+                                          self.seq_lens, self.inp.total_rows, self.inp.max_seq_len,
+                                          self.num_splits, self.o_part, self.lse_part, stream)
+            return
         if self.paged is not None:
             mla.mla_decode_latent_paged(self.dims, self.q_lat, self.kv_cache, *self._pages(), self.seq_lens,
                                         self.inp.max_seq_len, self.num_splits, self.o_part, self.lse_part, stream)
@@ -154,6 +187,19 @@ class DeviceStep:
 
     def cache_f64(self) -> np.ndarray:
         return bits_to_f64(self.kv_cache, self.inp.dtype)
+
+    def fp8_raw(self):
+        """(row bytes, scales) of an fp8 cache in the packed order."""
+        rows, scale = self.kv_cache.cpu().numpy(), self.kv_scale.cpu().numpy()
+        if self.paged is None:
+            return rows, scale
+        out_r, out_s = self.fp8.rows.copy(), self.fp8.scale.copy()
+        for b in range(self.inp.B):
+            n = int(self.inp.lens[b]) + 1
+            o = int(self.inp.row_offsets[b])
+            idx = self.paged.rows_of(b, n)
+            out_r[o:o + n], out_s[o:o + n] = rows[idx], scale[idx]
+        return out_r, out_s
 
     def cache_raw(self) -> np.ndarray:
         """The cache in storage form, in the packed order (a paged cache is

@@ -233,7 +233,8 @@ class PagedCache:
 
     page_rows: int
     block_table: np.ndarray   # [B, bt_stride] int32 physical page ids
-    cache: np.ndarray         # [total_pages * page_rows, r + d_rope], storage form
+    cache: np.ndarray         # [total_pages * page_rows, r + d_rope], storage form (fp8: row bytes)
+    scale: np.ndarray | None = None  # fp8 cache: [total_pages * page_rows] row scales
 
     @property
     def bt_stride(self) -> int:
@@ -249,33 +250,79 @@ class PagedCache:
         return self.block_table[b, t // self.page_rows].astype(np.int64) * self.page_rows + t % self.page_rows
 
 
-def paginate(step: StepInputs, page_rows: int, seed: int = 0, spare_pages: int = 3) -> PagedCache:
-    """Scatter the packed cache of ``step`` into pages of ``page_rows`` rows,
-    page ids shuffled with a seeded permutation (so the pages of different
-    sequences interleave), each sequence given the pages for its L_b + 1 rows
-    (the appended row included).  Unused page rows and the ``spare_pages``
-    never referenced hold NaN, so that a read through a wrong page cannot
-    pass."""
+def paginate(step: StepInputs, page_rows: int, seed: int = 0, spare_pages: int = 3,
+             fp8: "Fp8Cache | None" = None) -> PagedCache:
+    """Scatter the packed cache of ``step`` (or its fp8 form ``fp8``) into
+    pages of ``page_rows`` rows, page ids shuffled with a seeded permutation
+    (so the pages of different sequences interleave), each sequence given the
+    pages for its L_b + 1 rows (the appended row included).  Unused page rows
+    and the ``spare_pages`` never referenced hold NaN (fp8: NaN codes and
+    scales), so that a read through a wrong page cannot pass."""
     rng = np.random.default_rng(seed)
     need = [(int(L) + 1 + page_rows - 1) // page_rows for L in step.lens]
     bt_stride = max(need) + 1
     total_pages = sum(need) + spare_pages
     perm = rng.permutation(total_pages).astype(np.int32)
-    nan = np.uint16(0x7FC0) if step.dtype == BF16 else np.float32(np.nan)
-    cache = np.full((total_pages * page_rows, step.W), nan, dtype=step.kv_cache.dtype)
+    n_phys = total_pages * page_rows
+    if fp8 is None:
+        nan = np.uint16(0x7FC0) if step.dtype == BF16 else np.float32(np.nan)
+        src_rows, src_scale = step.kv_cache, None
+        cache = np.full((n_phys, step.W), nan, dtype=step.kv_cache.dtype)
+        scale = None
+    else:
+        src_rows, src_scale = fp8.rows, fp8.scale
+        cache = np.full((n_phys, fp8.rows.shape[1]), 0x7F, dtype=np.uint8)
+        scale = np.full(n_phys, np.nan, dtype=np.float32)
     block_table = np.full((step.B, bt_stride), -1, dtype=np.int32)
     k = 0
     for b in range(step.B):
         block_table[b, :need[b]] = perm[k:k + need[b]]
         k += need[b]
-    paged = PagedCache(page_rows, block_table, cache)
+    paged = PagedCache(page_rows, block_table, cache, scale)
     for b in range(step.B):
         n = int(step.lens[b]) + 1
         src = int(step.row_offsets[b])
-        cache[paged.rows_of(b, n)] = step.kv_cache[src:src + n]
+        dst = paged.rows_of(b, n)
+        cache[dst] = src_rows[src:src + n]
+        if scale is not None:
+            scale[dst] = src_scale[src:src + n]
     # unused entries point at a spare page (in range, never read for valid rows)
     block_table[block_table < 0] = perm[-1]
     return paged
+
+
+@dataclasses.dataclass
+class Fp8Cache:
+    """A latent cache in the fp8 row layout: per row, r E4M3 codes then the
+    d_rope bf16 RoPE values as little-endian bytes, plus one fp32 scale."""
+
+    rows: np.ndarray    # [total_rows, r + 2 * d_rope] uint8
+    scale: np.ndarray   # [total_rows] float32
+
+
+def make_fp8_cache(step: StepInputs, seed: int = 3) -> Fp8Cache:
+    """Cached rows of ``step`` in the fp8 layout, drawn directly as codes (no
+    quantisation here): sign and mantissa uniform, exponent field
+    round(N(12.8, 1.1)) clipped to [0, 15] (the NaN code becomes 448), and a
+    row scale 2^e with e uniform in {-8, -7}: values with an RMS near 0.85 and
+    a 99th percentile near 3, like the unit-RMS bf16 rows; the RoPE values are
+    the step's bf16 ones.  The
+    append slots hold NaN codes and a NaN scale."""
+    assert step.dtype == BF16, "the fp8 cache layout keeps bf16 RoPE values"
+    rng = np.random.default_rng(seed)
+    n, r = step.total_rows, step.r
+    expo = np.clip(np.rint(rng.normal(12.8, 1.1, size=(n, r))), 0, 15).astype(np.uint8)
+    codes = (rng.integers(0, 2, size=(n, r), dtype=np.uint8) << 7) | (expo << 3) | \
+        rng.integers(0, 8, size=(n, r), dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] -= 1
+    rows = np.empty((n, r + 2 * step.d_rope), dtype=np.uint8)
+    rows[:, :r] = codes
+    rows[:, r:] = np.ascontiguousarray(step.kv_cache[:, r:]).view(np.uint8)
+    scale = np.ldexp(1.0, rng.integers(-8, -6, size=n)).astype(np.float32)
+    slots = step.row_offsets + step.lens
+    rows[slots, :r] = 0x7F
+    scale[slots] = np.nan
+    return Fp8Cache(rows, scale)
 
 
 @dataclasses.dataclass

@@ -19,8 +19,11 @@
  *                     state (the step before the path)
  *   mla_*_paged       the calls that touch the cache, for a cache kept in
  *                     fixed-size pages behind a block table
- *   mla_combine_up_v  the last two in one call: the merge is formed where
- *                     W_UV consumes it and o_lat never goes to memory
+ *   mla_combine_up_v  mla_combine and mla_up_v in one call: the merge is
+ *                     formed where W_UV consumes it and o_lat never goes to
+ *                     memory
+ *   mla_*_fp8         the calls that touch the cache, for a cache whose
+ *                     latents are stored in 8-bit floating point
  *
  * Sources (page title, section):
  *   [P1] "DeepSeek MLA, Built From the Paper": section 1 (the cache holds
@@ -214,6 +217,54 @@ mla_status mla_absorb_rope_paged(const mla_dims* dims, const void* q_nope, const
                                  const int32_t* positions, const int32_t* block_table,
                                  int32_t bt_stride, int32_t page_rows, int64_t total_pages,
                                  void* q_lat, void* kv_cache, void* stream);
+
+/* FP8 latent cache ([P2] names FP8 quantisation of the latent cache among
+ * what a production implementation adds, and fixes no format; the one below
+ * is this library's).  Row layout, 640 bytes per cached token:
+ *   bytes [0, 512)   c_kv as OCP E4M3FN codes of c_kv / s (sign, 4 exponent
+ *                    bits with bias 7, 3 mantissa bits; 448 the largest value;
+ *                    code 0x7f/0xff is NaN and is never written)
+ *   bytes [512, 640) the rotated RoPE key, 64 bf16 values (as in the bf16 row)
+ * with s = kv_scale[row] (fp32 [rows], 16-byte aligned base), a power of two:
+ * the smallest 2^e, e an integer in [-116, 63], with max|c_kv| <= 448 * 2^e.
+ * The cached latent is the dequantised value code * s (exact in bf16).  Only
+ * the bf16 instance (heads 128, rank 512, d_rope 64); other dims give
+ * MLA_ERR_UNSUPPORTED.
+ *
+ * mla_decode_latent_fp8: mla_decode_latent over the dequantised cache, same
+ * q_lat, o_part and lse_part (so mla_combine / mla_combine_up_v apply
+ * unchanged).  kv_cache: device [total_rows][640] bytes; rows as for
+ * mla_decode_latent (row_offsets) or mla_decode_latent_paged (block table).
+ *
+ * mla_absorb_rope_fp8: mla_absorb_rope, except that the appended row is
+ * written in the fp8 layout: c_kv_new (bf16) is quantised with its own row
+ * exponent (nearest code, ties to even; magnitudes above 448 * s, possible
+ * only at the exponent clamp, saturate to 448), the rotated key is written as
+ * in the bf16 row, and kv_scale[row] = s.  Inputs must be finite. */
+mla_status mla_decode_latent_fp8(const mla_dims* dims, const void* q_lat, const void* kv_cache,
+                                 const float* kv_scale, const int64_t* row_offsets,
+                                 const int32_t* seq_lens, int64_t total_rows, int32_t max_seq_len,
+                                 int32_t num_splits, void* o_part, float* lse_part, void* stream);
+
+mla_status mla_decode_latent_fp8_paged(const mla_dims* dims, const void* q_lat, const void* kv_cache,
+                                       const float* kv_scale, const int32_t* block_table,
+                                       int32_t bt_stride, int32_t page_rows, int64_t total_pages,
+                                       const int32_t* seq_lens, int32_t max_seq_len,
+                                       int32_t num_splits, void* o_part, float* lse_part,
+                                       void* stream);
+
+mla_status mla_absorb_rope_fp8(const mla_dims* dims, const void* q_nope, const void* w_uk,
+                               const void* q_rope, const void* c_kv_new, const void* k_rope_new,
+                               const int32_t* positions, const int64_t* row_offsets,
+                               int64_t total_rows, void* q_lat, void* kv_cache, float* kv_scale,
+                               void* stream);
+
+mla_status mla_absorb_rope_fp8_paged(const mla_dims* dims, const void* q_nope, const void* w_uk,
+                                     const void* q_rope, const void* c_kv_new,
+                                     const void* k_rope_new, const int32_t* positions,
+                                     const int32_t* block_table, int32_t bt_stride,
+                                     int32_t page_rows, int64_t total_pages, void* q_lat,
+                                     void* kv_cache, float* kv_scale, void* stream);
 
 /* Latent KV production from the hidden state, the step before the append
  * ([P2] module structure: W_DKV, then the RMSNorm norm_kv over the latent;

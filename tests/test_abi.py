@@ -20,7 +20,7 @@ P16 = 0x1000  # an aligned, never-dereferenced stand-in address (validation fail
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(mla_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_five_calls():

@@ -32,7 +32,10 @@ BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk 
 FP32_PEAK_TFLOPS = 157.3
 MALL_BYTES = 256 * 2 ** 20
 COUNTERS = os.path.join(ROOT, "profiles", "decode_latent_counters.json")
-SOURCE = os.path.join(ROOT, "head_latent_attention_12_amd", "csrc", "mla.hip")
+# the bf16 decode kernel's sources (counter-derived traffic is reported only
+# while they are unchanged)
+SOURCES = [os.path.join(ROOT, "head_latent_attention_12_amd", "csrc", f)
+           for f in ("mla.hip", "mla_common.h", "decode_asm.inc")]
 
 
 def workload_label(inp) -> str:
@@ -41,7 +44,7 @@ def workload_label(inp) -> str:
             f"r={inp.r} d_rope={inp.d_rope} {lens}")
 
 
-def algorithmic(inp):
+def algorithmic(inp, fp8=False):
     """Algorithmic bytes and flops of the step and of the decode kernel alone.
 
     Bytes: every attended cache row read once, the appended row written once,
@@ -52,18 +55,22 @@ def algorithmic(inp):
     s = 2 if inp.dtype == "bf16" else 4
     rows = int(inp.seq_lens.sum())
     B, H, dh, dv, r, dr, W = inp.B, inp.H, inp.d_head, inp.d_v, inp.r, inp.d_rope, inp.W
-    step_bytes = (rows * W * s + B * W * s            # cache read + new row written
+    rb = r + 2 * dr + 4 if fp8 else W * s             # bytes per cache row (fp8: codes, bf16 RoPE, scale)
+    step_bytes = (rows * rb + B * rb                  # cache read + new row written
                   + 2 * H * dh * r * s                # W_UK, W_UV (d_v = d_head here)
                   + B * H * (dh + dr) * s + B * (r + dr) * s  # q_nope, q_rope, c_kv_new, k_rope_new
                   + B * H * dv * 4)                   # out (fp32)
     step_flops = 2 * H * (W + r) * rows + 2 * B * H * dh * r + 2 * B * H * dv * r
-    k3_bytes = rows * W * s + B * H * W * s            # cache rows + q_lat
+    k3_bytes = rows * rb + B * H * W * s               # cache rows + q_lat
     k3_flops = 2 * H * (W + r) * rows
     return rows, step_bytes, step_flops, k3_bytes, k3_flops
 
 
 def source_hash() -> str:
-    return hashlib.sha256(open(SOURCE, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def counter_traffic(workload: str):
@@ -84,10 +91,13 @@ CALIB_KERNEL = "neg_kernel"     # torch.neg on float32: one read and one write p
 
 
 def counters_run(workload: str, steps: int, warmup: int) -> None:
-    """The workload's timed steps, then the calibration kernel 4 times: the
-    program rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE profiles."""
+    """The workload's timed steps (also over an fp8 cache for the bf16
+    DeepSeek-V2 shapes), then the calibration kernel 4 times: the program
+    rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE profiles."""
     import torch
     run_workload(workload, steps, warmup, min_sets=5, verbose=True)
+    if workload.startswith("dsv2"):  # the same steps over an fp8 cache (its decode kernel's counters)
+        run_workload(workload, steps, warmup, min_sets=5, verbose=True, fp8=True)
     src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     for _ in range(4):
@@ -225,21 +235,23 @@ def capture_round(sets):
     return graph
 
 
-def run_workload(name, steps, warmup, min_sets, verbose=True, page_rows=None):
+def run_workload(name, steps, warmup, min_sets, verbose=True, page_rows=None, fp8=False):
     import torch
 
     from head_latent_attention_12_amd import mla, synthetic as syn
     from head_latent_attention_12_amd.step import DeviceStep
 
     inp = syn.make_inputs(name)
-    rows, step_bytes, step_flops, k3_bytes, k3_flops = algorithmic(inp)
-    set_bytes = inp.total_rows * inp.W * (2 if inp.dtype == "bf16" else 4) + 2 * inp.H * inp.d_head * inp.r * 2
+    rows, step_bytes, step_flops, k3_bytes, k3_flops = algorithmic(inp, fp8)
+    row_bytes = inp.r + 2 * inp.d_rope + 4 if fp8 else inp.W * (2 if inp.dtype == "bf16" else 4)
+    set_bytes = inp.total_rows * row_bytes + 2 * inp.H * inp.d_head * inp.r * 2
     n_sets = max(min_sets, int(np.ceil(2 * MALL_BYTES / set_bytes)))
     # each set has its own cache and weights (like successive layers); the
     # per-step temporaries (q_lat, split partials, o_lat, out) are one shared
     # workspace, as a multi-layer decode would reuse them
-    sets = [DeviceStep(inp, page_rows=page_rows, page_seed=0)]
-    sets += [DeviceStep(inp, scratch=sets[0], page_rows=page_rows, page_seed=i) for i in range(1, n_sets)]
+    sets = [DeviceStep(inp, page_rows=page_rows, page_seed=0, fp8=fp8)]
+    sets += [DeviceStep(inp, scratch=sets[0], page_rows=page_rows, page_seed=i, fp8=fp8, fp8_seed=3 + i)
+             for i in range(1, n_sets)]
     stream = torch.cuda.current_stream()
     for i in range(warmup):
         sets[i % n_sets].run()
@@ -306,9 +318,10 @@ def run_workload(name, steps, warmup, min_sets, verbose=True, page_rows=None):
 
     ms = wall * 1e3 / steps
     res = {
-        "name": name if page_rows is None else f"{name}_paged{page_rows}",
+        "name": (name if page_rows is None else f"{name}_paged{page_rows}") + ("_fp8" if fp8 else ""),
         "workload": workload_label(inp) + ("" if page_rows is None else
-                                           f", paged cache ({page_rows}-row pages, shuffled block table)"),
+                                           f", paged cache ({page_rows}-row pages, shuffled block table)")
+        + (", fp8 latent cache (E4M3 codes, one power-of-two scale per row, bf16 RoPE key)" if fp8 else ""),
         "cached_tokens_per_step": rows,
         "ms_per_step": ms,
         "device_ms_per_step": dev_ms,
@@ -374,11 +387,12 @@ def main():
     main_res = run_workload(args.workload, args.steps, args.warmup, min_sets=5)
     others = {}
     if not args.no_others:
-        for name, page_rows in (("dsv2_ragged", None), ("dsv2_long", None), ("dsv2_ragged", 64)):
-            if name == args.workload and page_rows is None:
+        for name, page_rows, fp8 in (("dsv2_ragged", None, False), ("dsv2_long", None, False),
+                                     ("dsv2_ragged", 64, False), ("dsv2", None, True), ("dsv2_ragged", None, True)):
+            if name == args.workload and page_rows is None and not fp8:
                 continue
             r = run_workload(name, max(20, args.steps // 4), max(5, args.warmup // 4), min_sets=2,
-                             page_rows=page_rows)
+                             page_rows=page_rows, fp8=fp8)
             others[r["name"]] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items()
                                  if k not in ("inp", "k3_bytes", "k3_flops", "step_bytes", "step_flops")}
         others["kv_down_dsv2"] = run_kv_down()

@@ -261,16 +261,30 @@ __global__ __launch_bounds__(kNW * 64, 1) void decode_latent_fp8_kernel(
       const float* sc = &scl[stage][0];
       ++step;
 
-      // scores
+      // scores: the code reads run one group of 4 k-steps ahead of the
+      // widening and the MFMAs (double-buffered raw operands), so that LDS
+      // latency overlaps the matrix work
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
       f32x16 sacc = zero16();
       const float rs = sc[l32];
+      auto srd = [&](int kk) -> u32x2 {
+        return *(const LDS_AS u32x2*)((LDS_AS char*)tl + s_row + 16 * (kk ^ gx));
+      };
+      u32x2 sraw[2][4];
 #pragma unroll
-      for (int kk = 0; kk < 32; ++kk) {
-        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-        const u32x2 v = *(const LDS_AS u32x2*)((LDS_AS char*)tl + s_row + 16 * (kk ^ gx));
-        sacc = M::mma(widen8(v.x, v.y, rs), qf[kk], sacc);
-        // bounds how far the scheduler hoists reads (register pressure)
-        if (kk % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+      for (int j = 0; j < 4; ++j) sraw[0][j] = srd(j);
+#pragma unroll
+      for (int g = 0; g < kKL / 4; ++g) {
+        if (g + 1 < kKL / 4) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) sraw[(g + 1) & 1][j] = srd(4 * (g + 1) + j);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          sacc = M::mma(widen8(sraw[g & 1][j].x, sraw[g & 1][j].y, rs), qf[4 * g + j], sacc);
+        __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int kk = kKL; kk < kKS; ++kk) {
@@ -278,6 +292,16 @@ __global__ __launch_bounds__(kNW * 64, 1) void decode_latent_fp8_kernel(
         const i16x8 a = *(const LDS_AS i16x8*)((LDS_AS char*)tl + l32 * kRowB + 16 * (32 + (c ^ (gx & 7))));
         const i16x8 q = *(const LDS_AS i16x8*)((LDS_AS char*)qr_lds + head * 128 + 16 * (c ^ ((head >> 1) & 7)));
         sacc = M::mma(a, q, sacc);
+      }
+      // the first P*V operands, read while the softmax runs
+      auto trd = [&](int cb, int kh) -> i32x2 {
+        return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (LDS_AS i32x2*)((LDS_AS char*)tl + (kh ? tb1 : tb0) + 16 * ((2 * cb) ^ (kh ? tx1 : tx0))));
+      };
+      i32x2 traw[2][4];
+      if (pass != 1) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) traw[0][j] = trd(j >> 1, j & 1);
       }
       // rows past the split end get -inf; the tile's max in log2 units
       const int valid = r1 - (r0 + i * kTile);
@@ -317,17 +341,21 @@ __global__ __launch_bounds__(kNW * 64, 1) void decode_latent_fp8_kernel(
       }
       const i16x8 pb0 = __builtin_bit_cast(i16x8, (u32x4){pk[0], pk[1], pk[2], pk[3]});
       const i16x8 pb1 = __builtin_bit_cast(i16x8, (u32x4){pk[4], pk[5], pk[6], pk[7]});
-      // O^T += codes^T (P s)^T
+      // O^T += codes^T (P s)^T, reads one group of 2 column blocks ahead
 #pragma unroll
-      for (int cb = 0; cb < kCB; ++cb) {
-        typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
-        const i32x2 a0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (LDS_AS i32x2*)((LDS_AS char*)tl + tb0 + 16 * ((2 * cb) ^ tx0)));
-        const i32x2 a1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (LDS_AS i32x2*)((LDS_AS char*)tl + tb1 + 16 * ((2 * cb) ^ tx1)));
-        o[cb] = M::mma(widen8((uint32_t)a0.x, (uint32_t)a0.y, 1.0f), pb0, o[cb]);
-        o[cb] = M::mma(widen8((uint32_t)a1.x, (uint32_t)a1.y, 1.0f), pb1, o[cb]);
-        if (cb % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+      for (int g = 0; g < kCB / 2; ++g) {
+        if (g + 1 < kCB / 2) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) traw[(g + 1) & 1][j] = trd(2 * (g + 1) + (j >> 1), j & 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int cb = 2 * g + (j >> 1);
+          const i32x2 a = traw[g & 1][j];
+          o[cb] = M::mma(widen8((uint32_t)a.x, (uint32_t)a.y, 1.0f), (j & 1) ? pb1 : pb0, o[cb]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     if (pass == 0 && !redo) {  // the last tile may have overflowed too

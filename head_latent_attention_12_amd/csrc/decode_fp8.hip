@@ -47,12 +47,14 @@ static_assert(kTile * kNch % (64 * kNW) == 0, "tile must split evenly over the w
 static_assert(kOps * (kStages - 2) <= 63, "vmcnt range");
 static_assert(kNW * 32 * kR * 2 <= kStages * kTileB, "the epilogue stages the bf16 partials in the ring");
 
-// Slot of logical 16-byte chunk c in LDS row t.  The 32 code chunks XOR with
-// (t >> 1) & 15 and the 8 RoPE chunks with (t >> 1) & 7, each inside its own
-// range, so a chunk read by 32 consecutive rows spreads over every bank group
-// (rows t and t + 1 start 32 banks apart).  An XOR is its own inverse.
+// Slot of logical 16-byte chunk c in LDS row t.  The 32 code chunks XOR their
+// low two bits with (t >> 1) & 3, the 8 RoPE chunks with (t >> 1) & 7, each
+// inside its own range (rows t and t + 1 start 32 banks apart).  A 2-bit XOR
+// keeps every code read at one of four per-lane bases plus an immediate
+// offset (no address arithmetic per read), for 2-way bank conflicts on the
+// code reads.  An XOR is its own inverse.
 __device__ __forceinline__ int f8_slot(int t, int c) {
-  return c < 32 ? (c ^ ((t >> 1) & 15)) : (32 + ((c - 32) ^ ((t >> 1) & 7)));
+  return c < 32 ? (c ^ ((t >> 1) & 3)) : (32 + ((c - 32) ^ ((t >> 1) & 7)));
 }
 
 // Eight E4M3 codes (lo: bytes 0-3, hi: bytes 4-7) times a power-of-two scale,
@@ -215,15 +217,19 @@ __global__ __launch_bounds__(kNW * 64, 1) void decode_latent_fp8_kernel(
   // of that chunk from each of the 8 rows, i.e. column 32 cb + lane % 32.  The
   // rows t_j = 16 kh + 8 (j >> 2) + 4 hf + (j & 3) are the ones whose weights
   // this lane holds in accumulator registers 8 kh + j.
-  const int g_l32 = (l32 >> 1) & 15;
-  const int s_row = l32 * kRowB + 8 * hf;
-  int tr_base[2], tr_x[2];
+  // code chunk 4 g + j of row t sits at 64 g + 16 (j ^ ((t >> 1) & 3))
+  const int g_l32 = (l32 >> 1) & 7;  // (the RoPE swizzle; its low two bits are the code swizzle)
+  int s_base[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) s_base[j] = l32 * kRowB + 8 * hf + 16 * (j ^ (g_l32 & 3));
+  int tr_base[2][2];  // [kh][cb & 1]: chunk 2 cb + (G & 1) = 4 (cb >> 1) + (2 (cb & 1) + (G & 1))
 #pragma unroll
   for (int kh = 0; kh < 2; ++kh) {
     const int j = (lane & 15) >> 1;
     const int t = 16 * kh + 8 * (j >> 2) + 4 * hf + (j & 3);
-    tr_base[kh] = t * kRowB + 8 * (lane & 1);
-    tr_x[kh] = ((t >> 1) & 15) ^ ((lane >> 4) & 1);
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+      tr_base[kh][par] = t * kRowB + 8 * (lane & 1) + 16 * ((2 * par + ((lane >> 4) & 1)) ^ ((t >> 1) & 3));
   }
 
   f32x16 o[kCB];
@@ -253,11 +259,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void decode_latent_fp8_kernel(
       if (i + kStages - 1 < ntiles) issue_tile(i + kStages - 1, (i + kStages - 1) % kStages);
       const int stage = i % kStages;
       const char* tl = smem + stage * kTileB;
-      // opaque per-tile copies of the swizzle terms: the 64 read addresses are
-      // then formed next to their reads instead of being hoisted out of the
-      // loop (64 live registers)
-      int gx = g_l32, tb0 = tr_base[0], tb1 = tr_base[1], tx0 = tr_x[0], tx1 = tr_x[1];
-      asm volatile("" : "+v"(gx), "+v"(tb0), "+v"(tb1), "+v"(tx0), "+v"(tx1));
+      const int tl_off = (int)(uintptr_t)((LDS_AS char*)tl);
       const float* sc = &scl[stage][0];
       ++step;
 
@@ -269,7 +271,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void decode_latent_fp8_kernel(
       f32x16 sacc = zero16();
       const float rs = sc[l32];
       auto srd = [&](int kk) -> u32x2 {
-        return *(const LDS_AS u32x2*)((LDS_AS char*)tl + s_row + 16 * (kk ^ gx));
+        return *(const LDS_AS u32x2*)((LDS_AS char*)(uintptr_t)(tl_off + s_base[kk & 3]) + 64 * (kk >> 2));
       };
       u32x2 sraw[2][4];
 #pragma unroll
@@ -289,14 +291,14 @@ __global__ __launch_bounds__(kNW * 64, 1) void decode_latent_fp8_kernel(
 #pragma unroll
       for (int kk = kKL; kk < kKS; ++kk) {
         const int c = 2 * (kk - kKL) + hf;
-        const i16x8 a = *(const LDS_AS i16x8*)((LDS_AS char*)tl + l32 * kRowB + 16 * (32 + (c ^ (gx & 7))));
+        const i16x8 a = *(const LDS_AS i16x8*)((LDS_AS char*)tl + l32 * kRowB + 16 * (32 + (c ^ g_l32)));
         const i16x8 q = *(const LDS_AS i16x8*)((LDS_AS char*)qr_lds + head * 128 + 16 * (c ^ ((head >> 1) & 7)));
         sacc = M::mma(a, q, sacc);
       }
       // the first P*V operands, read while the softmax runs
       auto trd = [&](int cb, int kh) -> i32x2 {
         return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (LDS_AS i32x2*)((LDS_AS char*)tl + (kh ? tb1 : tb0) + 16 * ((2 * cb) ^ (kh ? tx1 : tx0))));
+            (LDS_AS i32x2*)((LDS_AS char*)(uintptr_t)(tl_off + tr_base[kh][cb & 1]) + 64 * (cb >> 1)));
       };
       i32x2 traw[2][4];
       if (pass != 1) {

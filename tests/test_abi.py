@@ -192,6 +192,38 @@ def test_paged_argument_checks():
     _expect(3, mla.mla_decode_latent_paged, d, P16, P16 + 8, P16, 4, 64, 10, P16, 100, 2, P16, P16, 0)
 
 
+def test_fp8_argument_checks():
+    """Host-side checks of the fp8 cache calls (no kernel runs): only the bf16
+    (128, 512, 64) instance, a non-NULL 16-byte-aligned scale array, and the
+    checks of the bf16 counterparts (row offsets, pages, splits, alignment)."""
+    d = dsv2()
+    small = mla.make_dims(8, 16, 64, 64, 64, 32, mla.MLA_F32)
+
+    def dec(dims=d, scale=P16, off=P16, rows=100, splits=2, cache=P16):
+        mla.mla_decode_latent_fp8(dims, P16, cache, scale, off, P16, rows, 100, splits, P16, P16, 0)
+
+    def dec_paged(dims=d, scale=P16, page=64):
+        mla.mla_decode_latent_fp8_paged(dims, P16, P16, scale, P16, 4, page, 10, P16, 100, 2, P16, P16, 0)
+
+    def absorb(dims=d, scale=P16, off=P16, rows=100):
+        mla.mla_absorb_rope_fp8(dims, P16, P16, P16, P16, P16, P16, off, rows, P16, P16, scale, 0)
+
+    def absorb_paged(dims=d, scale=P16, page=64):
+        mla.mla_absorb_rope_fp8_paged(dims, P16, P16, P16, P16, P16, P16, P16, 4, page, 10, P16, P16, scale, 0)
+
+    for fn in (dec, dec_paged, absorb, absorb_paged):
+        _expect(2, lambda: fn(dims=small))        # no fp8 form of the fp32 instances
+        _expect(1, lambda: fn(scale=0))           # kv_scale NULL
+        _expect(3, lambda: fn(scale=P16 + 4))     # kv_scale misaligned
+    for fn in (dec, absorb):
+        _expect(1, lambda: fn(off=0))             # row_offsets NULL
+        _expect(1, lambda: fn(rows=0))            # no cache rows
+    for fn in (dec_paged, absorb_paged):
+        _expect(1, lambda: fn(page=48))           # page size not a power of two
+    _expect(4, lambda: dec(splits=4097))
+    _expect(3, lambda: dec(cache=P16 + 8))
+
+
 def test_paginate_layout():
     """The paged layout helper: every sequence's rows land on distinct pages of
     its own, the gather through the block table gives the packed rows back,

@@ -159,9 +159,13 @@ __global__ __launch_bounds__(kNW * 64, 1) void decode_latent_fp8_kernel(
   } else {
     last_rel = r1 - 1 - r0;
   }
-  auto tile_row = [&](int tile) -> int64_t {  // cache row of the tile's first row
+  // cache row of the tile's first row; rel0 = that row relative to the
+  // split's first (a packed split clamped at the cache end can have tiles that
+  // start past its last valid row: they start at that row instead, so that
+  // every copy offset below is non-negative and inside the cache)
+  auto tile_row = [&](int tile, int rel0) -> int64_t {
     if constexpr (PAGED) return cm.paged_row(b, r0 + tile * kTile, block_table);
-    else return row_lo + (int64_t)tile * kTile;
+    else return row_lo + rel0;
   };
 
   // DMA lanes: copy n of this wave fills physical chunk p = (wave * kDpw + n)
@@ -174,14 +178,15 @@ __global__ __launch_bounds__(kNW * 64, 1) void decode_latent_fp8_kernel(
     int ln = lane;
     asm volatile("" : "+v"(ln));
     asm volatile("" : "+s"(tile));
-    const int vmax = min(kTile - 1, last_rel - tile * kTile);  // rows past it repeat the last valid one
+    const int rel0 = min(tile * kTile, last_rel);
+    const int vmax = min(kTile - 1, last_rel - rel0);  // (>= 0) rows past it repeat the last valid one
     uint32_t off[kDpw];
 #pragma unroll
     for (int n = 0; n < kDpw; ++n) {
       const int p = (wave * kDpw + n) * 64 + ln, t = p / kNch;
       off[n] = (uint32_t)(min(t, vmax) * kRowB + 16 * f8_slot(t, p - t * kNch));
     }
-    const int64_t row0 = tile_row(tile);
+    const int64_t row0 = tile_row(tile, rel0);
     dma_tile((uint64_t)(cache + row0 * kRowB), (uint64_t)(scales + row0),
              lds_base + stage * kTileB + wave * kDpw * 1024,
              (int)(uintptr_t)((LDS_AS float*)&scl[stage][0]), off, (uint32_t)(4 * min(ln & 31, vmax)));

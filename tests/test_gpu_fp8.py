@@ -184,3 +184,30 @@ def test_fp8_deterministic_and_graph_replay():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(ds.out, out1)
+
+
+def test_fp8_inconsistent_metadata_stays_in_bounds():
+    """Device metadata the host cannot check (row offsets before and past the
+    cache, lengths past max_seq_len or negative, positions far out, page ids
+    out of range, lengths past the block table) is clamped inside the fp8
+    append and decode: the calls complete with wrong numbers, never a stray
+    access, and a correct fp8 step afterwards still matches the oracle."""
+    from head_latent_attention_12_amd.step import DeviceStep
+    inp = syn.make_inputs("dsv2", B=3, T=200)
+    ds = DeviceStep(inp, num_splits=4, fp8=True)
+    ds.row_offsets.copy_(torch.tensor([-(10 ** 9), inp.total_rows + 7, 10 ** 12], dtype=torch.int64))
+    ds.seq_lens.copy_(torch.tensor([10 ** 6, -3, int(inp.seq_lens[2])], dtype=torch.int32))
+    ds.positions.copy_(torch.tensor([10 ** 6, -9, 2 ** 30], dtype=torch.int32))
+    ds.run()
+    torch.cuda.synchronize()
+    dp = DeviceStep(inp, num_splits=4, page_rows=64, fp8=True)
+    bt = dp.block_table.clone()
+    bt[:, 0] = -7
+    bt[:, -1] = dp.paged.total_pages + 100
+    dp.block_table.copy_(bt)
+    dp.seq_lens.copy_(torch.tensor([10 ** 6, 1, 64 * dp.paged.bt_stride + 500], dtype=torch.int32))
+    dp.run()
+    torch.cuda.synchronize()
+    clean = _step(inp)
+    ref, quant = fp8_oracle(inp, clean.fp8)
+    check_fp8_step(inp, clean, ref, quant, "fp8 after bad metadata")

@@ -15,14 +15,16 @@
 // Work-group = (sequence, split), 4 waves x 32 heads, as the bf16 kernel.
 // Per 32-row tile (7-stage LDS ring filled by DMA, no register staging):
 //   S^T[t][h] = sum_k deq(cache[t][k]) q_lat[h][k]: A = cache row t (8 codes
-//     per lane, ds_read_b64, widened with the row's scale), B = q_lat^T held
-//     in registers; the 64 RoPE columns are bf16 already (ds_read_b128)
+//     per lane, ds_read_b64, widened with the row's scale), B = q_lat^T (the
+//     latent part held in registers, the RoPE part read from LDS); the 64 RoPE
+//     columns of the row are bf16 already (ds_read_b128)
 //   online softmax per head (one head per lane, as in the bf16 kernel)
 //   O^T[c][h] += sum_t code[t][c] (P[h][t] s_t): A = codes of column c over 8
 //     rows (ds_read_b64_tr_b8), widened unscaled; B = P^T with each row's
 //     scale folded in (exact: powers of two)
-// LDS bytes per tile and wave are half those of the bf16 kernel; the MFMA
-// work is the same.
+// Code reads run one group of 4 k-steps (P*V: 2 column blocks) ahead of the
+// widening and the MFMAs.  LDS bytes per tile and wave are half those of the
+// bf16 kernel; the MFMA work is the same.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>

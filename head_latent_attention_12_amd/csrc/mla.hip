@@ -4,13 +4,16 @@
 //   absorb_q_kernel          q~ = W_UK^T q_nope          (32x32 MFMA, W_UK staged in LDS; fp32)
 //   absorb_q_bf16_kernel     the same for bf16, weight tile and queries copied to LDS by DMA
 //   rope_append_kernel       RoPE(q_rope), append [c_kv_new | RoPE(k_rope_new)]
-//   absorb_rope_bf16_kernel  the two above in one launch (the absorption blocks do the RoPE work)
+//   absorb_rope_bf16_kernel  the two above in one launch (the absorption blocks do the RoPE work);
+//                            appends bf16 rows, or fp8 rows (E4M3 codes + a power-of-two row scale)
 //   decode_latent_kernel     split-KV flash decode over the latent cache (32x32 MFMA), packed or
 //                            paged cache
 //   combine_kernel           log-sum-exp merge of the splits
 //   up_v_*_kernel            out = W_UV o_lat             (32x32 MFMA)
 //   combine_up_v_*_kernel    the merge formed where W_UV consumes it (one launch)
 //   kv_down_*_kernel         c_kv_new, k_rope_new from the hidden state (W_DKV + RMSNorm, W_KR)
+// The decode kernel over an fp8 cache is in decode_fp8.hip; the device helpers
+// both files use are in mla_common.h.
 //
 // Sources (page title, section): "DeepSeek MLA, Built From the Paper" section 3
 // (absorption identity) and section 2 (decoupled RoPE key shared by the heads);

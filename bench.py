@@ -1,6 +1,6 @@
 """Benchmark: absorbed MLA decode step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dsv2] [--no-others]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dsv2_ragged] [--no-others]
 
 A step is one pass of the path over one batch: absorb_q, rope_append,
 decode_latent, then the split merge and W_UV as the one fused call
@@ -10,8 +10,13 @@ resident in HBM; the timed loop rotates over several independent input sets
 256 MB Infinity Cache cannot hold the cache and weights; the per-step
 temporaries share one workspace.  The timed steps replay a HIP graph that
 holds one step of every set in turn (as the layers of one decode step);
-back-to-back decode launches between HIP events give that kernel's
-duration.  Prints one JSON line.
+a HIP graph of back-to-back decode launches, replayed between HIP events on
+the launch stream, gives that kernel's duration.
+
+The headline workload is the ragged batch (B 64, cached lengths drawn in
+[512, 8192]): of the configurations that fit one GPU it moves the most bytes
+per step.  The batch of 16 at T 4096 and the two sequences at T 131072 get
+roofline records of their own.  Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -50,7 +55,8 @@ def algorithmic(inp, fp8=False):
     Bytes: every attended cache row read once, the appended row written once,
     W_UK and W_UV read once, q_nope/q_rope/new-token inputs read once, out
     written once.  Split partials, q_lat round trips and re-reads are
-    implementation overhead and are not counted.
+    implementation overhead and are not counted; the decode kernel's own
+    figure is the cache rows alone (1152 bytes per attended bf16 row).
     """
     s = 2 if inp.dtype == "bf16" else 4
     rows = int(inp.seq_lens.sum())
@@ -61,7 +67,7 @@ def algorithmic(inp, fp8=False):
                   + B * H * (dh + dr) * s + B * (r + dr) * s  # q_nope, q_rope, c_kv_new, k_rope_new
                   + B * H * dv * 4)                   # out (fp32)
     step_flops = 2 * H * (W + r) * rows + 2 * B * H * dh * r + 2 * B * H * dv * r
-    k3_bytes = rows * rb + B * H * W * s               # cache rows + q_lat
+    k3_bytes = rows * rb                              # every attended cache row read once
     k3_flops = 2 * H * (W + r) * rows
     return rows, step_bytes, step_flops, k3_bytes, k3_flops
 
@@ -287,8 +293,9 @@ def run_workload(name, steps, warmup, min_sets, verbose=True, page_rows=None, fp
     torch.cuda.synchronize()
     dev_ms = e0.elapsed_time(e1) / steps
 
-    # eager steps with HIP events around every decode launch (its duration for
-    # the roofline), timed as a whole too
+    # eager steps, timed as a whole, with HIP events around every decode
+    # launch (reported beside the roofline's duration: a pair around one
+    # launch also counts its dispatch latency)
     k3_start = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     k3_end = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     torch.cuda.synchronize()
@@ -303,17 +310,30 @@ def run_workload(name, steps, warmup, min_sets, verbose=True, page_rows=None, fp
     torch.cuda.synchronize()
     eager_ms = (time.perf_counter() - t1) * 1e3 / steps
     k3_event_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(k3_start, k3_end)]))
-    # the decode kernel's duration for the roofline: back-to-back launches over
-    # the rotated input sets between one event pair (a pair around a single
-    # launch also counts its dispatch latency, ~3 us)
-    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # the decode kernel's duration for the roofline: a HIP graph of
+    # back-to-back launches over the rotated input sets (no host gaps between
+    # them), replayed between one event pair on the launch stream
+    dec_graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        for ds in sets:
+            ds.decode_latent()
+    stream.wait_stream(side)
+    with torch.cuda.graph(dec_graph):
+        for ds in sets:
+            ds.decode_latent()
+    reps = max(1, steps // n_sets)
+    dec_graph.replay()
     torch.cuda.synchronize()
+    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     b0.record(stream)
-    for i in range(steps):
-        sets[i % n_sets].decode_latent()
+    for _ in range(reps):
+        dec_graph.replay()
     b1.record(stream)
     torch.cuda.synchronize()
-    k3_ms = b0.elapsed_time(b1) / steps
+    k3_ms = b0.elapsed_time(b1) / (reps * n_sets)
+    del dec_graph
     del graphs, round_graph
 
     ms = wall * 1e3 / steps
@@ -351,13 +371,50 @@ def run_workload(name, steps, warmup, min_sets, verbose=True, page_rows=None, fp
     return res
 
 
+def roofline_record(res, bf16=True):
+    """Roofline of the decode kernel (the step's dominant kernel) for one
+    workload: algorithmic bytes per launch = 1152 bytes per attended cache row
+    (each row read once) over the kernel's average launch duration; HBM bytes
+    per launch from the committed counter runs while the kernel's sources are
+    the ones they were taken on."""
+    traffic = counter_traffic(res["name"])
+    achieved = res["decode_kernel_GBps"]
+    return {
+        "kernel": "decode_latent_kernel",
+        "bound": "hbm",
+        "achieved": round(achieved, 1),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "traffic": (round(traffic / (res["decode_kernel_ms"] * 1e-3) / 1e9, 1) if traffic else None),
+        "traffic_bytes_per_launch": (round(traffic) if traffic else None),
+        "algorithmic_bytes_per_launch": res["k3_bytes"],
+        "attended_rows_per_launch": res["cached_tokens_per_step"],
+        "avg_launch_us": round(res["decode_kernel_ms"] * 1e3, 2),
+        "launch_timing": "HIP graph of back-to-back launches over the rotated input sets, replayed between HIP "
+                         "events on the launch stream",
+        "avg_launch_us_in_step": round(res["decode_kernel_event_ms"] * 1e3, 2),
+        "mfma_tflops": round(res["decode_kernel_TFLOPs"], 1),
+        "mfma_frac": round(res["decode_kernel_TFLOPs"] / (BF16_PEAK_TFLOPS if bf16 else FP32_PEAK_TFLOPS), 4),
+        "step_us": round(res["ms_per_step"] * 1e3, 2),
+        "step_algorithmic_bytes": res["step_bytes"],
+        "step_hbm_frac": round(res["step_GBps"] / HBM_PEAK_GBS, 4),
+        "num_splits": res["num_splits"],
+    }
+
+
+DSV2_WORKLOADS = ("dsv2", "dsv2_ragged", "dsv2_long")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="dsv2", choices=["tiny", "small", "dsv2", "dsv2_ragged", "dsv2_long"])
-    ap.add_argument("--no-others", action="store_true", help="skip the other DeepSeek-V2-shaped workloads")
+    ap.add_argument("--workload", default="dsv2_ragged",
+                    choices=["tiny", "small", "dsv2", "dsv2_ragged", "dsv2_long"])
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the paged, fp8 and upstream/fold legs (the three DeepSeek-V2 shapes always run)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--counters-run", action="store_true",
                     help="run the workload's steps and the calibration kernel only (profiled with rocprofv3 --pmc)")
@@ -385,22 +442,25 @@ def main():
         return
 
     main_res = run_workload(args.workload, args.steps, args.warmup, min_sets=5)
-    others = {}
-    if not args.no_others:
-        for name, page_rows, fp8 in (("dsv2_ragged", None, False), ("dsv2_long", None, False),
-                                     ("dsv2_ragged", 64, False), ("dsv2", None, True), ("dsv2_ragged", None, True)):
-            if name == args.workload and page_rows is None and not fp8:
-                continue
-            r = run_workload(name, max(20, args.steps // 4), max(5, args.warmup // 4), min_sets=2,
-                             page_rows=page_rows, fp8=fp8)
-            others[r["name"]] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items()
-                                 if k not in ("inp", "k3_bytes", "k3_flops", "step_bytes", "step_flops")}
-        others["kv_down_dsv2"] = run_kv_down()
-
     inp = main_res["inp"]
     bf16 = inp.dtype == "bf16"
-    traffic = counter_traffic(main_res["name"])
-    achieved = main_res["decode_kernel_GBps"]
+    by_workload = {}
+    if main_res["name"] in DSV2_WORKLOADS:
+        by_workload[main_res["name"]] = roofline_record(main_res)
+    others = {}
+    legs = [(n, None, False) for n in DSV2_WORKLOADS if n != args.workload]
+    if not args.no_others:
+        legs += [("dsv2_ragged", 64, False), ("dsv2", None, True), ("dsv2_ragged", None, True)]
+    for name, page_rows, fp8 in legs:
+        r = run_workload(name, max(20, args.steps // 4), max(5, args.warmup // 4), min_sets=2,
+                         page_rows=page_rows, fp8=fp8)
+        if page_rows is None and not fp8:
+            by_workload[r["name"]] = roofline_record(r)
+        others[r["name"]] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items()
+                             if k not in ("inp", "k3_flops", "step_flops")}
+    if not args.no_others:
+        others["kv_down_dsv2"] = run_kv_down()
+
     line = {
         "metric": "MLA decode cached-tokens/s + achieved HBM GB/s & MFMA util vs roofline (1 GPU)",
         "value": round(main_res["value"], 1),
@@ -421,26 +481,14 @@ def main():
             "num_splits": main_res["num_splits"], "input_sets_rotated": main_res["input_sets"],
             "parallelism": "single GPU (split-KV across work-groups)",
         },
-        "roofline": {
-            "kernel": "decode_latent_kernel",
-            "bound": "hbm",
-            "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": (round(traffic / (main_res["decode_kernel_ms"] * 1e-3) / 1e9, 1) if traffic else None),
-            "traffic_bytes_per_launch": (round(traffic) if traffic else None),
-            "algorithmic_bytes_per_launch": main_res["k3_bytes"],
-            "avg_launch_us": round(main_res["decode_kernel_ms"] * 1e3, 2),
-            "launch_timing": "HIP events around back-to-back launches of the kernel over the rotated input sets",
-            "avg_launch_us_in_step": round(main_res["decode_kernel_event_ms"] * 1e3, 2),
-            "mfma_tflops": round(main_res["decode_kernel_TFLOPs"], 1),
-            "mfma_frac": round(main_res["decode_kernel_TFLOPs"] / (BF16_PEAK_TFLOPS if bf16 else FP32_PEAK_TFLOPS), 4),
-        },
+        "roofline": {k: v for k, v in roofline_record(main_res, bf16).items()},
+        "roofline_by_workload": by_workload,
         "step": {
-            "timing": "HIP graph replay of the four calls per step (absorb_q, rope_append, decode_latent, combine_up_v); one graph holds one step of every rotated input set",
+            "timing": "HIP graph replay of the step's three launches (absorb_rope, decode_latent, combine_up_v); "
+                      "one graph holds one step of every rotated input set",
             "device_us_per_step": round(main_res["device_ms_per_step"] * 1e3, 2),
             "eager_us_per_step": round(main_res["eager_ms_per_step"] * 1e3, 2),
+            "algorithmic_bytes": main_res["step_bytes"],
             "GBps": round(main_res["step_GBps"], 1),
             "hbm_frac": round(main_res["step_GBps"] / HBM_PEAK_GBS, 4),
             "TFLOPs": round(main_res["step_TFLOPs"], 1),

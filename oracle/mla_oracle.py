@@ -75,11 +75,12 @@ def rope_frequencies(d: int, base: float) -> np.ndarray:
     return base ** (-2.0 * i / d)
 
 
-def rope(x: np.ndarray, pos: float, base: float) -> np.ndarray:
-    """Rotate each adjacent pair (x[2i], x[2i+1]) of the last axis by pos*theta_i."""
-    x = np.asarray(x, dtype=np.float64)
+def rope(x: np.ndarray, pos: float, base: float, dtype=np.float64) -> np.ndarray:
+    """Rotate each adjacent pair (x[2i], x[2i+1]) of the last axis by pos*theta_i
+    (evaluated in ``dtype``; float64 unless a test asks for a float32 run)."""
+    x = np.asarray(x, dtype=dtype)
     ang = float(pos) * rope_frequencies(x.shape[-1], base)
-    c, s = np.cos(ang), np.sin(ang)
+    c, s = np.cos(ang).astype(dtype), np.sin(ang).astype(dtype)
     xe, xo = x[..., 0::2], x[..., 1::2]
     out = np.empty_like(x)
     out[..., 0::2] = xe * c - xo * s
@@ -92,9 +93,9 @@ def rope(x: np.ndarray, pos: float, base: float) -> np.ndarray:
 # ---------------------------------------------------------------------------
 
 
-def softmax(s: np.ndarray) -> np.ndarray:
+def softmax(s: np.ndarray, dtype=np.float64) -> np.ndarray:
     """Softmax over the last axis: subtract the max, exponentiate, normalise."""
-    s = np.asarray(s, dtype=np.float64)
+    s = np.asarray(s, dtype=dtype)
     m = np.max(s, axis=-1, keepdims=True)
     e = np.exp(s - m)
     return e / np.sum(e, axis=-1, keepdims=True)
@@ -113,19 +114,20 @@ def logsumexp(s: np.ndarray) -> np.ndarray:
 # ---------------------------------------------------------------------------
 
 
-def appended_row(c_new: np.ndarray, k_rope_new: np.ndarray, pos: int, base: float) -> np.ndarray:
+def appended_row(c_new: np.ndarray, k_rope_new: np.ndarray, pos: int, base: float,
+                 dtype=np.float64) -> np.ndarray:
     """The cache row the step writes: [c_kv_new | RoPE(k_rope_new, pos)]."""
-    return np.concatenate([np.asarray(c_new, np.float64), rope(k_rope_new, pos, base)])
+    return np.concatenate([np.asarray(c_new, dtype), rope(k_rope_new, pos, base, dtype)])
 
 
 def append(c_cached: np.ndarray, krot_cached: np.ndarray, c_new: np.ndarray,
-           k_rope_new: np.ndarray, base: float):
+           k_rope_new: np.ndarray, base: float, dtype=np.float64):
     """Cache after the step: L cached rows plus the new one at position L."""
     L = c_cached.shape[0]
-    row = appended_row(c_new, k_rope_new, L, base)
+    row = appended_row(c_new, k_rope_new, L, base, dtype)
     r = c_cached.shape[1]
-    C = np.vstack([np.asarray(c_cached, np.float64), row[None, :r]])
-    KR = np.vstack([np.asarray(krot_cached, np.float64), row[None, r:]])
+    C = np.vstack([np.asarray(c_cached, dtype), row[None, :r]])
+    KR = np.vstack([np.asarray(krot_cached, dtype), row[None, r:]])
     return C, KR
 
 
@@ -139,23 +141,25 @@ def append(c_cached: np.ndarray, krot_cached: np.ndarray, c_new: np.ndarray,
 
 
 def naive_decode_seq(q_nope, q_rope, c_cached, krot_cached, c_new, k_rope_new,
-                     w_uk, w_uv, scale, base):
+                     w_uk, w_uv, scale, base, dtype=np.float64):
     """Output [H, d_v] of one sequence's decode step, naive form.
 
     q_nope [H, d_head], q_rope [H, d_rope] (unrotated), c_cached [L, r],
     krot_cached [L, d_rope] (rotated), c_new [r], k_rope_new [d_rope]
-    (unrotated), w_uk [H, d_head, r], w_uv [H, d_v, r].
+    (unrotated), w_uk [H, d_head, r], w_uv [H, d_v, r].  Evaluated in
+    ``dtype`` (float64 unless a test asks for a float32 run).
     """
-    C, KR = append(c_cached, krot_cached, c_new, k_rope_new, base)
+    C, KR = append(c_cached, krot_cached, c_new, k_rope_new, base, dtype)
     pos = c_cached.shape[0]
     H = q_nope.shape[0]
-    out = np.empty((H, w_uv.shape[1]))
+    q_nope, w_uk, w_uv = (np.asarray(a, dtype) for a in (q_nope, w_uk, w_uv))
+    out = np.empty((H, w_uv.shape[1]), dtype=dtype)
     for h in range(H):
         k_content = C @ w_uk[h].T                          # [L+1, d_head]
         v = C @ w_uv[h].T                                  # [L+1, d_v]
         k = np.concatenate([k_content, KR], axis=1)        # [L+1, d_head + d_rope]
-        q = np.concatenate([q_nope[h], rope(q_rope[h], pos, base)])
-        p = softmax(scale * (k @ q))
+        q = np.concatenate([q_nope[h], rope(q_rope[h], pos, base, dtype)])
+        p = softmax(dtype(scale) * (k @ q), dtype)
         out[h] = p @ v
     return out
 
@@ -169,7 +173,7 @@ def naive_decode_seq(q_nope, q_rope, c_cached, krot_cached, c_new, k_rope_new,
 
 
 def absorbed_decode_seq(q_nope, q_rope, c_cached, krot_cached, c_new, k_rope_new,
-                        w_uk, w_uv, scale, base):
+                        w_uk, w_uv, scale, base, dtype=np.float64):
     """Absorbed form of the same step; returns every intermediate.
 
     Returns a dict with
@@ -180,18 +184,90 @@ def absorbed_decode_seq(q_nope, q_rope, c_cached, krot_cached, c_new, k_rope_new
       o_lat   [H, r]           softmax-weighted sum of latents
       out     [H, d_v]         W_UV o_lat
     """
-    C, KR = append(c_cached, krot_cached, c_new, k_rope_new, base)
+    C, KR = append(c_cached, krot_cached, c_new, k_rope_new, base, dtype)
     pos = c_cached.shape[0]
     H, r = q_nope.shape[0], C.shape[1]
+    q_nope, w_uk, w_uv = (np.asarray(a, dtype) for a in (q_nope, w_uk, w_uv))
     q_tilde = np.stack([w_uk[h].T @ q_nope[h] for h in range(H)])        # [H, r]
-    q_r = np.stack([rope(q_rope[h], pos, base) for h in range(H)])       # [H, d_rope]
-    scores = scale * (q_tilde @ C.T + q_r @ KR.T)                        # [H, L+1]
-    p = softmax(scores)
+    q_r = np.stack([rope(q_rope[h], pos, base, dtype) for h in range(H)])  # [H, d_rope]
+    scores = dtype(scale) * (q_tilde @ C.T + q_r @ KR.T)                 # [H, L+1]
+    p = softmax(scores, dtype)
     o_lat = p @ C                                                        # [H, r]
     out = np.stack([w_uv[h] @ o_lat[h] for h in range(H)])               # [H, d_v]
     return dict(q_lat=np.concatenate([q_tilde, q_r], axis=1),
                 new_row=np.concatenate([C[-1], KR[-1]]),
                 scores=scores, lse=logsumexp(scores), o_lat=o_lat, out=out)
+
+
+# ---------------------------------------------------------------------------
+# Folding the up-projections into neighbouring weights ahead of time
+# [P2] "Absorbing projections (inference optimisation)": W_O absorbs W_UV
+# (a product of fixed weights computed once, after which the value
+# up-projection is skipped and the attention-weighted latents go straight to
+# the output space), and the same trick applies on the query side; [P5] "What
+# we didn't build, and why": at decode time the up-projection is folded into
+# the query and output matrices.  The readings (also in the design notes):
+#   * Query side: [P2]'s forward pass puts the RMSNorm norm_q between W_DQ and
+#     W_UQ, so a fold across it would not be an identity.  The exact fold is
+#     W_UK into W_UQ per head: q~[h] = W_UK[h]^T W_UQ[h] c_q, with c_q the
+#     normalised query latent and W_UQ[h] head h's d_head rows of the
+#     Linear(d_c_q -> H*d_head) weight.
+#   * Output side: [P2]'s shape comment multiplies (d_model, H*d_h) by
+#     (H*d_h, d_c) into one (d_model, d_c) matrix, which would sum the heads'
+#     latent outputs before they exist.  Each head has its own latent output,
+#     so the fold is per head, W_OV[h] = W_O[:, head h's d_v columns] W_UV[h]
+#     (d_model x d_c, the page's shape, once per head), and the output is the
+#     sum over heads y = sum_h W_OV[h] o_lat[h] (= W_O applied to the
+#     concatenated heads).
+# ---------------------------------------------------------------------------
+
+
+def query_projection(c_q: np.ndarray, w_uq: np.ndarray, n_heads: int) -> np.ndarray:
+    """q_nope [H, d_head] = W_UQ c_q split per head ([P2] forward pass:
+    q = W_UQ(c_q) reshaped to heads); w_uq is [H*d_head, d_c_q]."""
+    q = np.asarray(w_uq, np.float64) @ np.asarray(c_q, np.float64)
+    return q.reshape(n_heads, -1)
+
+
+def output_projection(out: np.ndarray, w_o: np.ndarray) -> np.ndarray:
+    """y [d_model] = W_O applied to the heads' outputs concatenated ([P2]
+    forward pass: out reshaped to H*d_h, then W_O); w_o is [d_model, H*d_v]."""
+    return np.asarray(w_o, np.float64) @ np.asarray(out, np.float64).reshape(-1)
+
+
+def fold_query(w_uq: np.ndarray, w_uk: np.ndarray) -> np.ndarray:
+    """W_QK [H, r, d_c_q]: W_QK[h] = W_UK[h]^T W_UQ[h], head h's block of
+    w_uq [H*d_head, d_c_q] being its rows h*d_head .. (h+1)*d_head - 1."""
+    H, dh, _ = w_uk.shape
+    w_uq = np.asarray(w_uq, np.float64)
+    return np.stack([np.asarray(w_uk[h], np.float64).T @ w_uq[h * dh:(h + 1) * dh] for h in range(H)])
+
+
+def fold_output(w_o: np.ndarray, w_uv: np.ndarray) -> np.ndarray:
+    """W_OV [d_model, H*r]: columns h*r .. (h+1)*r - 1 hold W_O[:, h*d_v ..
+    (h+1)*d_v - 1] W_UV[h]."""
+    H, dv, _ = w_uv.shape
+    w_o = np.asarray(w_o, np.float64)
+    return np.concatenate([w_o[:, h * dv:(h + 1) * dv] @ np.asarray(w_uv[h], np.float64) for h in range(H)],
+                          axis=1)
+
+
+def folded_decode_seq(c_q, q_rope, c_cached, krot_cached, c_new, k_rope_new, w_qk, w_ov, scale, base):
+    """One sequence's step with folded weights: q~[h] = W_QK[h] c_q, attention
+    in the latent space as in the absorbed form, y = W_OV o_lat (the heads'
+    latent outputs concatenated).  Returns q_tilde [H, r], lse [H],
+    o_lat [H, r] and y [d_model]."""
+    C, KR = append(c_cached, krot_cached, c_new, k_rope_new, base)
+    pos = c_cached.shape[0]
+    H = w_qk.shape[0]
+    c_q = np.asarray(c_q, np.float64)
+    q_tilde = np.stack([np.asarray(w_qk[h], np.float64) @ c_q for h in range(H)])   # [H, r]
+    q_r = np.stack([rope(q_rope[h], pos, base) for h in range(H)])                  # [H, d_rope]
+    scores = scale * (q_tilde @ C.T + q_r @ KR.T)                                   # [H, L+1]
+    p = softmax(scores)
+    o_lat = p @ C                                                                   # [H, r]
+    y = np.asarray(w_ov, np.float64) @ o_lat.reshape(-1)                            # [d_model]
+    return dict(q_tilde=q_tilde, lse=logsumexp(scores), o_lat=o_lat, y=y)
 
 
 # ---------------------------------------------------------------------------

@@ -257,7 +257,7 @@ def test_identity_detects_planted_mistakes(monkeypatch):
     assert normwise_rel(orc.absorbed_decode_seq(**bad)["out"], naive) > 1e3 * IDENTITY_TOL
     # the query rotated to the wrong position (off by one)
     real_rope = orc.rope
-    monkeypatch.setattr(orc, "rope", lambda x, pos, base: real_rope(x, pos + 1, base))
+    monkeypatch.setattr(orc, "rope", lambda x, pos, base, dtype=np.float64: real_rope(x, pos + 1, base, dtype))
     shifted = orc.absorbed_decode_seq(**case)["out"]
     monkeypatch.setattr(orc, "rope", real_rope)
     assert normwise_rel(shifted, naive) > 1e3 * IDENTITY_TOL
@@ -480,3 +480,143 @@ def test_fp8_row_exponent_and_quantised_row():
     np.testing.assert_array_equal(deq, orc.e4m3_decode(orc.e4m3_encode(c / s)) * s)
     normal = np.abs(c) >= 2.0 ** -6 * s
     assert np.all(np.abs(deq - c)[normal] <= 2.0 ** -4 * np.abs(c)[normal])
+
+
+# ---------------------------------------------------------------------------
+# Folded projections ("MLA from scratch", absorbing projections: W_O absorbs
+# W_UV, the query side absorbs the key up-projection; octlm "What we didn't
+# build, and why": the part most likely to hide a silent bug)
+# ---------------------------------------------------------------------------
+
+
+def _fold_case(rng, H, dh, dv, r, dr, L, dcq, dmodel):
+    case = _rand_case(rng, H, dh, dv, r, dr, L)
+    c_q = rng.standard_normal(dcq)
+    w_uq = rng.standard_normal((H * dh, dcq)) / math.sqrt(dcq)
+    w_o = rng.standard_normal((dmodel, H * dv)) / math.sqrt(H * dv)
+    return case, c_q, w_uq, w_o
+
+
+def _unfolded_y(case, c_q, w_uq, w_o):
+    """The page's forward pass: q = W_UQ c_q per head, naive attention, W_O."""
+    q_nope = orc.query_projection(c_q, w_uq, case["w_uk"].shape[0])
+    out = orc.naive_decode_seq(**dict(case, q_nope=q_nope))
+    return orc.output_projection(out, w_o)
+
+
+def _folded(case, c_q, w_qk, w_ov):
+    return orc.folded_decode_seq(c_q, case["q_rope"], case["c_cached"], case["krot_cached"], case["c_new"],
+                                 case["k_rope_new"], w_qk, w_ov, case["scale"], case["base"])
+
+
+def test_fold_identity_tiny_shapes():
+    rng = np.random.default_rng(31)
+    for H, dh, r, dr, L, dcq, dmodel in itertools.product((1, 3), (4, 8), (4, 8), (2, 4), (0, 1, 5), (6, 16), (5, 12)):
+        case, c_q, w_uq, w_o = _fold_case(rng, H, dh, dh + 2, r, dr, L, dcq, dmodel)
+        got = _folded(case, c_q, orc.fold_query(w_uq, case["w_uk"]), orc.fold_output(w_o, case["w_uv"]))
+        assert normwise_rel(got["y"], _unfolded_y(case, c_q, w_uq, w_o)) <= IDENTITY_TOL
+        q_nope = orc.query_projection(c_q, w_uq, H)
+        q_ref = np.stack([case["w_uk"][h].T @ q_nope[h] for h in range(H)])
+        assert normwise_rel(got["q_tilde"], q_ref) <= IDENTITY_TOL
+
+
+def test_fold_identity_deepseek_v2_heads(golden_dir):
+    """The DeepSeek-V2 head dims of the page's hyperparameter block (H 128,
+    d_head 128, r 512, d_rope 64, d_c' 1536); d_model is cut to 256 here
+    (5120 would make a 2.7 GB fp64 folded output matrix in a CPU test)."""
+    hp = _load(golden_dir, "hyperparameters.json")["deepseek_v2"]
+    rng = np.random.default_rng(32)
+    H, dh, r, dr, dcq = hp["n_heads"], hp["d_head"], hp["d_c_kv"], hp["d_head_rope"], hp["d_c_q"]
+    case, c_q, w_uq, w_o = _fold_case(rng, H, dh, dh, r, dr, 16, dcq, 256)
+    w_qk, w_ov = orc.fold_query(w_uq, case["w_uk"]), orc.fold_output(w_o, case["w_uv"])
+    assert w_qk.shape == (H, r, dcq) and w_ov.shape == (256, H * r)
+    got = _folded(case, c_q, w_qk, w_ov)
+    assert normwise_rel(got["y"], _unfolded_y(case, c_q, w_uq, w_o)) <= IDENTITY_TOL
+
+
+def test_fold_entries_brute_force():
+    """Every folded entry is the sum its definition states, added up with
+    math.fsum over the shared index (no matrix product)."""
+    rng = np.random.default_rng(33)
+    H, dh, dv, r, dcq, dmodel = 2, 3, 4, 5, 6, 7
+    w_uk = rng.standard_normal((H, dh, r))
+    w_uv = rng.standard_normal((H, dv, r))
+    w_uq = rng.standard_normal((H * dh, dcq))
+    w_o = rng.standard_normal((dmodel, H * dv))
+    w_qk, w_ov = orc.fold_query(w_uq, w_uk), orc.fold_output(w_o, w_uv)
+    for h in range(H):
+        for j in range(r):
+            for i in range(dcq):
+                ref = math.fsum(w_uk[h, d, j] * w_uq[h * dh + d, i] for d in range(dh))
+                assert w_qk[h, j, i] == pytest.approx(ref, rel=1e-13, abs=1e-13)
+            for m in range(dmodel):
+                ref = math.fsum(w_o[m, h * dv + d] * w_uv[h, d, j] for d in range(dv))
+                assert w_ov[m, h * r + j] == pytest.approx(ref, rel=1e-13, abs=1e-13)
+
+
+def test_fold_closed_forms():
+    """W_O = identity turns the folded output into the heads' outputs
+    concatenated; W_UQ made of identity blocks turns the folded query into
+    W_UK^T applied to c_q in every head (the absorbed form's q~)."""
+    rng = np.random.default_rng(34)
+    H, dh, dv, r, dr, L = 3, 8, 8, 8, 4, 6
+    case, c_q, _, _ = _fold_case(rng, H, dh, dv, r, dr, L, dh, H * dv)
+    w_uq = np.vstack([np.eye(dh)] * H)
+    w_o = np.eye(H * dv)
+    got = _folded(case, c_q, orc.fold_query(w_uq, case["w_uk"]), orc.fold_output(w_o, case["w_uv"]))
+    ref = orc.absorbed_decode_seq(**dict(case, q_nope=np.stack([c_q] * H)))
+    assert normwise_rel(got["y"], ref["out"].reshape(-1)) <= IDENTITY_TOL
+    assert normwise_rel(got["q_tilde"], ref["q_lat"][:, :r]) <= IDENTITY_TOL
+
+
+def test_fold_detects_planted_mistakes():
+    """The identity comparison must flag a wrong fold: a perturbed weight in
+    the folded path only, head blocks taken from the wrong rows or columns,
+    and the page's literal shape (the heads summed before the fold)."""
+    rng = np.random.default_rng(35)
+    H, dh, dv, r, dr, L, dcq, dmodel = 3, 8, 8, 8, 4, 9, 8, 10
+    case, c_q, w_uq, w_o = _fold_case(rng, H, dh, dv, r, dr, L, dcq, dmodel)
+    ref = _unfolded_y(case, c_q, w_uq, w_o)
+    w_qk, w_ov = orc.fold_query(w_uq, case["w_uk"]), orc.fold_output(w_o, case["w_uv"])
+    assert normwise_rel(_folded(case, c_q, w_qk, w_ov)["y"], ref) <= IDENTITY_TOL
+
+    def flagged(qk, ov):
+        return normwise_rel(_folded(case, c_q, qk, ov)["y"], ref) > 1e3 * IDENTITY_TOL
+
+    bad = w_uq.copy()
+    bad[1 * dh + 2, 3] += 1e-3
+    assert flagged(orc.fold_query(bad, case["w_uk"]), w_ov)
+    bad = w_o.copy()
+    bad[4, 2 * dv + 1] += 1e-3
+    assert flagged(w_qk, orc.fold_output(bad, case["w_uv"]))
+    bad = case["w_uv"].copy()
+    bad[0, 1, 2] += 1e-3
+    assert flagged(w_qk, orc.fold_output(w_o, bad))
+    # head h's query rows taken as rows h, h+H, ... (interleaved, not blocks)
+    inter = np.vstack([w_uq[h::H] for h in range(H)])
+    assert flagged(orc.fold_query(inter, case["w_uk"]), w_ov)
+    # head h's W_O columns taken interleaved
+    inter = np.hstack([w_o[:, h::H] for h in range(H)])
+    assert flagged(w_qk, orc.fold_output(inter, case["w_uv"]))
+    # one (d_model, r) matrix for all heads applied to the summed latents
+    summed = sum(w_o[:, h * dv:(h + 1) * dv] @ case["w_uv"][h] for h in range(H))
+    o_lat = _folded(case, c_q, w_qk, w_ov)["o_lat"]
+    assert normwise_rel(summed @ o_lat.sum(axis=0), ref) > 1e3 * IDENTITY_TOL
+
+
+def test_identity_error_order_in_float32(golden_dir):
+    """'DeepSeek MLA, Built From the Paper' section 3 prints max|naive -
+    absorbed| = 2.38e-07 without shapes or dtype; 2^-22 is a float32-sized
+    gap.  Both forms evaluated in float32 at the page's lab shape (8 heads of
+    32, rank 64 plus a 16-wide RoPE key, the tiny workload's inputs) differ by
+    that order, and in float64 by none of it."""
+    g = _load(golden_dir, "identity_error.json")
+    step = syn.make_inputs("tiny")
+    seqs, qn, qr, cn, kn, wuk, wuv = oracle_args(step)
+    args = (qn[0], qr[0], seqs[0][0], seqs[0][1], cn[0], kn[0], wuk, wuv, step.softmax_scale, step.rope_base)
+    f32 = np.abs(orc.naive_decode_seq(*args, dtype=np.float32)
+                 - orc.absorbed_decode_seq(*args, dtype=np.float32)["out"]).max()
+    f64 = np.abs(orc.naive_decode_seq(*args) - orc.absorbed_decode_seq(*args)["out"]).max()
+    page = g["max_abs_naive_minus_absorbed"]
+    assert page / 30 <= f32 <= page * 30, f32
+    assert f64 <= 1e-13

@@ -161,6 +161,62 @@ def ingest_counters(workload: str, fetch_dir: str, write_dir: str, command: str)
     return entry
 
 
+def summarize_trace(trace_dir: str, order: list[str]) -> str:
+    """Markdown summary of a rocprofv3 --kernel-trace csv run of this script:
+    the decode launches split into workloads where their grid changes (the
+    workloads run one after the other, in ``order``), every other dispatch
+    assigned to the workload of the nearest decode launch; per workload and
+    kernel the dispatch count and mean/min/max duration, and the decode
+    kernel's roofline fraction from its mean (1152 bytes per attended row)."""
+    import csv
+    import glob
+    from head_latent_attention_12_amd import synthetic as syn
+
+    rows = []
+    for f in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+        rows += list(csv.DictReader(open(f)))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    dec = [i for i, r in enumerate(rows) if "decode_latent" in r["Kernel_Name"]]
+    segs, last = [], None
+    for i in dec:
+        g = rows[i]["Grid_Size_X"]
+        if g != last:
+            segs.append([])
+            last = g
+        segs[-1].append(i)
+    if len(segs) != len(order):
+        raise SystemExit(f"{len(segs)} decode segments in the trace, {len(order)} workload names given")
+    bounds = [(int(rows[s[0]]["Start_Timestamp"]), int(rows[s[-1]]["End_Timestamp"])) for s in segs]
+    per = [dict() for _ in segs]
+    for r in rows:
+        t = int(r["Start_Timestamp"])
+        k = min(range(len(bounds)), key=lambda j: 0 if bounds[j][0] <= t <= bounds[j][1]
+                else min(abs(t - bounds[j][0]), abs(t - bounds[j][1])))
+        name = r["Kernel_Name"].replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+        per[k].setdefault(name, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    out = []
+    for wl, d, s in zip(order, per, segs):
+        inp = syn.make_inputs(wl) if wl in syn.WORKLOADS else None
+        wgs = int(rows[s[0]]["Grid_Size_X"]) // max(1, int(rows[s[0]]["Workgroup_Size_X"]))
+        out.append(f"## {wl} - decode grid {wgs} work-groups\n")
+        out.append("| kernel | dispatches | mean us | min us | max us |\n|---|---|---|---|---|")
+        step = 0.0
+        for name, v in sorted(d.items(), key=lambda kv: -np.mean(kv[1])):
+            if "rocclr" in name or "at::native" in name or "elementwise" in name:
+                continue
+            out.append(f"| {name} | {len(v)} | {np.mean(v):.2f} | {np.min(v):.2f} | {np.max(v):.2f} |")
+            step += float(np.mean(v))
+        out.append(f"| sum of the step's kernels | | {step:.2f} | | |\n")
+        if inp is not None:
+            rows_att = int(inp.seq_lens.sum())
+            dmean = float(np.mean([v for n, vs in d.items() if "decode_latent" in n for v in vs]))
+            out.append(f"Decode roofline from the mean: {rows_att} attended rows x 1152 B = "
+                       f"{rows_att * 1152 / 1e6:.1f} MB / {dmean:.2f} us = "
+                       f"{rows_att * 1152 / (dmean * 1e-6) / 1e9:.0f} GB/s = "
+                       f"{rows_att * 1152 / (dmean * 1e-6) / 1e9 / HBM_PEAK_GBS:.3f} of 8000 GB/s\n")
+    return "\n".join(out)
+
+
 def cpu_baseline(inp, budget_s: float):
     """Time the fp64 oracle (absorbed form) on this machine's host cores."""
     from threadpoolctl import threadpool_info
@@ -421,7 +477,14 @@ def main():
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn rocprofv3 FETCH_SIZE / WRITE_SIZE csv runs into profiles/decode_latent_counters.json")
     ap.add_argument("--counters-command", default="", help="command line recorded with ingested counters")
+    ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
+                    help="print a markdown summary of a rocprofv3 --kernel-trace csv run of this script")
+    ap.add_argument("--trace-order", default="dsv2_ragged,dsv2,dsv2_long",
+                    help="workloads of the traced run, in the order it ran them")
     args = ap.parse_args()
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace, args.trace_order.split(",")))
+        return
     if args.ingest_counters:
         print(json.dumps(ingest_counters(args.workload, *args.ingest_counters, args.counters_command), indent=1))
         return

@@ -12,6 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 SRC = os.path.join(CSRC, "mla.hip")
 SRC_FP8 = os.path.join(CSRC, "decode_fp8.hip")
+SRC_FOLD = os.path.join(CSRC, "fold.hip")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmla.so")
 
@@ -45,10 +46,10 @@ def _run(cmd, verbose):
 
 
 def build(verbose: bool = False, extra=()) -> str:
-    """Compile both translation units (each with its own flags) and link them."""
+    """Compile the translation units (each with its own flags) and link them."""
     tmp = LIB + ".tmp"
     objs = []
-    for src, flags in ((SRC, COMMON_FLAGS + MLA_FLAGS), (SRC_FP8, COMMON_FLAGS)):
+    for src, flags in ((SRC, COMMON_FLAGS + MLA_FLAGS), (SRC_FP8, COMMON_FLAGS), (SRC_FOLD, COMMON_FLAGS)):
         obj = os.path.join(CSRC, os.path.basename(src) + ".o")
         _run([hipcc(), *flags, *extra, "-I", INCLUDE, "-c", src, "-o", obj], verbose)
         objs.append(obj)

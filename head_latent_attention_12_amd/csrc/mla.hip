@@ -2506,6 +2506,94 @@ mla_status mla_kv_down(const mla_dims* dims, int32_t d_model, const void* h, con
   return launch_result("mla_kv_down");
 }
 
+// ---------------------------------------------------------------------------
+// Folded projections (kernels in fold.hip)
+// ---------------------------------------------------------------------------
+
+static mla_status check_fold_dims(const mla_dims* dims) {
+  mla_status st = check_dims_impl(dims);
+  if (st != MLA_OK) return st;
+  if (dims->dtype != MLA_BF16) return fail(MLA_ERR_UNSUPPORTED, "the folded projections are built for bf16 storage");
+  if (dims->rank % 64 != 0) return fail(MLA_ERR_UNSUPPORTED, "rank must be a multiple of 64");
+  if (((int64_t)dims->heads * dims->rank) % 256 != 0) return fail(MLA_ERR_UNSUPPORTED, "heads * rank must be a multiple of 256");
+  return MLA_OK;
+}
+
+static mla_status check_d_c_q(int32_t d_c_q) {
+  if (d_c_q < 1) return fail(MLA_ERR_INVALID_ARG, "d_c_q must be >= 1");
+  if (d_c_q % 256 != 0 || d_c_q > 65536) return fail(MLA_ERR_UNSUPPORTED, "d_c_q must be a multiple of 256, at most 65536");
+  return MLA_OK;
+}
+
+static mla_status check_d_model(int32_t d_model) {
+  if (d_model < 1) return fail(MLA_ERR_INVALID_ARG, "d_model must be >= 1");
+  if (d_model % 64 != 0 || d_model > 65536) return fail(MLA_ERR_UNSUPPORTED, "d_model must be a multiple of 64, at most 65536");
+  return MLA_OK;
+}
+
+static mla_status hip_result(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  return MLA_OK;
+}
+
+mla_status mla_fold_query(const mla_dims* dims, int32_t d_c_q, const void* w_uq, const void* w_uk, void* w_qk,
+                          void* stream) {
+  mla_status st = check_fold_dims(dims);
+  if (st != MLA_OK) return st;
+  if ((st = check_d_c_q(d_c_q)) != MLA_OK) return st;
+  if ((st = check_ptrs({w_uq, w_uk, w_qk})) != MLA_OK) return st;
+  g_last_error.clear();
+  return hip_result(mla_detail::launch_fold_query(dims->heads, dims->d_head, dims->rank, d_c_q, w_uq, w_uk, w_qk,
+                                                  (hipStream_t)stream),
+                    "mla_fold_query");
+}
+
+mla_status mla_fold_output(const mla_dims* dims, int32_t d_model, const void* w_o, const void* w_uv, void* w_ov,
+                           void* stream) {
+  mla_status st = check_fold_dims(dims);
+  if (st != MLA_OK) return st;
+  if ((st = check_d_model(d_model)) != MLA_OK) return st;
+  if ((st = check_ptrs({w_o, w_uv, w_ov})) != MLA_OK) return st;
+  g_last_error.clear();
+  return hip_result(mla_detail::launch_fold_output(dims->heads, dims->d_v, dims->rank, d_model, w_o, w_uv, w_ov,
+                                                   (hipStream_t)stream),
+                    "mla_fold_output");
+}
+
+mla_status mla_absorb_q_folded(const mla_dims* dims, int32_t d_c_q, const void* c_q, const void* w_qk, void* q_lat,
+                               void* stream) {
+  mla_status st = check_fold_dims(dims);
+  if (st != MLA_OK) return st;
+  if ((st = check_d_c_q(d_c_q)) != MLA_OK) return st;
+  if ((st = check_ptrs({c_q, w_qk, q_lat})) != MLA_OK) return st;
+  g_last_error.clear();
+  return hip_result(mla_detail::launch_absorb_q_folded(dims->batch, dims->heads, dims->rank,
+                                                       dims->rank + dims->d_rope, d_c_q, c_q, w_qk, q_lat,
+                                                       (hipStream_t)stream),
+                    "mla_absorb_q_folded");
+}
+
+mla_status mla_out_folded_workspace_size(const mla_dims* dims, int32_t d_model, size_t* bytes) {
+  mla_status st = check_fold_dims(dims);
+  if (st != MLA_OK) return st;
+  if ((st = check_d_model(d_model)) != MLA_OK) return st;
+  if (bytes == nullptr) return fail(MLA_ERR_INVALID_ARG, "bytes NULL");
+  *bytes = mla_detail::out_folded_workspace_bytes(dims->batch, d_model, (int64_t)dims->heads * dims->rank);
+  return MLA_OK;
+}
+
+mla_status mla_out_folded(const mla_dims* dims, int32_t d_model, const float* o_lat, const void* w_ov,
+                          void* workspace, float* y, void* stream) {
+  size_t ws = 0;
+  mla_status st = mla_out_folded_workspace_size(dims, d_model, &ws);
+  if (st != MLA_OK) return st;
+  if ((st = check_ptrs({o_lat, w_ov, workspace, y})) != MLA_OK) return st;
+  g_last_error.clear();
+  return hip_result(mla_detail::launch_out_folded(dims->batch, d_model, (int64_t)dims->heads * dims->rank, o_lat,
+                                                  w_ov, y, (float*)workspace, (hipStream_t)stream),
+                    "mla_out_folded");
+}
+
 mla_status mla_partials_size(const mla_dims* dims, int32_t num_splits, size_t* o_part_bytes, size_t* lse_part_bytes) {
   mla_status st = check_dims_impl(dims);
   if (st != MLA_OK) return st;

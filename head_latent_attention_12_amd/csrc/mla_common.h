@@ -273,3 +273,17 @@ hipError_t mla_launch_decode_fp8(const void* q_lat, const void* cache, const flo
                                  const mla_detail::CacheMap& cm,
                                  const int32_t* seq_lens, int32_t batch, int32_t num_splits, int32_t chunk,
                                  void* o_part, float* lse_part, float scale_log2, hipStream_t stream);
+
+// Folded projections (fold.hip), launched by the C-ABI entry points after
+// their argument checks.
+namespace mla_detail {
+hipError_t launch_fold_query(int H, int dh, int r, int dcq, const void* w_uq, const void* w_uk, void* w_qk,
+                             hipStream_t stream);
+hipError_t launch_fold_output(int H, int dv, int r, int d_model, const void* w_o, const void* w_uv, void* w_ov,
+                              hipStream_t stream);
+hipError_t launch_absorb_q_folded(int B, int H, int r, int W, int dcq, const void* c_q, const void* w_qk,
+                                  void* q_lat, hipStream_t stream);
+size_t out_folded_workspace_bytes(int B, int d_model, int64_t K);
+hipError_t launch_out_folded(int B, int d_model, int64_t K, const float* o_lat, const void* w_ov, float* y,
+                             float* workspace, hipStream_t stream);
+}  // namespace mla_detail

@@ -23,7 +23,10 @@ STATUS = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARG", 2: "MLA_ERR_UNSUPPORTED", 3: "M
 EXPORTS = ("mla_absorb_q", "mla_rope_append", "mla_decode_latent", "mla_combine", "mla_up_v",
            "mla_combine_up_v", "mla_absorb_rope", "mla_decode_latent_paged", "mla_rope_append_paged",
            "mla_absorb_rope_paged", "mla_decode_latent_fp8", "mla_decode_latent_fp8_paged",
-           "mla_absorb_rope_fp8", "mla_absorb_rope_fp8_paged", "mla_kv_down", "mla_kv_down_workspace_size", "mla_partials_size", "mla_plan_splits", "mla_check_dims", "mla_status_string", "mla_last_error")
+           "mla_absorb_rope_fp8", "mla_absorb_rope_fp8_paged", "mla_kv_down", "mla_kv_down_workspace_size",
+           "mla_fold_query", "mla_fold_output", "mla_absorb_q_folded", "mla_out_folded",
+           "mla_out_folded_workspace_size", "mla_partials_size", "mla_plan_splits", "mla_check_dims",
+           "mla_status_string", "mla_last_error")
 
 
 class MlaDims(ctypes.Structure):
@@ -68,6 +71,11 @@ def lib() -> ctypes.CDLL:
             "mla_absorb_rope_fp8_paged": (i32, [D, P, P, P, P, P, P, P, i32, i32, i64, P, P, P, P]),
             "mla_kv_down": (i32, [D, i32, P, P, P, P, ctypes.c_float, P, P, P, P]),
             "mla_kv_down_workspace_size": (i32, [D, i32, ctypes.POINTER(ctypes.c_size_t)]),
+            "mla_fold_query": (i32, [D, i32, P, P, P, P]),
+            "mla_fold_output": (i32, [D, i32, P, P, P, P]),
+            "mla_absorb_q_folded": (i32, [D, i32, P, P, P, P]),
+            "mla_out_folded": (i32, [D, i32, P, P, P, P, P]),
+            "mla_out_folded_workspace_size": (i32, [D, i32, ctypes.POINTER(ctypes.c_size_t)]),
             "mla_partials_size": (i32, [D, i32, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]),
             "mla_plan_splits": (i32, [D, i32, i64, i32]),
             "mla_check_dims": (i32, [D]),
@@ -209,6 +217,33 @@ def mla_kv_down_workspace_size(dims, d_model) -> int:
 def mla_kv_down(dims, d_model, h, w_dkv, w_kr, norm_w, eps, workspace, c_kv_new, k_rope_new, stream=None):
     _check("mla_kv_down", lib().mla_kv_down(ctypes.byref(dims), int(d_model), _p(h), _p(w_dkv), _p(w_kr), _p(norm_w),
                                             float(eps), _p(workspace), _p(c_kv_new), _p(k_rope_new), _s(stream)))
+
+
+def mla_fold_query(dims, d_c_q, w_uq, w_uk, w_qk, stream=None):
+    _check("mla_fold_query", lib().mla_fold_query(ctypes.byref(dims), int(d_c_q), _p(w_uq), _p(w_uk), _p(w_qk),
+                                                  _s(stream)))
+
+
+def mla_fold_output(dims, d_model, w_o, w_uv, w_ov, stream=None):
+    _check("mla_fold_output", lib().mla_fold_output(ctypes.byref(dims), int(d_model), _p(w_o), _p(w_uv), _p(w_ov),
+                                                    _s(stream)))
+
+
+def mla_absorb_q_folded(dims, d_c_q, c_q, w_qk, q_lat, stream=None):
+    _check("mla_absorb_q_folded", lib().mla_absorb_q_folded(ctypes.byref(dims), int(d_c_q), _p(c_q), _p(w_qk),
+                                                            _p(q_lat), _s(stream)))
+
+
+def mla_out_folded_workspace_size(dims, d_model) -> int:
+    n = ctypes.c_size_t(0)
+    _check("mla_out_folded_workspace_size", lib().mla_out_folded_workspace_size(ctypes.byref(dims), int(d_model),
+                                                                                ctypes.byref(n)))
+    return n.value
+
+
+def mla_out_folded(dims, d_model, o_lat, w_ov, workspace, y, stream=None):
+    _check("mla_out_folded", lib().mla_out_folded(ctypes.byref(dims), int(d_model), _p(o_lat), _p(w_ov),
+                                                  _p(workspace), _p(y), _s(stream)))
 
 
 def mla_partials_size(dims, num_splits):

@@ -355,3 +355,34 @@ def make_kv_down_inputs(B: int, d_model: int, r: int = 512, d_rope: int = 64, se
     g = 1.0 + 0.1 * rng.standard_normal(r)
     return KvDownInputs(B, d_model, r, d_rope, eps, bf16_bits_from_f64(h), bf16_bits_from_f64(w_dkv),
                         bf16_bits_from_f64(w_kr), bf16_bits_from_f64(g))
+
+
+@dataclasses.dataclass
+class FoldInputs:
+    """Weights and query latent of the folded projections (bf16 bits), for a
+    step whose attention dims come from a StepInputs."""
+
+    d_c_q: int
+    d_model: int
+    c_q: np.ndarray      # [B, d_c_q]        normalised query latent
+    w_uq: np.ndarray     # [H * d_head, d_c_q]  Linear(d_c_q -> H*d_head) weight
+    w_o: np.ndarray      # [d_model, H * d_v]   Linear(H*d_v -> d_model) weight
+
+    def f64(self, field: str) -> np.ndarray:
+        return bf16_bits_to_f64(getattr(self, field))
+
+
+def make_fold_inputs(step: StepInputs, d_c_q: int = 1536, d_model: int = 5120, seed: int = 21) -> FoldInputs:
+    """Seeded bf16 inputs of the folded projections at the page's DeepSeek-V2
+    sizes (d_c' 1536, d_model 5120) by default: c_q rows drawn N(0, 1) and
+    scaled to unit RMS (the output of the query RMSNorm, no gain), W_UQ ~
+    N(0, 1/d_c_q), W_O ~ N(0, 1/(H*d_v)), in that order."""
+    rng = np.random.default_rng(seed)
+    H, dh, dv = step.H, step.d_head, step.d_v
+    c_q = _unit_rms_rows(rng.standard_normal((step.B, d_c_q)))
+    w_uq = bf16_bits_from_f64(rng.standard_normal((H * dh, d_c_q)) / math.sqrt(d_c_q))
+    w_o = np.empty((d_model, H * dv), dtype=np.uint16)
+    for m0 in range(0, d_model, 512):  # in row blocks (bounded fp64 temporaries)
+        m1 = min(d_model, m0 + 512)
+        w_o[m0:m1] = bf16_bits_from_f64(rng.standard_normal((m1 - m0, H * dv)) / math.sqrt(H * dv))
+    return FoldInputs(d_c_q, d_model, bf16_bits_from_f64(c_q), w_uq, w_o)

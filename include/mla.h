@@ -24,6 +24,10 @@
  *                     memory
  *   mla_*_fp8         the calls that touch the cache, for a cache whose
  *                     latents are stored in 8-bit floating point
+ *   mla_fold_*        the up-projections multiplied into the query and output
+ *                     weights ahead of time; mla_absorb_q_folded and
+ *                     mla_out_folded use them in place of mla_absorb_q and
+ *                     mla_up_v + the output projection
  *
  * Sources (page title, section):
  *   [P1] "DeepSeek MLA, Built From the Paper": section 1 (the cache holds
@@ -283,6 +287,51 @@ mla_status mla_kv_down(const mla_dims* dims, int32_t d_model, const void* h, con
                        void* c_kv_new, void* k_rope_new, void* stream);
 
 mla_status mla_kv_down_workspace_size(const mla_dims* dims, int32_t d_model, size_t* bytes);
+
+/* Folded projections ([P2] absorbing projections: W_O absorbs W_UV, a
+ * product of fixed weights computed once, after which the attention-weighted
+ * latents go straight to the output space, and the query side absorbs the
+ * key up-projection the same way; [P5] "What we didn't build, and why": at
+ * decode time the up-projection is folded into the query and output
+ * matrices).  Readings: [P2]'s forward pass has an RMSNorm between W_DQ and
+ * W_UQ, so the exact query fold is W_UK into W_UQ per head; [P2]'s single
+ * (d_model, d_c) output matrix would sum the heads' latent outputs, so the
+ * output fold is per head and the output sums over heads.
+ *
+ * Shapes: c_q [B][d_c_q] the normalised query latent (RMSNorm(W_DQ x)),
+ * w_uq [H*d_head][d_c_q] (the Linear(d_c_q -> H*d_head) weight; rows
+ * h*d_head.. are head h's), w_o [d_model][H*d_v] (the Linear(H*d_v -> d_model)
+ * weight), w_qk [H][r][d_c_q], w_ov [d_model][H*r], y [B][d_model] float32.
+ * bf16 storage only (other dtypes: MLA_ERR_UNSUPPORTED); d_c_q a multiple of
+ * 256, d_model a multiple of 64, both at most 65536; rank a multiple of 64.
+ *
+ * mla_fold_query:  w_qk[h][j][i] = sum_d w_uk[h][d][j] * w_uq[h*d_head + d][i]
+ * mla_fold_output: w_ov[m][h*r + j] = sum_d w_o[m][h*d_v + d] * w_uv[h][d][j]
+ *   (fp32 accumulation, each folded weight rounded once to bf16; done once
+ *   per set of weights, not per step)
+ * mla_absorb_q_folded: q_lat[b][h][j] = sum_i w_qk[h][j][i] * c_q[b][i], j < r
+ *   (fp32 accumulation, one rounding; replaces mla_absorb_q, columns
+ *   [r, r + d_rope) untouched)
+ * mla_out_folded: y[b][m] = sum_h sum_j w_ov[m][h*r + j] * o_lat[b][h][j]
+ *   (replaces mla_up_v followed by W_O; o_lat from mla_combine enters the
+ *   bf16 product as a high and a low bf16 part; fp32 accumulation summed over
+ *   a fixed split of the k range, so repeated calls give the same bits).
+ *   workspace: device memory of mla_out_folded_workspace_size bytes (fp32
+ *   partial sums), owned by the caller; calls that share one workspace must
+ *   not overlap. */
+mla_status mla_fold_query(const mla_dims* dims, int32_t d_c_q, const void* w_uq, const void* w_uk,
+                          void* w_qk, void* stream);
+
+mla_status mla_fold_output(const mla_dims* dims, int32_t d_model, const void* w_o, const void* w_uv,
+                           void* w_ov, void* stream);
+
+mla_status mla_absorb_q_folded(const mla_dims* dims, int32_t d_c_q, const void* c_q, const void* w_qk,
+                               void* q_lat, void* stream);
+
+mla_status mla_out_folded(const mla_dims* dims, int32_t d_model, const float* o_lat, const void* w_ov,
+                          void* workspace, float* y, void* stream);
+
+mla_status mla_out_folded_workspace_size(const mla_dims* dims, int32_t d_model, size_t* bytes);
 
 /* Bytes of o_part and lse_part for `num_splits` splits. */
 mla_status mla_partials_size(const mla_dims* dims, int32_t num_splits, size_t* o_part_bytes,

@@ -262,3 +262,30 @@ def test_kv_down_argument_checks():
     _expect(1, mla.mla_kv_down, d, 512, P16, P16, P16, P16, -1.0, P16, P16, P16, 0)
     f = mla.make_dims(8, 16, 64, 64, 64, 32, mla.MLA_F32)
     _expect(2, mla.mla_kv_down, f, 512, P16, P16, P16, P16, 1e-6, P16, P16, P16, 0)
+
+
+def test_fold_argument_checks():
+    """Folded projections: bf16 only, d_c_q a multiple of 256, d_model a
+    multiple of 64, no NULL or misaligned pointers; the output product's
+    workspace holds one fp32 partial per (k group, sequence, output) of a
+    batch slice of up to 64 sequences (eight k groups of 8192 at H 128, r 512)."""
+    d = dsv2()
+    assert mla.mla_out_folded_workspace_size(d, 5120) == 8 * 16 * 5120 * 4
+    assert mla.mla_out_folded_workspace_size(mla.make_dims(100, 128, 128, 128, 512, 64, mla.MLA_BF16), 256) \
+        == 8 * 64 * 256 * 4
+    _expect(2, mla.mla_out_folded_workspace_size, d, 100)
+    _expect(1, mla.mla_out_folded_workspace_size, d, 0)
+    _expect(2, mla.mla_fold_query, d, 1000, P16, P16, P16, 0)           # d_c_q not a multiple of 256
+    _expect(1, mla.mla_fold_query, d, 0, P16, P16, P16, 0)
+    _expect(1, mla.mla_fold_query, d, 1536, 0, P16, P16, 0)
+    _expect(3, mla.mla_fold_query, d, 1536, P16, P16 + 2, P16, 0)
+    _expect(2, mla.mla_fold_output, d, 5000, P16, P16, P16, 0)          # d_model not a multiple of 64
+    _expect(1, mla.mla_fold_output, d, 5120, P16, 0, P16, 0)
+    _expect(3, mla.mla_fold_output, d, 5120, P16, P16, P16 + 8, 0)
+    _expect(1, mla.mla_absorb_q_folded, d, 1536, P16, P16, 0, 0)
+    _expect(2, mla.mla_absorb_q_folded, d, 96, P16, P16, P16, 0)
+    _expect(1, mla.mla_out_folded, d, 5120, P16, P16, 0, P16, 0)        # workspace NULL
+    _expect(3, mla.mla_out_folded, d, 5120, P16, P16, P16, P16 + 4, 0)
+    f = mla.make_dims(8, 16, 64, 64, 64, 32, mla.MLA_F32)
+    _expect(2, mla.mla_fold_query, f, 256, P16, P16, P16, 0)
+    _expect(2, mla.mla_out_folded, f, 512, P16, P16, P16, P16, 0)

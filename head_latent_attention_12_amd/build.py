@@ -45,23 +45,43 @@ def _run(cmd, verbose):
         raise RuntimeError(f"hipcc failed ({res.returncode}): {' '.join(cmd)}")
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    """Compile the translation units (each with its own flags) and link them."""
-    tmp = LIB + ".tmp"
+# Host-side AddressSanitizer and UndefinedBehaviorSanitizer for the library's
+# argument checks and planning code (the device code is built as usual): each
+# -fsanitize= applies to the host pass only.
+SANITIZE_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+
+
+def build(verbose: bool = False, extra=(), sanitize: bool = False, out: str | None = None) -> str:
+    """Compile the translation units (each with its own flags) and link them
+    into ``out`` (default: the package's libmla.so).  ``sanitize``: host code
+    built with ASan and UBSan (load it with the clang ASan runtime preloaded)."""
+    lib = out or LIB
+    tmp = lib + ".tmp"
+    san = SANITIZE_HOST if sanitize else []
     objs = []
     for src, flags in ((SRC, COMMON_FLAGS + MLA_FLAGS), (SRC_FP8, COMMON_FLAGS), (SRC_FOLD, COMMON_FLAGS)):
-        obj = os.path.join(CSRC, os.path.basename(src) + ".o")
-        _run([hipcc(), *flags, *extra, "-I", INCLUDE, "-c", src, "-o", obj], verbose)
+        obj = os.path.join(os.path.dirname(lib), os.path.basename(src) + (".san.o" if sanitize else ".o"))
+        _run([hipcc(), *flags, *san, *extra, "-I", INCLUDE, "-c", src, "-o", obj], verbose)
         objs.append(obj)
     try:
-        _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+        _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *san, *objs, "-o", tmp], verbose)
     finally:
         for obj in objs:
             if os.path.exists(obj):
                 os.remove(obj)
     _check_kernel_stubs(tmp)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def asan_runtime() -> str:
+    """The clang ASan runtime matching hipcc's host compiler (to preload)."""
+    res = subprocess.run([hipcc(), "--print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = res.stdout.strip()
+    if res.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("the clang ASan runtime was not found next to hipcc")
+    return path
 
 
 def _check_kernel_stubs(path: str) -> None:

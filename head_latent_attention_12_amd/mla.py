@@ -12,7 +12,9 @@ import ctypes
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmla.so")
+# the in-tree library; MLA_LIBRARY names another build of it (the host-sanitized
+# build that the argument-check tests also run against)
+LIB_PATH = os.environ.get("MLA_LIBRARY") or os.path.join(_PKG, "libmla.so")
 
 MLA_F32 = 0
 MLA_BF16 = 1

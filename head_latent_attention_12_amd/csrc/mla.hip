@@ -36,6 +36,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <type_traits>
 
@@ -2258,6 +2259,39 @@ mla_status check_decode_args(const mla_dims* dims, const void* q_lat, const void
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// Scratch memory of the no-allocation entry point: a fixed device array (each
+// GPU the library runs on holds its own copy until the process ends).  Host
+// code never passes the array's name to a kernel (on the host it is only a
+// stand-in for the symbol): the device address is looked up once per device,
+// with that device current, and kept.
+// ---------------------------------------------------------------------------
+
+constexpr size_t kScratchBytes = (size_t)4 << 20;
+constexpr int kScratchDevices = 64;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+static std::mutex g_scratch_mutex;
+static float* g_scratch_ptr[kScratchDevices] = {};
+
+// The current device's copy of `scratch` (looked up on its first use there).
+static mla_status scratch_on_current_device(float** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= kScratchDevices) return fail(MLA_ERR_UNSUPPORTED, "device index above 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(MLA_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_scratch_ptr[dev] = (float*)p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MLA_OK;
+}
+
 extern "C" {
 
 mla_status mla_decode_latent(const mla_dims* dims, const void* q_lat, const void* kv_cache, const int64_t* row_offsets,
@@ -2592,6 +2626,32 @@ mla_status mla_out_folded(const mla_dims* dims, int32_t d_model, const float* o_
   return hip_result(mla_detail::launch_out_folded(dims->batch, d_model, (int64_t)dims->heads * dims->rank, o_lat,
                                                   w_ov, y, (float*)workspace, (hipStream_t)stream),
                     "mla_out_folded");
+}
+
+mla_status mla_kv_down_noalloc(const mla_dims* dims, int32_t d_model, const void* h, const void* w_dkv,
+                               const void* w_kr, const void* norm_w, float eps, void* c_kv_new, void* k_rope_new,
+                               void* stream) {
+  size_t ws = 0;
+  mla_status st = mla_kv_down_workspace_size(dims, d_model, &ws);
+  if (st != MLA_OK) return st;
+  if ((st = check_ptrs({h, w_dkv, w_kr, norm_w, c_kv_new, k_rope_new})) != MLA_OK) return st;
+  if (dims->dtype != MLA_BF16) return fail(MLA_ERR_UNSUPPORTED, "kv_down is built for bf16 storage");
+  if (dims->rank + dims->d_rope > 1024) return fail(MLA_ERR_UNSUPPORTED, "rank + d_rope above 1024");
+  if (!(eps >= 0.f)) return fail(MLA_ERR_INVALID_ARG, "eps must be >= 0");
+  if (ws > kScratchBytes)
+    return fail(MLA_ERR_WORKSPACE, "mla_kv_down_noalloc: (d_model / 512) * batch * (rank + d_rope) * 4 bytes of "
+                                   "partial sums exceed its 4 MiB scratch; use mla_kv_down with a workspace");
+  float* part = nullptr;
+  if ((st = scratch_on_current_device(&part)) != MLA_OK) return st;
+  g_last_error.clear();
+  hipStream_t s = (hipStream_t)stream;
+  const int nf = dims->rank + dims->d_rope, nchunks = d_model / kKvChunk;
+  hipLaunchKernelGGL(kv_down_partial_kernel, dim3(((nf + 31) / 32) * nchunks), dim3(256), 0, s, (const u16*)h,
+                     (const u16*)w_dkv, (const u16*)w_kr, dims->batch, d_model, dims->rank, dims->d_rope, part);
+  hipLaunchKernelGGL(kv_down_final_kernel, dim3(dims->batch), dim3(256), 0, s, (const float*)part, nchunks,
+                     dims->batch, dims->rank, dims->d_rope, (const u16*)norm_w, eps, (u16*)c_kv_new,
+                     (u16*)k_rope_new);
+  return launch_result("mla_kv_down_noalloc");
 }
 
 mla_status mla_partials_size(const mla_dims* dims, int32_t num_splits, size_t* o_part_bytes, size_t* lse_part_bytes) {

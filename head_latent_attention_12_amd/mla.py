@@ -26,6 +26,7 @@ EXPORTS = ("mla_absorb_q", "mla_rope_append", "mla_decode_latent", "mla_combine"
            "mla_combine_up_v", "mla_absorb_rope", "mla_decode_latent_paged", "mla_rope_append_paged",
            "mla_absorb_rope_paged", "mla_decode_latent_fp8", "mla_decode_latent_fp8_paged",
            "mla_absorb_rope_fp8", "mla_absorb_rope_fp8_paged", "mla_kv_down", "mla_kv_down_workspace_size",
+           "mla_kv_down_noalloc",
            "mla_fold_query", "mla_fold_output", "mla_absorb_q_folded", "mla_out_folded",
            "mla_out_folded_workspace_size", "mla_partials_size", "mla_plan_splits", "mla_check_dims",
            "mla_status_string", "mla_last_error")
@@ -73,6 +74,7 @@ def lib() -> ctypes.CDLL:
             "mla_absorb_rope_fp8_paged": (i32, [D, P, P, P, P, P, P, P, i32, i32, i64, P, P, P, P]),
             "mla_kv_down": (i32, [D, i32, P, P, P, P, ctypes.c_float, P, P, P, P]),
             "mla_kv_down_workspace_size": (i32, [D, i32, ctypes.POINTER(ctypes.c_size_t)]),
+            "mla_kv_down_noalloc": (i32, [D, i32, P, P, P, P, ctypes.c_float, P, P, P]),
             "mla_fold_query": (i32, [D, i32, P, P, P, P]),
             "mla_fold_output": (i32, [D, i32, P, P, P, P]),
             "mla_absorb_q_folded": (i32, [D, i32, P, P, P, P]),
@@ -219,6 +221,12 @@ def mla_kv_down_workspace_size(dims, d_model) -> int:
 def mla_kv_down(dims, d_model, h, w_dkv, w_kr, norm_w, eps, workspace, c_kv_new, k_rope_new, stream=None):
     _check("mla_kv_down", lib().mla_kv_down(ctypes.byref(dims), int(d_model), _p(h), _p(w_dkv), _p(w_kr), _p(norm_w),
                                             float(eps), _p(workspace), _p(c_kv_new), _p(k_rope_new), _s(stream)))
+
+
+def mla_kv_down_noalloc(dims, d_model, h, w_dkv, w_kr, norm_w, eps, c_kv_new, k_rope_new, stream=None):
+    _check("mla_kv_down_noalloc", lib().mla_kv_down_noalloc(ctypes.byref(dims), int(d_model), _p(h), _p(w_dkv),
+                                                            _p(w_kr), _p(norm_w), float(eps), _p(c_kv_new),
+                                                            _p(k_rope_new), _s(stream)))
 
 
 def mla_fold_query(dims, d_c_q, w_uq, w_uk, w_qk, stream=None):

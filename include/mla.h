@@ -288,6 +288,22 @@ mla_status mla_kv_down(const mla_dims* dims, int32_t d_model, const void* h, con
 
 mla_status mla_kv_down_workspace_size(const mla_dims* dims, int32_t d_model, size_t* bytes);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * mla_kv_down with its fp32 partial sums in a fixed 4 MiB device array of
+ * the library instead of a caller workspace.  Same arguments and results as
+ * mla_kv_down without `workspace`; calls whose partial sums
+ * (mla_kv_down_workspace_size) exceed 4 MiB return MLA_ERR_WORKSPACE.  It
+ * allocates nothing: the array is part of the library's code object, one
+ * copy per device, found on the first call on that device.  Every call on a
+ * device shares that device's array, so calls that overlap on one device
+ * (on different streams, or from several host threads) race; calls in one
+ * stream's order do not.  The kernels write every partial sum before they
+ * read any, so nothing carried over from an earlier call is used. */
+mla_status mla_kv_down_noalloc(const mla_dims* dims, int32_t d_model, const void* h, const void* w_dkv,
+                               const void* w_kr, const void* norm_w, float eps, void* c_kv_new,
+                               void* k_rope_new, void* stream);
+
 /* Folded projections ([P2] absorbing projections: W_O absorbs W_UV, a
  * product of fixed weights computed once, after which the attention-weighted
  * latents go straight to the output space, and the query side absorbs the

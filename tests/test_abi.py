@@ -289,3 +289,18 @@ def test_fold_argument_checks():
     f = mla.make_dims(8, 16, 64, 64, 64, 32, mla.MLA_F32)
     _expect(2, mla.mla_fold_query, f, 256, P16, P16, P16, 0)
     _expect(2, mla.mla_out_folded, f, 512, P16, P16, P16, P16, 0)
+
+
+def test_kv_down_noalloc_argument_checks():
+    """mla_kv_down_noalloc: the checks of mla_kv_down, and partial sums
+    beyond its 4 MiB scratch refused on the host (MLA_ERR_WORKSPACE)."""
+    d = dsv2()
+    _expect(2, mla.mla_kv_down_noalloc, d, 768, P16, P16, P16, P16, 1e-6, P16, P16, 0)
+    _expect(1, mla.mla_kv_down_noalloc, d, 512, 0, P16, P16, P16, 1e-6, P16, P16, 0)
+    _expect(3, mla.mla_kv_down_noalloc, d, 512, P16, P16, P16, P16 + 2, 1e-6, P16, P16, 0)
+    _expect(1, mla.mla_kv_down_noalloc, d, 512, P16, P16, P16, P16, -1.0, P16, P16, 0)
+    big = mla.make_dims(256, 128, 128, 128, 512, 64, mla.MLA_BF16)
+    assert mla.mla_kv_down_workspace_size(big, 8192) > 4 << 20
+    _expect(4, mla.mla_kv_down_noalloc, big, 8192, P16, P16, P16, P16, 1e-6, P16, P16, 0)
+    f = mla.make_dims(8, 16, 64, 64, 64, 32, mla.MLA_F32)
+    _expect(2, mla.mla_kv_down_noalloc, f, 512, P16, P16, P16, P16, 1e-6, P16, P16, 0)

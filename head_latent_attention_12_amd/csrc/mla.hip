@@ -2666,42 +2666,93 @@ mla_status mla_partials_size(const mla_dims* dims, int32_t num_splits, size_t* o
   return MLA_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+constexpr int64_t kSplitCost = 8, kItemCost = 12;
+
+int32_t device_cus(int32_t num_cus) {
+  if (num_cus > 0) return num_cus;
+  int dev = 0;
+  hipDeviceProp_t prop;
+  if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess) return 0;
+  return prop.multiProcessorCount;
+}
+
+// Estimated decode time of `items` work-groups of `chunk` rows, in units of
+// tiles / num_cus.  A work-group runs on one compute unit at a time and the
+// items are dealt evenly over the 8 XCDs, so the decode takes (rounds of
+// work-groups per CU) x (tiles per split + a fixed per-split cost for the
+// prologue and the partial's store, about kSplitCost tiles).  Every
+// non-empty split also adds its partial to what all work-groups start by
+// loading at once and to what the merge reads back: about kItemCost tiles per
+// CU's worth of splits.
+int64_t split_cost(int64_t items, int64_t chunk, int64_t num_cus) {
+  const int64_t cus_per_xcd = std::max<int64_t>(1, num_cus / 8);
+  const int64_t per_xcd = (items + 7) / 8;
+  const int64_t rounds = (per_xcd + cus_per_xcd - 1) / cus_per_xcd;
+  return rounds * (chunk / 32 + kSplitCost) * num_cus + kItemCost * items;
+}
+
+}  // namespace
+
+extern "C" {
+
 int32_t mla_plan_splits(const mla_dims* dims, int32_t max_seq_len, int64_t total_rows, int32_t num_cus) {
   if (check_dims_impl(dims) != MLA_OK) return 0;
   if (max_seq_len < 1 || total_rows < 1) return 0;
-  if (num_cus <= 0) {
-    int dev = 0;
-    hipDeviceProp_t prop;
-    if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess) return 0;
-    num_cus = prop.multiProcessorCount;
-  }
-  // Pick the split count with the smallest estimated step time.  A split is
-  // one work-group and a compute unit runs one at a time, dealt evenly over
-  // the 8 XCDs, so the decode time is (rounds of work-groups per CU) x (tiles
-  // per split + a fixed per-split cost for the prologue and the partial's
-  // store, about kSplitCost tiles).  Every non-empty split also adds its
-  // partial to what all work-groups start by loading at once and to what the
-  // merge reads back: about kItemCost tiles per CU's worth of splits.  Only
-  // the total and the longest length are known here: the non-empty splits are
-  // at most B * ceil(max / chunk), and for mixed lengths about total / chunk
-  // plus the partial last split of every sequence (counted as 0.6 of a split
-  // each, a little above the mean).  Ties go to fewer splits.
-  constexpr int64_t kSplitCost = 8, kItemCost = 12;
-  const int64_t B = dims->batch, cus_per_xcd = std::max<int64_t>(1, num_cus / 8);
+  if ((num_cus = device_cus(num_cus)) <= 0) return 0;
+  // The split count with the smallest estimated decode time (split_cost).
+  // Only the total and the longest length are known here: the non-empty
+  // splits are at most B * ceil(max / chunk), and for mixed lengths about
+  // total / chunk plus the partial last split of every sequence (counted as
+  // 0.6 of a split each, a little above the mean).  Ties go to fewer splits.
+  const int64_t B = dims->batch;
   const int64_t s_max = std::min<int64_t>(kMaxSplits, ((int64_t)max_seq_len + 31) / 32);
   int64_t best = 1, best_cost = INT64_MAX;
   for (int64_t sp = 1; sp <= s_max; ++sp) {
     const int64_t chunk = chunk_rows(max_seq_len, (int32_t)sp);
     const int64_t full = B * (((int64_t)max_seq_len + chunk - 1) / chunk);
     const int64_t est = std::min(full, (total_rows + chunk - 1) / chunk + (6 * B + 9) / 10);
-    const int64_t per_xcd = (est + 7) / 8;
-    const int64_t rounds = (per_xcd + cus_per_xcd - 1) / cus_per_xcd;
-    // in units of tiles / num_cus
-    const int64_t cost = rounds * (chunk / 32 + kSplitCost) * num_cus + kItemCost * est;
+    const int64_t cost = split_cost(est, chunk, num_cus);
     if (cost < best_cost) best_cost = cost, best = sp;
   }
-  const int64_t splits = best;
-  return (int32_t)std::max<int64_t>(1, splits);
+  return (int32_t)std::max<int64_t>(1, best);
 }
+
+int32_t mla_plan_splits_for_lengths(const mla_dims* dims, const int32_t* seq_lens, int32_t num_cus,
+                                    int32_t* plan_max_seq_len) {
+  if (check_dims_impl(dims) != MLA_OK || seq_lens == nullptr || plan_max_seq_len == nullptr) return 0;
+  if ((num_cus = device_cus(num_cus)) <= 0) return 0;
+  int64_t max_len = 0;
+  for (int32_t b = 0; b < dims->batch; ++b) {
+    if (seq_lens[b] < 1) return 0;
+    max_len = std::max<int64_t>(max_len, seq_lens[b]);
+  }
+  // Every chunk of whole tiles is a candidate, with the split count it needs
+  // (the largest per-sequence count) and the exact number of non-empty
+  // splits, counted as the decode kernel counts its work items; the cost is
+  // that of mla_plan_splits.  The chunk is then reached through
+  // max_seq_len' = chunk * splits (>= every length), since the kernels take
+  // ceil(max_seq_len' / splits) rounded up to whole tiles as the chunk.
+  int64_t best_s = 1, best_chunk = ((max_len + 31) / 32) * 32, best_cost = INT64_MAX;
+  for (int64_t tiles = (max_len + 31) / 32; tiles >= 1; --tiles) {
+    const int64_t chunk = 32 * tiles;
+    int64_t items = 0, splits = 0;
+    for (int32_t b = 0; b < dims->batch; ++b) {
+      const int64_t n = (seq_lens[b] + chunk - 1) / chunk;
+      items += n;
+      splits = std::max(splits, n);
+    }
+    if (splits > kMaxSplits || chunk * splits > INT32_MAX) break;  // (finer chunks only need more)
+    const int64_t cost = split_cost(items, chunk, num_cus);
+    if (cost < best_cost) best_cost = cost, best_s = splits, best_chunk = chunk;
+  }
+  *plan_max_seq_len = (int32_t)(best_chunk * best_s);
+  return (int32_t)best_s;
+}
+
+
 
 }  // extern "C"

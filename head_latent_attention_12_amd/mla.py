@@ -28,7 +28,8 @@ EXPORTS = ("mla_absorb_q", "mla_rope_append", "mla_decode_latent", "mla_combine"
            "mla_absorb_rope_fp8", "mla_absorb_rope_fp8_paged", "mla_kv_down", "mla_kv_down_workspace_size",
            "mla_kv_down_noalloc",
            "mla_fold_query", "mla_fold_output", "mla_absorb_q_folded", "mla_out_folded",
-           "mla_out_folded_workspace_size", "mla_partials_size", "mla_plan_splits", "mla_check_dims",
+           "mla_out_folded_workspace_size", "mla_partials_size", "mla_plan_splits", "mla_plan_splits_for_lengths",
+           "mla_check_dims",
            "mla_status_string", "mla_last_error")
 
 
@@ -82,6 +83,7 @@ def lib() -> ctypes.CDLL:
             "mla_out_folded_workspace_size": (i32, [D, i32, ctypes.POINTER(ctypes.c_size_t)]),
             "mla_partials_size": (i32, [D, i32, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]),
             "mla_plan_splits": (i32, [D, i32, i64, i32]),
+            "mla_plan_splits_for_lengths": (i32, [D, ctypes.POINTER(i32), i32, ctypes.POINTER(i32)]),
             "mla_check_dims": (i32, [D]),
             "mla_status_string": (ctypes.c_char_p, [i32]),
             "mla_last_error": (ctypes.c_char_p, []),
@@ -268,6 +270,17 @@ def mla_plan_splits(dims, max_seq_len, total_rows, num_cus=0) -> int:
     if n < 1:
         raise MlaError("mla_plan_splits", 1, lib().mla_last_error().decode())
     return n
+
+
+def mla_plan_splits_for_lengths(dims, seq_lens, num_cus=0) -> tuple[int, int]:
+    """seq_lens: host sequence of dims.batch ints (rows attended per sequence).
+    Returns (num_splits, max_seq_len to pass with it)."""
+    arr = (ctypes.c_int32 * int(dims.batch))(*[int(x) for x in seq_lens])
+    mls = ctypes.c_int32(0)
+    n = lib().mla_plan_splits_for_lengths(ctypes.byref(dims), arr, int(num_cus), ctypes.byref(mls))
+    if n < 1:
+        raise MlaError("mla_plan_splits_for_lengths", 1, lib().mla_last_error().decode())
+    return n, mls.value
 
 
 def mla_check_dims(dims) -> int:

@@ -34,14 +34,17 @@ class DeviceStep:
 
     def __init__(self, inp: StepInputs, num_splits: int | None = None, device: str = "cuda:0",
                  weights: "DeviceStep | None" = None, scratch: "DeviceStep | None" = None,
-                 page_rows: int | None = None, page_seed: int = 0, fp8: bool = False, fp8_seed: int = 3):
+                 page_rows: int | None = None, page_seed: int = 0, fp8: bool = False, fp8_seed: int = 3,
+                 max_seq_len: int | None = None):
         """``weights``: share W_UK/W_UV with another step (same layer).
         ``scratch``: share the per-step temporaries (q_lat, split partials,
         o_lat, lse, out) with another step of the same shape, as successive
         layers of one decode step would.  ``page_rows``: keep the cache in
         pages of that many rows behind a block table (the paged calls).
         ``fp8``: keep the cache in the fp8 row layout (codes drawn with
-        ``fp8_seed``, the fp8 calls)."""
+        ``fp8_seed``, the fp8 calls).  ``num_splits`` None: the planner's split
+        count and max_seq_len; given: that count with ``max_seq_len`` (default
+        the longest length), which together fix the splits' rows."""
         self.inp = inp
         self.device = device
         self.dims = mla.make_dims(inp.B, inp.H, inp.d_head, inp.d_v, inp.r, inp.d_rope,
@@ -75,17 +78,21 @@ class DeviceStep:
         if scratch is not None:
             self.q_lat, self.o_lat, self.lse, self.out = scratch.q_lat, scratch.o_lat, scratch.lse, scratch.out
             self.num_splits, self.o_part, self.lse_part = scratch.num_splits, scratch.o_part, scratch.lse_part
+            self.max_seq_len = scratch.max_seq_len
             return
         self.q_lat = torch.zeros((inp.B, inp.H, inp.W), dtype=st, device=device)
-        self.set_splits(num_splits)
+        self.set_splits(num_splits, max_seq_len)
         self.o_lat = torch.empty((inp.B, inp.H, inp.r), dtype=torch.float32, device=device)
         self.lse = torch.empty((inp.B, inp.H), dtype=torch.float32, device=device)
         self.out = torch.empty((inp.B, inp.H, inp.d_v), dtype=torch.float32, device=device)
 
-    def set_splits(self, num_splits: int | None) -> None:
+    def set_splits(self, num_splits: int | None, max_seq_len: int | None = None) -> None:
         inp = self.inp
-        if num_splits is None:
-            num_splits = mla.mla_plan_splits(self.dims, inp.max_seq_len, inp.total_rows)
+        # the max_seq_len passed to the decode calls: with a planned split count
+        # the planner's value (at least every length), which sets the chunk
+        self.max_seq_len = inp.max_seq_len if max_seq_len is None else int(max_seq_len)
+        if num_splits is None:  # the lengths are known on the host here
+            num_splits, self.max_seq_len = mla.mla_plan_splits_for_lengths(self.dims, inp.seq_lens)
         self.num_splits = int(num_splits)
         o_bytes, _ = mla.mla_partials_size(self.dims, self.num_splits)
         self.o_part = torch.empty((o_bytes // 4,), dtype=torch.int32, device=self.device)  # raw partials buffer
@@ -136,19 +143,19 @@ class DeviceStep:
         if self.fp8 is not None:
             if self.paged is not None:
                 mla.mla_decode_latent_fp8_paged(self.dims, self.q_lat, self.kv_cache, self.kv_scale, *self._pages(),
-                                                self.seq_lens, self.inp.max_seq_len, self.num_splits, self.o_part,
+                                                self.seq_lens, self.max_seq_len, self.num_splits, self.o_part,
                                                 self.lse_part, stream)
             else:
                 mla.mla_decode_latent_fp8(self.dims, self.q_lat, self.kv_cache, self.kv_scale, self.row_offsets,
-                                          self.seq_lens, self.inp.total_rows, self.inp.max_seq_len,
+                                          self.seq_lens, self.inp.total_rows, self.max_seq_len,
                                           self.num_splits, self.o_part, self.lse_part, stream)
             return
         if self.paged is not None:
             mla.mla_decode_latent_paged(self.dims, self.q_lat, self.kv_cache, *self._pages(), self.seq_lens,
-                                        self.inp.max_seq_len, self.num_splits, self.o_part, self.lse_part, stream)
+                                        self.max_seq_len, self.num_splits, self.o_part, self.lse_part, stream)
             return
         mla.mla_decode_latent(self.dims, self.q_lat, self.kv_cache, self.row_offsets, self.seq_lens,
-                              self.inp.total_rows, self.inp.max_seq_len, self.num_splits, self.o_part,
+                              self.inp.total_rows, self.max_seq_len, self.num_splits, self.o_part,
                               self.lse_part, stream)
 
     def combine(self, stream=None):

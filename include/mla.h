@@ -360,6 +360,17 @@ mla_status mla_partials_size(const mla_dims* dims, int32_t num_splits, size_t* o
 int32_t mla_plan_splits(const mla_dims* dims, int32_t max_seq_len, int64_t total_rows,
                         int32_t num_cus);
 
+/* The same choice when the caller knows the lengths on the host (seq_lens:
+ * host memory, dims->batch values, each >= 1): every chunk of whole 32-row
+ * tiles is a candidate, with the exact number of non-empty splits it makes
+ * (so that a batch of mixed lengths can fill the compute units in one
+ * round).  Returns the split count S (>= 1; 0 on invalid arguments) and, in
+ * *plan_max_seq_len, the max_seq_len to pass with it to the decode calls:
+ * chunk * S, at least every length, for which ceil(max_seq_len / S) rounded
+ * up to whole tiles is the planned chunk. */
+int32_t mla_plan_splits_for_lengths(const mla_dims* dims, const int32_t* seq_lens, int32_t num_cus,
+                                    int32_t* plan_max_seq_len);
+
 /* MLA_OK if the dims are valid and have a kernel instantiation. */
 mla_status mla_check_dims(const mla_dims* dims);
 

@@ -169,6 +169,53 @@ def test_plan_splits_prefers_one_round_over_finer_splits():
     assert s >= 8
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_plan_splits_for_lengths_ragged(seed):
+    """With the lengths known, ragged batches of 64 sequences (512..8192
+    cached tokens) get a chunk whose non-empty splits fill the 256 CUs in one
+    round (at most 32 per XCD) with splits no longer than the length-blind
+    plan's; the returned max_seq_len is at least every length and yields that
+    chunk."""
+    import numpy as np
+    lens = np.random.default_rng(100 + seed).integers(512, 8192, size=64, endpoint=True) + 1
+    d = mla.make_dims(64, 128, 128, 128, 512, 64, mla.MLA_BF16)
+    s, mls = mla.mla_plan_splits_for_lengths(d, lens, 256)
+    assert mls >= lens.max() and 1 <= s <= 4096
+    chunk = -(-(-(-mls // s)) // 32) * 32
+    items = int(sum(-(-int(l) // chunk) for l in lens))
+    assert max(-(-int(l) // chunk) for l in lens) <= s
+    assert -(-items // 8) <= 32, (s, chunk, items)
+    s0 = mla.mla_plan_splits(d, int(lens.max()), int(lens.sum()), 256)
+    chunk0 = -(-(-(-int(lens.max()) // s0)) // 32) * 32
+    assert chunk <= chunk0
+
+
+def test_plan_splits_for_lengths_seeded_ragged_workload():
+    """The seeded ragged workload: 37-tile splits, 253 work items (the
+    length-blind plan takes 42-tile splits)."""
+    from head_latent_attention_12_amd import synthetic as syn
+    inp = syn.make_inputs("dsv2_ragged")
+    d = mla.make_dims(inp.B, 128, 128, 128, 512, 64, mla.MLA_BF16)
+    s, mls = mla.mla_plan_splits_for_lengths(d, inp.seq_lens, 256)
+    chunk = -(-(-(-mls // s)) // 32) * 32
+    assert chunk == 37 * 32
+    assert int(sum(-(-int(l) // chunk) for l in inp.seq_lens)) == 253
+
+
+@pytest.mark.parametrize("B,L,expect", [(16, 4097, 13), (2, 131073, 125)])
+def test_plan_splits_for_lengths_uniform(B, L, expect):
+    d = mla.make_dims(B, 128, 128, 128, 512, 64, mla.MLA_BF16)
+    s, mls = mla.mla_plan_splits_for_lengths(d, [L] * B, 256)
+    assert s == expect == mla.mla_plan_splits(d, L, B * L, 256)
+    assert mls >= L
+
+
+def test_plan_splits_for_lengths_rejects_bad_args():
+    d = mla.make_dims(3, 128, 128, 128, 512, 64, mla.MLA_BF16)
+    with pytest.raises(mla.MlaError):
+        mla.mla_plan_splits_for_lengths(d, [5, 0, 7], 256)
+
+
 def test_paged_argument_checks():
     """Host-side checks of the paged calls: page size a power of two from 32
     to 65536, a block table, at least one page and one entry per sequence."""

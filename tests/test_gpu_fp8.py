@@ -48,9 +48,10 @@ def fp8_oracle(inp, fp8: syn.Fp8Cache, batch_ids=None):
     return ref, quant
 
 
-def _step(inp, num_splits=None, page_rows=None, fp8_seed=3):
+def _step(inp, num_splits=None, page_rows=None, fp8_seed=3, max_seq_len=None):
     from head_latent_attention_12_amd.step import DeviceStep
-    ds = DeviceStep(inp, num_splits=num_splits, page_rows=page_rows, page_seed=7, fp8=True, fp8_seed=fp8_seed)
+    ds = DeviceStep(inp, num_splits=num_splits, page_rows=page_rows, page_seed=7, fp8=True, fp8_seed=fp8_seed,
+                    max_seq_len=max_seq_len)
     ds.run()
     torch.cuda.synchronize()
     return ds
@@ -123,7 +124,7 @@ def test_fp8_paged_matches_packed_and_oracle(name, override, page_rows, splits):
     packed fp8 step, and against the oracle."""
     inp = syn.make_inputs(name, **override)
     packed = _step(inp, num_splits=splits)
-    ds = _step(inp, num_splits=packed.num_splits, page_rows=page_rows)
+    ds = _step(inp, num_splits=packed.num_splits, max_seq_len=packed.max_seq_len, page_rows=page_rows)
     assert torch.equal(ds.q_lat, packed.q_lat)
     assert torch.equal(ds.lse_part, packed.lse_part)
     assert torch.equal(ds.out, packed.out) and torch.equal(ds.lse, packed.lse)

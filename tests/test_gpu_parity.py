@@ -366,7 +366,8 @@ def test_paged_step_matches_packed_and_oracle(name, override, page_rows, splits)
     from head_latent_attention_12_amd.step import DeviceStep
     inp = syn.make_inputs(name, **override)
     packed = _run(inp, num_splits=splits)
-    ds = DeviceStep(inp, num_splits=packed.num_splits, page_rows=page_rows, page_seed=7)
+    ds = DeviceStep(inp, num_splits=packed.num_splits, max_seq_len=packed.max_seq_len, page_rows=page_rows,
+                    page_seed=7)
     ds.run()
     torch.cuda.synchronize()
     assert torch.equal(ds.q_lat, packed.q_lat)

@@ -1332,9 +1332,10 @@ __global__ __launch_bounds__(64) void up_v_f32_kernel(const float* __restrict__ 
 //   merge: a unit is a (sequence, part) pair covering the splits s = part
 //     (mod WPR) of that sequence; WPR is the largest power of two with
 //     rows * WPR <= 8 (1 from 5 rows up), so that short chunks still use
-//     every wave, and then each wave holds at most one unit.  A wave takes up to UPW units and issues the loads of all their
-//     splits (one contiguous 1 KB partial row each, 16 bytes per lane)
-//     together with the log-sum-exp reads, so one round trip serves them.
+//     every wave, and then each wave holds at most one unit.  A wave takes
+//     up to UPW units: it reads their log-sum-exps, then issues the loads of
+//     all their splits that hold data (one contiguous 1 KB partial row each,
+//     16 bytes per lane) together, so a second round trip serves them.
 //     Units of one sequence add their sums through LDS.  The merged fp32 row
 //     enters LDS as a hi and a lo bf16 row (16-byte chunk k of row t at slot
 //     k ^ (t & 15)).
@@ -1397,15 +1398,18 @@ __device__ __forceinline__ void cuv_put_row(char* ot, int t, int lane, const flo
 // each in flight.  The splits of a unit are taken 64 at a time: lane i holds
 // the log-sum-exp of the group's split i (one load), the group raises the
 // unit's running maximum (the sums so far rescaled), and split i's weight is
-// read from lane i.  Only splits that exist are loaded, and an empty split's
-// bytes are never used.  Leaves the merged rows in ot and, if lse_out is not
-// null, the merged log-sum-exps there.
-template <int UPW, int NB>
+// read from lane i.  A split past its sequence's last (fewer rows than
+// num_splits chunks) has log-sum-exp -inf and was never written: its row is
+// not loaded, so a ragged batch reads only the rows that hold data.  Leaves
+// the merged rows in ot and, if lse_out is not null, the merged
+// log-sum-exps there.  NWAVES: the work-group's waves.
+template <int UPW, int NB, int NWAVES = kCuvWaves>
 __device__ __forceinline__ void cuv_merge(const u16* __restrict__ o_part, const float* __restrict__ lse_part,
                                           int S, int H, int h, int b0, int nb, int WPR, int wave, int lane,
                                           char* ot, float (*xs)[64][8], float* xm, float* xw,
                                           float* __restrict__ lse_out) {
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  static_assert(64 % NB == 0, "a batch of splits lies in one group of 64");
   constexpr int R = 512;
   const int units = nb * WPR;
   const int part = wave % WPR;                                // the same for all units of a wave
@@ -1414,14 +1418,14 @@ __device__ __forceinline__ void cuv_merge(const u16* __restrict__ o_part, const 
   int trow[UPW];
   int64_t base[UPW];  // (b*S + part)*H + h: split i of the unit is row base + i*WPR*H of o_part / lse_part
   // The partial rows are read through a buffer resource over the sequence's
-  // S*H*R values (at most 512 MB): a split that does not exist gets an offset
-  // past the end, which returns zeros without a memory access, so every load
-  // of a batch is issued unconditionally.
+  // S*H*R values (at most 512 MB): every lane's offset is 16*lane and each
+  // row's (uniform) byte offset goes in the scalar offset, so a batch of loads
+  // needs no offset registers.
   __amdgpu_buffer_rsrc_t rsrc[UPW];
   const uint32_t nrec = (uint32_t)S * (uint32_t)H * (R * 2);
 #pragma unroll
   for (int k = 0; k < UPW; ++k) {
-    const int u = wave + kCuvWaves * k;
+    const int u = wave + NWAVES * k;
     uok[k] = u < units;
     trow[k] = uok[k] ? u / WPR : 0;
     base[k] = ((int64_t)(b0 + trow[k]) * S + part) * H + h;
@@ -1439,45 +1443,44 @@ __device__ __forceinline__ void cuv_merge(const u16* __restrict__ o_part, const 
   }
   for (int g0 = 0; g0 < spu; g0 += 64) {
     const int gn = min(64, spu - g0);  // splits of this group (per unit)
-    float lv[UPW], ev[UPW];
+    float ev[UPW];
+    uint64_t live[UPW];  // bit i: split g0 + i holds data (finite log-sum-exp)
+    int nlive = 0;       // one past the last such split over the wave's units
 #pragma unroll
     for (int k = 0; k < UPW; ++k) {
-      lv[k] = -INFINITY;
-      if (uok[k] && lane < gn) lv[k] = lse_part[base[k] + (int64_t)(g0 + lane) * istride];
+      float lv = -INFINITY;
+      if (uok[k] && lane < gn) lv = lse_part[base[k] + (int64_t)(g0 + lane) * istride];
+      live[k] = __ballot(lv != -INFINITY);
+      nlive = max(nlive, live[k] == 0 ? 0 : 64 - __builtin_clzll(live[k]));
+      // the group raises the unit's running maximum
+      const float mn = fmaxf(mx[k], wave_max_f(lv));
+      ev[k] = 0.f;
+      if (mn != -INFINITY) {
+        const float c = __expf(mx[k] - mn);  // 0 while mx = -inf
+        wsum[k] *= c;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[k][e] *= c;
+        mx[k] = mn;
+        ev[k] = lv == -INFINITY ? 0.f : __expf(lv - mn);
+        wsum[k] += wave_sum_f(ev[k]);
+      }
     }
-    for (int u0 = 0; u0 < gn; u0 += NB) {
+    for (int u0 = 0; u0 < nlive; u0 += NB) {
       u32x4 raw[UPW][NB];
 #pragma unroll
       for (int k = 0; k < UPW; ++k)
 #pragma unroll
         for (int u = 0; u < NB; ++u) {
-          const uint32_t off = (uok[k] && u0 + u < gn)
-                                   ? (uint32_t)((part + WPR * (g0 + u0 + u)) * H + h) * (R * 2) + 16 * lane
-                                   : nrec;
-          raw[k][u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc[k], off, 0, 0));
+          raw[k][u] = u32x4{0u, 0u, 0u, 0u};
+          if (((live[k] >> (u0 + u)) & 1) == 0) continue;  // (u0 + u < 64: NB divides 64)
+          const uint32_t soff = (uint32_t)((part + WPR * (g0 + u0 + u)) * H + h) * (R * 2);
+          raw[k][u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc[k], 16 * lane, soff, 0));
         }
-      if (u0 == 0) {  // the group's log-sum-exps (loaded before these rows) update the maxima
-#pragma unroll
-        for (int k = 0; k < UPW; ++k) {
-          const float mn = fmaxf(mx[k], wave_max_f(lv[k]));
-          ev[k] = 0.f;
-          if (mn != -INFINITY) {
-            const float c = __expf(mx[k] - mn);  // 0 while mx = -inf
-            wsum[k] *= c;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[k][e] *= c;
-            mx[k] = mn;
-            ev[k] = lv[k] == -INFINITY ? 0.f : __expf(lv[k] - mn);
-            wsum[k] += wave_sum_f(ev[k]);
-          }
-        }
-      }
 #pragma unroll
       for (int k = 0; k < UPW; ++k)
 #pragma unroll
         for (int u = 0; u < NB; ++u) {
-          if (!(uok[k] && u0 + u < gn)) continue;
-          // the split's weight (0 for an empty split, whose bytes are not used)
+          // the split's weight (0 for a split without data, which was not loaded)
           const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ev[k]), u0 + u));
           if (c == 0.f) continue;
           const u32x4 v = raw[k][u];
@@ -1500,7 +1503,7 @@ __device__ __forceinline__ void cuv_merge(const u16* __restrict__ o_part, const 
       cuv_put_row(ot, trow[k], lane, o);
       if (lse_out != nullptr && lane == 0) lse_out[(int64_t)(b0 + trow[k]) * H + h] = mx[k] + __logf(wsum[k]);
     }
-  } else {  // one unit per wave (units <= 8): the parts of a sequence are waves t*WPR .. t*WPR + WPR-1
+  } else {  // one unit per wave (units <= NWAVES): the parts of a sequence are waves t*WPR .. t*WPR + WPR-1
     if (uok[0]) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) xs[wave][lane][e] = acc[0][e];
@@ -1689,6 +1692,86 @@ __global__ __launch_bounds__(kCuvWaves * 64) void combine_up_v_bf16_d128_kernel(
     }
     __syncthreads();  // the next chunk rewrites these bytes
   }
+}
+
+// The d_v = 128 merge with 16 waves (more than 16 sequences per work-group):
+// two sequences per wave and chunk with 8 split rows each in flight, so that
+// up to 8 splits arrive in one round trip.  The head's W_UV is touched into
+// L2 at the start (one line per thread) and read into registers after each
+// chunk's merge: wave w holds rows 32*(w % 4) .. +31 over latent quarter w / 4
+// (8 fragments), and the four quarters are added through LDS.
+constexpr int kCuvWaves16 = 16;
+
+__global__ __launch_bounds__(kCuvWaves16 * 64) void combine_up_v_bf16_d128_w16_kernel(
+    const u16* __restrict__ o_part, const float* __restrict__ lse_part, int num_splits,
+    const u16* __restrict__ w_uv, int B, int H, float* __restrict__ out, float* __restrict__ lse_out) {
+  using M = Mma<u16>;
+  constexpr int R = 512, DV = 128, WROW = R * 2, NWV = kCuvWaves16;
+  __shared__ __attribute__((aligned(16))) char ot[kCuvRows * 2 * WROW];  // merged rows (hi | lo)
+  __shared__ float xs[NWV][64][8];
+  __shared__ float xm[NWV], xw[NWV];
+  static_assert(NWV * 4 * 64 * 16 <= kCuvRows * 2 * WROW, "the quarter sums fit the merged rows' bytes");
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hf = lane >> 5, l32 = lane & 31;
+  int h, part;
+  {
+    const int bid = (int)blockIdx.x;
+    const int grp = bid / (kXcds * 2);
+    const int rem = bid - grp * (kXcds * 2);
+    h = grp * kXcds + rem % kXcds;
+    part = rem / kXcds;
+  }
+  if (h >= H) return;
+  const int half = (B + 1) / 2;
+  const int b_lo = part * half, b_hi = min(B, b_lo + half);
+  const int db = wave & 3, jq = wave >> 2;
+  const u16* wrow = w_uv + ((int64_t)h * DV + 32 * db + l32) * R + 128 * jq + 8 * hf;
+  // the head's 128 KB of W_UV is 1024 lines of 128 bytes: one per thread
+  const uint32_t touch = *(const uint32_t*)(w_uv + (int64_t)h * DV * R + 64 * threadIdx.x);
+  for (int b0 = b_lo; b0 < b_hi; b0 += kCuvRows) {
+    const int nb = min(kCuvRows, b_hi - b0);
+    // waves per sequence: the largest power of two with nb * WPR <= 16 (1 from 9 rows up)
+    const int WPR = nb >= 9 ? 1 : (nb >= 5 ? 2 : (nb >= 3 ? 4 : (nb == 2 ? 8 : 16)));
+    if (nb * WPR > NWV) {
+      cuv_merge<2, 8, NWV>(o_part, lse_part, num_splits, H, h, b0, nb, WPR, wave, lane, ot, xs, xm, xw, lse_out);
+    } else {
+      cuv_merge<1, 16, NWV>(o_part, lse_part, num_splits, H, h, b0, nb, WPR, wave, lane, ot, xs, xm, xw, lse_out);
+    }
+    // the fragments are read here, after the merge (an opaque copy of the
+    // address keeps them from being hoisted out of the loop and held through it)
+    const u16* wp = wrow;
+    asm volatile("" : "+v"(wp));
+    i16x8 a[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) a[u] = *(const i16x8*)(wp + 16 * u);
+    __syncthreads();  // merged rows written
+    f32x16 acc = zero16();
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int ch = 16 * jq + 2 * u + hf;  // 16-byte chunk: k = 128*jq + 16*u + 8*hf .. +7
+      const int sl = 16 * (ch ^ (l32 & 15));
+      const i16x8 bh = *(const LDS_AS i16x8*)((LDS_AS char*)ot + l32 * 2 * WROW + sl);
+      const i16x8 bl = *(const LDS_AS i16x8*)((LDS_AS char*)ot + l32 * 2 * WROW + WROW + sl);
+      acc = M::mma(a[u], bh, acc);
+      acc = M::mma(a[u], bl, acc);
+    }
+    __syncthreads();  // every wave has read the merged rows: their bytes take the quarter sums
+    LDS_AS f32x4* red = (LDS_AS f32x4*)(LDS_AS char*)ot;  // [wave][row quarter][lane]
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      red[(wave * 4 + q) * 64 + lane] = f32x4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+    __syncthreads();
+    if (l32 < nb) {
+      // wave w adds rows 8q + 4hf .. +3 of block db (q = w / 4) over the four latent quarters
+      const int q = jq;
+      const f32x4 sum = ((red[(db * 4 + q) * 64 + lane] + red[((db + 4) * 4 + q) * 64 + lane]) +
+                         red[((db + 8) * 4 + q) * 64 + lane]) + red[((db + 12) * 4 + q) * 64 + lane];
+      *(f32x4*)(out + ((int64_t)(b0 + l32) * H + h) * DV + 32 * db + 8 * q + 4 * hf) = sum;
+    }
+    __syncthreads();  // the next chunk rewrites these bytes
+  }
+  if (B < 0 && touch == 0u) out[0] = 0.f;  // (never true: keeps the touch loads)
 }
 
 __global__ __launch_bounds__(64) void combine_up_v_f32_kernel(const float* __restrict__ o_part,
@@ -2489,9 +2572,15 @@ mla_status mla_combine_up_v(const mla_dims* dims, const void* o_part, const floa
     // the per-block kernel measured faster (B 2: 15.1 against 16.0 us).
     if (dims->d_v == 128 && dims->batch > 2) {
       const int blocks = (dims->heads + kXcds - 1) / kXcds * kXcds * 2;  // whole groups of 8 heads, two halves
-      hipLaunchKernelGGL(combine_up_v_bf16_d128_kernel, dim3(blocks), dim3(kCuvWaves * 64), 0, s,
-                         (const u16*)o_part, lse_part, num_splits, (const u16*)w_uv, dims->batch, dims->heads, out,
-                         lse);
+      if ((dims->batch + 1) / 2 > 16) {  // more than 16 sequences per half: two per wave with 16 waves
+        hipLaunchKernelGGL(combine_up_v_bf16_d128_w16_kernel, dim3(blocks), dim3(kCuvWaves16 * 64), 0, s,
+                           (const u16*)o_part, lse_part, num_splits, (const u16*)w_uv, dims->batch, dims->heads,
+                           out, lse);
+      } else {
+        hipLaunchKernelGGL(combine_up_v_bf16_d128_kernel, dim3(blocks), dim3(kCuvWaves * 64), 0, s,
+                           (const u16*)o_part, lse_part, num_splits, (const u16*)w_uv, dims->batch, dims->heads,
+                           out, lse);
+      }
       return launch_result("mla_combine_up_v");
     }
     const int nh = dims->d_v % 64 == 0 ? 2 : 1;

@@ -174,12 +174,14 @@ def test_edge_lengths(name, lens):
     check_step(inp, ds, oracle_step(inp), tag=f"{name} lens={lens[:8]}")
 
 
-@pytest.mark.parametrize("B", [1, 2, 3, 4, 5, 6, 7, 8, 9, 31, 32, 33, 40, 64, 65])
+@pytest.mark.parametrize("B", [1, 2, 3, 4, 5, 6, 7, 8, 9, 31, 32, 33, 40, 64, 65, 68, 70, 76])
 @pytest.mark.parametrize("splits", [1, 3, 40])
 def test_combine_up_v_batch_shapes(B, splits):
     """The fused merge + W_UV call over the batch sizes where its work layout
-    changes (waves per sequence 8, 4, 2, 1; up to four sequences per wave;
-    chunks of 32 sequences with a short last chunk) and split counts from
+    changes: 8 waves up to 16 sequences per half-batch (waves per sequence
+    8, 4, 2, 1; up to four sequences per wave), 16 waves above (one or two
+    sequences per wave; a short last chunk of 1, 2, 3 or 6 sequences takes
+    16, 8, 4 or 2 waves each), chunks of 32 sequences, and split counts from
     one to more than one load batch, against the oracle and against the
     separate combine and up_v calls on the same partials."""
     inp = syn.make_inputs("dsv2", B=B, T=(1, 400))

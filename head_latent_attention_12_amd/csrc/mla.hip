@@ -1025,8 +1025,8 @@ __device__ __forceinline__ void absorb_bf16_block(int bid, const u16* __restrict
   // RoPE (fused launch): block (h, blk) rotates head h's query pairs of the
   // sequences b = blk (mod nblk), and block h*nblk + blk appends the cache row
   // of sequence h*nblk + blk (mod H*nblk).  The first UQ pairs per thread and
-  // the first appended row are loaded before the DMA below is issued, and
-  // rotated and stored while it is in flight.
+  // the first appended row are loaded before the DMA below is issued (their
+  // latency overlaps it), and rotated and stored after it.
   constexpr int UQ = 2, CVA = 2;  // pairs per thread; c_kv_new quads per thread (R <= 1024)
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
   const int half = ROPE ? ra.DR / 2 : 1;
@@ -1077,9 +1077,12 @@ __device__ __forceinline__ void absorb_bf16_block(int bid, const u16* __restrict
     const char* src = (const char*)(w_uk + ((int64_t)h * DH + d) * R + j0) + 16 * c;
     __builtin_amdgcn_global_load_lds(src, (LDS_AS char*)wt + (wave * WCOP + n) * 1024, 16, 0, 0);
   }
-  // The RoPE work needs only the loads issued before the copies (they return
-  // first, so waiting for them does not wait for the copies): it runs while
-  // the copies are in flight.
+  // The RoPE work needs only the loads issued before the copies, but the
+  // compiler's wait before their first use counts every vector memory
+  // operation (s_waitcnt vmcnt(0)), so it starts once the copies have landed.
+  // (Making it overlap the copies takes exact wait accounting: a branch-free
+  // issue, an s_waitcnt the compiler sees, and the frequency table read with
+  // scalar loads; measured, that form was not faster.)
   if constexpr (ROPE) {
     const int W2 = R + ra.DR;
     auto qstore = [&](int pidx, uint32_t x, int pos, double th) {

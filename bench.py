@@ -92,6 +92,7 @@ def counter_traffic(workload: str):
     return e.get("hbm_bytes_per_launch")
 
 
+OUTSIDE_STEP = ("kv_down", "fold_gemm", "wstream")  # kernels of calls that are not part of the decode step
 CALIB_BYTES = 512 * 2 ** 20     # calibration kernel: reads and writes this many bytes (above the 256 MB MALL)
 CALIB_KERNEL = "neg_kernel"     # torch.neg on float32: one read and one write per element
 
@@ -161,6 +162,54 @@ def ingest_counters(workload: str, fetch_dir: str, write_dir: str, command: str)
     return entry
 
 
+def _short_name(name: str) -> str:
+    return name.replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+
+
+def summarize_counters(fetch_dir: str, write_dir: str, sq_dir: str | None = None) -> str:
+    """Markdown table of a counters run (rocprofv3 --pmc FETCH_SIZE, then
+    WRITE_SIZE, and optionally SQ counters, each a pass of its own over
+    ``bench.py --counters-run``): per kernel the dispatch count, the mean
+    fetched and written MB per dispatch (KiB scaled by the calibration
+    kernel's reading of its known size) and the mean of each SQ counter."""
+    fetch, write = _per_dispatch(fetch_dir, "FETCH_SIZE"), _per_dispatch(write_dir, "WRITE_SIZE")
+    cal_f = [v for n, vs in fetch.items() if CALIB_KERNEL in n for v in vs]
+    cal_w = [v for n, vs in write.items() if CALIB_KERNEL in n for v in vs]
+    if not cal_f or not cal_w:
+        raise SystemExit("no calibration kernel rows in the counter runs")
+    sf = (CALIB_BYTES / 1024.0) / float(np.median(cal_f))
+    sw = (CALIB_BYTES / 1024.0) / float(np.median(cal_w))
+    out = [f"Calibration ({CALIB_KERNEL}, {CALIB_BYTES} bytes read and written): FETCH_SIZE "
+           f"{float(np.median(cal_f)):.0f} KiB -> scale {sf:.4f}; WRITE_SIZE {float(np.median(cal_w)):.0f} KiB "
+           f"-> scale {sw:.4f}\n",
+           "| kernel | dispatches | fetched MB | written MB |", "|---|---|---|---|"]
+    names = sorted({n for n in fetch if CALIB_KERNEL not in n and "at::native" not in n and "rocclr" not in n},
+                   key=lambda n: -float(np.mean(fetch[n])))
+    for n in names:
+        f = float(np.mean(fetch[n])) * 1024.0 * sf / 1e6
+        w = float(np.mean(write.get(n, [0.0]))) * 1024.0 * sw / 1e6
+        out.append(f"| {_short_name(n)} | {len(fetch[n])} | {f:.2f} | {w:.2f} |")
+    if sq_dir:
+        import csv
+        import glob
+        per = {}
+        for fcsv in glob.glob(os.path.join(sq_dir, "**", "*counter_collection.csv"), recursive=True):
+            for row in csv.DictReader(open(fcsv)):
+                key = (row["Kernel_Name"], row.get("Dispatch_Id") or row.get("Correlation_Id"), row["Counter_Name"])
+                per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
+        agg = {}
+        for (n, _, c), v in per.items():
+            agg.setdefault((n, c), []).append(v)
+        counters = sorted({c for (_, c) in agg})
+        out.append("\nSQ / GRBM counters, mean per dispatch (summed over the chip):\n")
+        out.append("| kernel | " + " | ".join(counters) + " |")
+        out.append("|---|" + "---|" * len(counters))
+        for n in sorted({n for (n, _) in agg if CALIB_KERNEL not in n and "at::native" not in n}):
+            vals = [f"{float(np.mean(agg[(n, c)])):.4g}" if (n, c) in agg else "" for c in counters]
+            out.append(f"| {_short_name(n)} | " + " | ".join(vals) + " |")
+    return "\n".join(out)
+
+
 def summarize_trace(trace_dir: str, order: list[str]) -> str:
     """Markdown summary of a rocprofv3 --kernel-trace csv run of this script:
     the decode launches split into workloads where their grid changes (the
@@ -188,12 +237,17 @@ def summarize_trace(trace_dir: str, order: list[str]) -> str:
         raise SystemExit(f"{len(segs)} decode segments in the trace, {len(order)} workload names given")
     bounds = [(int(rows[s[0]]["Start_Timestamp"]), int(rows[s[-1]]["End_Timestamp"])) for s in segs]
     per = [dict() for _ in segs]
+    outside = {}
     for r in rows:
         t = int(r["Start_Timestamp"])
         k = min(range(len(bounds)), key=lambda j: 0 if bounds[j][0] <= t <= bounds[j][1]
                 else min(abs(t - bounds[j][0]), abs(t - bounds[j][1])))
-        name = r["Kernel_Name"].replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
-        per[k].setdefault(name, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        name = _short_name(r["Kernel_Name"])
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        if any(x in name for x in OUTSIDE_STEP):
+            outside.setdefault(name, []).append(dur)
+            continue
+        per[k].setdefault(name, []).append(dur)
     out = []
     for wl, d, s in zip(order, per, segs):
         inp = syn.make_inputs(wl) if wl in syn.WORKLOADS else None
@@ -214,6 +268,11 @@ def summarize_trace(trace_dir: str, order: list[str]) -> str:
                        f"{rows_att * 1152 / 1e6:.1f} MB / {dmean:.2f} us = "
                        f"{rows_att * 1152 / (dmean * 1e-6) / 1e9:.0f} GB/s = "
                        f"{rows_att * 1152 / (dmean * 1e-6) / 1e9 / HBM_PEAK_GBS:.3f} of 8000 GB/s\n")
+    if outside:
+        out.append("## Kernels outside the step (latent KV production, folded projections)\n")
+        out.append("| kernel | dispatches | mean us | min us | max us |\n|---|---|---|---|---|")
+        for name, v in sorted(outside.items()):
+            out.append(f"| {name} | {len(v)} | {np.mean(v):.2f} | {np.min(v):.2f} | {np.max(v):.2f} |")
     return "\n".join(out)
 
 
@@ -278,6 +337,70 @@ def run_kv_down(B=16, d_model=5120, launches=50):
             "us_per_call": round(us, 2), "algorithmic_bytes": nbytes,
             "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
             "timing": "HIP events around back-to-back calls over 8 weight sets"}
+
+
+def run_fold(B=16, d_c_q=1536, d_model=5120, launches=30):
+    """The folded projections at the DeepSeek-V2 shape (H 128, d_head = d_v =
+    128, r 512, d_c' 1536, d_model 5120): W_QK = W_UK^T W_UQ per head and
+    W_OV = W_O W_UV per head are formed once, then mla_absorb_q_folded and
+    mla_out_folded are timed with HIP events around back-to-back launches,
+    rotating over weight sets that together exceed the Infinity Cache.  Both
+    are weight streams (B = 16 columns): their roofline is HBM on the folded
+    weights, which are larger than the unfolded ones they replace."""
+    import torch
+
+    from head_latent_attention_12_amd import mla, synthetic as syn
+    from head_latent_attention_12_amd.step import _dev
+
+    inp = syn.make_inputs("dsv2", B=B, T=64)  # (the fold does not touch the cache)
+    fin = syn.make_fold_inputs(inp, d_c_q=d_c_q, d_model=d_model)
+    H, r = inp.H, inp.r
+    dims = mla.make_dims(B, H, inp.d_head, inp.d_v, r, inp.d_rope, mla.MLA_BF16, inp.softmax_scale, inp.rope_base)
+    w_uq, w_uk, w_o, w_uv = _dev(fin.w_uq, "cuda"), _dev(inp.w_uk, "cuda"), _dev(fin.w_o, "cuda"), _dev(inp.w_uv, "cuda")
+    c_q = _dev(fin.c_q, "cuda")
+    n_q, n_o = 3, 2  # 3 x 201 MB and 2 x 671 MB of folded weights: past the 256 MB Infinity Cache
+    w_qk = [torch.empty((H, r, d_c_q), dtype=torch.int16, device="cuda") for _ in range(n_q)]
+    w_ov = [torch.empty((d_model, H * r), dtype=torch.int16, device="cuda") for _ in range(n_o)]
+    for w in w_qk:
+        mla.mla_fold_query(dims, d_c_q, w_uq, w_uk, w)
+    for w in w_ov:
+        mla.mla_fold_output(dims, d_model, w_o, w_uv, w)
+    q_lat = torch.zeros((B, H, r + inp.d_rope), dtype=torch.int16, device="cuda")
+    o_lat = torch.randn((B, H, r), dtype=torch.float32, device="cuda")
+    ws = torch.empty(mla.mla_out_folded_workspace_size(dims, d_model) // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty((B, d_model), dtype=torch.float32, device="cuda")
+
+    def timed(call, n_sets):
+        for i in range(3):
+            call(i % n_sets)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(launches):
+            call(i % n_sets)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / launches
+
+    us_q = timed(lambda i: mla.mla_absorb_q_folded(dims, d_c_q, c_q, w_qk[i], q_lat), n_q)
+    us_o = timed(lambda i: mla.mla_out_folded(dims, d_model, o_lat, w_ov[i], ws, y), n_o)
+    bytes_q = H * r * d_c_q * 2 + B * d_c_q * 2 + B * H * r * 2
+    bytes_o = d_model * H * r * 2 + B * H * r * 4 + B * d_model * 4
+    unfolded_q = H * inp.d_head * (d_c_q + r) * 2   # W_UQ + W_UK, the weights the fold replaces
+    unfolded_o = H * inp.d_v * (d_model + r) * 2    # W_O + W_UV
+    print(f"# fold B={B} d_c'={d_c_q} d_model={d_model}: absorb_q_folded {us_q:.2f} us "
+          f"({bytes_q / (us_q * 1e-6) / 1e9:.0f} GB/s), out_folded {us_o:.2f} us "
+          f"({bytes_o / (us_o * 1e-6) / 1e9:.0f} GB/s)", file=sys.stderr, flush=True)
+    return {"workload": f"folded projections bf16 B={B} H={H} r={r} d_c_q={d_c_q} d_model={d_model}",
+            "absorb_q_folded": {"us_per_call": round(us_q, 2), "algorithmic_bytes": bytes_q,
+                                "GBps": round(bytes_q / (us_q * 1e-6) / 1e9, 1),
+                                "hbm_frac": round(bytes_q / (us_q * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                                "unfolded_weight_bytes": unfolded_q},
+            "out_folded": {"us_per_call": round(us_o, 2), "algorithmic_bytes": bytes_o,
+                           "GBps": round(bytes_o / (us_o * 1e-6) / 1e9, 1),
+                           "hbm_frac": round(bytes_o / (us_o * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                           "unfolded_weight_bytes": unfolded_o},
+            "timing": "HIP events around back-to-back calls, rotating over folded weight sets"}
 
 
 def capture_round(sets):
@@ -477,11 +600,16 @@ def main():
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn rocprofv3 FETCH_SIZE / WRITE_SIZE csv runs into profiles/decode_latent_counters.json")
     ap.add_argument("--counters-command", default="", help="command line recorded with ingested counters")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DIR",
+                    help="FETCH_DIR WRITE_DIR [SQ_DIR]: markdown table of rocprofv3 --pmc runs of --counters-run")
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
                     help="print a markdown summary of a rocprofv3 --kernel-trace csv run of this script")
     ap.add_argument("--trace-order", default="dsv2_ragged,dsv2,dsv2_long",
                     help="workloads of the traced run, in the order it ran them")
     args = ap.parse_args()
+    if args.summarize_counters:
+        print(summarize_counters(*args.summarize_counters[:3]))
+        return
     if args.summarize_trace:
         print(summarize_trace(args.summarize_trace, args.trace_order.split(",")))
         return
@@ -523,6 +651,7 @@ def main():
                              if k not in ("inp", "k3_flops", "step_flops")}
     if not args.no_others:
         others["kv_down_dsv2"] = run_kv_down()
+        others["fold_dsv2"] = run_fold()
 
     line = {
         "metric": "MLA decode cached-tokens/s + achieved HBM GB/s & MFMA util vs roofline (1 GPU)",

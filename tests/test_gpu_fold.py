@@ -181,3 +181,16 @@ def test_out_folded_is_deterministic(dsv2_fold):
     mla.mla_out_folded(ds.dims, fin.d_model, ds.o_lat, w_ov, ws, y2)
     torch.cuda.synchronize()
     assert torch.equal(y, y2)
+
+
+def test_folded_step_ragged_full_size():
+    """The folded step on the full ragged DeepSeek-V2 batch (64 sequences,
+    lengths U[512, 8192], the planned splits) with the page's d_c' 1536 and
+    d_model 5120, against the unfolded fp64 forward pass."""
+    inp = syn.make_inputs("dsv2_ragged")
+    fin = syn.make_fold_inputs(inp, seed=24)
+    ds, w_qk, _, y = folded_step(inp, fin)
+    q_ref, y_ref = unfolded_reference(inp, fin)
+    w_qk_abs = orc.fold_query(np.abs(fin.f64("w_uq")), np.abs(inp.f64("w_uk")))
+    check_q(inp, fin, ds, q_ref, w_qk_abs, "folded dsv2_ragged B64")
+    check_y(y.cpu().numpy().astype(np.float64), y_ref, "folded dsv2_ragged B64")

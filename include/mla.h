@@ -174,7 +174,9 @@ mla_status mla_decode_latent(const mla_dims* dims, const void* q_lat, const void
  *   m = max_s lse_part[b][s][h];  w_s = exp(lse_part[b][s][h] - m)
  *   o_lat[b][h] = sum_s w_s o_part(b, s, h, :) / sum_s w_s
  *   lse[b][h]   = m + ln sum_s w_s                (lse may be NULL)
- * Splits whose lse_part is -inf are skipped. */
+ * Splits whose lse_part is -inf are skipped and their o_part rows are not
+ * read (mla_decode_latent writes none for a split past its sequence's rows),
+ * here and in mla_combine_up_v. */
 mla_status mla_combine(const mla_dims* dims, const void* o_part, const float* lse_part,
                        int32_t num_splits, float* o_lat, float* lse, void* stream);
 

@@ -8,8 +8,8 @@ combine_up_v.  Inputs are seeded synthetic tensors already
 resident in HBM; the timed loop rotates over several independent input sets
 (each with its own cache and weights, like successive layers) so that the
 256 MB Infinity Cache cannot hold the cache and weights; the per-step
-temporaries share one workspace.  The timed steps replay a HIP graph that
-holds one step of every set in turn (as the layers of one decode step);
+temporaries share one workspace.  The K timed steps are one HIP graph that
+cycles over the sets (as the layers of successive decode steps);
 a HIP graph of back-to-back decode launches, replayed between HIP events on
 the launch stream, gives that kernel's duration.
 
@@ -403,8 +403,9 @@ def run_fold(B=16, d_c_q=1536, d_model=5120, launches=30):
             "timing": "HIP events around back-to-back calls, rotating over folded weight sets"}
 
 
-def capture_round(sets):
-    """One HIP graph with one step of each input set, in order."""
+def capture_steps(sets, steps):
+    """One HIP graph holding `steps` steps, cycling over the input sets in order
+    (as the layers of successive decode steps would run)."""
     import torch
 
     graph = torch.cuda.CUDAGraph()
@@ -415,8 +416,8 @@ def capture_round(sets):
             ds.run()  # one eager pass on the capture stream before recording
     torch.cuda.current_stream().wait_stream(side)
     with torch.cuda.graph(graph):
-        for ds in sets:
-            ds.run()
+        for i in range(steps):
+            sets[i % len(sets)].run()
     return graph
 
 
@@ -442,22 +443,17 @@ def run_workload(name, steps, warmup, min_sets, verbose=True, page_rows=None, fp
         sets[i % n_sets].run()
     torch.cuda.synchronize()
 
-    # the timed steps, recorded as HIP graphs (the kernels are the same as
-    # eager launches; a graph removes the host-side launch cost between them):
-    # one graph holds one step of every set in turn, as the layers of one
-    # decode step would run, and per-set graphs cover a remainder of steps
-    graphs = [ds.capture() for ds in sets]
-    round_graph = capture_round(sets)
-    n_rounds, n_rest = divmod(steps, n_sets)
+    # the timed steps, recorded as one HIP graph (the kernels are the same as
+    # eager launches; the graph removes the host-side launch cost between
+    # them): the K steps cycle over the sets in turn, as the layers of
+    # successive decode steps would run.  It is replayed once untimed first
+    # (the first replay uploads the graph).
+    steps_graph = capture_steps(sets, steps)
 
     def timed_steps():
-        for _ in range(n_rounds):
-            round_graph.replay()
-        for i in range(n_rest):
-            graphs[i].replay()
+        steps_graph.replay()
 
-    for _ in range(max(1, warmup // n_sets)):
-        round_graph.replay()
+    steps_graph.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     timed_steps()
@@ -513,7 +509,7 @@ def run_workload(name, steps, warmup, min_sets, verbose=True, page_rows=None, fp
     torch.cuda.synchronize()
     k3_ms = b0.elapsed_time(b1) / (reps * n_sets)
     del dec_graph
-    del graphs, round_graph
+    del steps_graph
 
     ms = wall * 1e3 / steps
     res = {
@@ -676,8 +672,8 @@ def main():
         "roofline": {k: v for k, v in roofline_record(main_res, bf16).items()},
         "roofline_by_workload": by_workload,
         "step": {
-            "timing": "HIP graph replay of the step's three launches (absorb_rope, decode_latent, combine_up_v); "
-                      "one graph holds one step of every rotated input set",
+            "timing": "one HIP graph of the K timed steps (three launches each: absorb_rope, decode_latent, "
+                      "combine_up_v), cycling over the rotated input sets",
             "device_us_per_step": round(main_res["device_ms_per_step"] * 1e3, 2),
             "eager_us_per_step": round(main_res["eager_ms_per_step"] * 1e3, 2),
             "algorithmic_bytes": main_res["step_bytes"],

@@ -199,6 +199,11 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (LDS DMA base)
   const int hf = lane >> 5, l32 = lane & 31;
+  // every kernel argument, fetched in one batch at entry (otherwise the
+  // compiler loads them in dependent rounds between the work lookup's steps)
+  asm volatile("" ::"s"(q_lat), "s"(cache), "s"(cm.row_offsets), "s"(cm.total_rows), "s"(cm.total_pages),
+               "s"(cm.bt_stride), "s"(cm.page_shift), "s"(block_table), "s"(seq_lens), "s"(batch), "s"(num_splits),
+               "s"(chunk), "s"(o_part), "s"(lse_part), "s"(scale_log2));
   DecodeItem it;
   if (!decode_item<PAGED, S::GROUPS>(seq_lens, cm, batch, num_splits, chunk, it)) return;
   const int b = it.b, s = it.s, n_b = it.n_b, seq_len = it.seq_len;
@@ -994,11 +999,17 @@ __device__ __forceinline__ uint32_t rope_pair_bf16(uint32_t x, int pos, double t
 // before the one wait, so a work-group pays a single HBM round trip up front.
 // Query rows are stored with their 16-byte chunks XOR-swizzled by row, which
 // makes the fragment reads (lane = sequence) conflict-free.
+// The bf16 instance's latent and RoPE widths are compile-time constants here
+// (the block index split and the RoPE pair indexing are then shifts, not
+// divisions); the launchers check them.
+constexpr int kAbsorbR = 512, kAbsorbDR = 64;
+
 template <int DH, bool ROPE, bool PAGED>
 __device__ __forceinline__ void absorb_bf16_block(int bid, const u16* __restrict__ q_nope,
-                                                  const u16* __restrict__ w_uk, int B, int H, int R,
+                                                  const u16* __restrict__ w_uk, int B, int H,
                                                   u16* __restrict__ q_lat, int W, char* wt, char* qs,
                                                   const RopeArgs& ra, const RopeFreqs& freqs) {
+  constexpr int R = kAbsorbR, DR = kAbsorbDR;
   using M = Mma<u16>;
   constexpr int COLS = 64, ROWB = 2 * COLS, NCH = ROWB / 16, KS = DH / M::KSTEP;
   constexpr int QROWS = 64, QROWB = 2 * DH, QCH = QROWB / 16;
@@ -1006,7 +1017,7 @@ __device__ __forceinline__ void absorb_bf16_block(int bid, const u16* __restrict
   constexpr int QCOP = QROWS * QROWB / 1024 / 2;  // query DMA copies per wave
   static_assert(WCOP >= 1 && QCOP >= 1 && (QCH & (QCH - 1)) == 0, "shape");
 
-  const int nblk = R / COLS;
+  constexpr int nblk = R / COLS;
   // the nblk column blocks of a head run on one XCD (its L2 then serves the
   // head's queries to all of them); the grid covers whole groups of 8 heads
   int h, blk;
@@ -1029,7 +1040,7 @@ __device__ __forceinline__ void absorb_bf16_block(int bid, const u16* __restrict
   // latency overlaps it), and rotated and stored after it.
   constexpr int UQ = 2, CVA = 2;  // pairs per thread; c_kv_new quads per thread (R <= 1024)
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-  const int half = ROPE ? ra.DR / 2 : 1;
+  const int half = ROPE ? DR / 2 : 1;
   const int tid = (int)threadIdx.x;
   const int nq = blk < B ? (B - blk + nblk - 1) / nblk * half : 0;  // this block's query pairs
   const int ab0 = h * nblk + blk;                                   // first sequence whose row it appends
@@ -1043,14 +1054,14 @@ __device__ __forceinline__ void absorb_bf16_block(int bid, const u16* __restrict
     for (int u = 0; u < UQ; ++u) {
       const int pidx = min(tid + 128 * u, max(nq - 1, 0));
       const int bb = min(blk + nblk * (pidx / half), B - 1), i = pidx % half;
-      qx[u] = *(const uint32_t*)(ra.q_rope + ((int64_t)bb * H + h) * ra.DR + 2 * i);
+      qx[u] = *(const uint32_t*)(ra.q_rope + ((int64_t)bb * H + h) * DR + 2 * i);
       qpos[u] = ra.positions[bb];
       qth[u] = freqs.theta[i];
     }
     const int ab = min(ab0, B - 1), ti = min(tid, half - 1);
     apos = ra.positions[ab];
     if constexpr (!PAGED) aoff = ra.cm.row_offsets[ab];  // (paged: the page is read after the wait)
-    kx = *(const uint32_t*)(ra.k_rope_new + (int64_t)ab * ra.DR + 2 * ti);
+    kx = *(const uint32_t*)(ra.k_rope_new + (int64_t)ab * DR + 2 * ti);
     ath = freqs.theta[ti];
 #pragma unroll
     for (int u = 0; u < CVA; ++u) cvv[u] = *(const u32x2*)(ra.c_kv_new + (int64_t)ab * R + min(4 * (tid + 128 * u), R - 4));
@@ -1084,7 +1095,7 @@ __device__ __forceinline__ void absorb_bf16_block(int bid, const u16* __restrict
   // issue, an s_waitcnt the compiler sees, and the frequency table read with
   // scalar loads; measured, that form was not faster.)
   if constexpr (ROPE) {
-    const int W2 = R + ra.DR;
+    const int W2 = R + DR;
     auto qstore = [&](int pidx, uint32_t x, int pos, double th) {
       const int bb = blk + nblk * (pidx / half), i = pidx % half;
       *(uint32_t*)(q_lat + ((int64_t)bb * H + h) * W2 + R + 2 * i) = rope_pair_bf16(x, pos, th);
@@ -1094,7 +1105,7 @@ __device__ __forceinline__ void absorb_bf16_block(int bid, const u16* __restrict
       if (tid + 128 * u < nq) qstore(tid + 128 * u, qx[u], qpos[u], qth[u]);
     for (int pidx = tid + 128 * UQ; pidx < nq; pidx += 128) {  // beyond UQ*128 pairs (B > 8*UQ*128/d_rope)
       const int bb = blk + nblk * (pidx / half), i = pidx % half;
-      qstore(pidx, *(const uint32_t*)(ra.q_rope + ((int64_t)bb * H + h) * ra.DR + 2 * i), ra.positions[bb],
+      qstore(pidx, *(const uint32_t*)(ra.q_rope + ((int64_t)bb * H + h) * DR + 2 * i), ra.positions[bb],
              freqs.theta[i]);
     }
     // the appended rows: [c_kv_new | RoPE(k_rope_new)] (c_kv_new bit for bit)
@@ -1110,7 +1121,7 @@ __device__ __forceinline__ void absorb_bf16_block(int bid, const u16* __restrict
     auto append8 = [&](int bb, int pos, int64_t off, const u32x2 (&cv)[CVA], uint32_t k, double th) {
       __shared__ float wmax[2];
       const int64_t row = ra.cm.row(bb, pos, off);
-      uint8_t* crow = ra.cache8 + row * (R + 2 * ra.DR);
+      uint8_t* crow = ra.cache8 + row * (R + 2 * DR);
       const float v0 = bf2f((u16)(cv[0].x & 0xffffu)), v1 = bf2f((u16)(cv[0].x >> 16));
       const float v2 = bf2f((u16)(cv[0].y & 0xffffu)), v3 = bf2f((u16)(cv[0].y >> 16));
       float mx = fmaxf(fmaxf(fabsf(v0), fabsf(v1)), fmaxf(fabsf(v2), fabsf(v3)));
@@ -1137,7 +1148,7 @@ __device__ __forceinline__ void absorb_bf16_block(int bid, const u16* __restrict
 #pragma unroll
       for (int u = 0; u < CVA; ++u) cv[u] = *(const u32x2*)(ra.c_kv_new + (int64_t)bb * R + min(4 * (tid + 128 * u), R - 4));
       const int64_t off = PAGED ? 0 : ra.cm.row_offsets[bb];
-      const uint32_t k = *(const uint32_t*)(ra.k_rope_new + (int64_t)bb * ra.DR + 2 * ti);
+      const uint32_t k = *(const uint32_t*)(ra.k_rope_new + (int64_t)bb * DR + 2 * ti);
       if (fp8) append8(bb, ra.positions[bb], off, cv, k, freqs.theta[ti]);
       else append(bb, ra.positions[bb], off, cv, k, freqs.theta[ti]);
     }
@@ -1191,7 +1202,8 @@ __global__ __launch_bounds__(128) void absorb_q_bf16_kernel(const u16* __restric
                                                             u16* __restrict__ q_lat, int W) {
   __shared__ __attribute__((aligned(1024))) char wt[AbsorbLds<DH>::WT];
   __shared__ __attribute__((aligned(1024))) char qs[AbsorbLds<DH>::QS];
-  absorb_bf16_block<DH, false, false>((int)blockIdx.x, q_nope, w_uk, B, H, R, q_lat, W, wt, qs, RopeArgs{}, RopeFreqs{});
+  (void)R;  // kAbsorbR (checked by the launcher)
+  absorb_bf16_block<DH, false, false>((int)blockIdx.x, q_nope, w_uk, B, H, q_lat, W, wt, qs, RopeArgs{}, RopeFreqs{});
 }
 
 // ---------------------------------------------------------------------------
@@ -1991,7 +2003,16 @@ __global__ __launch_bounds__(128) void absorb_rope_bf16_kernel(const u16* __rest
                                                                RopeArgs ra, RopeFreqs freqs, u16* __restrict__ q_lat) {
   __shared__ __attribute__((aligned(1024))) char wt[AbsorbLds<DH>::WT];
   __shared__ __attribute__((aligned(1024))) char qs[AbsorbLds<DH>::QS];
-  absorb_bf16_block<DH, true, PAGED>((int)blockIdx.x, q_nope, w_uk, B, H, R, q_lat, R + ra.DR, wt, qs, ra, freqs);
+  // Every kernel argument the block uses, fetched in one batch at entry: left
+  // to itself the compiler loads them in dependent rounds, one between each
+  // of the branches below, before the first copy is issued.
+  asm volatile("" ::"s"(q_nope), "s"(w_uk), "s"(B), "s"(H), "s"(q_lat), "s"(ra.q_rope), "s"(ra.c_kv_new),
+               "s"(ra.k_rope_new), "s"(ra.positions), "s"(ra.cm.row_offsets), "s"(ra.cm.block_table),
+               "s"(ra.cm.total_rows), "s"(ra.cm.total_pages), "s"(ra.cm.bt_stride), "s"(ra.cm.page_shift),
+               "s"(ra.cache), "s"(ra.cache8), "s"(ra.scale8));
+  (void)R;  // kAbsorbR (checked by the launcher)
+  absorb_bf16_block<DH, true, PAGED>((int)blockIdx.x, q_nope, w_uk, B, H, q_lat, kAbsorbR + kAbsorbDR, wt, qs, ra,
+                                     freqs);
 }
 
 // ---------------------------------------------------------------------------
@@ -2090,7 +2111,7 @@ mla_status launch_absorb(const mla_dims& d, const void* q_nope, const void* w_uk
 template <int DH>
 mla_status launch_absorb_bf16(const mla_dims& d, const void* q_nope, const void* w_uk, void* q_lat,
                               hipStream_t stream) {
-  if (d.rank % 64 != 0) return fail(MLA_ERR_UNSUPPORTED, "rank must be a multiple of 64");
+  if (d.rank != kAbsorbR || d.d_rope != kAbsorbDR) return fail(MLA_ERR_UNSUPPORTED, "bf16 needs rank 512, d_rope 64");
   const int blocks = (d.heads + kXcds - 1) / kXcds * kXcds * (d.rank / 64);  // whole groups of 8 heads
   hipLaunchKernelGGL((absorb_q_bf16_kernel<DH>), dim3(blocks), dim3(128), 0, stream, (const u16*)q_nope,
                      (const u16*)w_uk, d.batch, d.heads, d.rank, (u16*)q_lat, d.rank + d.d_rope);
@@ -2102,7 +2123,7 @@ mla_status launch_absorb_rope_bf16(const mla_dims& d, const void* q_nope, const 
                                    const void* c_kv_new, const void* k_rope_new, const int32_t* positions,
                                    const CacheMap& cm, const RopeFreqs& freqs, void* q_lat, void* kv_cache,
                                    hipStream_t stream, uint8_t* cache8 = nullptr, float* scale8 = nullptr) {
-  if (d.rank % 64 != 0) return fail(MLA_ERR_UNSUPPORTED, "rank must be a multiple of 64");
+  if (d.rank != kAbsorbR || d.d_rope != kAbsorbDR) return fail(MLA_ERR_UNSUPPORTED, "bf16 needs rank 512, d_rope 64");
   const int blocks = (d.heads + kXcds - 1) / kXcds * kXcds * (d.rank / 64);  // whole groups of 8 heads
   const RopeArgs ra{(const u16*)q_rope, (const u16*)c_kv_new, (const u16*)k_rope_new, positions, cm, d.d_rope,
                     (u16*)kv_cache, cache8, scale8};

@@ -165,17 +165,22 @@ __device__ __forceinline__ float xor32(float v, F op) {
   return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// Sum and inclusive prefix sum of an int over the 64 lanes of a wave.
+// Sum and inclusive prefix sum of an int over the 64 lanes of a wave, with
+// DPP lane moves (no LDS round trips): prefix sums within each row of 16
+// lanes by shifts of 1, 2, 4 and 8 lanes (a lane shifted in from before its
+// row start reads 0), then the last lane of row 0 is added to row 1 and that
+// of row 2 to row 3 (row_bcast:15), then lane 31 to rows 2 and 3
+// (row_bcast:31).  Every lane of the wave must be active.
 __device__ __forceinline__ int wave_prefix_sum(int v) {
-  const int lane = (int)(threadIdx.x & 63);
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int u = __shfl_up(v, d);
-    if (lane >= d) v += u;
-  }
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
   return v;
 }
-__device__ __forceinline__ int wave_sum(int v) { return __shfl(wave_prefix_sum(v), 63); }
+__device__ __forceinline__ int wave_sum(int v) { return __builtin_amdgcn_readlane(wave_prefix_sum(v), 63); }
 
 // A 64-bit value known to be uniform across the wave, in SGPRs
 // (readfirstlane returns int: each half goes through uint32_t so that the low
@@ -253,7 +258,7 @@ __device__ __forceinline__ bool decode_item(const int32_t* __restrict__ seq_lens
         row_off = __shfl(off, first);
         break;
       }
-      base = __shfl(incl, 63);
+      base = __builtin_amdgcn_readlane(incl, 63);
     }
     b = __builtin_amdgcn_readfirstlane(b);
     s = __builtin_amdgcn_readfirstlane(s);

@@ -1741,9 +1741,9 @@ __global__ __launch_bounds__(kCuvWaves16 * 64) void combine_up_v_bf16_d128_w16_k
   const int half = (B + 1) / 2;
   const int b_lo = part * half, b_hi = min(B, b_lo + half);
   const int db = wave & 3, jq = wave >> 2;
+  // this wave's quarter of the head's W_UV (8 fragments), loaded once, first:
+  // its 128 KB then streams in alongside the partial rows of the merge
   const u16* wrow = w_uv + ((int64_t)h * DV + 32 * db + l32) * R + 128 * jq + 8 * hf;
-  // the head's 128 KB of W_UV is 1024 lines of 128 bytes: one per thread
-  const uint32_t touch = *(const uint32_t*)(w_uv + (int64_t)h * DV * R + 64 * threadIdx.x);
   for (int b0 = b_lo; b0 < b_hi; b0 += kCuvRows) {
     const int nb = min(kCuvRows, b_hi - b0);
     // waves per sequence: the largest power of two with nb * WPR <= 16 (1 from 9 rows up)
@@ -1753,8 +1753,6 @@ __global__ __launch_bounds__(kCuvWaves16 * 64) void combine_up_v_bf16_d128_w16_k
     } else {
       cuv_merge<1, 16, NWV>(o_part, lse_part, num_splits, H, h, b0, nb, WPR, wave, lane, ot, xs, xm, xw, lse_out);
     }
-    // the fragments are read here, after the merge (an opaque copy of the
-    // address keeps them from being hoisted out of the loop and held through it)
     const u16* wp = wrow;
     asm volatile("" : "+v"(wp));
     i16x8 a[8];
@@ -1786,7 +1784,6 @@ __global__ __launch_bounds__(kCuvWaves16 * 64) void combine_up_v_bf16_d128_w16_k
     }
     __syncthreads();  // the next chunk rewrites these bytes
   }
-  if (B < 0 && touch == 0u) out[0] = 0.f;  // (never true: keeps the touch loads)
 }
 
 __global__ __launch_bounds__(64) void combine_up_v_f32_kernel(const float* __restrict__ o_part,

@@ -1365,15 +1365,34 @@ constexpr int kCuvWaves = 8;
 constexpr int kCuvRows = 32;      // sequences per chunk (the MFMA's N)
 constexpr int kCuvMaxRankF32 = 256;
 
+// A value combined over the 64 lanes of a wave, the result in every lane:
+// DPP moves inside each row of 16 lanes (swap neighbours, swap pairs, mirror
+// within 8, mirror within 16), then the rows exchanged with permlane16 and
+// permlane32 swaps (no LDS round trips).  Every lane must be active.
+template <typename F>
+__device__ __forceinline__ float wave_reduce_f(float v, F op) {
+  auto dpp = [](float x, int ctrl) -> float {
+    switch (ctrl) {  // (the control is a constant of the instruction)
+      case 0xb1: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xb1, 0xf, 0xf, false));
+      case 0x4e: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4e, 0xf, 0xf, false));
+      case 0x141: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xf, 0xf, false));
+      default: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xf, 0xf, false));
+    }
+  };
+  v = op(v, dpp(v, 0xb1));   // quad_perm [1,0,3,2]
+  v = op(v, dpp(v, 0x4e));   // quad_perm [2,3,0,1]
+  v = op(v, dpp(v, 0x141));  // row_half_mirror
+  v = op(v, dpp(v, 0x140));  // row_mirror
+  const uint32_t u = __float_as_uint(v);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = op(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+  return xor32(v, op);
+}
 __device__ __forceinline__ float wave_max_f(float v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d));
-  return v;
+  return wave_reduce_f(v, [](float a, float b) { return fmaxf(a, b); });
 }
 __device__ __forceinline__ float wave_sum_f(float v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d);
-  return v;
+  return wave_reduce_f(v, [](float a, float b) { return a + b; });
 }
 
 // Log-sum-exp statistics of one (sequence, head) over its S splits (lse at

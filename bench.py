@@ -268,6 +268,21 @@ def summarize_trace(trace_dir: str, order: list[str]) -> str:
                        f"{rows_att * 1152 / 1e6:.1f} MB / {dmean:.2f} us = "
                        f"{rows_att * 1152 / (dmean * 1e-6) / 1e9:.0f} GB/s = "
                        f"{rows_att * 1152 / (dmean * 1e-6) / 1e9 / HBM_PEAK_GBS:.3f} of 8000 GB/s\n")
+        # the decode launches by what ran just before them: absorb_rope (inside
+        # a step) or another decode launch (the back-to-back graph whose mean
+        # the bench's roofline record uses)
+        ctx = {"in a step (after absorb_rope)": [], "back to back (after a decode launch)": []}
+        for i in s:
+            prev = rows[i - 1]["Kernel_Name"] if i > 0 else ""
+            key = ("in a step (after absorb_rope)" if "absorb" in prev else
+                   "back to back (after a decode launch)" if "decode_latent" in prev else None)
+            if key is not None:
+                ctx[key].append((int(rows[i]["End_Timestamp"]) - int(rows[i]["Start_Timestamp"])) / 1e3)
+        for key, v in ctx.items():
+            if v:
+                out.append(f"- decode launches {key}: {len(v)}, mean {np.mean(v):.2f} us, median "
+                           f"{np.median(v):.2f} us")
+        out.append("")
     if outside:
         out.append("## Kernels outside the step (latent KV production, folded projections)\n")
         out.append("| kernel | dispatches | mean us | min us | max us |\n|---|---|---|---|---|")

@@ -1033,38 +1033,89 @@ __device__ __forceinline__ void absorb_bf16_block(int bid, const u16* __restrict
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hf = lane >> 5, l32 = lane & 31;
 
-  // RoPE (fused launch): block (h, blk) rotates head h's query pairs of the
-  // sequences b = blk (mod nblk), and block h*nblk + blk appends the cache row
-  // of sequence h*nblk + blk (mod H*nblk).  The first UQ pairs per thread and
-  // the first appended row are loaded before the DMA below is issued (their
-  // latency overlaps it), and rotated and stored after it.
-  constexpr int UQ = 2, CVA = 2;  // pairs per thread; c_kv_new quads per thread (R <= 1024)
+  // RoPE (fused launch, waves 2 and 3 of the work-group): block (h, blk)
+  // rotates head h's query pairs of the sequences b = blk (mod nblk), and
+  // block h*nblk + blk appends the cache row of sequence h*nblk + blk (mod
+  // H*nblk).  These waves touch no LDS and wait only for their own loads, so
+  // the rotations run while waves 0 and 1 wait for their copies; they then
+  // join the absorption waves' barriers (one, plus two per further block of
+  // 64 sequences) and leave.
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-  const int half = ROPE ? DR / 2 : 1;
-  const int tid = (int)threadIdx.x;
-  const int nq = blk < B ? (B - blk + nblk - 1) / nblk * half : 0;  // this block's query pairs
-  const int ab0 = h * nblk + blk;                                   // first sequence whose row it appends
-  uint32_t qx[UQ], kx = 0;
-  int qpos[UQ], apos = 0;
-  double qth[UQ], ath = 0.0;
-  int64_t aoff = 0;
-  u32x2 cvv[CVA];
   if constexpr (ROPE) {
+    if (threadIdx.x >= 128) {
+      constexpr int half = DR / 2;
+      const int tid = (int)threadIdx.x - 128;
+      const int nq = blk < B ? (B - blk + nblk - 1) / nblk * half : 0;  // this block's query pairs
+      const int W2 = R + DR;
+      // pairs in batches of two per thread, both batches' loads issued before
+      // either is rotated (one round trip for up to 64 sequences)
+      constexpr int UQ = 2;
+      for (int p0 = tid; p0 < nq; p0 += 128 * UQ) {
+        uint32_t x[UQ];
+        int pos[UQ];
 #pragma unroll
-    for (int u = 0; u < UQ; ++u) {
-      const int pidx = min(tid + 128 * u, max(nq - 1, 0));
-      const int bb = min(blk + nblk * (pidx / half), B - 1), i = pidx % half;
-      qx[u] = *(const uint32_t*)(ra.q_rope + ((int64_t)bb * H + h) * DR + 2 * i);
-      qpos[u] = ra.positions[bb];
-      qth[u] = freqs.theta[i];
+        for (int u = 0; u < UQ; ++u) {
+          const int pidx = min(p0 + 128 * u, nq - 1);
+          const int bb = blk + nblk * (pidx / half), i = pidx % half;
+          x[u] = *(const uint32_t*)(ra.q_rope + ((int64_t)bb * H + h) * DR + 2 * i);
+          pos[u] = ra.positions[bb];
+        }
+#pragma unroll
+        for (int u = 0; u < UQ; ++u) {
+          const int pidx = p0 + 128 * u;
+          if (pidx >= nq) break;
+          const int bb = blk + nblk * (pidx / half), i = pidx % half;
+          *(uint32_t*)(q_lat + ((int64_t)bb * H + h) * W2 + R + 2 * i) = rope_pair_bf16(x[u], pos[u], freqs.theta[i]);
+        }
+      }
+      // the appended rows, by wave 2 (eight latent values per lane): [c_kv_new |
+      // RoPE(k_rope_new)] with c_kv_new bit for bit, or the fp8 row: codes of
+      // c_kv_new / 2^e with e from the row's max |c_kv_new| (a wave-wide
+      // maximum), then the rotated key and the scale
+      static_assert(R == 8 * 64, "one wave holds the appended latent, eight values per lane");
+      if (tid < 64) {
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        const bool fp8 = ra.cache8 != nullptr;
+        for (int bb = h * nblk + blk; bb < B; bb += H * nblk) {
+          const int ti = min(tid, half - 1);
+          const u32x4 cv = *(const u32x4*)(ra.c_kv_new + (int64_t)bb * R + 8 * tid);
+          const uint32_t k = *(const uint32_t*)(ra.k_rope_new + (int64_t)bb * DR + 2 * ti);
+          const int pos = ra.positions[bb];
+          const int64_t off = PAGED ? 0 : ra.cm.row_offsets[bb];
+          const int64_t row = ra.cm.row(bb, pos, off);
+          const uint32_t kr = rope_pair_bf16(k, pos, freqs.theta[ti]);
+          if (!fp8) {
+            u16* crow = ra.cache + row * W2;
+            *(u32x4*)(crow + 8 * tid) = cv;
+            if (tid < half) *(uint32_t*)(crow + R + 2 * tid) = kr;
+          } else {
+            uint8_t* crow = ra.cache8 + row * (R + 2 * DR);
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              v[2 * e] = bf2f((u16)(cv[e] & 0xffffu));
+              v[2 * e + 1] = bf2f((u16)(cv[e] >> 16));
+            }
+            float mx = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(v[e]));
+            const int ex = fp8_row_exponent(wave_reduce_f(mx, [](float a, float b) { return fmaxf(a, b); }));
+            const float inv = ldexpf(1.f, -ex);
+            uint32_t c[2];
+#pragma unroll
+            for (int w = 0; w < 2; ++w)
+              c[w] = e4m3_code(v[4 * w] * inv) | (e4m3_code(v[4 * w + 1] * inv) << 8) |
+                     (e4m3_code(v[4 * w + 2] * inv) << 16) | (e4m3_code(v[4 * w + 3] * inv) << 24);
+            *(u32x2*)(crow + 8 * tid) = u32x2{c[0], c[1]};
+            if (tid < half) *(uint32_t*)(crow + R + 4 * tid) = kr;
+            if (tid == 0) ra.scale8[row] = ldexpf(1.f, ex);
+          }
+        }
+      }
+      const int nbar = 1 + 2 * ((B + QROWS - 1) / QROWS - 1);
+      for (int n = 0; n < nbar; ++n) __syncthreads();
+      return;
     }
-    const int ab = min(ab0, B - 1), ti = min(tid, half - 1);
-    apos = ra.positions[ab];
-    if constexpr (!PAGED) aoff = ra.cm.row_offsets[ab];  // (paged: the page is read after the wait)
-    kx = *(const uint32_t*)(ra.k_rope_new + (int64_t)ab * DR + 2 * ti);
-    ath = freqs.theta[ti];
-#pragma unroll
-    for (int u = 0; u < CVA; ++u) cvv[u] = *(const u32x2*)(ra.c_kv_new + (int64_t)ab * R + min(4 * (tid + 128 * u), R - 4));
   }
   // LDS chunk p of the query block holds row p / QCH, chunk (p % QCH) ^ (row % QCH)
   auto issue_q = [&](int b0) {
@@ -1088,72 +1139,6 @@ __device__ __forceinline__ void absorb_bf16_block(int bid, const u16* __restrict
     const char* src = (const char*)(w_uk + ((int64_t)h * DH + d) * R + j0) + 16 * c;
     __builtin_amdgcn_global_load_lds(src, (LDS_AS char*)wt + (wave * WCOP + n) * 1024, 16, 0, 0);
   }
-  // The RoPE work needs only the loads issued before the copies, but the
-  // compiler's wait before their first use counts every vector memory
-  // operation (s_waitcnt vmcnt(0)), so it starts once the copies have landed.
-  // (Making it overlap the copies takes exact wait accounting: a branch-free
-  // issue, an s_waitcnt the compiler sees, and the frequency table read with
-  // scalar loads; measured, that form was not faster.)
-  if constexpr (ROPE) {
-    const int W2 = R + DR;
-    auto qstore = [&](int pidx, uint32_t x, int pos, double th) {
-      const int bb = blk + nblk * (pidx / half), i = pidx % half;
-      *(uint32_t*)(q_lat + ((int64_t)bb * H + h) * W2 + R + 2 * i) = rope_pair_bf16(x, pos, th);
-    };
-#pragma unroll
-    for (int u = 0; u < UQ; ++u)
-      if (tid + 128 * u < nq) qstore(tid + 128 * u, qx[u], qpos[u], qth[u]);
-    for (int pidx = tid + 128 * UQ; pidx < nq; pidx += 128) {  // beyond UQ*128 pairs (B > 8*UQ*128/d_rope)
-      const int bb = blk + nblk * (pidx / half), i = pidx % half;
-      qstore(pidx, *(const uint32_t*)(ra.q_rope + ((int64_t)bb * H + h) * DR + 2 * i), ra.positions[bb],
-             freqs.theta[i]);
-    }
-    // the appended rows: [c_kv_new | RoPE(k_rope_new)] (c_kv_new bit for bit)
-    auto append = [&](int bb, int pos, int64_t off, const u32x2 (&cv)[CVA], uint32_t k, double th) {
-      u16* crow = ra.cache + ra.cm.row(bb, pos, off) * W2;
-#pragma unroll
-      for (int u = 0; u < CVA; ++u)
-        if (4 * (tid + 128 * u) < R) *(u32x2*)(crow + 4 * (tid + 128 * u)) = cv[u];
-      if (tid < half) *(uint32_t*)(crow + R + 2 * tid) = rope_pair_bf16(k, pos, th);
-    };
-    // fp8 cache (R == 512: one quad of c_kv_new per thread): the row's
-    // exponent from the block-wide max |c_kv_new|, then the codes
-    auto append8 = [&](int bb, int pos, int64_t off, const u32x2 (&cv)[CVA], uint32_t k, double th) {
-      __shared__ float wmax[2];
-      const int64_t row = ra.cm.row(bb, pos, off);
-      uint8_t* crow = ra.cache8 + row * (R + 2 * DR);
-      const float v0 = bf2f((u16)(cv[0].x & 0xffffu)), v1 = bf2f((u16)(cv[0].x >> 16));
-      const float v2 = bf2f((u16)(cv[0].y & 0xffffu)), v3 = bf2f((u16)(cv[0].y >> 16));
-      float mx = fmaxf(fmaxf(fabsf(v0), fabsf(v1)), fmaxf(fabsf(v2), fabsf(v3)));
-#pragma unroll
-      for (int d = 32; d >= 1; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d));
-      __syncthreads();  // (a block may append several rows) the previous maxima are read
-      if ((tid & 63) == 0) wmax[tid >> 6] = mx;
-      __syncthreads();
-      const int e = fp8_row_exponent(fmaxf(wmax[0], wmax[1]));
-      const float inv = ldexpf(1.f, -e);
-      *(uint32_t*)(crow + 4 * tid) = e4m3_code(v0 * inv) | (e4m3_code(v1 * inv) << 8) |
-                                     (e4m3_code(v2 * inv) << 16) | (e4m3_code(v3 * inv) << 24);
-      if (tid < half) *(uint32_t*)(crow + R + 4 * tid) = rope_pair_bf16(k, pos, th);
-      if (tid == 0) ra.scale8[row] = ldexpf(1.f, e);
-    };
-    const bool fp8 = ra.cache8 != nullptr;
-    if (ab0 < B) {
-      if (fp8) append8(ab0, apos, aoff, cvv, kx, ath);
-      else append(ab0, apos, aoff, cvv, kx, ath);
-    }
-    for (int bb = ab0 + H * nblk; bb < B; bb += H * nblk) {  // more than H*nblk sequences
-      const int ti = min(tid, half - 1);
-      u32x2 cv[CVA];
-#pragma unroll
-      for (int u = 0; u < CVA; ++u) cv[u] = *(const u32x2*)(ra.c_kv_new + (int64_t)bb * R + min(4 * (tid + 128 * u), R - 4));
-      const int64_t off = PAGED ? 0 : ra.cm.row_offsets[bb];
-      const uint32_t k = *(const uint32_t*)(ra.k_rope_new + (int64_t)bb * DR + 2 * ti);
-      if (fp8) append8(bb, ra.positions[bb], off, cv, k, freqs.theta[ti]);
-      else append(bb, ra.positions[bb], off, cv, k, freqs.theta[ti]);
-    }
-  }
-
   __syncthreads();  // (waits for this work-group's DMA)
   typename M::Frag af[KS];
 #pragma unroll
@@ -1365,29 +1350,6 @@ constexpr int kCuvWaves = 8;
 constexpr int kCuvRows = 32;      // sequences per chunk (the MFMA's N)
 constexpr int kCuvMaxRankF32 = 256;
 
-// A value combined over the 64 lanes of a wave, the result in every lane:
-// DPP moves inside each row of 16 lanes (swap neighbours, swap pairs, mirror
-// within 8, mirror within 16), then the rows exchanged with permlane16 and
-// permlane32 swaps (no LDS round trips).  Every lane must be active.
-template <typename F>
-__device__ __forceinline__ float wave_reduce_f(float v, F op) {
-  auto dpp = [](float x, int ctrl) -> float {
-    switch (ctrl) {  // (the control is a constant of the instruction)
-      case 0xb1: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xb1, 0xf, 0xf, false));
-      case 0x4e: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4e, 0xf, 0xf, false));
-      case 0x141: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xf, 0xf, false));
-      default: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xf, 0xf, false));
-    }
-  };
-  v = op(v, dpp(v, 0xb1));   // quad_perm [1,0,3,2]
-  v = op(v, dpp(v, 0x4e));   // quad_perm [2,3,0,1]
-  v = op(v, dpp(v, 0x141));  // row_half_mirror
-  v = op(v, dpp(v, 0x140));  // row_mirror
-  const uint32_t u = __float_as_uint(v);
-  const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  v = op(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
-  return xor32(v, op);
-}
 __device__ __forceinline__ float wave_max_f(float v) {
   return wave_reduce_f(v, [](float a, float b) { return fmaxf(a, b); });
 }
@@ -2014,7 +1976,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(const T* __restrict__ 
 // (see absorb_bf16_block); q~ and the rotated RoPE part are disjoint columns
 // of q_lat.
 template <int DH, bool PAGED>
-__global__ __launch_bounds__(128) void absorb_rope_bf16_kernel(const u16* __restrict__ q_nope,
+__global__ __launch_bounds__(256) void absorb_rope_bf16_kernel(const u16* __restrict__ q_nope,
                                                                const u16* __restrict__ w_uk, int B, int H, int R,
                                                                RopeArgs ra, RopeFreqs freqs, u16* __restrict__ q_lat) {
   __shared__ __attribute__((aligned(1024))) char wt[AbsorbLds<DH>::WT];
@@ -2144,11 +2106,11 @@ mla_status launch_absorb_rope_bf16(const mla_dims& d, const void* q_nope, const 
   const RopeArgs ra{(const u16*)q_rope, (const u16*)c_kv_new, (const u16*)k_rope_new, positions, cm, d.d_rope,
                     (u16*)kv_cache, cache8, scale8};
   if (cm.block_table != nullptr) {
-    hipLaunchKernelGGL((absorb_rope_bf16_kernel<DH, true>), dim3(blocks), dim3(128), 0, stream, (const u16*)q_nope,
+    hipLaunchKernelGGL((absorb_rope_bf16_kernel<DH, true>), dim3(blocks), dim3(256), 0, stream, (const u16*)q_nope,
                        (const u16*)w_uk, d.batch, d.heads, d.rank, ra, freqs, (u16*)q_lat);
     return launch_result("mla_absorb_rope_paged");
   }
-  hipLaunchKernelGGL((absorb_rope_bf16_kernel<DH, false>), dim3(blocks), dim3(128), 0, stream, (const u16*)q_nope,
+  hipLaunchKernelGGL((absorb_rope_bf16_kernel<DH, false>), dim3(blocks), dim3(256), 0, stream, (const u16*)q_nope,
                      (const u16*)w_uk, d.batch, d.heads, d.rank, ra, freqs, (u16*)q_lat);
   return launch_result("mla_absorb_rope");
 }

@@ -165,6 +165,29 @@ __device__ __forceinline__ float xor32(float v, F op) {
   return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// A value combined over the 64 lanes of a wave, the result in every lane:
+// DPP moves inside each row of 16 lanes (swap neighbours, swap pairs, mirror
+// within 8, mirror within 16), then the rows exchanged with permlane16 and
+// permlane32 swaps (no LDS round trips).  Every lane must be active.
+template <typename F>
+__device__ __forceinline__ float wave_reduce_f(float v, F op) {
+  auto dpp = [](float x, int ctrl) -> float {
+    switch (ctrl) {  // (the control is a constant of the instruction)
+      case 0xb1: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xb1, 0xf, 0xf, false));
+      case 0x4e: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4e, 0xf, 0xf, false));
+      case 0x141: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xf, 0xf, false));
+      default: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xf, 0xf, false));
+    }
+  };
+  v = op(v, dpp(v, 0xb1));   // quad_perm [1,0,3,2]
+  v = op(v, dpp(v, 0x4e));   // quad_perm [2,3,0,1]
+  v = op(v, dpp(v, 0x141));  // row_half_mirror
+  v = op(v, dpp(v, 0x140));  // row_mirror
+  const uint32_t u = __float_as_uint(v);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = op(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+  return xor32(v, op);
+}
 // Sum and inclusive prefix sum of an int over the 64 lanes of a wave, with
 // DPP lane moves (no LDS round trips): prefix sums within each row of 16
 // lanes by shifts of 1, 2, 4 and 8 lanes (a lane shifted in from before its

@@ -174,6 +174,28 @@ def test_edge_lengths(name, lens):
     check_step(inp, ds, oracle_step(inp), tag=f"{name} lens={lens[:8]}")
 
 
+@pytest.mark.parametrize("B", [1030, 2100])
+def test_large_batch(B):
+    """More sequences than the absorption blocks append rows for (1024 blocks
+    at H 128: a block appends a second or third row) and many blocks of 64
+    queries per absorption block (the RoPE waves of the fused launch join
+    every barrier of the absorption waves), short cached lengths."""
+    inp = syn.make_inputs("dsv2", B=B, T=(0, 40))
+    ds = _run(inp)
+    check_step(inp, ds, oracle_step(inp), tag=f"dsv2 B={B}")
+    # the fp8 append on the same batch: every appended row's codes and scale
+    from head_latent_attention_12_amd.step import DeviceStep
+    d8 = DeviceStep(inp, fp8=True)
+    d8.absorb_rope()
+    torch.cuda.synchronize()
+    rows, scale = d8.fp8_raw()
+    slots = inp.row_offsets + inp.lens
+    for k in range(0, B, max(1, B // 64)):
+        exp_codes, exp_scale = orc.fp8_quantize_row(syn.bf16_bits_to_f64(inp.c_kv_new[k]))
+        assert scale[slots[k]] == exp_scale, k
+        np.testing.assert_array_equal(rows[slots[k]][:inp.r], exp_codes)
+
+
 @pytest.mark.parametrize("B", [1, 2, 3, 4, 5, 6, 7, 8, 9, 31, 32, 33, 40, 64, 65, 68, 70, 76])
 @pytest.mark.parametrize("splits", [1, 3, 40])
 def test_combine_up_v_batch_shapes(B, splits):

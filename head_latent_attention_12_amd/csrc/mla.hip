@@ -240,10 +240,35 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
   } else {
     last_rel = r1 - 1 - r0;
   }
+  // Paged: the page ids of the split's first 64 pages, one per lane (loaded
+  // once, clamped as in CacheMap::paged_row), so that a tile's page comes from
+  // a lane read instead of a memory access inside the tile loop; a split
+  // reaching past 64 pages reads the block table for the tiles beyond.
+  const int pg_first = PAGED ? (r0 >> cm.page_shift) : 0;
+  int pg_lane = 0;
+  if constexpr (PAGED) {
+    int pi = pg_first + lane;
+    pi = pi < 0 ? 0 : (pi >= cm.bt_stride ? cm.bt_stride - 1 : pi);
+    const int64_t pg = block_table[(int64_t)b * cm.bt_stride + pi];
+    pg_lane = (int)(pg < 0 ? 0 : (pg >= cm.total_pages ? cm.total_pages - 1 : pg));
+  }
   // first byte of the split's tile `tile` (32 consecutive cache rows)
   auto tile_ptr = [&](int tile) -> const char* {
     if constexpr (PAGED) {
-      return (const char*)cache + cm.paged_row(b, r0 + tile * TILE, block_table) * ROWB;
+      const int t = r0 + tile * TILE;
+      const int rel = (t >> cm.page_shift) - pg_first;
+      int64_t pg;
+      if (rel < 64) {
+        pg = __builtin_amdgcn_readlane(pg_lane, rel);
+      } else {  // one scalar read of the block table (loaded and waited for in one asm statement)
+        int pi = t >> cm.page_shift;
+        pi = pi < 0 ? 0 : (pi >= cm.bt_stride ? cm.bt_stride - 1 : pi);
+        const uint64_t addr = uniform_u64((uint64_t)(block_table + (int64_t)b * cm.bt_stride + pi));
+        int v;
+        asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(addr) : "memory");
+        pg = v < 0 ? 0 : (v >= cm.total_pages ? cm.total_pages - 1 : v);
+      }
+      return (const char*)cache + ((pg << cm.page_shift) + (t & ((1 << cm.page_shift) - 1))) * ROWB;
     } else {
       return split_base + (int64_t)tile * TILE * ROWB;
     }

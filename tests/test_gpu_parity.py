@@ -373,6 +373,7 @@ PAGED_CASES = [
     ("dsv2", dict(lens=[0, 31, 32, 63, 64, 65, 127, 128]), 64, None),  # the new row opens a page, or not
     ("dsv2", dict(B=2, T=3000), 32, None),
     ("dsv2", dict(B=2, T=3000), 32, 2),      # long splits: a new page every tile of the steady loop
+    ("dsv2", dict(B=2, T=3000), 32, 1),      # one split over 94 pages: the page ids past the first 64
     ("small", dict(B=3, T=1500), 128, 1),    # fp32 path, one split, pages of four tiles
     ("dsv2_ragged", dict(B=6, T=(1, 700)), 256, None),
     ("dsv2_ragged", {}, 64, None),

@@ -1716,11 +1716,12 @@ __global__ __launch_bounds__(kCuvWaves * 64) void combine_up_v_bf16_d128_kernel(
 }
 
 // The d_v = 128 merge with 16 waves (more than 16 sequences per work-group):
-// two sequences per wave and chunk with 8 split rows each in flight, so that
-// up to 8 splits arrive in one round trip.  The head's W_UV is touched into
-// L2 at the start (one line per thread) and read into registers after each
-// chunk's merge: wave w holds rows 32*(w % 4) .. +31 over latent quarter w / 4
-// (8 fragments), and the four quarters are added through LDS.
+// two sequences per wave and chunk with 4 split rows each in flight (with 16
+// waves that is 128 KB per work-group, more than the latency needs).  The
+// head's W_UV is read into registers at the start, so that its 128 KB stream
+// in with the partial rows: wave w holds rows 32*(w % 4) .. +31 over latent
+// quarter w / 4 (8 fragments, the registers that the halved batch of rows
+// leaves free), and the four quarters are added through LDS.
 constexpr int kCuvWaves16 = 16;
 
 __global__ __launch_bounds__(kCuvWaves16 * 64) void combine_up_v_bf16_d128_w16_kernel(
@@ -1747,23 +1748,20 @@ __global__ __launch_bounds__(kCuvWaves16 * 64) void combine_up_v_bf16_d128_w16_k
   const int half = (B + 1) / 2;
   const int b_lo = part * half, b_hi = min(B, b_lo + half);
   const int db = wave & 3, jq = wave >> 2;
-  // this wave's quarter of the head's W_UV (8 fragments), loaded once, first:
-  // its 128 KB then streams in alongside the partial rows of the merge
+  // this wave's quarter of the head's W_UV (8 fragments), loaded once, first
   const u16* wrow = w_uv + ((int64_t)h * DV + 32 * db + l32) * R + 128 * jq + 8 * hf;
+  i16x8 a[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) a[u] = *(const i16x8*)(wrow + 16 * u);
   for (int b0 = b_lo; b0 < b_hi; b0 += kCuvRows) {
     const int nb = min(kCuvRows, b_hi - b0);
     // waves per sequence: the largest power of two with nb * WPR <= 16 (1 from 9 rows up)
     const int WPR = nb >= 9 ? 1 : (nb >= 5 ? 2 : (nb >= 3 ? 4 : (nb == 2 ? 8 : 16)));
     if (nb * WPR > NWV) {
-      cuv_merge<2, 8, NWV>(o_part, lse_part, num_splits, H, h, b0, nb, WPR, wave, lane, ot, xs, xm, xw, lse_out);
+      cuv_merge<2, 4, NWV>(o_part, lse_part, num_splits, H, h, b0, nb, WPR, wave, lane, ot, xs, xm, xw, lse_out);
     } else {
-      cuv_merge<1, 16, NWV>(o_part, lse_part, num_splits, H, h, b0, nb, WPR, wave, lane, ot, xs, xm, xw, lse_out);
+      cuv_merge<1, 8, NWV>(o_part, lse_part, num_splits, H, h, b0, nb, WPR, wave, lane, ot, xs, xm, xw, lse_out);
     }
-    const u16* wp = wrow;
-    asm volatile("" : "+v"(wp));
-    i16x8 a[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) a[u] = *(const i16x8*)(wp + 16 * u);
     __syncthreads();  // merged rows written
     f32x16 acc = zero16();
 #pragma unroll

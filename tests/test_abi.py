@@ -315,11 +315,15 @@ def test_fold_argument_checks():
     """Folded projections: bf16 only, d_c_q a multiple of 256, d_model a
     multiple of 64, no NULL or misaligned pointers; the output product's
     workspace holds one fp32 partial per (k group, sequence, output) of a
-    batch slice of up to 64 sequences (eight k groups of 8192 at H 128, r 512)."""
+    batch slice of up to 64 sequences.  k groups at H 128, r 512 (K 65536),
+    from the plan with the fewest estimated bytes per compute unit: B 16,
+    d_model 5120 -> 160-row blocks, 32 of them, 8 groups of 8192 (one
+    work-group per compute unit); B 100, d_model 256 -> slices of 64 and 36
+    sequences, 128-row blocks, 64 groups of 1024 (the 16-tile minimum)."""
     d = dsv2()
     assert mla.mla_out_folded_workspace_size(d, 5120) == 8 * 16 * 5120 * 4
     assert mla.mla_out_folded_workspace_size(mla.make_dims(100, 128, 128, 128, 512, 64, mla.MLA_BF16), 256) \
-        == 8 * 64 * 256 * 4
+        == 64 * 64 * 256 * 4
     _expect(2, mla.mla_out_folded_workspace_size, d, 100)
     _expect(1, mla.mla_out_folded_workspace_size, d, 0)
     _expect(2, mla.mla_fold_query, d, 1000, P16, P16, P16, 0)           # d_c_q not a multiple of 256

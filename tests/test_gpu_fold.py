@@ -194,3 +194,53 @@ def test_folded_step_ragged_full_size():
     w_qk_abs = orc.fold_query(np.abs(fin.f64("w_uq")), np.abs(inp.f64("w_uk")))
     check_q(inp, fin, ds, q_ref, w_qk_abs, "folded dsv2_ragged B64")
     check_y(y.cpu().numpy().astype(np.float64), y_ref, "folded dsv2_ragged B64")
+
+
+@pytest.mark.parametrize("B", [5, 40])
+def test_folded_products_small_shapes(B):
+    """mla_absorb_q_folded and mla_out_folded alone at the DeepSeek-V2 head
+    dims with d_c' 256 and d_model 320 (not a multiple of 128: the output
+    product's 64-row work-groups) and a batch that fits one or two 32-column
+    blocks.  q~ against the oracle's fold of
+    W_UQ and W_UK applied to c_q (the bound of check_q); y against the fp64
+    product of the kernel's own folded weight with o_lat: the only error left
+    is fp32 o_lat entering the bf16 MFMA as a high and a low part (a residual
+    below 2^-17 of each value) and fp32 accumulation, well inside 2^-12 of
+    |W_OV| |o_lat|."""
+    from head_latent_attention_12_amd import mla
+    inp = syn.make_inputs("dsv2", B=B, T=4, seed=31)
+    H, r, dh, dcq, dm = inp.H, inp.r, inp.d_head, 256, 320
+    fin = syn.make_fold_inputs(inp, d_c_q=dcq, d_model=dm, seed=32)
+    dims = mla.make_dims(B, H, dh, dh, r, inp.d_rope, mla.MLA_BF16, inp.softmax_scale, inp.rope_base)
+    w_uq, w_uk, w_o, w_uv, c_q = (_dev(fin.w_uq), _dev(inp.w_uk), _dev(fin.w_o), _dev(inp.w_uv), _dev(fin.c_q))
+    w_qk = torch.empty((H, r, dcq), dtype=torch.int16, device="cuda")
+    w_ov = torch.empty((dm, H * r), dtype=torch.int16, device="cuda")
+    mla.mla_fold_query(dims, dcq, w_uq, w_uk, w_qk)
+    mla.mla_fold_output(dims, dm, w_o, w_uv, w_ov)
+    q_lat = torch.zeros((B, H, r + inp.d_rope), dtype=torch.int16, device="cuda")
+    mla.mla_absorb_q_folded(dims, dcq, c_q, w_qk, q_lat)
+    o_lat = torch.as_tensor(np.random.default_rng(33).standard_normal((B, H, r)), dtype=torch.float32).cuda()
+    ws = torch.empty(mla.mla_out_folded_workspace_size(dims, dm) // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty((B, dm), dtype=torch.float32, device="cuda")
+    mla.mla_out_folded(dims, dm, o_lat, w_ov, ws, y)
+    torch.cuda.synchronize()
+
+    cq, wuq, wuk = fin.f64("c_q"), fin.f64("w_uq"), inp.f64("w_uk")
+    q_ref = np.stack([np.stack([wuk[h].T @ qn[h] for h in range(H)])
+                      for qn in (orc.query_projection(cq[b], wuq, H) for b in range(B))])
+    w_qk_abs = orc.fold_query(np.abs(wuq), np.abs(wuk))
+    env = (w_qk_abs.reshape(H * r, dcq) @ np.abs(cq).T).T.reshape(B, H, r)
+    got_q = _bits(q_lat)[:, :, :r]
+    err_q = np.abs(got_q - q_ref)
+    assert np.all(err_q <= 2.0 ** -8 * np.abs(q_ref) + 2.0 ** -8 * env), f"q~ B{B}"
+    assert np.all(_bits(q_lat)[:, :, r:] == 0), "the RoPE columns are not the folded product's"
+
+    w = _bits(w_ov)
+    x = o_lat.cpu().numpy().astype(np.float64).reshape(B, H * r)
+    y_ref = x @ w.T
+    env_y = np.abs(x) @ np.abs(w).T
+    err_y = np.abs(y.cpu().numpy().astype(np.float64) - y_ref)
+    print(f"[small folded B{B}] q~ worst err/bound "
+          f"{np.max(err_q / (2.0 ** -8 * np.abs(q_ref) + 2.0 ** -8 * env)):.3f}, "
+          f"y max err / envelope {np.max(err_y / env_y):.2e}", flush=True)
+    assert np.all(err_y <= 2.0 ** -12 * env_y), f"y B{B}"

@@ -16,8 +16,8 @@
 //                        staged through LDS with k contiguous
 //   wstream_kernel       decode-time product Y[b][n] = sum_k X[b][k] W[n][k]
 //                        over a folded weight W with k-contiguous rows: tiles
-//                        of W and of the batch rows X streamed into a 3-stage
-//                        LDS ring by DMA, W fragments as MFMA A operands and
+//                        of W and of the batch rows X streamed into a 3- or
+//                        4-stage LDS ring by DMA, W fragments as MFMA A operands and
 //                        X fragments as B operands, the four waves of a
 //                        work-group on four quarters of each tile's k range
 //                        summed through LDS at the end; fp32 X enters the

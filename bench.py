@@ -654,7 +654,10 @@ def main():
     if not args.no_others:
         legs += [("dsv2_ragged", 64, False), ("dsv2", None, True), ("dsv2_ragged", None, True)]
     for name, page_rows, fp8 in legs:
-        r = run_workload(name, max(20, args.steps // 4), max(5, args.warmup // 4), min_sets=2,
+        # as many timed steps as the headline: the wall clock of one graph replay
+        # carries a fixed launch and synchronisation cost that fewer steps would
+        # not spread as thin
+        r = run_workload(name, args.steps, max(5, args.warmup // 4), min_sets=2,
                          page_rows=page_rows, fp8=fp8)
         if page_rows is None and not fp8:
             by_workload[r["name"]] = roofline_record(r)

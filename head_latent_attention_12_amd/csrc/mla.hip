@@ -684,11 +684,14 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_latent_kernel(
       }
     }
     __syncthreads();  // (the rows of a wave are written and read by that wave only)
+    // System-scope stores (sc0 sc1) write the partial rows through the XCD's
+    // L2 instead of leaving up to its whole capacity dirty for the writeback
+    // that ends the kernel; the merge that reads them runs next either way.
     T* op = o_part + (((int64_t)b * num_splits + s) * H + wave * 32) * R + 8 * lane;
 #pragma unroll 8
     for (int t = 0; t < 32; ++t) {
       const u32x4 v = *(const LDS_AS u32x4*)(wrows + t * (R * 2) + 16 * (lane ^ (t & 15)));
-      *(u32x4*)(op + (int64_t)t * R) = v;
+      asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1" ::"v"(op + (int64_t)t * R), "v"(v) : "memory");
     }
     if (hf == 0) lse_out[head] = (m_ref + __log2f(l_tot)) * kLn2;
   } else if (head_ok) {

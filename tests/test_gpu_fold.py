@@ -196,12 +196,12 @@ def test_folded_step_ragged_full_size():
     check_y(y.cpu().numpy().astype(np.float64), y_ref, "folded dsv2_ragged B64")
 
 
-@pytest.mark.parametrize("B", [5, 40])
+@pytest.mark.parametrize("B", [5, 24, 40])
 def test_folded_products_small_shapes(B):
     """mla_absorb_q_folded and mla_out_folded alone at the DeepSeek-V2 head
     dims with d_c' 256 and d_model 320 (not a multiple of 128: the output
-    product's 64-row work-groups) and a batch that fits one or two 32-column
-    blocks.  q~ against the oracle's fold of
+    product's 64-row work-groups) and a batch whose X tiles hold 16, 32 and 64
+    rows (one or two 32-column blocks).  q~ against the oracle's fold of
     W_UQ and W_UK applied to c_q (the bound of check_q); y against the fp64
     product of the kernel's own folded weight with o_lat: the only error left
     is fp32 o_lat entering the bf16 MFMA as a high and a low part (a residual

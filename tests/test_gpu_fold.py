@@ -244,3 +244,53 @@ def test_folded_products_small_shapes(B):
           f"{np.max(err_q / (2.0 ** -8 * np.abs(q_ref) + 2.0 ** -8 * env)):.3f}, "
           f"y max err / envelope {np.max(err_y / env_y):.2e}", flush=True)
     assert np.all(err_y <= 2.0 ** -12 * env_y), f"y B{B}"
+
+
+def test_folded_products_graph_replay():
+    """mla_absorb_q_folded and mla_out_folded (its split-k partial sums in the
+    caller's workspace, then the fixed-order reduction) recorded as one HIP
+    graph: every replay, with eager work on the outputs and the workspace and
+    synchronisation between replays, reproduces the eager bits."""
+    from head_latent_attention_12_amd import mla
+    B, dcq, dm = 24, 512, 320
+    inp = syn.make_inputs("dsv2", B=B, T=4, seed=34)
+    fin = syn.make_fold_inputs(inp, d_c_q=dcq, d_model=dm, seed=35)
+    H, r = inp.H, inp.r
+    dims = mla.make_dims(B, H, inp.d_head, inp.d_v, r, inp.d_rope, mla.MLA_BF16, inp.softmax_scale, inp.rope_base)
+    w_uq, w_uk, w_o, w_uv, c_q = (_dev(fin.w_uq), _dev(inp.w_uk), _dev(fin.w_o), _dev(inp.w_uv), _dev(fin.c_q))
+    w_qk = torch.empty((H, r, dcq), dtype=torch.int16, device="cuda")
+    w_ov = torch.empty((dm, H * r), dtype=torch.int16, device="cuda")
+    mla.mla_fold_query(dims, dcq, w_uq, w_uk, w_qk)
+    mla.mla_fold_output(dims, dm, w_o, w_uv, w_ov)
+    q_lat = torch.zeros((B, H, r + inp.d_rope), dtype=torch.int16, device="cuda")
+    o_lat = torch.as_tensor(np.random.default_rng(36).standard_normal((B, H, r)), dtype=torch.float32).cuda()
+    ws = torch.empty(mla.mla_out_folded_workspace_size(dims, dm) // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty((B, dm), dtype=torch.float32, device="cuda")
+
+    def products():
+        mla.mla_absorb_q_folded(dims, dcq, c_q, w_qk, q_lat)
+        mla.mla_out_folded(dims, dm, o_lat, w_ov, ws, y)
+
+    products()
+    torch.cuda.synchronize()
+    eager_q, eager_y = q_lat.clone(), y.clone()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        products()
+    torch.cuda.current_stream().wait_stream(side)
+    with torch.cuda.graph(graph):
+        products()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        y.fill_(float("nan"))
+        ws.fill_(float("nan"))
+        q_lat.fill_(-1)
+        junk = torch.randn(1 << 20, device="cuda").sum()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        assert torch.equal(y, eager_y), f"replay {rep}: y differs from the eager run"
+        assert torch.equal(q_lat[:, :, :r], eager_q[:, :, :r]), f"replay {rep}: q~ differs from the eager run"

@@ -402,6 +402,34 @@ def test_paged_step_matches_packed_and_oracle(name, override, page_rows, splits)
     check_step(inp, ds, oracle_step(inp), tag=f"{name} {override} paged {page_rows}")
 
 
+def test_paged_graph_replay_matches_eager():
+    """The step over a paged cache recorded as a HIP graph (the block-table
+    lookups in the prologue and the appended row's page included): every
+    replay, with eager work on the outputs and synchronisation between
+    replays, reproduces the eager bits."""
+    from head_latent_attention_12_amd.step import DeviceStep
+    inp = syn.make_inputs("dsv2", B=3, T=2100)
+    ds = DeviceStep(inp, page_rows=32, page_seed=11)
+    ds.run()
+    torch.cuda.synchronize()
+    eager = {k: getattr(ds, k).clone() for k in ("out", "lse", "q_lat", "lse_part")}
+    cache = ds.cache_raw()
+    graph = ds.capture()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for k in ("out", "lse", "lse_part"):
+            getattr(ds, k).fill_(float("nan"))
+        junk = torch.randn(1 << 20, device=ds.out.device).sum()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        for k, v in eager.items():
+            assert torch.equal(getattr(ds, k), v), f"replay {rep}: {k} differs from the eager run"
+        np.testing.assert_array_equal(ds.cache_raw(), cache)
+    check_step(inp, ds, oracle_step(inp), tag="dsv2 paged graph")
+
+
 # ---------------------------------------------------------------------------
 # latent KV production from the hidden state
 # ---------------------------------------------------------------------------

@@ -24,3 +24,34 @@ def normwise_rel(got, ref):
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     return float(np.max(np.abs(got - ref)) / np.max(np.abs(ref)))
+
+
+# The parity gate of the GPU tests (fp32: normwise relative error; bf16: the
+# absolute max/mean bounds, plus bounds relative to the output's scale: the
+# rounding of q~ and of the softmax weights to bf16 gives weight errors of a
+# few 2^-9, i.e. output errors of a few 0.1% of max|out| at worst and far
+# less on average).
+F32_GATE = 1e-4
+BF16_MAX, BF16_MEAN = 2e-2, 5e-3
+BF16_TIGHT_MAX_REL, BF16_TIGHT_MEAN_REL = 1e-2, 1e-3
+
+
+def gate_failures(dtype, got, ref):
+    """The bounds of the parity gate that ``got`` breaks against ``ref`` (an
+    empty list: it passes).  ``dtype`` is the storage dtype, "f32" or "bf16"."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    err = np.abs(got - ref)
+    if dtype == "f32":
+        return ["f32 normwise"] if normwise_rel(got, ref) > F32_GATE else []
+    fails = []
+    if err.max() > BF16_MAX:
+        fails.append("bf16 max abs")
+    if err.mean() > BF16_MEAN:
+        fails.append("bf16 mean abs")
+    scale = np.abs(ref).max()
+    if err.max() > BF16_TIGHT_MAX_REL * scale:
+        fails.append("bf16 max rel to scale")
+    if err.mean() > BF16_TIGHT_MEAN_REL * scale:
+        fails.append("bf16 mean rel to scale")
+    return fails

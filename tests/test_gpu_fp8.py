@@ -212,3 +212,53 @@ def test_fp8_inconsistent_metadata_stays_in_bounds():
     clean = _step(inp)
     ref, quant = fp8_oracle(inp, clean.fp8)
     check_fp8_step(inp, clean, ref, quant, "fp8 after bad metadata")
+
+
+def test_fp8_cache_rows_past_4gib():
+    """The fp8 cache with the second sequence's rows 5 GiB in (byte offsets
+    past 2^32), the rows between NaN codes and NaN scales: both sequences
+    match the oracle, the appended rows land in their slots, nothing else
+    changes."""
+    import dataclasses
+    from head_latent_attention_12_amd.step import DeviceStep
+    inp = syn.make_inputs("dsv2", lens=[300, 700])
+    ds = DeviceStep(inp, fp8=True, fp8_seed=3)
+    ref, quant = fp8_oracle(inp, ds.fp8)
+    r = inp.r
+    o1, n1 = int(inp.row_offsets[1]), int(inp.seq_lens[1])
+    row_b = ds.kv_cache.shape[1]
+    gap = -(-5 * (1 << 30) // row_b)
+    small, small_s = ds.kv_cache, ds.kv_scale
+    big = torch.full((gap + n1, row_b), 0x7F, dtype=small.dtype, device=small.device)
+    big_s = torch.full((gap + n1,), float("nan"), dtype=torch.float32, device=small.device)
+    big[:o1], big[gap:] = small[:o1], small[o1:]
+    big_s[:o1], big_s[gap:] = small_s[:o1], small_s[o1:]
+    ds.kv_cache, ds.kv_scale = big, big_s
+    ds.row_offsets.copy_(torch.tensor([0, gap], dtype=torch.int64))
+    ds.inp = dataclasses.replace(inp, row_offsets=np.array([0, gap], np.int64), total_rows=gap + n1)
+    slots = [int(inp.lens[0]), gap + int(inp.lens[1])]
+    assert slots[1] * row_b >= 4 * (1 << 30)
+    ds.run()
+    torch.cuda.synchronize()
+    tag = "fp8 cache past 4 GiB"
+    q_lat = ds.q_lat_f64()
+    qt_ref = ref["q_lat"][:, :, :r]
+    assert np.all(np.abs(q_lat[:, :, :r] - qt_ref) <= 2.0 ** -8 * np.abs(qt_ref) + 1e-6 * np.abs(qt_ref).max())
+    np.testing.assert_allclose(ds.lse.cpu().numpy().astype(np.float64), ref["lse"], rtol=0, atol=2e-2)
+    check_out(inp, ds.out.cpu().numpy().astype(np.float64), ref["out"], tag)
+    # the appended rows: codes, scale and rotated key bytes
+    rope_bits = syn.bf16_bits_from_f64(ref["new_row"][:, r:])
+    for b in range(2):
+        row = big[slots[b]].cpu().numpy()
+        np.testing.assert_array_equal(row[:r], quant[b][0], err_msg=tag)
+        np.testing.assert_array_equal(row[r:].view(np.uint16), rope_bits[b], err_msg=tag)
+        assert float(big_s[slots[b]]) == quant[b][1], tag
+    # the other rows: the live regions as before, the rows between still NaN
+    for first, end, src in ((0, o1, 0), (gap, gap + n1, o1)):
+        keep = torch.ones(end - first, dtype=torch.bool, device=big.device)
+        for b in range(2):
+            if first <= slots[b] < end:
+                keep[slots[b] - first] = False
+        assert torch.equal(big[first:end][keep], small[src:src + end - first][keep]), tag
+        assert torch.equal(big_s[first:end][keep].view(torch.int32), small_s[src:src + end - first][keep].view(torch.int32)), tag
+    assert bool((big[o1:gap] == 0x7F).all()) and bool(torch.isnan(big_s[o1:gap]).all()), tag

@@ -455,6 +455,80 @@ def test_kv_down_matches_oracle(B, d_model):
         assert np.all(err <= bound), tag
 
 
+GIB = 1 << 30
+BF16_NAN = 0x7FC0  # a quiet NaN in bf16 bits
+
+
+@pytest.mark.parametrize("paged", [False, True], ids=["packed", "paged"])
+def test_cache_rows_past_4gib(paged):
+    """Cache rows whose byte offsets pass 2^32: the second sequence's rows
+    (packed) or every page (paged, 64-row pages) start 5 GiB into a cache
+    whose other rows are NaN.  Both sequences match the oracle, the appended
+    rows land in their slots, and no other row changes."""
+    import dataclasses
+    import types
+    from head_latent_attention_12_amd.step import DeviceStep
+    inp = syn.make_inputs("dsv2", lens=[300, 700])
+    ref = oracle_step(inp)
+    row_b = inp.W * 2
+    lens = [int(x) for x in inp.lens]
+    if not paged:
+        ds = DeviceStep(inp)
+        o1, n1 = int(inp.row_offsets[1]), int(inp.seq_lens[1])
+        gap = -(-5 * GIB // row_b)  # first row of sequence 1
+        small = ds.kv_cache
+        big = torch.full((gap + n1, inp.W), BF16_NAN, dtype=torch.int16, device=small.device)
+        big[:o1] = small[:o1]
+        big[gap:] = small[o1:]
+        ds.kv_cache = big
+        ds.row_offsets.copy_(torch.tensor([0, gap], dtype=torch.int64))
+        ds.inp = dataclasses.replace(inp, row_offsets=np.array([0, gap], np.int64), total_rows=gap + n1)
+        slots = [lens[0], gap + lens[1]]
+        live = [(0, o1, 0), (gap, gap + n1, o1)]  # (first, end, first row in the small cache)
+    else:
+        ds = DeviceStep(inp, page_rows=64, page_seed=5)
+        pc = ds.paged
+        p0 = -(-5 * GIB // (64 * row_b))  # every page moves up by p0 pages
+        small = ds.kv_cache
+        big = torch.full((p0 * 64 + small.shape[0], inp.W), BF16_NAN, dtype=torch.int16, device=small.device)
+        big[p0 * 64:] = small
+        ds.kv_cache = big
+        ds.block_table += p0
+        # the block table's view for the paged calls: the page count of the big cache
+        ds.paged = types.SimpleNamespace(page_rows=64, bt_stride=pc.bt_stride, total_pages=p0 + pc.total_pages)
+        slots = [(int(pc.block_table[b, lens[b] // 64]) + p0) * 64 + lens[b] % 64 for b in range(2)]
+        live = [(p0 * 64, big.shape[0], 0)]
+    assert min(slots[1:]) * row_b >= 4 * GIB
+    ds.run()
+    torch.cuda.synchronize()
+    tag = "cache past 4 GiB, " + ("paged" if paged else "packed")
+    # q_lat, out and lse against the oracle
+    q_lat = ds.q_lat_f64()
+    qt_ref = ref["q_lat"][:, :, :inp.r]
+    assert np.all(np.abs(q_lat[:, :, :inp.r] - qt_ref) <= 2.0 ** -8 * np.abs(qt_ref) + 1e-6 * np.abs(qt_ref).max())
+    np.testing.assert_array_equal(q_lat[:, :, inp.r:],
+                                  syn.bf16_bits_to_f64(syn.bf16_bits_from_f64(ref["q_lat"][:, :, inp.r:])))
+    np.testing.assert_allclose(ds.lse.cpu().numpy().astype(np.float64), ref["lse"], rtol=0, atol=2e-2)
+    check_out(inp, ds.out.cpu().numpy().astype(np.float64), ref["out"], tag)
+    # the appended rows in their slots
+    new_bits = torch.from_numpy(syn.bf16_bits_from_f64(ref["new_row"]).view(np.int16)).to(big.device)
+    for b in range(2):
+        assert torch.equal(big[slots[b]], new_bits[b]), (tag, b)
+    # every other row as before: the live regions equal the original cache
+    # except the slots, and the rows between them are still NaN
+    gaps, prev = [], 0
+    for first, end, src in live:
+        expect = small[src:src + (end - first)].clone()
+        for b in range(2):
+            if first <= slots[b] < end:
+                expect[slots[b] - first] = new_bits[b]
+        assert torch.equal(big[first:end], expect), tag
+        gaps.append((prev, first))
+        prev = end
+    for first, end in gaps:
+        assert bool((big[first:end] == BF16_NAN).all()), (tag, first, end)
+
+
 def test_inconsistent_metadata_stays_in_bounds():
     """Device metadata the host cannot check (row offsets, page ids, lengths
     past the cache or the block table) is clamped inside the kernels: the

@@ -1014,12 +1014,18 @@ __device__ __forceinline__ uint32_t e4m3_code(float y) {
   return sign | code;
 }
 
+// A bf16 pair (x0, x1) turned by the angle whose sine and cosine are (sn, cn),
+// rounded once
+__device__ __forceinline__ uint32_t rope_rotate_bf16(uint32_t x, double sn, double cn) {
+  const double x0 = (double)bf2f((u16)(x & 0xffffu)), x1 = (double)bf2f((u16)(x >> 16));
+  return (uint32_t)d2bf(x0 * cn - x1 * sn) | ((uint32_t)d2bf(x0 * sn + x1 * cn) << 16);
+}
+
 // RoPE of pair i of a bf16 pair (x0, x1) at position pos, rounded once
 __device__ __forceinline__ uint32_t rope_pair_bf16(uint32_t x, int pos, double theta) {
   double sn, cn;
   sincos_reduced((double)pos * theta, &sn, &cn);
-  const double x0 = (double)bf2f((u16)(x & 0xffffu)), x1 = (double)bf2f((u16)(x >> 16));
-  return (uint32_t)d2bf(x0 * cn - x1 * sn) | ((uint32_t)d2bf(x0 * sn + x1 * cn) << 16);
+  return rope_rotate_bf16(x, sn, cn);
 }
 
 // bf16: the weight tile and the queries of 64 sequences at a time are copied
@@ -1061,52 +1067,54 @@ __device__ __forceinline__ void absorb_bf16_block(int bid, const u16* __restrict
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hf = lane >> 5, l32 = lane & 31;
 
-  // RoPE (fused launch, waves 2 and 3 of the work-group): block (h, blk)
-  // rotates head h's query pairs of the sequences b = blk (mod nblk), and
-  // block h*nblk + blk appends the cache row of sequence h*nblk + blk (mod
-  // H*nblk).  These waves touch no LDS and wait only for their own loads, so
-  // the rotations run while waves 0 and 1 wait for their copies; they then
-  // join the absorption waves' barriers (one, plus two per further block of
-  // 64 sequences) and leave.
+  // RoPE (fused launch, waves 2 and 3 of the work-group).  The query
+  // rotations come in units of (sequence, 8 heads): work-group g = h*nblk +
+  // blk takes units g, g + H*nblk, ...; in wave 2, lane l turns pair l % 32
+  // of heads 8*group + l/32 + 2k (k = 0..3), so that the angle's sine and
+  // cosine (fp64, the costly part) are formed once per four rotations.
+  // Wave 3 appends the cache row of sequence h*nblk + blk (mod H*nblk).
+  // These waves touch no LDS and wait only for their own loads, so their work
+  // runs while waves 0 and 1 wait for their copies; they then join the
+  // absorption waves' barriers (one, plus two per further block of 64
+  // sequences) and leave.
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
   if constexpr (ROPE) {
     if (threadIdx.x >= 128) {
       constexpr int half = DR / 2;
+      static_assert(half == 32, "a lane's pair is its lane index mod 32");
       const int tid = (int)threadIdx.x - 128;
-      const int nq = blk < B ? (B - blk + nblk - 1) / nblk * half : 0;  // this block's query pairs
       const int W2 = R + DR;
-      // pairs in batches of two per thread, both batches' loads issued before
-      // either is rotated (one round trip for up to 64 sequences)
-      constexpr int UQ = 2;
-      for (int p0 = tid; p0 < nq; p0 += 128 * UQ) {
-        uint32_t x[UQ];
-        int pos[UQ];
+      if (tid < 64) {
+        const int hgs = (H + 7) / 8;  // head groups of 8
+        const int units = B * hgs;
+        const int i = tid & 31;
+        for (int u = h * nblk + blk; u < units; u += H * nblk) {
+          const int bb = u / hgs, h0 = 8 * (u - bb * hgs) + (tid >> 5);
+          // the four pairs' loads, then the angle, then the rotations
+          uint32_t x[4];
 #pragma unroll
-        for (int u = 0; u < UQ; ++u) {
-          const int pidx = min(p0 + 128 * u, nq - 1);
-          const int bb = blk + nblk * (pidx / half), i = pidx % half;
-          x[u] = *(const uint32_t*)(ra.q_rope + ((int64_t)bb * H + h) * DR + 2 * i);
-          pos[u] = ra.positions[bb];
-        }
+          for (int k = 0; k < 4; ++k)
+            x[k] = *(const uint32_t*)(ra.q_rope + ((int64_t)bb * H + min(h0 + 2 * k, H - 1)) * DR + 2 * i);
+          double sn, cn;
+          sincos_reduced((double)ra.positions[bb] * freqs.theta[i], &sn, &cn);
 #pragma unroll
-        for (int u = 0; u < UQ; ++u) {
-          const int pidx = p0 + 128 * u;
-          if (pidx >= nq) break;
-          const int bb = blk + nblk * (pidx / half), i = pidx % half;
-          *(uint32_t*)(q_lat + ((int64_t)bb * H + h) * W2 + R + 2 * i) = rope_pair_bf16(x[u], pos[u], freqs.theta[i]);
+          for (int k = 0; k < 4; ++k)
+            if (h0 + 2 * k < H)
+              *(uint32_t*)(q_lat + ((int64_t)bb * H + h0 + 2 * k) * W2 + R + 2 * i) = rope_rotate_bf16(x[k], sn, cn);
         }
       }
-      // the appended rows, by wave 2 (eight latent values per lane): [c_kv_new |
+      // the appended rows, by wave 3 (eight latent values per lane): [c_kv_new |
       // RoPE(k_rope_new)] with c_kv_new bit for bit, or the fp8 row: codes of
       // c_kv_new / 2^e with e from the row's max |c_kv_new| (a wave-wide
       // maximum), then the rotated key and the scale
       static_assert(R == 8 * 64, "one wave holds the appended latent, eight values per lane");
-      if (tid < 64) {
+      if (tid >= 64) {
+        const int al = tid - 64;  // lane of wave 3
         typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
         const bool fp8 = ra.cache8 != nullptr;
         for (int bb = h * nblk + blk; bb < B; bb += H * nblk) {
-          const int ti = min(tid, half - 1);
-          const u32x4 cv = *(const u32x4*)(ra.c_kv_new + (int64_t)bb * R + 8 * tid);
+          const int ti = min(al, half - 1);
+          const u32x4 cv = *(const u32x4*)(ra.c_kv_new + (int64_t)bb * R + 8 * al);
           const uint32_t k = *(const uint32_t*)(ra.k_rope_new + (int64_t)bb * DR + 2 * ti);
           const int pos = ra.positions[bb];
           const int64_t off = PAGED ? 0 : ra.cm.row_offsets[bb];
@@ -1114,8 +1122,8 @@ __device__ __forceinline__ void absorb_bf16_block(int bid, const u16* __restrict
           const uint32_t kr = rope_pair_bf16(k, pos, freqs.theta[ti]);
           if (!fp8) {
             u16* crow = ra.cache + row * W2;
-            *(u32x4*)(crow + 8 * tid) = cv;
-            if (tid < half) *(uint32_t*)(crow + R + 2 * tid) = kr;
+            *(u32x4*)(crow + 8 * al) = cv;
+            if (al < half) *(uint32_t*)(crow + R + 2 * al) = kr;
           } else {
             uint8_t* crow = ra.cache8 + row * (R + 2 * DR);
             float v[8];
@@ -1134,9 +1142,9 @@ __device__ __forceinline__ void absorb_bf16_block(int bid, const u16* __restrict
             for (int w = 0; w < 2; ++w)
               c[w] = e4m3_code(v[4 * w] * inv) | (e4m3_code(v[4 * w + 1] * inv) << 8) |
                      (e4m3_code(v[4 * w + 2] * inv) << 16) | (e4m3_code(v[4 * w + 3] * inv) << 24);
-            *(u32x2*)(crow + 8 * tid) = u32x2{c[0], c[1]};
-            if (tid < half) *(uint32_t*)(crow + R + 4 * tid) = kr;
-            if (tid == 0) ra.scale8[row] = ldexpf(1.f, ex);
+            *(u32x2*)(crow + 8 * al) = u32x2{c[0], c[1]};
+            if (al < half) *(uint32_t*)(crow + R + 4 * al) = kr;
+            if (al == 0) ra.scale8[row] = ldexpf(1.f, ex);
           }
         }
       }

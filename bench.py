@@ -628,7 +628,7 @@ def main():
         print(json.dumps(ingest_counters(args.workload, *args.ingest_counters, args.counters_command), indent=1))
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
+        print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for --gpus {args.gpus}). "
               "Sequences are independent, so batch data-parallel scaling across GPUs needs no exchange.",
               file=sys.stderr)
         sys.exit(2)
